@@ -1,0 +1,141 @@
+/*
+ * wc.h — C ABI of the WildCat hot path on AMD Instinct MI355X (gfx950).
+ *
+ * WildCat approximates softmax attention by attending only over a small weighted coreset of
+ * the keys (page "WildCat: Near-Linear Attention in Theory and Practice",
+ * gptget.net/papers/2602.10056, Abstract).  Per head the path is
+ *
+ *   1. coreset selection by randomly pivoted Cholesky (RPCholesky) on the kernel matrix
+ *      H = exp(beta K K^T), beta = 1/sqrt(d), each pivot drawn from the residual diagonal
+ *      (gist.science/de/paper/2602.10056, "Methodik", part 1);
+ *   2. Nystroem weights W = H_SS^{-1} H_{S,:} [V, 1]  (r x (dv+1)); the first dv columns are
+ *      the pages' compressed values V_S = W_pages V, the last is W_pages 1, the softmax
+ *      normaliser (same page, "Methodik", part 2);
+ *   3. attention of every query over the weighted coreset:
+ *      Y = exp(beta Q K_S^T) W,  O = Y[:, :dv] / Y[:, dv].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - `wc_problem` is a host pointer.  Every other pointer is a DEVICE pointer (memory of the
+ *    current HIP device) and must be 16-byte aligned.  The caller owns all memory; the
+ *    library never allocates, frees or retains device memory, and keeps no mutable global
+ *    state, so calls are re-entrant.  Inputs are never modified; outputs must not alias
+ *    inputs or the workspace.
+ *  - Layouts are dense row-major: Q [heads][m][d], K [heads][n][d], V [heads][n][dv],
+ *    O [heads][m][dv] in the problem's dtype; F [heads][r][n] float (column t of the n x r
+ *    factor is contiguous); W [heads][r][dv+1] float; pivots [heads][r] int32;
+ *    u_forced [heads][r] float; diag [heads][n] float; trace [heads][r+1] double;
+ *    rank [heads] int32; flags [heads] uint32.
+ *  - `heads` counts every (batch, head) pair.  Supported: d, dv in {64, 128};
+ *    dtype WC_F32 or WC_BF16; 1 <= r <= min(n, 4096); n, m >= 1 (m may be 0 for
+ *    wc_attend/wc_forward: nothing is written then); heads == 0 is a no-op.
+ *  - Every call validates its arguments on the host BEFORE any HIP call; on failure it
+ *    returns a non-zero status and enqueues nothing.  On success the work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and the call returns without
+ *    waiting.  A failed launch returns WC_ERR_DEVICE.  No call throws.
+ *  - Numeric conditions found on the device are reported per head, readable after the
+ *    stream is synchronised: rank[h] = number of pivots actually taken, and flags[h]:
+ *       WC_FLAG_BREAKDOWN  rank < r: the residual trace or a pivot's residual reached <= 0
+ *       WC_FLAG_NONFINITE  a non-finite value reached the pivot loop
+ *       WC_FLAG_DENOM      some query row had a normaliser Y[:, dv] <= 0
+ *    After a breakdown pivots[rank..r-1] = -1, F columns rank..r-1 = 0, and weights and
+ *    attention use the first rank pivots only.
+ *  - Workspace: `ws` must hold at least wc_workspace_bytes() bytes for the same problem.
+ */
+#ifndef WC_H_
+#define WC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WC_ABI_VERSION 1
+
+typedef enum {
+  WC_OK = 0,
+  WC_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, r > n, ... */
+  WC_ERR_UNSUPPORTED = 2, /* d, dv or dtype outside the supported set, r > 4096 */
+  WC_ERR_WORKSPACE = 3,   /* ws NULL or smaller than wc_workspace_bytes() */
+  WC_ERR_DEVICE = 4       /* a HIP call or kernel launch failed */
+} wc_status;
+
+typedef enum { WC_F32 = 0, WC_BF16 = 1 } wc_dtype;
+
+enum { WC_FLAG_BREAKDOWN = 1u, WC_FLAG_NONFINITE = 2u, WC_FLAG_DENOM = 4u };
+
+typedef struct {
+  int32_t heads; /* batch * heads, each an independent problem */
+  int32_t n;     /* keys (and values) per head */
+  int32_t m;     /* queries per head */
+  int32_t d;     /* key/query width: 64 or 128 */
+  int32_t dv;    /* value width: 64 or 128 */
+  int32_t r;     /* coreset size (pivot steps) */
+  int32_t dtype; /* wc_dtype of Q, K, V and O */
+} wc_problem;
+
+/* ABI version of the loaded library (WC_ABI_VERSION it was built with). */
+int32_t wc_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* wc_status_string(wc_status s);
+
+/* Workspace bytes needed by wc_rpcholesky, wc_weights, wc_attend and wc_forward for this
+ * problem (one size serves all four).  *bytes is set on WC_OK only. */
+wc_status wc_workspace_bytes(const wc_problem* p, size_t* bytes);
+
+/* Randomly pivoted partial Cholesky of H = exp(beta K K^T) with r pivots per head
+ * (gist.science/de/paper/2602.10056, "Methodik" part 1: partial Cholesky of the kernel
+ * matrix, pivot sampled from the residual diagonal).
+ *
+ * Step t: p = max(diag, 0); T = sum p (fp64); s = min{i : C_i > u_t T} for the running sum C
+ * of p; g = H[:, s] - F[:, :t] F[s, :t]^T; F[:, t] = g / sqrt(g[s]); diag -= F[:, t]^2;
+ * diag[s] = 0.
+ *   K        in   [heads][n][d], dtype
+ *   u_forced in   [heads][r] float in [0,1), or NULL: then u_t comes from Philox4x64-10
+ *                 with counter (t, head, 0, 0) and key (seed, 0), u = (x0 >> 40) * 2^-24
+ *   pivots   out  [heads][r]
+ *   F        out  [heads][r][n]
+ *   diag     out  [heads][n] final residual diagonal, or NULL
+ *   trace    out  [heads][r+1]: trace[t] = T before step t, trace[r] after the last, or NULL
+ *   rank, flags out [heads]                                                              */
+wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_forced,
+                        uint64_t seed, int32_t* pivots, float* F, float* diag, double* trace,
+                        int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Nystroem weights W = H_SS^{-1} H_{S,:} [V, 1] for the first rank[h] pivots
+ * (gist.science/de/paper/2602.10056, "Methodik" part 2: W = h(K_S,K_S)^+ h(K_S,K), V_S = W V).
+ * Computed through the factor of wc_rpcholesky: with L = F[S, :] (lower triangular,
+ * L L^T = H_SS) and H_{:,S} = F L^T, W = L^{-T} F^T [V, 1].
+ *   K, V          in  [heads][n][d], [heads][n][dv], dtype
+ *   pivots, rank  in  as returned by wc_rpcholesky
+ *   F             in  [heads][r][n], the factor returned by wc_rpcholesky for these pivots
+ *   W             out [heads][r][dv+1]; rows rank..r-1 are zero                            */
+wc_status wc_weights(const wc_problem* p, const void* K, const void* V, const int32_t* pivots,
+                     const int32_t* rank, const float* F, float* W, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Attention of every query over the weighted coreset (page gptget.net/papers/2602.10056,
+ * Abstract: attend only over a small weighted coreset): Y = exp(beta Q K_S^T) W,
+ * O = Y[:, :dv] / Y[:, dv], with K_S the keys at the first rank[h] pivots.
+ *   Q           in  [heads][m][d], dtype
+ *   K, pivots, rank, W   in  as above
+ *   O           out [heads][m][dv], dtype
+ *   flags       in/out [heads]: WC_FLAG_DENOM is OR-ed in                                   */
+wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int32_t* pivots,
+                    const int32_t* rank, const float* W, void* O, uint32_t* flags, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* The whole forward: wc_rpcholesky, wc_weights and wc_attend in one call (the factor and the
+ * weights live in the workspace).  pivots may be NULL; rank and flags are required.        */
+wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
+                     const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
+                     int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WC_H_ */

@@ -1,0 +1,238 @@
+"""fp64 CPU oracle of the WildCat hot path (per head).  Test infrastructure only.
+
+Sources (the pages, cited by title and section):
+  * "WildCat: Near-Linear Attention in Theory and Practice", gist.science/de/paper/2602.10056,
+    section "Methodik": part 1 (coreset selection by randomly pivoted Cholesky on the kernel
+    matrix H = exp(beta K K^T), pivot drawn from the diagonal of the residual kernel matrix),
+    part 2 (Nystroem weights W = h(K_S, K_S)^+ h(K_S, K), value compression V_S = W V).
+    The French mirror gist.science/fr/paper/2602.10056, "Methodologie", states the same.
+  * The abstract (gptget.net/papers/2602.10056, "Abstract"): attend only over a small weighted
+    coreset chosen by randomly pivoted Cholesky and weighted optimally.
+
+Where the pages leave a step open, the reading is:
+  * beta = 1/sqrt(d) (softmax kernel exp(<x, y>/sqrt(d))).
+  * One bin: r sequential pivot steps over all n keys of a head.
+  * Step t: p = max(diag, 0); C = running sum of p (sequential, fp64); T = C[n-1];
+    s = min{i : C_i > u_t T}; g = H[:, s] - F[:, :t] F[s, :t]^T; F[:, t] = g / sqrt(g[s]);
+    diag -= F[:, t]^2; diag[s] = 0.  Breakdown (T <= 0, g[s] <= 0 or either not finite)
+    stops the loop with rank = t.
+  * Weights in the r x (dv+1) form W = H_SS^{-1} H_{S,:} [V, 1]: the pages' V_S with the
+    all-ones column appended, which carries the softmax normaliser.  H_SS is solved by
+    Cholesky (it is positive definite for distinct keys, so the pseudo-inverse the pages
+    write coincides with the inverse).
+  * Output O = Y[:, :dv] / Y[:, dv] with Y = exp(beta Q K_S^T) W; no shift is applied.
+
+Every function here is plain numpy/scipy in float64.  Inputs given in fp32 or bf16 are
+upcast exactly.  Nothing in this package is shared with, or imported by, the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.linalg import cho_factor, cho_solve
+
+FLAG_BREAKDOWN = 1  # rank < r: the residual vanished (T <= 0) or a pivot's g[s] <= 0
+FLAG_NONFINITE = 2  # a non-finite value reached the pivot loop
+FLAG_DENOM = 4      # some query row had a Nystroem denominator Y[:, dv] <= 0
+
+
+def beta_of(d: int) -> float:
+    """beta = 1/sqrt(d): the softmax kernel exp(<x, y>/sqrt(d))."""
+    return 1.0 / np.sqrt(d)
+
+
+def kernel(X, Y, beta):
+    """Softmax kernel block h(X, Y) = exp(beta X Y^T) ("Methodik" part 1, matrix H)."""
+    return np.exp(beta * (np.asarray(X, np.float64) @ np.asarray(Y, np.float64).T))
+
+
+def initial_residual(K, beta):
+    """diag(H) = exp(beta |k_i|^2): the residual diagonal before the first pivot."""
+    K = np.asarray(K, np.float64)
+    return np.exp(beta * np.einsum("ij,ij->i", K, K))
+
+
+def sample_pivot(diag, u):
+    """Inverse-CDF draw from the residual diagonal ("Methodik" part 1, pivoting rule).
+
+    Returns (s, T, C): s = min{i : C_i > u T} over the running sum C of max(diag, 0),
+    or s = -1 when the total T is not positive and finite.  If rounding puts u T at or
+    beyond C[n-1], the last index with positive mass is taken.
+    """
+    p = np.maximum(np.asarray(diag, np.float64), 0.0)
+    C = np.cumsum(p)
+    T = C[-1] if len(C) else 0.0
+    if not (np.isfinite(T) and T > 0.0):
+        return -1, T, C
+    s = int(np.searchsorted(C, float(u) * T, side="right"))
+    if s >= len(C):
+        s = int(np.nonzero(p > 0.0)[0][-1])
+    return s, T, C
+
+
+def rpcholesky(K, r, uniforms, beta=None):
+    """Randomly pivoted partial Cholesky of H = exp(beta K K^T) with r pivots.
+
+    ``uniforms``: r values u_t in [0, 1) (forced, or the Philox draws of oracle.philox).
+    Returns dict with pivots [r] (-1 after rank), F [n, r] (zero after rank),
+    diag [n] (final residual diagonal), trace [r + 1] (T_t = sum max(diag, 0) before
+    step t, T_r after the last step; zero after rank), rank, flags.
+    """
+    K = np.asarray(K, np.float64)
+    n, d = K.shape
+    beta = beta_of(d) if beta is None else beta
+    if not 1 <= r <= n:
+        raise ValueError("need 1 <= r <= n")
+    diag = initial_residual(K, beta)
+    F = np.zeros((n, r))
+    pivots = -np.ones(r, np.int64)
+    trace = np.zeros(r + 1)
+    rank, flags = r, 0
+    if not np.all(np.isfinite(K)):
+        flags |= FLAG_NONFINITE
+    for t in range(r):
+        s, T, _ = sample_pivot(diag, uniforms[t])
+        trace[t] = T if np.isfinite(T) else 0.0
+        if s < 0:
+            rank, flags = t, flags | FLAG_BREAKDOWN | (0 if np.isfinite(T) else FLAG_NONFINITE)
+            break
+        h = np.exp(beta * (K @ K[s]))          # column s of H
+        g = h - F[:, :t] @ F[s, :t]            # minus what the first t pivots explain
+        if not (np.isfinite(g[s]) and g[s] > 0.0):
+            rank, flags = t, flags | FLAG_BREAKDOWN | (0 if np.isfinite(g[s]) else FLAG_NONFINITE)
+            break
+        F[:, t] = g / np.sqrt(g[s])
+        diag = diag - F[:, t] ** 2
+        diag[s] = 0.0
+        pivots[t] = s
+    else:
+        trace[r] = np.cumsum(np.maximum(diag, 0.0))[-1]
+    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
+
+
+def snap_uniforms(K, r, raw_uniforms, beta=None):
+    """Forced-uniform mode: move each u_t to the middle of the CDF interval it selects.
+
+    Runs the pivot loop with the raw draws; at step t the selected index s keeps its
+    interval [C_{s-1}, C_s) of the oracle's running sum, and u_t becomes the centre of that
+    interval divided by T, rounded to a multiple of 2^-24 (exact in fp32).  Any other
+    implementation whose running sum is within half the interval of the oracle's then picks
+    the same pivot.  Returns (snapped [r] float32, margin [r]): margin_t is the distance
+    from u_t T to the nearer interval end, over T.  Steps after a breakdown keep u = 0.
+    """
+    K = np.asarray(K, np.float64)
+    n, d = K.shape
+    beta = beta_of(d) if beta is None else beta
+    snapped = np.zeros(r, np.float32)
+    margin = np.zeros(r)
+    diag = initial_residual(K, beta)
+    F = np.zeros((n, r))
+    for t in range(r):
+        s, T, C = sample_pivot(diag, raw_uniforms[t])
+        if s < 0:
+            break
+        lo = C[s - 1] if s > 0 else 0.0
+        u = np.round((lo + 0.5 * (C[s] - lo)) / T * 2.0 ** 24) * 2.0 ** -24
+        u = min(max(u, 0.0), 1.0 - 2.0 ** -24)
+        s2, _, _ = sample_pivot(diag, u)
+        if s2 != s:
+            raise RuntimeError(f"snapping moved pivot at step {t}: {s} -> {s2}")
+        snapped[t] = u
+        margin[t] = min(u * T - lo, C[s] - u * T) / T
+        h = np.exp(beta * (K @ K[s]))
+        g = h - F[:, :t] @ F[s, :t]
+        if not (np.isfinite(g[s]) and g[s] > 0.0):
+            break
+        F[:, t] = g / np.sqrt(g[s])
+        diag = diag - F[:, t] ** 2
+        diag[s] = 0.0
+    return snapped, margin
+
+
+def weights(K, V, pivots, beta=None):
+    """Nystroem weights W = H_SS^{-1} H_{S,:} [V, 1]  (r x (dv+1)).
+
+    "Methodik" part 2: W_pages = h(K_S, K_S)^+ h(K_S, K) and V_S = W_pages V; the returned
+    matrix is [V_S, W_pages 1].  ``pivots`` holds the rank valid pivots.
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    beta = beta_of(K.shape[1]) if beta is None else beta
+    S = np.asarray(pivots, np.int64)
+    KS = K[S]
+    H_SS = kernel(KS, KS, beta)
+    V1 = np.hstack([V, np.ones((V.shape[0], 1))])
+    B = kernel(KS, K, beta) @ V1
+    return cho_solve(cho_factor(H_SS, lower=True), B)
+
+
+def attend(Q, K, pivots, W, beta=None):
+    """Attention of every query over the weighted coreset.
+
+    Y = exp(beta Q K_S^T) W and O = Y[:, :dv] / Y[:, dv].  Returns (O, denom, kappa) where
+    denom = Y[:, dv] and kappa = sum |P| |W[:, dv]| / |Y[:, dv]| is the row's condition
+    number for the normaliser (large kappa: the output row is ill-conditioned).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    beta = beta_of(K.shape[1]) if beta is None else beta
+    S = np.asarray(pivots, np.int64)
+    dv = W.shape[1] - 1
+    P = kernel(Q, K[S], beta)
+    Y = P @ W
+    denom = Y[:, dv]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        O = Y[:, :dv] / denom[:, None]
+        kappa = (np.abs(P) @ np.abs(W[:, dv])) / np.abs(denom)
+    return O, denom, kappa
+
+
+def forward(Q, K, V, r, uniforms, beta=None):
+    """One head of the WildCat forward: pivots -> weights -> attend."""
+    K = np.asarray(K, np.float64)
+    beta = beta_of(K.shape[1]) if beta is None else beta
+    rpc = rpcholesky(K, r, uniforms, beta)
+    S = rpc["pivots"][: rpc["rank"]]
+    W = weights(K, V, S, beta)
+    O, denom, kappa = attend(Q, K, S, W, beta)
+    flags = rpc["flags"] | (FLAG_DENOM if np.any(~(denom > 0.0)) else 0)
+    return dict(O=O, W=W, denom=denom, kappa=kappa, pivots=rpc["pivots"], rank=rpc["rank"],
+                flags=flags, F=rpc["F"], diag=rpc["diag"], trace=rpc["trace"])
+
+
+def exact_attention(Q, K, V, beta=None):
+    """Exact softmax attention softmax(beta Q K^T) V, with a row-max shift."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    beta = beta_of(K.shape[1]) if beta is None else beta
+    L = beta * (Q @ K.T)
+    L -= L.max(axis=1, keepdims=True)
+    E = np.exp(L)
+    return (E @ V) / E.sum(axis=1, keepdims=True)
+
+
+def factor_rows_given_pivots(K, pivots, rows, beta=None):
+    """Rows of the partial Cholesky factor F determined by a fixed pivot sequence.
+
+    With L the Cholesky factor of H_SS (pivots in order), F[i, :] = L^{-1} H[S, i]; this is
+    what the pivot loop produces for any row once the pivots are fixed, so rows of a large
+    factor can be checked one by one.  Returns (F_rows [len(rows), r], diag_rows).
+    """
+    from scipy.linalg import solve_triangular
+
+    K = np.asarray(K, np.float64)
+    beta = beta_of(K.shape[1]) if beta is None else beta
+    S = np.asarray(pivots, np.int64)
+    KS = K[S]
+    L = np.linalg.cholesky(kernel(KS, KS, beta))
+    Hr = kernel(KS, K[rows], beta)                  # [r, len(rows)]
+    Fr = solve_triangular(L, Hr, lower=True).T
+    diag_rows = initial_residual(K[rows], beta) - np.einsum("ij,ij->i", Fr, Fr)
+    return Fr, diag_rows
+
+
+def rel_fro(a, b):
+    """Relative Frobenius error |a - b|_F / |b|_F."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
