@@ -1,0 +1,199 @@
+"""Thin Python binding of the WildCat C ABI (include/wc.h), same names as the C entry points.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and contiguity,
+outputs and the workspace are allocated with torch, and raw device pointers plus the
+current HIP stream are handed to libwc.so.  Every step of the computation runs in the HIP
+kernels of that library; if it is not built this module raises on import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwc.so")
+
+WC_OK, WC_ERR_INVALID_ARG, WC_ERR_UNSUPPORTED, WC_ERR_WORKSPACE, WC_ERR_DEVICE = range(5)
+WC_F32, WC_BF16 = 0, 1
+WC_FLAG_BREAKDOWN, WC_FLAG_NONFINITE, WC_FLAG_DENOM = 1, 2, 4
+
+
+class WcProblem(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("n", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dv", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class WcError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"WildCat HIP library not built: {LIB_PATH} is missing "
+                          "(run python -m coreset_head_rpcholesky_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, u64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64
+    P = ctypes.POINTER(WcProblem)
+    sig = {
+        "wc_abi_version": ([], ctypes.c_int32),
+        "wc_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "wc_workspace_bytes": ([P, ctypes.POINTER(sz)], ctypes.c_int),
+        "wc_rpcholesky": ([P, vp, vp, u64, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_weights": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_attend": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_forward": ([P, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+LIB = _load()
+
+
+def wc_abi_version() -> int:
+    return int(LIB.wc_abi_version())
+
+
+def status_string(status: int) -> str:
+    return LIB.wc_status_string(int(status)).decode()
+
+
+wc_status_string = status_string
+
+
+def problem(heads, n, m, d, dv, r, dtype) -> WcProblem:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: WC_F32, torch.bfloat16: WC_BF16}[dtype]
+    return WcProblem(int(heads), int(n), int(m), int(d), int(dv), int(r), int(dtype))
+
+
+def wc_workspace_bytes(p: WcProblem) -> int:
+    out = ctypes.c_size_t(0)
+    st = LIB.wc_workspace_bytes(ctypes.byref(p), ctypes.byref(out))
+    if st != WC_OK:
+        raise WcError("wc_workspace_bytes", st)
+    return int(out.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_in(name, t, dtype, shape, device):
+    if t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def workspace(p: WcProblem, device) -> torch.Tensor:
+    """A workspace tensor large enough for every entry point on problem ``p``."""
+    nbytes = max(wc_workspace_bytes(p), 256)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws(p, device, ws):
+    if ws is None:
+        ws = workspace(p, device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def wc_rpcholesky(K: torch.Tensor, r: int, *, u_forced=None, seed: int = 0, ws=None,
+                  with_diag: bool = True, with_trace: bool = True, stream=None):
+    """Randomly pivoted Cholesky of exp(beta K K^T) per head.  K: [H, n, d] f32 or bf16."""
+    H, n, d = K.shape
+    dev = K.device
+    p = problem(H, n, 0, d, 64, r, K.dtype)
+    if u_forced is not None:
+        _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
+    pivots = torch.empty((H, r), dtype=torch.int32, device=dev)
+    F = torch.empty((H, r, n), dtype=torch.float32, device=dev)
+    diag = torch.empty((H, n), dtype=torch.float32, device=dev) if with_diag else None
+    trace = torch.empty((H, r + 1), dtype=torch.float64, device=dev) if with_trace else None
+    rank = torch.empty((H,), dtype=torch.int32, device=dev)
+    flags = torch.empty((H,), dtype=torch.int32, device=dev)
+    ws, nb = _ws(p, dev, ws)
+    st = LIB.wc_rpcholesky(ctypes.byref(p), _ptr(K), _ptr(u_forced), int(seed) & (2**64 - 1),
+                           _ptr(pivots), _ptr(F), _ptr(diag), _ptr(trace), _ptr(rank), _ptr(flags),
+                           _ptr(ws), nb, _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_rpcholesky", st)
+    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
+
+
+def wc_weights(V: torch.Tensor, pivots, rank, F, *, ws=None, stream=None):
+    """Nystroem weights W [H, r, dv+1] (fp32) from the factor F and pivots of wc_rpcholesky."""
+    H, n, dv = V.shape
+    r = pivots.shape[1]
+    dev = V.device
+    p = problem(H, n, 0, 64, dv, r, V.dtype)
+    _check_in("pivots", pivots, torch.int32, (H, r), dev)
+    _check_in("rank", rank, torch.int32, (H,), dev)
+    _check_in("F", F, torch.float32, (H, r, n), dev)
+    W = torch.empty((H, r, dv + 1), dtype=torch.float32, device=dev)
+    ws, nb = _ws(p, dev, ws)
+    st = LIB.wc_weights(ctypes.byref(p), _ptr(V), _ptr(pivots), _ptr(rank), _ptr(F), _ptr(W),
+                        _ptr(ws), nb, _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_weights", st)
+    return W
+
+
+def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, ws=None,
+              stream=None):
+    """O = row-normalised exp(beta Q K_S^T) W; returns (O [H, m, dv], flags)."""
+    H, m, d = Q.shape
+    n = K.shape[1]
+    r = pivots.shape[1]
+    dv = W.shape[2] - 1
+    dev = Q.device
+    p = problem(H, n, m, d, dv, r, Q.dtype)
+    _check_in("K", K, Q.dtype, (H, n, d), dev)
+    _check_in("W", W, torch.float32, (H, r, dv + 1), dev)
+    if flags is None:
+        flags = torch.zeros((H,), dtype=torch.int32, device=dev)
+    O = torch.empty((H, m, dv), dtype=Q.dtype, device=dev)
+    ws, nb = _ws(p, dev, ws)
+    st = LIB.wc_attend(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(pivots), _ptr(rank), _ptr(W),
+                       _ptr(O), _ptr(flags), _ptr(ws), nb, _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_attend", st)
+    return O, flags
+
+
+def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_forced=None,
+               seed: int = 0, ws=None, out=None, stream=None):
+    """The whole WildCat forward; returns dict(O, pivots, rank, flags)."""
+    H, m, d = Q.shape
+    n = K.shape[1]
+    dv = V.shape[2]
+    dev = Q.device
+    p = problem(H, n, m, d, dv, r, Q.dtype)
+    _check_in("K", K, Q.dtype, (H, n, d), dev)
+    _check_in("V", V, Q.dtype, (H, n, dv), dev)
+    if u_forced is not None:
+        _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
+    if out is None:
+        out = dict(O=torch.empty((H, m, dv), dtype=Q.dtype, device=dev),
+                   pivots=torch.empty((H, r), dtype=torch.int32, device=dev),
+                   rank=torch.empty((H,), dtype=torch.int32, device=dev),
+                   flags=torch.empty((H,), dtype=torch.int32, device=dev))
+    ws, nb = _ws(p, dev, ws)
+    st = LIB.wc_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(u_forced),
+                        int(seed) & (2**64 - 1), _ptr(out["O"]), _ptr(out["pivots"]),
+                        _ptr(out["rank"]), _ptr(out["flags"]), _ptr(ws), nb, _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_forward", st)
+    return out

@@ -1,0 +1,282 @@
+// C ABI of the WildCat hot path: argument validation, workspace carving and dispatch.
+//
+// Every entry point validates on the host before touching HIP; on failure it returns a
+// status and enqueues nothing.  Dispatch: heads of at most 256 bf16 keys with r <= 32 run
+// the resident kernel (one workgroup per head, the whole forward in one launch); all other
+// problems run the streaming pivot loop (one launch per pivot step), the factor-based
+// weights and the matrix-core attention.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/wc.h"
+#include "wc_kernels.h"
+
+namespace {
+
+constexpr int kMaxR = 4096;
+constexpr int kMaxBlocks = 4096;  // row blocks of the streaming pivot loop per head
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+wc_status check_problem(const wc_problem* p) {
+  if (!p) return WC_ERR_INVALID_ARG;
+  if (p->heads < 0 || p->n < 1 || p->m < 0 || p->r < 1) return WC_ERR_INVALID_ARG;
+  if (p->r > p->n) return WC_ERR_INVALID_ARG;
+  if ((p->d != 64 && p->d != 128) || (p->dv != 64 && p->dv != 128)) return WC_ERR_UNSUPPORTED;
+  if (p->dtype != WC_F32 && p->dtype != WC_BF16) return WC_ERR_UNSUPPORTED;
+  if (p->r > kMaxR) return WC_ERR_UNSUPPORTED;
+  if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
+  return WC_OK;
+}
+
+// A required device pointer: non-null and 16-byte aligned.
+bool req(const void* ptr) { return ptr != nullptr && aligned16(ptr); }
+// An optional device pointer: null, or 16-byte aligned.
+bool opt(const void* ptr) { return ptr == nullptr || aligned16(ptr); }
+
+bool resident_ok(const wc_problem& p) {
+  return p.dtype == WC_BF16 && p.n <= wc::kResidentThreads && p.r <= wc::kResidentR;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  int rows, nblk, nchunk, chunk_rows, nsplit, rp;
+  size_t diag0, diag1, part0, part1, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Ypart;
+  size_t total;
+};
+
+Layout make_layout(const wc_problem& p) {
+  Layout L{};
+  const size_t H = (size_t)p.heads, n = (size_t)p.n, r = (size_t)p.r, m = (size_t)p.m;
+  const size_t nc = (size_t)p.dv + 1;
+  // pivot loop: rows per workgroup, enough workgroups to fill the chip
+  L.rows = 1024;
+  if (H * ((n + 1023) / 1024) < 512) L.rows = 512;
+  if (L.rows == 512 && H * ((n + 511) / 512) < 512) L.rows = 256;
+  L.nblk = (int)((n + L.rows - 1) / L.rows);
+  // weights: row chunks so that (r/64 groups) x chunks x heads >= 1024 workgroups
+  const size_t jg = (r + 63) / 64;
+  size_t nchunk = (1024 + jg * H - 1) / (jg * H);
+  const size_t maxchunk = (n + 63) / 64;
+  if (nchunk > maxchunk) nchunk = maxchunk;
+  if (nchunk < 1) nchunk = 1;
+  size_t crow = (n + nchunk - 1) / nchunk;
+  crow = (crow + 63) & ~size_t(63);
+  L.chunk_rows = (int)crow;
+  L.nchunk = (int)((n + crow - 1) / crow);
+  // attention: split the coreset when the queries alone give too few workgroups
+  L.rp = (int)((r + 31) & ~size_t(31));
+  const size_t nchk = (size_t)L.rp / 32;
+  const size_t qtiles = (m + 127) / 128;
+  size_t nsplit = 1;
+  if (qtiles * H < 512 && qtiles > 0) {
+    nsplit = (512 + qtiles * H - 1) / (qtiles * H);
+    if (nsplit > nchk) nsplit = nchk;
+    const size_t per = (nchk + nsplit - 1) / nsplit;
+    nsplit = (nchk + per - 1) / per;
+  }
+  L.nsplit = (int)nsplit;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  L.diag0 = take(H * n * 4);
+  L.diag1 = take(H * n * 4);
+  L.part0 = take(H * L.nblk * 8);
+  L.part1 = take(H * L.nblk * 8);
+  L.F = take(H * r * n * 4);
+  L.piv = take(H * r * 4);
+  L.L = take(H * r * r * 4);
+  L.Xpart = take(H * L.nchunk * r * nc * 4);
+  L.X = take(H * r * nc * 4);
+  L.W = take(H * r * nc * 4);
+  L.KSh = take(H * L.rp * p.d * 2);
+  L.KSl = take(H * L.rp * p.d * 2);
+  L.Wph = take(H * p.dv * L.rp * 2);
+  L.Wpl = take(H * p.dv * L.rp * 2);
+  L.Wden = take(H * L.rp * 4);
+  L.Ypart = take(L.nsplit > 1 ? H * L.nsplit * m * nc * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+template <typename Tp>
+Tp* at(void* ws, size_t off) { return reinterpret_cast<Tp*>(static_cast<char*>(ws) + off); }
+
+wc_status check_ws(const wc_problem& p, const void* ws, size_t ws_bytes, Layout* lay) {
+  *lay = make_layout(p);
+  if (!ws || !aligned16(ws) || ws_bytes < lay->total) return WC_ERR_WORKSPACE;
+  return WC_OK;
+}
+
+float beta_log2e(int d) { return (float)(1.4426950408889634 / std::sqrt((double)d)); }
+
+wc_status dev(hipError_t e) { return e == hipSuccess ? WC_OK : WC_ERR_DEVICE; }
+
+hipError_t run_rpc_stream(const wc_problem& p, const Layout& L, void* ws, const void* K,
+                          const float* u_forced, uint64_t seed, int32_t* pivots, float* F,
+                          float* diag, double* trace, int32_t* rank, uint32_t* flags,
+                          hipStream_t st) {
+  wc::StreamRpcArgs a{};
+  a.K = K;
+  a.bf16 = p.dtype == WC_BF16;
+  a.u_forced = u_forced;
+  a.seed = seed;
+  a.H = p.heads; a.n = p.n; a.d = p.d; a.r = p.r;
+  a.rows = L.rows; a.nblk = L.nblk;
+  a.beta_log2e = beta_log2e(p.d);
+  a.F = F;
+  a.diag0 = at<float>(ws, L.diag0);
+  a.diag1 = at<float>(ws, L.diag1);
+  a.part0 = at<double>(ws, L.part0);
+  a.part1 = at<double>(ws, L.part1);
+  a.pivots = pivots; a.trace = trace; a.rank = rank; a.flags = flags; a.diag_out = diag;
+  return wc::launch_rpc_stream(a, st);
+}
+
+hipError_t run_weights(const wc_problem& p, const Layout& L, void* ws, const void* V,
+                       const int32_t* pivots, const int32_t* rank, const float* F, float* W,
+                       hipStream_t st) {
+  wc::WeightsArgs a{};
+  a.V = V;
+  a.bf16 = p.dtype == WC_BF16;
+  a.H = p.heads; a.n = p.n; a.dv = p.dv; a.r = p.r;
+  a.F = F; a.pivots = pivots; a.rank = rank;
+  a.L = at<float>(ws, L.L);
+  a.Xpart = at<float>(ws, L.Xpart);
+  a.nchunk = L.nchunk; a.chunk_rows = L.chunk_rows;
+  a.X = at<float>(ws, L.X);
+  a.W = W;
+  return wc::launch_weights(a, st);
+}
+
+hipError_t run_attend(const wc_problem& p, const Layout& L, void* ws, const void* Q,
+                      const void* K, const int32_t* pivots, const int32_t* rank,
+                      const float* W, void* O, uint32_t* flags, hipStream_t st) {
+  wc::AttendArgs a{};
+  a.Q = Q; a.K = K;
+  a.bf16 = p.dtype == WC_BF16;
+  a.H = p.heads; a.n = p.n; a.m = p.m; a.d = p.d; a.dv = p.dv; a.r = p.r;
+  a.beta_log2e = beta_log2e(p.d);
+  a.pivots = pivots; a.rank = rank; a.W = W;
+  a.KSh = at<uint16_t>(ws, L.KSh);
+  a.KSl = p.dtype == WC_F32 ? at<uint16_t>(ws, L.KSl) : nullptr;
+  a.Wph = at<uint16_t>(ws, L.Wph);
+  a.Wpl = p.dtype == WC_F32 ? at<uint16_t>(ws, L.Wpl) : nullptr;
+  a.Wden = at<float>(ws, L.Wden);
+  a.Ypart = L.nsplit > 1 ? at<float>(ws, L.Ypart) : nullptr;
+  a.nsplit = L.nsplit;
+  a.O = O; a.flags = flags;
+  return wc::launch_attend(a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wc_abi_version(void) { return WC_ABI_VERSION; }
+
+const char* wc_status_string(wc_status s) {
+  switch (s) {
+    case WC_OK: return "ok";
+    case WC_ERR_INVALID_ARG: return "invalid argument";
+    case WC_ERR_UNSUPPORTED: return "unsupported problem (d, dv, dtype or size)";
+    case WC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case WC_ERR_DEVICE: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+wc_status wc_workspace_bytes(const wc_problem* p, size_t* bytes) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (!bytes) return WC_ERR_INVALID_ARG;
+  *bytes = p->heads == 0 ? 0 : make_layout(*p).total;
+  return WC_OK;
+}
+
+wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_forced,
+                        uint64_t seed, int32_t* pivots, float* F, float* diag, double* trace,
+                        int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes,
+                        void* stream) {
+  wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (p->heads == 0) return WC_OK;
+  if (!req(K) || !req(pivots) || !req(F) || !req(rank) || !req(flags) || !opt(u_forced) ||
+      !opt(diag) || !opt(trace))
+    return WC_ERR_INVALID_ARG;
+  Layout L;
+  if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (resident_ok(*p)) {
+    wc::ResidentArgs a{};
+    a.K = static_cast<const uint16_t*>(K);
+    a.u_forced = u_forced; a.seed = seed;
+    a.n = p->n; a.m = p->m; a.r = p->r;
+    a.beta_log2e = beta_log2e(p->d);
+    a.pivots = pivots; a.F = F; a.diag = diag; a.trace = trace; a.rank = rank; a.flags = flags;
+    return dev(wc::launch_resident(a, p->heads, p->d, p->dv, s));
+  }
+  return dev(run_rpc_stream(*p, L, ws, K, u_forced, seed, pivots, F, diag, trace, rank, flags, s));
+}
+
+wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
+                     const int32_t* rank, const float* F, float* W, void* ws, size_t ws_bytes,
+                     void* stream) {
+  wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (p->heads == 0) return WC_OK;
+  if (!req(V) || !req(pivots) || !req(rank) || !req(F) || !req(W)) return WC_ERR_INVALID_ARG;
+  Layout L;
+  if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
+  return dev(run_weights(*p, L, ws, V, pivots, rank, F, W, static_cast<hipStream_t>(stream)));
+}
+
+wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int32_t* pivots,
+                    const int32_t* rank, const float* W, void* O, uint32_t* flags, void* ws,
+                    size_t ws_bytes, void* stream) {
+  wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (p->heads == 0) return WC_OK;
+  if (!req(K) || !req(pivots) || !req(rank) || !req(W) || !req(flags)) return WC_ERR_INVALID_ARG;
+  if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
+  Layout L;
+  if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
+  return dev(run_attend(*p, L, ws, Q, K, pivots, rank, W, O, flags, static_cast<hipStream_t>(stream)));
+}
+
+wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
+                     const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
+                     int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (p->heads == 0) return WC_OK;
+  if (!req(K) || !req(V) || !req(rank) || !req(flags) || !opt(u_forced) || !opt(pivots))
+    return WC_ERR_INVALID_ARG;
+  if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
+  Layout L;
+  if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (resident_ok(*p) && p->m > 0) {
+    wc::ResidentArgs a{};
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.u_forced = u_forced; a.seed = seed;
+    a.n = p->n; a.m = p->m; a.r = p->r;
+    a.beta_log2e = beta_log2e(p->d);
+    a.O = static_cast<uint16_t*>(O);
+    a.pivots = pivots; a.rank = rank; a.flags = flags;
+    return dev(wc::launch_resident(a, p->heads, p->d, p->dv, s));
+  }
+  int32_t* piv = pivots ? pivots : at<int32_t>(ws, L.piv);
+  float* F = at<float>(ws, L.F);
+  float* W = at<float>(ws, L.W);
+  hipError_t e = run_rpc_stream(*p, L, ws, K, u_forced, seed, piv, F, nullptr, nullptr, rank, flags, s);
+  if (e == hipSuccess) e = run_weights(*p, L, ws, V, piv, rank, F, W, s);
+  if (e == hipSuccess) e = run_attend(*p, L, ws, Q, K, piv, rank, W, O, flags, s);
+  return dev(e);
+}
+
+}  // extern "C"

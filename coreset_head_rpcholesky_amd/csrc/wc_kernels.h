@@ -1,0 +1,105 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// device-side flag bits (same values as WC_FLAG_* in include/wc.h)
+#define WC_DFLAG_BREAKDOWN 1u
+#define WC_DFLAG_NONFINITE 2u
+#define WC_DFLAG_DENOM 4u
+
+namespace wc {
+
+// ---- resident path: one workgroup per head (n <= 256, bf16, r <= 32) ----
+constexpr int kResidentThreads = 256;  // one key row per thread: n <= 256
+constexpr int kResidentR = 32;         // r <= 32 (the pivot loop is unrolled over r)
+struct ResidentArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const float* u_forced;
+  uint64_t seed;
+  int n, m, r;
+  float beta_log2e;
+  uint16_t* O;        // NULL: pivot loop only
+  int32_t* pivots;    // [H][r] or NULL
+  float* F;           // [H][r][n] or NULL
+  float* diag;        // [H][n] or NULL
+  double* trace;      // [H][r+1] or NULL
+  int32_t* rank;      // [H]
+  uint32_t* flags;    // [H]
+  float* W;           // [H][r][dv+1] or NULL
+};
+hipError_t launch_resident_64_64(const ResidentArgs& a, int heads, hipStream_t st);
+hipError_t launch_resident_64_128(const ResidentArgs& a, int heads, hipStream_t st);
+hipError_t launch_resident_128_64(const ResidentArgs& a, int heads, hipStream_t st);
+hipError_t launch_resident_128_128(const ResidentArgs& a, int heads, hipStream_t st);
+inline hipError_t launch_resident(const ResidentArgs& a, int heads, int d, int dv, hipStream_t st) {
+  if (d == 64) return dv == 64 ? launch_resident_64_64(a, heads, st) : launch_resident_64_128(a, heads, st);
+  return dv == 64 ? launch_resident_128_64(a, heads, st) : launch_resident_128_128(a, heads, st);
+}
+
+// ---- streaming pivot loop: one launch per pivot step over all heads ----
+struct StreamRpcArgs {
+  const void* K;        // [H][n][d], float or bf16
+  int bf16;
+  const float* u_forced;
+  uint64_t seed;
+  int H, n, d, r;
+  int rows;             // rows per workgroup: 256, 512 or 1024
+  int nblk;             // row blocks per head, ceil(n / rows) <= 4096
+  float beta_log2e;
+  float* F;             // [H][r][n]
+  float* diag0;         // [H][n] double-buffered residual diagonal
+  float* diag1;
+  double* part0;        // [H][nblk] double-buffered block masses
+  double* part1;
+  int32_t* pivots;      // [H][r]
+  double* trace;        // [H][r+1] or NULL
+  int32_t* rank;        // [H]
+  uint32_t* flags;      // [H]
+  float* diag_out;      // [H][n] or NULL
+};
+constexpr int kStreamThreads = 256;
+hipError_t launch_rpc_stream(const StreamRpcArgs& a, hipStream_t st);
+
+// ---- weights: W = L^{-T} F^T [V, 1] ----
+struct WeightsArgs {
+  const void* V;          // [H][n][dv]
+  int bf16;
+  int H, n, dv, r;
+  const float* F;         // [H][r][n]
+  const int32_t* pivots;  // [H][r]
+  const int32_t* rank;    // [H]
+  float* L;               // ws [H][r][r]   L[t][j] = F[j][s_t]
+  float* Xpart;           // ws [H][nchunk][r][dv+1]
+  int nchunk, chunk_rows;
+  float* X;               // ws [H][r][dv+1]
+  float* W;               // out [H][r][dv+1]
+};
+hipError_t launch_weights(const WeightsArgs& a, hipStream_t st);
+
+// ---- attend: O = (exp(beta Q K_S^T) W)[:, :dv] / (...)[:, dv] ----
+struct AttendArgs {
+  const void* Q;          // [H][m][d]
+  const void* K;          // [H][n][d]
+  int bf16;
+  int H, n, m, d, dv, r;
+  float beta_log2e;
+  const int32_t* pivots;
+  const int32_t* rank;
+  const float* W;         // [H][r][dv+1]
+  uint16_t* KSh;          // ws [H][rp][d]    coreset keys, bf16 hi (rp = r rounded up to 32)
+  uint16_t* KSl;          // ws [H][rp][d]    bf16 lo (fp32 inputs only)
+  uint16_t* Wph;          // ws [H][dv][rp]   permuted W^T, bf16 hi
+  uint16_t* Wpl;          // ws [H][dv][rp]   bf16 lo (fp32 inputs only)
+  float* Wden;            // ws [H][rp]       W[:, dv]
+  float* Ypart;           // ws [H][nsplit][m][dv+1] partial sums when nsplit > 1
+  int nsplit;
+  void* O;                // [H][m][dv]
+  uint32_t* flags;        // [H]
+};
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+}  // namespace wc

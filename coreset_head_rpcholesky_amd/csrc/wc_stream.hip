@@ -1,0 +1,344 @@
+// Streaming randomly pivoted Cholesky for heads of any length (page
+// gist.science/de/paper/2602.10056, "Methodik" part 1: partial Cholesky of H = exp(beta K K^T),
+// each pivot drawn from the diagonal of the residual kernel matrix).
+//
+// One launch per pivot step covers every head; a head's n rows are split into blocks of
+// `rows` rows, one workgroup each.  The kernel boundary is the only global barrier:
+//   * at the start of step t every workgroup of a head reads the fp64 masses of all blocks
+//     (written at step t-1), finds T and the block holding u_t T, rescans that block's
+//     residual diagonal and so resolves the same pivot s as every other workgroup;
+//   * it gathers k_s and F[s, :t], forms g_s = H_ss - |F[s, :t]|^2, then for its own rows
+//     g_i = exp(beta k_i.k_s) - F[i, :t].F[s, :t], F[i, t] = g_i / sqrt(g_s),
+//     diag_i -= F[i, t]^2 (diag_s = 0), and writes its block's new fp64 mass.
+// The residual diagonal and the block masses are double-buffered so that step t reads only
+// what step t-1 wrote.  Column t of F is a contiguous run of n floats (F is [r][n]), so the
+// correction F[i, :t].F[s, :t] streams F column by column with coalesced loads.
+#include "wc_device.h"
+#include "wc_kernels.h"
+
+namespace wc {
+
+constexpr int NT = kStreamThreads;  // 256
+constexpr int NW = NT / 64;
+
+// dot(k_i, ks) for one key row against a key staged in LDS as fp32, fixed order.
+template <int D>
+__device__ __forceinline__ float row_dot(const uint16_t* krow, const float* ks) {
+  float a0 = 0.f, a1 = 0.f;
+  const uint4* src = reinterpret_cast<const uint4*>(krow);
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    const uint4 v = src[q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0 = fmaf(__uint_as_float(w[e] << 16), ks[8 * q + 2 * e], a0);
+      a1 = fmaf(__uint_as_float(w[e] & 0xffff0000u), ks[8 * q + 2 * e + 1], a1);
+    }
+  }
+  return a0 + a1;
+}
+template <int D>
+__device__ __forceinline__ float row_dot(const float* krow, const float* ks) {
+  float a0 = 0.f, a1 = 0.f;
+  const float4* src = reinterpret_cast<const float4*>(krow);
+#pragma unroll
+  for (int q = 0; q < D / 4; ++q) {
+    const float4 v = src[q];
+    a0 = fmaf(v.x, ks[4 * q], a0);
+    a1 = fmaf(v.y, ks[4 * q + 1], a1);
+    a0 = fmaf(v.z, ks[4 * q + 2], a0);
+    a1 = fmaf(v.w, ks[4 * q + 3], a1);
+  }
+  return a0 + a1;
+}
+
+// Block-wide fp64 sum in a fixed order (wave trees, then waves in order); all threads get it.
+__device__ __forceinline__ double block_sum(double x, double* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  x = wave_sum(x);
+  __syncthreads();
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[w];
+  return s;
+}
+
+// Block-wide exclusive scan of one fp64 value per thread (thread order); returns the
+// exclusive prefix, and the total through *tot.  Fixed order, identical in every workgroup.
+__device__ __forceinline__ double block_excl_scan(double x, double* red, double* tot) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const double inc = wave_incl_scan(x);
+  __syncthreads();
+  if (lane == 63) red[wid] = inc;
+  __syncthreads();
+  double pre = 0.0, all = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w == wid) pre = all;
+    all += red[w];
+  }
+  *tot = all;
+  return pre + (inc - x);
+}
+
+__device__ __forceinline__ int block_min_int(int v, int* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  int s = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) s = min(s, red[w]);
+  return s;
+}
+__device__ __forceinline__ int block_max_int(int v, int* red) {
+  return -block_min_int(-v, red);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_key_lds(const T* krow, float* ks) {
+  for (int e = threadIdx.x; e < D; e += NT) ks[e] = ld_elem<T>(krow + e);
+}
+
+// Initial residual diag_i = exp(beta |k_i|^2) and per-block masses.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) rpc_init_kernel(StreamRpcArgs a, int rows) {
+  __shared__ double red[NW];
+  const int h = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
+  const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * a.n * D;
+  double mass = 0.0;
+  for (int k = 0; k * NT < rows; ++k) {
+    const int i = b * rows + k * NT + tid;
+    if (i < a.n) {
+      const T* kr = K + (size_t)i * D;
+      float ksq[D];
+#pragma unroll
+      for (int e = 0; e < D; ++e) ksq[e] = ld_elem<T>(kr + e);
+      const float d0 = __builtin_amdgcn_exp2f(row_dot<D>(kr, ksq) * a.beta_log2e);
+      a.diag0[(size_t)h * a.n + i] = d0;
+      mass += mass_of(d0);
+    }
+  }
+  const double tot = block_sum(mass, red);
+  if (tid == 0) {
+    a.part0[(size_t)h * a.nblk + b] = tot;
+    if (b == 0) {
+      a.rank[h] = a.r;
+      a.flags[h] = 0u;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows, int t) {
+  __shared__ double red[NW];
+  __shared__ int ired[NW];
+  __shared__ __attribute__((aligned(16))) float s_ks[D];
+  extern __shared__ __attribute__((aligned(16))) double s_dyn[];
+  double* s_part = s_dyn;                                   // [nblk]
+  float* s_fs = reinterpret_cast<float*>(s_dyn + a.nblk);   // [r]
+  const int h = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
+  if (a.rank[h] < t) return;  // this head broke down at an earlier step
+  const int n = a.n, nblk = a.nblk;
+  const double* part = (t & 1) ? a.part1 : a.part0;
+  double* part_nx = (t & 1) ? a.part0 : a.part1;
+  const float* dg_in = ((t & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
+  float* dg_out = ((t & 1) ? a.diag0 : a.diag1) + (size_t)h * n;
+  const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * n * D;
+  float* F = a.F + (size_t)h * a.r * n;
+
+  // ---- 1. total mass T and the block holding u_t T ----
+  // thread tid owns the contiguous run of blocks [tid*per, tid*per + per)
+  const int per = (nblk + NT - 1) / NT;
+  double mine = 0.0;
+  for (int e = 0; e < per; ++e) {
+    const int bb = tid * per + e;
+    if (bb < nblk) {
+      const double v = part[(size_t)h * nblk + bb];
+      s_part[bb] = v;
+      mine += v;
+    }
+  }
+  double Ttot;
+  const double excl = block_excl_scan(mine, red, &Ttot);
+  const bool lead = (b == 0 && tid == 0);
+  if (!(Ttot > 0.0) || !__builtin_isfinite(Ttot)) {
+    if (lead) {
+      a.rank[h] = t;
+      a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(Ttot) ? 0u : WC_DFLAG_NONFINITE);
+      if (a.trace) a.trace[(size_t)h * (a.r + 1) + t] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
+    }
+    return;
+  }
+  const float u = pivot_uniform(a.u_forced, a.seed, h, a.r, t);
+  const double uT = (double)u * Ttot;
+  int cand = 0x7fffffff, lastpos = -1;
+  double run = excl;
+  for (int e = 0; e < per; ++e) {
+    const int bb = tid * per + e;
+    if (bb < nblk) {
+      const double v = s_part[bb];
+      run += v;
+      if (cand == 0x7fffffff && v > 0.0 && run > uT) cand = bb;
+      if (v > 0.0) lastpos = bb;
+    }
+  }
+  int bstar = block_min_int(cand, ired);
+  if (bstar == 0x7fffffff) bstar = block_max_int(lastpos, ired);
+  // exclusive offset of block bstar, recomputed in the same order as `run`
+  __syncthreads();
+  if (tid == bstar / per) {
+    double o = excl;
+    for (int e = 0; e < bstar - tid * per; ++e) o += s_part[tid * per + e];
+    red[0] = o;
+  }
+  __syncthreads();
+  const double boff = red[0];
+
+  // ---- 2. the pivot row inside block bstar ----
+  // thread tid owns rows [r0 + tid*rpt, r0 + tid*rpt + rpt)
+  const int rpt = rows / NT;
+  const int r0 = bstar * rows;
+  double pm[4];
+  double tmass = 0.0;
+  for (int e = 0; e < rpt; ++e) {
+    const int i = r0 + tid * rpt + e;
+    pm[e] = (i < n) ? mass_of(dg_in[i]) : 0.0;
+    tmass += pm[e];
+  }
+  double btot;
+  __syncthreads();
+  const double rexcl = block_excl_scan(tmass, red, &btot);
+  int scand = 0x7fffffff, slast = -1;
+  double c = boff + rexcl;
+  for (int e = 0; e < rpt; ++e) {
+    c += pm[e];
+    const int i = r0 + tid * rpt + e;
+    if (scand == 0x7fffffff && c > uT && pm[e] > 0.0) scand = i;
+    if (pm[e] > 0.0) slast = i;
+  }
+  int s = block_min_int(scand, ired);
+  if (s == 0x7fffffff) s = block_max_int(slast, ired);
+  if (s < 0 || s >= n) {  // no row with mass in the selected block: cannot happen for finite T > 0
+    if (lead) {
+      a.rank[h] = t;
+      a.flags[h] |= WC_DFLAG_BREAKDOWN | WC_DFLAG_NONFINITE;
+    }
+    return;
+  }
+
+  // ---- 3. gather k_s and F[s, :t]; g_s ----
+  load_key_lds<T, D>(K + (size_t)s * D, s_ks);
+  double sq = 0.0;
+  for (int j = tid; j < t; j += NT) {
+    const float v = F[(size_t)j * n + s];
+    s_fs[j] = v;
+  }
+  __syncthreads();
+  float hss = 0.f;
+  {
+    float part_sq = 0.f;
+    for (int j = tid; j < t; j += NT) part_sq = fmaf(s_fs[j], s_fs[j], part_sq);
+    sq = (double)part_sq;
+  }
+  const double sqt = block_sum(sq, red);
+  hss = __builtin_amdgcn_exp2f(row_dot<D>(K + (size_t)s * D, s_ks) * a.beta_log2e);
+  const float gs = hss - (float)sqt;
+  if (!(gs > 0.f) || !__builtin_isfinite(gs)) {
+    if (lead) {
+      a.rank[h] = t;
+      a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(gs) ? 0u : WC_DFLAG_NONFINITE);
+      if (a.trace) a.trace[(size_t)h * (a.r + 1) + t] = Ttot;
+    }
+    return;
+  }
+  if (lead) {
+    a.pivots[(size_t)h * a.r + t] = s;
+    if (a.trace) a.trace[(size_t)h * (a.r + 1) + t] = Ttot;
+  }
+  const float rs = 1.0f / sqrtf(gs);
+
+  // ---- 4. this block's rows: new column of F, residual update, block mass ----
+  double mass = 0.0;
+  for (int k = 0; k * NT < rows; ++k) {
+    const int i = b * rows + k * NT + tid;
+    if (i >= n) break;
+    const float hcol = __builtin_amdgcn_exp2f(row_dot<D>(K + (size_t)i * D, s_ks) * a.beta_log2e);
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    const float* Fi = F + i;
+    int j = 0;
+    for (; j + 4 <= t; j += 4) {
+      c0 = fmaf(Fi[(size_t)j * n], s_fs[j], c0);
+      c1 = fmaf(Fi[(size_t)(j + 1) * n], s_fs[j + 1], c1);
+      c2 = fmaf(Fi[(size_t)(j + 2) * n], s_fs[j + 2], c2);
+      c3 = fmaf(Fi[(size_t)(j + 3) * n], s_fs[j + 3], c3);
+    }
+    for (; j < t; ++j) c0 = fmaf(Fi[(size_t)j * n], s_fs[j], c0);
+    const float g = hcol - ((c0 + c1) + (c2 + c3));
+    const float f = g * rs;
+    F[(size_t)t * n + i] = f;
+    const float dnew = (i == s) ? 0.f : dg_in[i] - f * f;
+    dg_out[i] = dnew;
+    mass += mass_of(dnew);
+  }
+  const double tot = block_sum(mass, red);
+  if (tid == 0) part_nx[(size_t)h * nblk + b] = tot;
+}
+
+// Final bookkeeping per head: trace after the last step, -1 pivots and zero F columns
+// after a breakdown, copy of the final residual diagonal.
+template <int DUMMY>
+__global__ void __launch_bounds__(NT) rpc_final_kernel(StreamRpcArgs a) {
+  __shared__ double red[NW];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int rk = a.rank[h];
+  const int n = a.n, nblk = a.nblk;
+  const double* part = (rk & 1) ? a.part1 : a.part0;
+  const float* dg = ((rk & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
+  if (rk == a.r && a.trace) {
+    const int per = (nblk + NT - 1) / NT;
+    double mine = 0.0;
+    for (int e = 0; e < per; ++e) {
+      const int bb = tid * per + e;
+      if (bb < nblk) mine += part[(size_t)h * nblk + bb];
+    }
+    double T;
+    block_excl_scan(mine, red, &T);
+    if (tid == 0) a.trace[(size_t)h * (a.r + 1) + a.r] = T;
+  }
+  if (a.trace)
+    for (int t = rk + 1 + tid; t <= a.r; t += NT) a.trace[(size_t)h * (a.r + 1) + t] = 0.0;
+  for (int t = rk + tid; t < a.r; t += NT) a.pivots[(size_t)h * a.r + t] = -1;
+  for (size_t e = (size_t)rk * n + tid; e < (size_t)a.r * n; e += NT) a.F[(size_t)h * a.r * n + e] = 0.f;
+  if (a.diag_out)
+    for (int i = tid; i < n; i += NT) a.diag_out[(size_t)h * n + i] = dg[i];
+}
+
+template <typename T, int D>
+static hipError_t run_rpc(const StreamRpcArgs& a, int rows, hipStream_t st) {
+  const dim3 grid(a.nblk, a.H);
+  const size_t lds = (size_t)a.nblk * sizeof(double) + (size_t)a.r * sizeof(float);
+  hipLaunchKernelGGL((rpc_init_kernel<T, D>), grid, dim3(NT), 0, st, a, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int t = 0; t < a.r; ++t) {
+    hipLaunchKernelGGL((rpc_step_kernel<T, D>), grid, dim3(NT), lds, st, a, rows, t);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((rpc_final_kernel<0>), dim3(a.H), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rpc_stream(const StreamRpcArgs& a, hipStream_t st) {
+  const int rows = a.rows;
+  if (a.bf16) return a.d == 64 ? run_rpc<uint16_t, 64>(a, rows, st) : run_rpc<uint16_t, 128>(a, rows, st);
+  return a.d == 64 ? run_rpc<float, 64>(a, rows, st) : run_rpc<float, 128>(a, rows, st);
+}
+
+}  // namespace wc

@@ -108,13 +108,13 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
 
 /* Nystroem weights W = H_SS^{-1} H_{S,:} [V, 1] for the first rank[h] pivots
  * (gist.science/de/paper/2602.10056, "Methodik" part 2: W = h(K_S,K_S)^+ h(K_S,K), V_S = W V).
- * Computed through the factor of wc_rpcholesky: with L = F[S, :] (lower triangular,
- * L L^T = H_SS) and H_{:,S} = F L^T, W = L^{-T} F^T [V, 1].
- *   K, V          in  [heads][n][d], [heads][n][dv], dtype
+ * Computed through the factor of wc_rpcholesky, so the keys are not needed again: with
+ * L = F[S, :] (lower triangular, L L^T = H_SS) and H_{:,S} = F L^T, W = L^{-T} F^T [V, 1].
+ *   V             in  [heads][n][dv], dtype
  *   pivots, rank  in  as returned by wc_rpcholesky
  *   F             in  [heads][r][n], the factor returned by wc_rpcholesky for these pivots
  *   W             out [heads][r][dv+1]; rows rank..r-1 are zero                            */
-wc_status wc_weights(const wc_problem* p, const void* K, const void* V, const int32_t* pivots,
+wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
                      const int32_t* rank, const float* F, float* W, void* ws, size_t ws_bytes,
                      void* stream);
 

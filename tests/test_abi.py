@@ -1,0 +1,134 @@
+"""The C ABI on the host: the library loads, exports every symbol include/wc.h declares, and
+its argument validation returns the documented status before any HIP call (no device is
+touched: every call below fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "coreset_head_rpcholesky_amd", "libwc.so")
+HEADER = os.path.join(ROOT, "include", "wc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libwc.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wc_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ctypes.CDLL(LIB)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype")]
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"wc_rpcholesky", "wc_weights", "wc_attend", "wc_forward",
+                          "wc_workspace_bytes", "wc_status_string", "wc_abi_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    lib.wc_abi_version.restype = ctypes.c_int32
+    assert lib.wc_abi_version() == 1
+    lib.wc_status_string.restype = ctypes.c_char_p
+    seen = set()
+    for s in range(6):
+        txt = lib.wc_status_string(s)
+        assert txt
+        seen.add(txt)
+    assert len(seen) == 6
+
+
+def ws_bytes(lib, p):
+    out = ctypes.c_size_t(0)
+    st = lib.wc_workspace_bytes(ctypes.byref(p), ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("fields,expect", [
+    ((1, 1024, 1024, 64, 64, 32, 0), 0),
+    ((768, 197, 197, 64, 64, 32, 1), 0),
+    ((0, 10, 10, 64, 64, 5, 1), 0),         # no heads: valid, no work
+    ((1, 10, 0, 128, 128, 10, 1), 0),       # no queries: valid
+    ((1, 10, 10, 64, 64, 11, 1), 1),        # r > n
+    ((1, 10, 10, 64, 64, 0, 1), 1),         # r = 0
+    ((-1, 10, 10, 64, 64, 5, 1), 1),        # negative heads
+    ((1, 0, 10, 64, 64, 1, 1), 1),          # no keys
+    ((1, 100, 10, 32, 64, 5, 1), 2),        # unsupported d
+    ((1, 100, 10, 64, 96, 5, 1), 2),        # unsupported dv
+    ((1, 100, 10, 64, 64, 5, 7), 2),        # unsupported dtype
+    ((1, 10000, 10, 64, 64, 4097, 1), 2),   # r above the supported maximum
+])
+def test_workspace_bytes_validation(lib, fields, expect):
+    st, nbytes = ws_bytes(lib, Problem(*fields))
+    assert st == expect
+    if st == 0 and fields[0] > 0:
+        assert nbytes > 0 and nbytes % 256 == 0
+
+
+def test_null_problem_and_null_out(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.wc_workspace_bytes(None, ctypes.byref(out)) == 1
+    assert lib.wc_workspace_bytes(ctypes.byref(Problem(1, 10, 10, 64, 64, 5, 1)), None) == 1
+
+
+A = ctypes.c_void_p(0x10000)      # aligned fake device address: never dereferenced
+MIS = ctypes.c_void_p(0x10008)    # misaligned
+
+
+def call_rpc(lib, p, K=A, piv=A, F=A, rank=A, flags=A, u=None, diag=None, trace=None, ws=A, nb=1 << 40):
+    return lib.wc_rpcholesky(ctypes.byref(p), K, u, ctypes.c_uint64(1), piv, F, diag, trace, rank,
+                             flags, ws, ctypes.c_size_t(nb), None)
+
+
+def test_rpcholesky_argument_errors(lib):
+    p = Problem(4, 300, 300, 64, 64, 16, 1)
+    assert call_rpc(lib, p, K=None) == 1
+    assert call_rpc(lib, p, piv=None) == 1
+    assert call_rpc(lib, p, F=None) == 1
+    assert call_rpc(lib, p, rank=None) == 1
+    assert call_rpc(lib, p, flags=None) == 1
+    assert call_rpc(lib, p, K=MIS) == 1
+    assert call_rpc(lib, p, u=MIS) == 1
+    assert call_rpc(lib, p, diag=MIS) == 1
+    assert call_rpc(lib, p, ws=None) == 3
+    assert call_rpc(lib, p, ws=MIS) == 3
+    _, need = ws_bytes(lib, p)
+    assert call_rpc(lib, p, nb=need - 1) == 3
+    assert call_rpc(lib, Problem(4, 300, 300, 64, 64, 301, 1)) == 1
+    assert call_rpc(lib, Problem(4, 300, 300, 80, 64, 16, 1)) == 2
+    assert call_rpc(lib, Problem(0, 300, 300, 64, 64, 16, 1), K=None) == 0  # no heads: no-op
+
+
+def test_weights_attend_forward_argument_errors(lib):
+    p = Problem(2, 5000, 64, 128, 128, 256, 0)
+    big = ctypes.c_size_t(1 << 40)
+    u64 = ctypes.c_uint64(0)
+    w = lib.wc_weights
+    assert w(ctypes.byref(p), None, A, A, A, A, A, big, None) == 1
+    assert w(ctypes.byref(p), A, A, A, A, None, A, big, None) == 1
+    assert w(ctypes.byref(p), A, A, A, A, A, None, big, None) == 3
+    at = lib.wc_attend
+    assert at(ctypes.byref(p), None, A, A, A, A, A, A, A, big, None) == 1      # Q needed when m > 0
+    assert at(ctypes.byref(p), A, A, A, A, A, MIS, A, A, big, None) == 1
+    assert at(ctypes.byref(p), A, A, A, A, A, A, None, A, big, None) == 1      # flags required
+    p0 = Problem(2, 5000, 0, 128, 128, 256, 0)
+    assert at(ctypes.byref(p0), None, A, A, A, A, None, A, None, big, None) == 3  # m = 0: Q, O optional
+    fw = lib.wc_forward
+    assert fw(ctypes.byref(p), A, A, None, None, u64, A, None, A, A, A, big, None) == 1
+    assert fw(ctypes.byref(p), A, A, A, MIS, u64, A, None, A, A, A, big, None) == 1
+    assert fw(ctypes.byref(p), A, A, A, None, u64, A, MIS, A, A, A, big, None) == 1
+    assert fw(ctypes.byref(p), A, A, A, None, u64, A, None, None, A, A, big, None) == 1
+    assert fw(ctypes.byref(p), A, A, A, None, u64, A, None, A, A, A, ctypes.c_size_t(10), None) == 3
+    assert fw(ctypes.byref(Problem(2, 5000, 64, 128, 128, 0, 0)), A, A, A, None, u64, A, None, A, A, A,
+              big, None) == 1
