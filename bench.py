@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the WildCat forward (coreset selection + weights + attention) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit197]
+
+A step is one whole forward (randomly pivoted Cholesky, Nystroem weights, attention over the
+coreset) over every head of one batch of seeded synthetic inputs that are already resident
+in HBM.  The default workload is the ViT-classification-shaped one (64 x 12 heads, n = 197,
+d = 64, r = 32, bf16); the other workloads of coreset_head_rpcholesky_amd.synth can be
+selected with --workload.  Prints one JSON line.
+
+Beside the GPU number it reports:
+  * roofline of the dominant kernel: algorithmic bytes (or flops) of one launch over its
+    average duration, timed with HIP events on the stream the kernel is launched on;
+  * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same workload;
+  * exact softmax attention (PyTorch SDPA) on the same tensors, for context.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WildCat forward tokens/sec (coreset+weights+attend); % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+# Kernel sources whose counters a stored traffic figure belongs to.
+KERNEL_SOURCES = {
+    "resident": ["wc_resident.hip", "wc_device.h", "wc_kernels.h"],
+    "stream": ["wc_stream.hip", "wc_device.h", "wc_kernels.h"],
+}
+COUNTER_FILES = {
+    "vit197": "profiles/resident_kernel_vit197_counters.txt",
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "coreset_head_rpcholesky_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = COUNTER_FILES.get(workload)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    vals = {}
+    for line in open(os.path.join(ROOT, path)):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha") != source_hash(kind):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def workload_accounting(w):
+    """Algorithmic bytes and flops of one forward over all heads (per-head figures x heads)."""
+    b = 2 if w.dtype == "bf16" else 4
+    H, n, m, d, dv, r = w.heads, w.n, w.m, w.d, w.dv, w.r
+    compulsory = H * ((m * d + n * d + n * dv) * b + m * dv * b)
+    pivot_bytes = H * (n * r * d * b + 2 * n * r * (r - 1) + 12 * n * r)
+    pivot_flops = H * (2 * n * r * d + n * r * (r - 1))
+    weight_flops = H * (2 * r * n * (dv + 1) + r * r * (dv + 1))
+    attend_flops = H * 2 * m * r * (d + dv + 1)
+    return dict(compulsory_bytes=compulsory, pivot_bytes=pivot_bytes, pivot_flops=pivot_flops,
+                weight_flops=weight_flops, attend_flops=attend_flops)
+
+
+def cpu_baseline(w, Q, K, V, budget_s: float):
+    """The fp64 oracle on as many heads as fit in the time budget; tokens/s scaled to the
+    whole workload (tokens per head = tokens / heads)."""
+    import numpy as np
+
+    from oracle import philox
+    from oracle import wildcat as ow
+
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        cores = min(16, os.cpu_count() or 1)
+        limiter = threadpool_limits(cores)
+        info = threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in info] + [1])
+    except Exception:  # pragma: no cover
+        limiter, cores = None, 1
+    t0 = time.perf_counter()
+    done = 0
+    for h in range(w.heads):
+        u = np.array(philox.pivot_uniforms(42, h, w.r))
+        ow.forward(Q[h], K[h], V[h], w.r, u)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
+    tokens = w.tokens * done / w.heads
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.heads} heads of one {w.name} forward, fp64 numpy/scipy, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vit197")
+    ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run a plain copy kernel of this size first (for counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU: every head is independent, so "
+                          "more GPUs would shard heads with no communication; only --gpus 1 "
+                          "is measured"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from coreset_head_rpcholesky_amd import binding, synth
+
+    w = synth.WORKLOADS[args.workload]
+    dt_t = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Qn, Kn, Vn = synth.make_inputs(w.name)
+
+    def up(x):
+        return torch.from_numpy(x).to(dev, dt_t).contiguous()
+
+    Q, K, V = up(Qn), up(Kn), up(Vn)
+    p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t)
+    ws = binding.workspace(p, dev)
+    out = dict(O=torch.empty((w.heads, w.m, w.dv), dtype=dt_t, device=dev),
+               pivots=torch.empty((w.heads, w.r), dtype=torch.int32, device=dev),
+               rank=torch.empty((w.heads,), dtype=torch.int32, device=dev),
+               flags=torch.empty((w.heads,), dtype=torch.int32, device=dev))
+
+    if args.copy_calibration_mb > 0:
+        nel = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        binding.wc_forward(Q, K, V, w.r, seed=args.seed, ws=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms = evs[0].elapsed_time(evs[args.steps]) / args.steps
+    value = w.tokens / (ms / 1e3)
+    rank = out["rank"].cpu().numpy()
+    flags = out["flags"].cpu().numpy()
+
+    acc = workload_accounting(w)
+    resident = w.dtype == "bf16" and w.n <= 256 and w.r <= 32
+    if resident:
+        # one launch per step: the resident kernel; only compulsory bytes reach HBM
+        kernel_ms = float(np.mean(per))
+        achieved = acc["compulsory_bytes"] / (kernel_ms / 1e3) / 1e9
+        traffic = stored_traffic(w.name, "resident")
+        roof = {"kernel": "resident_kernel (pivot loop + weights + attention, one workgroup per head)",
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": acc["compulsory_bytes"],
+                "avg_launch_ms": round(kernel_ms, 5)}
+    else:
+        # the pivot loop dominates: time wc_rpcholesky alone with events on the same stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        binding.wc_rpcholesky(K, w.r, seed=args.seed, ws=ws, with_diag=False, with_trace=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        loop_ms = e0.elapsed_time(e1)
+        achieved = acc["pivot_bytes"] / (loop_ms / 1e3) / 1e9
+        roof = {"kernel": f"rpc_step_kernel x {w.r} launches (streaming pivot loop)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_loop": acc["pivot_bytes"], "loop_ms": round(loop_ms, 3)}
+
+    exact = None
+    if not args.no_exact:
+        try:
+            import torch.nn.functional as Fn
+            for _ in range(2):
+                Fn.scaled_dot_product_attention(Q, K, V)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                Fn.scaled_dot_product_attention(Q, K, V)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ems = e0.elapsed_time(e1) / reps
+            exact = {"ms_per_step": round(ems, 4), "tokens_per_s": round(w.tokens / (ems / 1e3), 1),
+                     "op": "torch.nn.functional.scaled_dot_product_attention"}
+        except Exception as e:  # pragma: no cover
+            exact = {"error": str(e)[:200]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, Qn, Kn, Vn, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "heads": w.heads, "n": w.n,
+                   "m": w.m, "d": w.d, "dv": w.dv, "r": w.r, "tokens_per_step": w.tokens,
+                   "pivot_uniforms": f"Philox4x64-10 seed {args.seed}"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "exact_attention": exact,
+        "checks": {"rank_min": int(rank.min()), "flags_or": int(np.bitwise_or.reduce(flags)),
+                   "wall_s_timed": round(wall, 4)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

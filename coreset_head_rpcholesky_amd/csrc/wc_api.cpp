@@ -44,7 +44,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int rows, nblk, nchunk, chunk_rows, nsplit, rp;
-  size_t diag0, diag1, part0, part1, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Ypart;
+  size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Ypart;
   size_t total;
 };
 
@@ -85,6 +85,7 @@ Layout make_layout(const wc_problem& p) {
   L.diag1 = take(H * n * 4);
   L.part0 = take(H * L.nblk * 8);
   L.part1 = take(H * L.nblk * 8);
+  L.unif = take(H * r * 4);
   L.F = take(H * r * n * 4);
   L.piv = take(H * r * 4);
   L.L = take(H * r * r * 4);
@@ -123,6 +124,7 @@ hipError_t run_rpc_stream(const wc_problem& p, const Layout& L, void* ws, const 
   a.bf16 = p.dtype == WC_BF16;
   a.u_forced = u_forced;
   a.seed = seed;
+  a.uniforms = u_forced ? const_cast<float*>(u_forced) : at<float>(ws, L.unif);
   a.H = p.heads; a.n = p.n; a.d = p.d; a.r = p.r;
   a.rows = L.rows; a.nblk = L.nblk;
   a.beta_log2e = beta_log2e(p.d);

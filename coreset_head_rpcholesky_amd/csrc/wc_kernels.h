@@ -46,6 +46,7 @@ struct StreamRpcArgs {
   int bf16;
   const float* u_forced;
   uint64_t seed;
+  float* uniforms;      // [H][r]: u_forced, or filled from Philox before the first step
   int H, n, d, r;
   int rows;             // rows per workgroup: 256, 512 or 1024
   int nblk;             // row blocks per head, ceil(n / rows) <= 4096

@@ -114,7 +114,8 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
 
   __shared__ double s_wsum[NW];
   __shared__ int s_piv;
-  __shared__ float s_gs;
+  __shared__ float s_gs, s_rs;
+  __shared__ float s_u[R];
   __shared__ uint32_t s_flag;
   __shared__ __attribute__((aligned(16))) uint32_t s_ks[D2];
   __shared__ __attribute__((aligned(16))) float s_fs[R];
@@ -149,6 +150,8 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     s_flag = 0u;
     s_piv = -1;
   }
+  // the r pivot uniforms, drawn once (first use is after the first barrier)
+  if (tid < r) s_u[tid] = pivot_uniform(a.u_forced, a.seed, h, r, tid);
   int rk = r;
   uint32_t flg = 0u;
 
@@ -171,8 +174,7 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
       alive = false;
       return;
     }
-    const float u = pivot_uniform(a.u_forced, a.seed, h, r, t);
-    const double uT = (double)u * T;
+    const double uT = (double)s_u[t] * T;
     double acc = 0.0, pre = 0.0;
     int wstar = -1, wlast = -1;
 #pragma unroll
@@ -194,7 +196,9 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     }
     if (winner) {
       s_piv = tid;
-      s_gs = d0 - dot_prefix<t>(fr, fr);
+      const float g = d0 - dot_prefix<t>(fr, fr);
+      s_gs = g;
+      s_rs = 1.0f / sqrtf(g);
 #pragma unroll
       for (int q = 0; q < D2; ++q) s_ks[q] = kr[q];
 #pragma unroll
@@ -219,7 +223,7 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
       alive = false;
       return;
     }
-    const float rs = 1.0f / sqrtf(gs);
+    const float rs = s_rs;
     const float hcol = __builtin_amdgcn_exp2f(dot_bf16<D2>(kr, s_ks) * bl2e);
     const float gi = hcol - dot_prefix<t>(fr, s_fs);
     const float f = valid ? gi * rs : 0.f;

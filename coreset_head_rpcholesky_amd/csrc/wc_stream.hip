@@ -105,6 +105,13 @@ __device__ __forceinline__ void load_key_lds(const T* krow, float* ks) {
   for (int e = threadIdx.x; e < D; e += NT) ks[e] = ld_elem<T>(krow + e);
 }
 
+// Pivot uniforms of every (head, step), drawn once before the loop.
+__global__ void __launch_bounds__(256) uniforms_kernel(StreamRpcArgs a) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (size_t)a.H * a.r) return;
+  a.uniforms[e] = philox_uniform(a.seed, (uint32_t)(e / a.r), (uint32_t)(e % a.r));
+}
+
 // Initial residual diag_i = exp(beta |k_i|^2) and per-block masses.
 template <typename T, int D>
 __global__ void __launch_bounds__(NT) rpc_init_kernel(StreamRpcArgs a, int rows) {
@@ -175,8 +182,7 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
     }
     return;
   }
-  const float u = pivot_uniform(a.u_forced, a.seed, h, a.r, t);
-  const double uT = (double)u * Ttot;
+  const double uT = (double)a.uniforms[(size_t)h * a.r + t] * Ttot;
   int cand = 0x7fffffff, lastpos = -1;
   double run = excl;
   for (int e = 0; e < per; ++e) {
@@ -320,11 +326,17 @@ __global__ void __launch_bounds__(NT) rpc_final_kernel(StreamRpcArgs a) {
 }
 
 template <typename T, int D>
-static hipError_t run_rpc(const StreamRpcArgs& a, int rows, hipStream_t st) {
+static hipError_t run_rpc(StreamRpcArgs a, int rows, hipStream_t st) {
   const dim3 grid(a.nblk, a.H);
   const size_t lds = (size_t)a.nblk * sizeof(double) + (size_t)a.r * sizeof(float);
+  hipError_t e;
+  if (!a.u_forced) {
+    const size_t nu = (size_t)a.H * a.r;
+    hipLaunchKernelGGL(uniforms_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((rpc_init_kernel<T, D>), grid, dim3(NT), 0, st, a, rows);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   for (int t = 0; t < a.r; ++t) {
     hipLaunchKernelGGL((rpc_step_kernel<T, D>), grid, dim3(NT), lds, st, a, rows, t);
