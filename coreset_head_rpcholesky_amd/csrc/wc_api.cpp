@@ -52,10 +52,10 @@ Layout make_layout(const wc_problem& p) {
   Layout L{};
   const size_t H = (size_t)p.heads, n = (size_t)p.n, r = (size_t)p.r, m = (size_t)p.m;
   const size_t nc = (size_t)p.dv + 1;
-  // pivot loop: rows per workgroup, enough workgroups to fill the chip
-  L.rows = 1024;
-  if (H * ((n + 1023) / 1024) < 512) L.rows = 512;
-  if (L.rows == 512 && H * ((n + 511) / 512) < 512) L.rows = 256;
+  // pivot loop: 1024 rows per workgroup (4 contiguous rows per thread, 16-byte accesses)
+  // when n is a multiple of 4 and that still gives enough workgroups to fill the chip;
+  // otherwise 256 rows (one per thread)
+  L.rows = (n % 4 == 0 && H * ((n + 1023) / 1024) >= 512) ? 1024 : 256;
   L.nblk = (int)((n + L.rows - 1) / L.rows);
   // weights: row chunks so that (r/64 groups) x chunks x heads >= 1024 workgroups
   const size_t jg = (r + 63) / 64;

@@ -48,7 +48,7 @@ struct StreamRpcArgs {
   uint64_t seed;
   float* uniforms;      // [H][r]: u_forced, or filled from Philox before the first step
   int H, n, d, r;
-  int rows;             // rows per workgroup: 256, 512 or 1024
+  int rows;             // rows per workgroup: 256, or 1024 when n % 4 == 0
   int nblk;             // row blocks per head, ceil(n / rows) <= 4096
   float beta_log2e;
   float* F;             // [H][r][n]

@@ -26,7 +26,7 @@ template <int D>
 __device__ __forceinline__ float row_dot(const uint16_t* krow, const float* ks) {
   float a0 = 0.f, a1 = 0.f;
   const uint4* src = reinterpret_cast<const uint4*>(krow);
-#pragma unroll
+#pragma unroll 4
   for (int q = 0; q < D / 8; ++q) {
     const uint4 v = src[q];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -42,7 +42,7 @@ template <int D>
 __device__ __forceinline__ float row_dot(const float* krow, const float* ks) {
   float a0 = 0.f, a1 = 0.f;
   const float4* src = reinterpret_cast<const float4*>(krow);
-#pragma unroll
+#pragma unroll 4
   for (int q = 0; q < D / 4; ++q) {
     const float4 v = src[q];
     a0 = fmaf(v.x, ks[4 * q], a0);
@@ -51,6 +51,35 @@ __device__ __forceinline__ float row_dot(const float* krow, const float* ks) {
     a1 = fmaf(v.w, ks[4 * q + 3], a1);
   }
   return a0 + a1;
+}
+
+// RPT contiguous floats (RPT = 4: one 16-byte access; the caller guarantees alignment).
+template <int RPT>
+__device__ __forceinline__ void load_rows(const float* p, float* v) {
+  if constexpr (RPT == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) v[e] = p[e];
+  }
+}
+template <int RPT>
+__device__ __forceinline__ void store_rows(float* p, const float* v) {
+  if constexpr (RPT == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) p[e] = v[e];
+  }
+}
+
+// dot(k_i, k_s) for the RPT contiguous rows i0 .. i0 + RPT - 1 (k_s staged in LDS as fp32);
+// the same association order as row_dot.
+template <typename T, int D, int RPT>
+__device__ __forceinline__ void multi_row_dot(const T* K, int i0, int n, const float* ks, float* out) {
+#pragma unroll
+  for (int e = 0; e < RPT; ++e) out[e] = (i0 + e < n) ? row_dot<D>(K + (size_t)(i0 + e) * D, ks) : 0.f;
 }
 
 // Block-wide fp64 sum in a fixed order (wave trees, then waves in order); all threads get it.
@@ -141,7 +170,7 @@ __global__ void __launch_bounds__(NT) rpc_init_kernel(StreamRpcArgs a, int rows)
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int RPT>
 __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows, int t) {
   __shared__ double red[NW];
   __shared__ int ired[NW];
@@ -270,27 +299,50 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
   const float rs = 1.0f / sqrtf(gs);
 
   // ---- 4. this block's rows: new column of F, residual update, block mass ----
+  // Thread tid owns the RPT contiguous rows i0 .. i0 + RPT - 1, so column j of F arrives as one
+  // RPT-wide load per thread and a wave reads RPT * 256 contiguous bytes; U columns are in
+  // flight at once to keep enough bytes outstanding per CU for HBM.
   double mass = 0.0;
-  for (int k = 0; k * NT < rows; ++k) {
-    const int i = b * rows + k * NT + tid;
-    if (i >= n) break;
-    const float hcol = __builtin_amdgcn_exp2f(row_dot<D>(K + (size_t)i * D, s_ks) * a.beta_log2e);
-    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
-    const float* Fi = F + i;
+  const int i0 = b * rows + tid * RPT;
+  if (i0 < n) {
+    float hcol[RPT];
+    multi_row_dot<T, D, RPT>(K, i0, n, s_ks, hcol);
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) hcol[e] = __builtin_amdgcn_exp2f(hcol[e] * a.beta_log2e);
+    float acc[RPT];
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) acc[e] = 0.f;
+    constexpr int U = RPT == 4 ? 8 : 16;
+    const float* Fi = F + i0;
     int j = 0;
-    for (; j + 4 <= t; j += 4) {
-      c0 = fmaf(Fi[(size_t)j * n], s_fs[j], c0);
-      c1 = fmaf(Fi[(size_t)(j + 1) * n], s_fs[j + 1], c1);
-      c2 = fmaf(Fi[(size_t)(j + 2) * n], s_fs[j + 2], c2);
-      c3 = fmaf(Fi[(size_t)(j + 3) * n], s_fs[j + 3], c3);
+    for (; j + U <= t; j += U) {
+      float fv[U][RPT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_rows<RPT>(Fi + (size_t)(j + u) * n, fv[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float fs = s_fs[j + u];
+#pragma unroll
+        for (int e = 0; e < RPT; ++e) acc[e] = fmaf(fv[u][e], fs, acc[e]);
+      }
     }
-    for (; j < t; ++j) c0 = fmaf(Fi[(size_t)j * n], s_fs[j], c0);
-    const float g = hcol - ((c0 + c1) + (c2 + c3));
-    const float f = g * rs;
-    F[(size_t)t * n + i] = f;
-    const float dnew = (i == s) ? 0.f : dg_in[i] - f * f;
-    dg_out[i] = dnew;
-    mass += mass_of(dnew);
+    for (; j < t; ++j) {
+      float fv[RPT];
+      load_rows<RPT>(Fi + (size_t)j * n, fv);
+      const float fs = s_fs[j];
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) acc[e] = fmaf(fv[e], fs, acc[e]);
+    }
+    float f[RPT], din[RPT], dnew[RPT];
+    load_rows<RPT>(dg_in + i0, din);
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      f[e] = (hcol[e] - acc[e]) * rs;
+      dnew[e] = (i0 + e == s) ? 0.f : din[e] - f[e] * f[e];
+      mass += mass_of(dnew[e]);
+    }
+    store_rows<RPT>(F + (size_t)t * n + i0, f);
+    store_rows<RPT>(dg_out + i0, dnew);
   }
   const double tot = block_sum(mass, red);
   if (tid == 0) part_nx[(size_t)h * nblk + b] = tot;
@@ -339,7 +391,10 @@ static hipError_t run_rpc(StreamRpcArgs a, int rows, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   for (int t = 0; t < a.r; ++t) {
-    hipLaunchKernelGGL((rpc_step_kernel<T, D>), grid, dim3(NT), lds, st, a, rows, t);
+    if (rows == 4 * NT)
+      hipLaunchKernelGGL((rpc_step_kernel<T, D, 4>), grid, dim3(NT), lds, st, a, rows, t);
+    else
+      hipLaunchKernelGGL((rpc_step_kernel<T, D, 1>), grid, dim3(NT), lds, st, a, rows, t);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
