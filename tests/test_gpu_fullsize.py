@@ -1,0 +1,121 @@
+"""Parity at the full sizes of the five workloads, in the launch configuration bench.py times
+(one wc_forward over all heads, captured in a HIP graph and replayed).
+
+vit197, iid1k and img4096 are checked element by element against the oracle under snapped
+forced uniforms.  kv32k and long128k are too large for the oracle's whole pivot loop, so they
+run in seeded (Philox) mode like the bench and are checked on sampled outputs the oracle can
+compute one by one:
+  * the first pivots, which the oracle reproduces from the same Philox draws;
+  * factor rows F[i, :] for sampled rows i, which are fixed once the pivots are
+    (F[i, :] = L^{-1} H[S, i] with L the Cholesky factor of H_SS);
+  * W and O for sampled queries from the GPU's pivots (given the pivots, W and O are unique);
+  * properties at any size: distinct pivots, full rank, non-increasing trace, no flags."""
+import numpy as np
+import pytest
+
+from coreset_head_rpcholesky_amd import synth
+from oracle import philox
+from oracle import wildcat as ow
+from tests.gpu_util import TOL, dev, host, rel, snapped
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wc():
+    import torch  # noqa: F401
+
+    from coreset_head_rpcholesky_amd import binding
+    return binding
+
+
+def forward_graph(wc, Q, K, V, r, u_forced=None, seed=42):
+    """wc_forward captured in a HIP graph and replayed, as bench.py launches it."""
+    import torch
+
+    H, m, d = Q.shape
+    p = wc.problem(H, K.shape[1], m, d, V.shape[2], r, Q.dtype)
+    ws = wc.workspace(p, Q.device)
+    out = wc.wc_forward(Q, K, V, r, u_forced=u_forced, seed=seed, ws=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            wc.wc_forward(Q, K, V, r, u_forced=u_forced, seed=seed, ws=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,heads", [("vit197", None), ("iid1k", None), ("img4096", None)])
+def test_elementwise_full(wc, name, heads):
+    w = synth.WORKLOADS[name]
+    Q, K, V = synth.make_inputs(name, heads=heads)
+    U = snapped(K, w.r)
+    out = forward_graph(wc, dev(Q, w.dtype), dev(K, w.dtype), dev(V, w.dtype), w.r, u_forced=dev(U))
+    O, piv, rank, flags = host(out["O"]), host(out["pivots"]), host(out["rank"]), host(out["flags"])
+    assert np.all(rank == w.r) and np.all(flags == 0)
+    worst = 0.0
+    for h in range(K.shape[0]):
+        ref = ow.forward(Q[h], K[h], V[h], w.r, U[h])
+        assert np.array_equal(piv[h], ref["pivots"]), h
+        e = rel(O[h], ref["O"])
+        worst = max(worst, e)
+        assert e < TOL[w.dtype], (h, e)
+    print(f"{name}: {K.shape[0]} heads, pivots exact, worst relative error {worst:.2e}")
+
+
+def test_vit197_seeded_mode(wc):
+    """The bench's own mode (Philox seed 42): the device draws the oracle's uniforms, so the
+    pivots agree wherever no draw falls within rounding of an interval end."""
+    w = synth.WORKLOADS["vit197"]
+    Q, K, V = synth.make_inputs("vit197")
+    out = forward_graph(wc, dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), w.r, seed=42)
+    O, piv = host(out["O"]), host(out["pivots"])
+    agree = 0
+    for h in range(w.heads):
+        ref = ow.forward(Q[h], K[h], V[h], w.r, philox.pivot_uniforms(42, h, w.r))
+        if np.array_equal(piv[h], ref["pivots"]):
+            agree += 1
+            assert rel(O[h], ref["O"]) < TOL["bf16"], h
+    assert agree >= w.heads - 2, agree
+
+
+@pytest.mark.parametrize("name,check_heads,nq", [("kv32k", (0, 31), None), ("long128k", (0, 7), 256)])
+def test_sampled_full(wc, name, check_heads, nq):
+    import torch
+
+    w = synth.WORKLOADS[name]
+    Q, K, V = synth.make_inputs(name)
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    out = forward_graph(wc, Qd, Kd, Vd, w.r, seed=42)
+    O, piv = host(out["O"]), host(out["pivots"])
+    assert np.all(host(out["rank"]) == w.r) and np.all(host(out["flags"]) == 0)
+    del out
+    torch.cuda.empty_cache()
+    rpc = wc.wc_rpcholesky(Kd, w.r, seed=42, with_diag=False)
+    assert np.array_equal(host(rpc["pivots"]), piv)  # the standalone call and the forward agree
+    trace = host(rpc["trace"])
+    rng = np.random.default_rng(0)
+    beta = 1.0 / np.sqrt(w.d)
+    for h in check_heads:
+        S = piv[h]
+        assert len(set(S.tolist())) == w.r and S.min() >= 0 and S.max() < w.n
+        assert np.all(np.diff(trace[h]) <= 1e-6 * trace[h][0])
+        # first pivots from the same Philox draws
+        ref3 = ow.rpcholesky(K[h], 3, philox.pivot_uniforms(42, h, 3), beta)
+        assert np.array_equal(S[:3], ref3["pivots"])
+        # sampled factor rows, fixed by the pivots
+        rows = np.concatenate([rng.choice(w.n, 48, replace=False), S[[0, 1, w.r // 2, w.r - 1]]])
+        Fr, _ = ow.factor_rows_given_pivots(K[h], S, rows, beta)
+        Fg = host(rpc["F"][h][:, torch.as_tensor(rows, device="cuda")]).T
+        assert rel(Fg, Fr) < 1e-3, rel(Fg, Fr)
+        # weights and sampled outputs from the GPU's pivots
+        Wo = ow.weights(K[h], V[h], S, beta)
+        qs = np.arange(w.m) if nq is None else rng.choice(w.m, nq, replace=False)
+        Oo, den, kappa = ow.attend(Q[h][qs], K[h], S, Wo, beta)
+        ok = kappa < 1e6
+        assert rel(O[h][qs][ok], Oo[ok]) < TOL["bf16"], rel(O[h][qs][ok], Oo[ok])

@@ -184,3 +184,34 @@ def test_deterministic(wc, n, dtype):
     b = wc.wc_forward(*args, seed=77)
     assert np.array_equal(host(a["pivots"]), host(b["pivots"]))
     assert np.array_equal(host(a["O"]), host(b["O"]))
+
+
+@pytest.mark.parametrize("n,dtype", [(197, "bf16"), (1500, "bf16"), (600, "f32")])
+def test_graph_replay_matches_eager(wc, n, dtype):
+    """The forward captured in a HIP graph gives the eager result on every replay (the path
+    records no memset nodes); eager work and synchronisations run between the replays."""
+    import torch
+
+    Q, K, V = synth.random_inputs(4, n, 70, 64, 64, seed=13, dtype=dtype, kind="mixture")
+    Qd, Kd, Vd = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    p = wc.problem(4, n, 70, 64, 64, 32, Qd.dtype)
+    ws = wc.workspace(p, "cuda")
+    out = wc.wc_forward(Qd, Kd, Vd, 32, seed=99, ws=ws)
+    ref = {k: v.clone() for k, v in out.items()}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            wc.wc_forward(Qd, Kd, Vd, 32, seed=99, ws=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for v in out.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (rep, k)
+        wc.wc_forward(Qd, Kd, Vd, 32, seed=5, ws=ws)  # unrelated eager work in between
+        torch.cuda.synchronize()
