@@ -29,22 +29,27 @@ __global__ void __launch_bounds__(256) gather_L_kernel(WeightsArgs a) {
     L[j] = (t < rk && j <= t) ? F[(size_t)j * a.n + s] : 0.f;
 }
 
-// X partial over rows [i0, i0 + chunk_rows) for 64 rows of X (j0 .. j0+63).
-// 4 waves; MFMA tiles (jt in {0,1}) x (ct < DV/32), tile k of wave w is w + 4k.
-template <typename TV, int DV>
+// X partial over rows [i0, i0 + chunk_rows) for 128 rows of X (j0 .. j0 + 127).
+// 4 waves; MFMA tiles (jt < 4) x (ct < DV/32), tile k of wave w is w + 4k.  Each 64-row
+// sub-pass of F (hi/lo bf16) and V^T is staged in LDS; the next sub-pass is loaded into
+// registers while the matrix cores work on the current one.
+constexpr int XJG = 128;  // rows of X per workgroup
+constexpr int XSUB = 64;  // key rows per sub-pass
+
+template <typename TV, int DV, bool VEC>
 __global__ void __launch_bounds__(256) x_partial_kernel(WeightsArgs a) {
-  constexpr int SUB = 64;               // rows staged per pass
-  constexpr int SP = SUB + 8;           // padded LDS row (bf16)
+  constexpr int SP = XSUB + 8;          // padded LDS row (bf16)
   constexpr bool SPLITV = sizeof(TV) == 4;
-  constexpr int NCT = DV / 32, NTILE = 2 * NCT, TPW = NTILE / 4;
-  __shared__ __attribute__((aligned(16))) __bf16 sFh[64 * SP];
-  __shared__ __attribute__((aligned(16))) __bf16 sFl[64 * SP];
+  constexpr int NCT = DV / 32, NTILE = 4 * NCT, TPW = NTILE / 4;
+  constexpr int VPT = DV / 4;           // V elements per thread per sub-pass (row ii, quarter cq)
+  __shared__ __attribute__((aligned(16))) __bf16 sFh[XJG * SP];
+  __shared__ __attribute__((aligned(16))) __bf16 sFl[XJG * SP];
   __shared__ __attribute__((aligned(16))) __bf16 sVh[DV * SP];
   __shared__ __attribute__((aligned(16))) __bf16 sVl[SPLITV ? DV * SP : 8];
   const int jg = blockIdx.x, chunk = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int n = a.n, r = a.r;
-  const int j0 = jg * 64;
+  const int j0 = jg * XJG;
   const int i0 = chunk * a.chunk_rows;
   const int i1 = min(n, i0 + a.chunk_rows);
   const float* F = a.F + (size_t)h * r * n;
@@ -54,50 +59,91 @@ __global__ void __launch_bounds__(256) x_partial_kernel(WeightsArgs a) {
   for (int k = 0; k < TPW; ++k)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
-  // ones column: thread owns row j0 + tid/4 and a quarter of each staged pass
+  // F: thread owns row j0 + fj, keys 32 fq .. 32 fq + 31 of the sub-pass
+  const int fj = tid >> 1, fq = tid & 1;
+  const bool frow = j0 + fj < r;
+  // V: thread owns key row ii of the sub-pass, value columns VPT cq .. VPT cq + VPT - 1
+  const int ii = tid >> 2, cq = tid & 3;
   float colsum = 0.f;
-  const int fj = tid >> 2, fq = tid & 3;
-  for (int ib = i0; ib < i1; ib += SUB) {
-    __syncthreads();
-    // stage F[j0 + fj][ib + 16 fq .. +16] as hi/lo bf16
-    {
-      const int j = j0 + fj;
+  float fr[32];
+  float vr[VPT];
+  auto load = [&](int ib) {
+    const int ibase = ib + 32 * fq;
+    const float* src = F + (size_t)(j0 + fj) * n + ibase;
+    if (VEC && frow && ibase + 32 <= i1) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = ib + 16 * fq + e;
-        const float f = (j < r && i < i1) ? F[(size_t)j * n + i] : 0.f;
-        colsum += f;
-        __bf16 hi, lo;
-        split_bf16(f, hi, lo);
-        sFh[fj * SP + 16 * fq + e] = hi;
-        sFl[fj * SP + 16 * fq + e] = lo;
+      for (int q = 0; q < 8; ++q) {
+        const float4 x = reinterpret_cast<const float4*>(src)[q];
+        fr[4 * q] = x.x; fr[4 * q + 1] = x.y; fr[4 * q + 2] = x.z; fr[4 * q + 3] = x.w;
       }
-    }
-    // stage V[ib .. ib+63][:] transposed: thread handles row ib + tid/4, a quarter of DV
-    {
-      const int ii = tid >> 2, cq = tid & 3;
-      const int i = ib + ii;
+    } else {
 #pragma unroll
-      for (int e = 0; e < DV / 4; ++e) {
-        const int c = cq * (DV / 4) + e;
-        const float v = (i < i1) ? ld_elem<TV>(V + (size_t)i * DV + c) : 0.f;
-        if (SPLITV) {
-          __bf16 hi, lo;
-          split_bf16(v, hi, lo);
-          sVh[c * SP + ii] = hi;
-          sVl[c * SP + ii] = lo;
-        } else {
-          sVh[c * SP + ii] = (__bf16)v;
+      for (int e = 0; e < 32; ++e) fr[e] = (frow && ibase + e < i1) ? src[e] : 0.f;
+    }
+    const int i = ib + ii;
+    const TV* vs = V + (size_t)i * DV + cq * VPT;
+    if (i < i1) {
+      if constexpr (sizeof(TV) == 2) {
+#pragma unroll
+        for (int q = 0; q < VPT / 8; ++q) {
+          const uint4 x = reinterpret_cast<const uint4*>(vs)[q];
+          const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vr[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+            vr[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < VPT / 4; ++q) {
+          const float4 x = reinterpret_cast<const float4*>(vs)[q];
+          vr[4 * q] = x.x; vr[4 * q + 1] = x.y; vr[4 * q + 2] = x.z; vr[4 * q + 3] = x.w;
         }
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) vr[e] = 0.f;
+    }
+  };
+  if (i0 < i1) load(i0);
+  for (int ib = i0; ib < i1; ib += XSUB) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        colsum += fr[8 * q + e];
+        __bf16 hi, lo;
+        split_bf16(fr[8 * q + e], hi, lo);
+        hv[e] = hi;
+        lv[e] = lo;
+      }
+      *reinterpret_cast<bf16x8*>(sFh + fj * SP + 32 * fq + 8 * q) = hv;
+      *reinterpret_cast<bf16x8*>(sFl + fj * SP + 32 * fq + 8 * q) = lv;
+    }
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) {
+      const int c = cq * VPT + e;
+      if (SPLITV) {
+        __bf16 hi, lo;
+        split_bf16(vr[e], hi, lo);
+        sVh[c * SP + ii] = hi;
+        sVl[c * SP + ii] = lo;
+      } else {
+        sVh[c * SP + ii] = (__bf16)vr[e];
+      }
     }
     __syncthreads();
+    if (ib + XSUB < i1) load(ib + XSUB);  // next sub-pass in flight during the MFMAs
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       const int tile = wid + 4 * k;
       const int jt = tile / NCT, ct = tile % NCT;
+      if (j0 + jt * 32 >= r) continue;
 #pragma unroll
-      for (int kk = 0; kk < SUB; kk += 16) {
+      for (int kk = 0; kk < XSUB; kk += 16) {
         const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sFh + (jt * 32 + l32) * SP + kk + 8 * g);
         const bf16x8 al = *reinterpret_cast<const bf16x8*>(sFl + (jt * 32 + l32) * SP + kk + 8 * g);
         const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sVh + (ct * 32 + l32) * SP + kk + 8 * g);
@@ -122,8 +168,7 @@ __global__ void __launch_bounds__(256) x_partial_kernel(WeightsArgs a) {
     }
   }
   colsum += __shfl_xor(colsum, 1, 64);
-  colsum += __shfl_xor(colsum, 2, 64);
-  if (fq == 0 && j0 + fj < r) X[(size_t)(j0 + fj) * (DV + 1) + DV] = colsum;
+  if (fq == 0 && frow) X[(size_t)(j0 + fj) * (DV + 1) + DV] = colsum;
 }
 
 __global__ void __launch_bounds__(256) x_reduce_kernel(WeightsArgs a) {
@@ -214,7 +259,11 @@ static hipError_t run_weights(const WeightsArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(gather_L_kernel, dim3(a.r, a.H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((x_partial_kernel<TV, DV>), dim3((a.r + 63) / 64, a.nchunk, a.H), dim3(256), 0, st, a);
+  const dim3 xg((a.r + XJG - 1) / XJG, a.nchunk, a.H);
+  if (a.n % 4 == 0 && a.chunk_rows % 4 == 0)
+    hipLaunchKernelGGL((x_partial_kernel<TV, DV, true>), xg, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((x_partial_kernel<TV, DV, false>), xg, dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t per = (size_t)a.r * (DV + 1);
   hipLaunchKernelGGL(x_reduce_kernel, dim3((unsigned)((per + 255) / 256), a.H), dim3(256), 0, st, a);
