@@ -67,10 +67,13 @@ Layout make_layout(const wc_problem& p) {
   crow = (crow + 63) & ~size_t(63);
   L.chunk_rows = (int)crow;
   L.nchunk = (int)((n + crow - 1) / crow);
-  // attention: split the coreset when the queries alone give too few workgroups
-  L.rp = (int)((r + 31) & ~size_t(31));
-  const size_t nchk = (size_t)L.rp / 32;
-  const size_t qtiles = (m + 127) / 128;
+  // attention: split the coreset when the queries alone give too few workgroups (chunks of
+  // 64 coreset rows, 256 queries per workgroup for bf16, 32 and 128 for fp32)
+  L.rp = (int)((r + 63) & ~size_t(63));
+  const size_t cw = p.dtype == WC_BF16 ? 64 : 32;
+  const size_t qw = p.dtype == WC_BF16 ? 128 * wc::kAttendNQ : 128;
+  const size_t nchk = (size_t)L.rp / cw;
+  const size_t qtiles = (m + qw - 1) / qw;
   size_t nsplit = 1;
   if (qtiles * H < 512 && qtiles > 0) {
     nsplit = (512 + qtiles * H - 1) / (qtiles * H);

@@ -31,7 +31,7 @@ template <typename T, int D, int DV>
 __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int rp = (a.r + 31) & ~31;
+  const int rp = (a.r + 63) & ~63;
   const int rk = a.rank[h];
   const bool valid = j < rk;
   const int s = valid ? a.pivots[(size_t)h * a.r + j] : 0;
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   __shared__ float sWd[32];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y, sp = blockIdx.z;
-  const int m = a.m, rp = (a.r + 31) & ~31, nchk = rp / 32;
+  const int m = a.m, rp = (a.r + 63) & ~63, nchk = rp / 32;
   const int q = blockIdx.x * 128 + wid * 32 + l32;
   const bool qv = q < m;
   const float bl2e = a.beta_log2e;
@@ -173,6 +173,165 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   }
 }
 
+// bf16 inputs: each wave takes NQ x 32 queries; coreset chunks of 64 are double-buffered in
+// LDS and the next chunk is loaded into registers while the current one is computed; one
+// barrier per chunk.
+template <int D, int DV, int NQ>
+__global__ void __launch_bounds__(256) attend_bf16_kernel(AttendArgs a) {
+  constexpr int CH = 64, KP = D + 8, WP = CH + 8, NCT = DV / 32;
+  constexpr int QPB = 4 * 32 * NQ;  // queries per workgroup
+  constexpr int KV = CH * D / 8 / 256;   // uint4 of K_S per thread per chunk
+  constexpr int WV = DV * CH / 8 / 256;  // uint4 of W^T per thread per chunk
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][CH * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 sW[2][DV * WP];
+  __shared__ float sWd[2][CH];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int h = blockIdx.y, sp = blockIdx.z;
+  const int m = a.m, rp = (a.r + 63) & ~63, nchk = rp / CH;
+  const float bl2e = a.beta_log2e;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * m * D;
+  const int qbase = blockIdx.x * QPB + wid * 32 * NQ;
+
+  bf16x8 qb[NQ][D / 16];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const int q = qbase + 32 * s + l32;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (q < m) {
+        qb[s][kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)0.f;
+      }
+    }
+  }
+  f32x16 y[NQ][NCT];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) y[s][ct][v] = 0.f;
+  float den[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) den[s] = 0.f;
+  const int per = (nchk + a.nsplit - 1) / a.nsplit;
+  const int cb = sp * per, ce = min(nchk, cb + per);
+  const uint16_t* KSh = a.KSh + (size_t)h * rp * D;
+  const uint16_t* Wph = a.Wph + (size_t)h * DV * rp;
+  const float* Wden = a.Wden + (size_t)h * rp;
+  uint4 kreg[KV], wreg[WV];
+  float dreg = 0.f;
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = tid + 256 * i, jj = e / (D / 8), k8 = e % (D / 8);
+      kreg[i] = *reinterpret_cast<const uint4*>(KSh + (size_t)(c * CH + jj) * D + 8 * k8);
+    }
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int e = tid + 256 * i, cc = e / (CH / 8), k8 = e % (CH / 8);
+      wreg[i] = *reinterpret_cast<const uint4*>(Wph + (size_t)cc * rp + c * CH + 8 * k8);
+    }
+    if (tid < CH) dreg = Wden[c * CH + tid];
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = tid + 256 * i, jj = e / (D / 8), k8 = e % (D / 8);
+      *reinterpret_cast<uint4*>(&sK[buf][jj * KP + 8 * k8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int e = tid + 256 * i, cc = e / (CH / 8), k8 = e % (CH / 8);
+      *reinterpret_cast<uint4*>(&sW[buf][cc * WP + 8 * k8]) = wreg[i];
+    }
+    if (tid < CH) sWd[buf][tid] = dreg;
+  };
+  if (cb < ce) {
+    fetch(cb);
+    store(0);
+  }
+  for (int c = cb; c < ce; ++c) {
+    const int buf = (c - cb) & 1;
+    __syncthreads();
+    // both sub-chunks' score MFMAs are issued first, so the exponentials of one overlap the
+    // matrix-core work of the other
+    constexpr int NSUB = CH / 32;
+    f32x16 sc[NSUB][NQ];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[sub][s][v] = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&sK[buf][(sub * 32 + l32) * KP + 16 * kk + 8 * g]);
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) sc[sub][s] = mfma32(kh, qb[s][kk], sc[sub][s]);
+      }
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      bf16x8 pb[NQ][2];
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = __builtin_amdgcn_exp2f(sc[sub][s][v] * bl2e);
+          den[s] = fmaf(p, sWd[buf][sub * 32 + 8 * (v >> 2) + 4 * g + (v & 3)], den[s]);
+          pb[s][v >> 3][v & 7] = (__bf16)p;
+        }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const bf16x8 wh = *reinterpret_cast<const bf16x8*>(&sW[buf][(ct * 32 + l32) * WP + sub * 32 + 16 * qq + 8 * g]);
+#pragma unroll
+          for (int s = 0; s < NQ; ++s) y[s][ct] = mfma32(wh, pb[s][qq], y[s][ct]);
+        }
+    }
+    if (c + 1 < ce) {  // the other buffer was last read before this iteration's barrier
+      fetch(c + 1);
+      store(buf ^ 1);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const float dn = den[s] + __shfl_xor(den[s], 32, 64);
+    const int q = qbase + 32 * s + l32;
+    if (q >= m) continue;
+    if (a.nsplit == 1) {
+      if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
+      const float inv = 1.0f / dn;
+      uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int col = ct * 32 + 8 * v4 + 4 * g;
+          uint16_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[s][ct][4 * v4 + e] * inv));
+          uint2 pk;
+          pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+          pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+          *reinterpret_cast<uint2*>(O + col) = pk;
+        }
+    } else {
+      float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
+      if (g == 0) Yp[DV] = dn;
+    }
+  }
+}
+
 template <typename T, int DV>
 __global__ void __launch_bounds__(256) attend_reduce_kernel(AttendArgs a) {
   const int h = blockIdx.y;
@@ -194,11 +353,15 @@ __global__ void __launch_bounds__(256) attend_reduce_kernel(AttendArgs a) {
 
 template <typename T, int D, int DV>
 static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
-  const int rp = (a.r + 31) & ~31;
+  static_assert(kAttendNQ == 1 || kAttendNQ == 2, "32 or 64 queries per wave");
+  const int rp = (a.r + 63) & ~63;
   hipLaunchKernelGGL((attend_prep_kernel<T, D, DV>), dim3(rp, a.H), dim3(128), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
-  hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((attend_bf16_kernel<D, DV, kAttendNQ>), dim3((a.m + 128 * kAttendNQ - 1) / (128 * kAttendNQ), a.H, a.nsplit), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.nsplit > 1) {
     hipLaunchKernelGGL((attend_reduce_kernel<T, DV>), dim3((a.m + 255) / 256, a.H), dim3(256), 0, st, a);

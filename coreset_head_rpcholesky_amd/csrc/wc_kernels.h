@@ -91,7 +91,7 @@ struct AttendArgs {
   const int32_t* pivots;
   const int32_t* rank;
   const float* W;         // [H][r][dv+1]
-  uint16_t* KSh;          // ws [H][rp][d]    coreset keys, bf16 hi (rp = r rounded up to 32)
+  uint16_t* KSh;          // ws [H][rp][d]    coreset keys, bf16 hi (rp = r rounded up to 64)
   uint16_t* KSl;          // ws [H][rp][d]    bf16 lo (fp32 inputs only)
   uint16_t* Wph;          // ws [H][dv][rp]   permuted W^T, bf16 hi
   uint16_t* Wpl;          // ws [H][dv][rp]   bf16 lo (fp32 inputs only)
@@ -101,6 +101,7 @@ struct AttendArgs {
   void* O;                // [H][m][dv]
   uint32_t* flags;        // [H]
 };
+constexpr int kAttendNQ = 1;  // 32-query tiles per wave in the bf16 attention kernel
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
 }  // namespace wc
