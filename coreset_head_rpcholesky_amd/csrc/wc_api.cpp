@@ -67,11 +67,11 @@ Layout make_layout(const wc_problem& p) {
   crow = (crow + 63) & ~size_t(63);
   L.chunk_rows = (int)crow;
   L.nchunk = (int)((n + crow - 1) / crow);
-  // attention: split the coreset when the queries alone give too few workgroups (chunks of
-  // 64 coreset rows, 256 queries per workgroup for bf16, 32 and 128 for fp32)
-  L.rp = (int)((r + 63) & ~size_t(63));
-  const size_t cw = p.dtype == WC_BF16 ? 64 : 32;
-  const size_t qw = p.dtype == WC_BF16 ? 128 * wc::kAttendNQ : 128;
+  // attention: split the coreset when the queries alone give too few workgroups (blocks of
+  // 128 coreset rows and 128 queries per workgroup for bf16, 32 and 128 for fp32)
+  L.rp = wc::attend_rows((int)r);
+  const size_t cw = p.dtype == WC_BF16 ? 128 : 32;
+  const size_t qw = 128;
   const size_t nchk = (size_t)L.rp / cw;
   const size_t qtiles = (m + qw - 1) / qw;
   size_t nsplit = 1;

@@ -27,11 +27,23 @@ __device__ __forceinline__ int perm32_a(int j) {
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
+// Tile-major layouts of the staged operands, per head.  K_S is cut into 64-row chunks, each an
+// array [D/8][64 rows][8] of bf16: a chunk is one contiguous block, and the 16-byte pieces that
+// 64 consecutive lanes need for one MFMA operand (same 8 columns, consecutive rows) are
+// consecutive.  W^T (value column cc, permuted coreset position p) likewise, with chunks of 64
+// positions stored as [8][DV][8].
+__device__ __forceinline__ size_t ks_index(int j, int e, int D) {
+  return ((size_t)((j >> 6) * (D / 8) + (e >> 3)) * 64 + (j & 63)) * 8 + (e & 7);
+}
+__device__ __forceinline__ size_t wt_index(int cc, int p, int DV) {
+  return ((size_t)((p >> 6) * 8 + ((p & 63) >> 3)) * DV + cc) * 8 + (p & 7);
+}
+
 template <typename T, int D, int DV>
 __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int rp = (a.r + 63) & ~63;
+  const int rp = attend_rows(a.r);
   const int rk = a.rank[h];
   const bool valid = j < rk;
   const int s = valid ? a.pivots[(size_t)h * a.r + j] : 0;
@@ -40,8 +52,9 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
     const float v = valid ? ld_elem<T>(K + e) : 0.f;
     __bf16 hi, lo;
     split_bf16(v, hi, lo);
-    a.KSh[((size_t)h * rp + j) * D + e] = bf16_bits(hi);
-    if (SPLIT) a.KSl[((size_t)h * rp + j) * D + e] = bf16_bits(lo);
+    const size_t o = (size_t)h * rp * D + ks_index(j, e, D);
+    a.KSh[o] = bf16_bits(hi);
+    if (SPLIT) a.KSl[o] = bf16_bits(lo);
   }
   const int p = perm32_a(j);
   const float* W = a.W + ((size_t)h * a.r + (valid ? j : 0)) * (DV + 1);
@@ -49,8 +62,9 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
     const float w = valid ? W[c] : 0.f;
     __bf16 hi, lo;
     split_bf16(w, hi, lo);
-    a.Wph[((size_t)h * DV + c) * rp + p] = bf16_bits(hi);
-    if (SPLIT) a.Wpl[((size_t)h * DV + c) * rp + p] = bf16_bits(lo);
+    const size_t o = (size_t)h * DV * rp + wt_index(c, p, DV);
+    a.Wph[o] = bf16_bits(hi);
+    if (SPLIT) a.Wpl[o] = bf16_bits(lo);
   }
   if (tid == 0) a.Wden[(size_t)h * rp + j] = valid ? W[DV] : 0.f;
 }
@@ -66,7 +80,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   __shared__ float sWd[32];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y, sp = blockIdx.z;
-  const int m = a.m, rp = (a.r + 63) & ~63, nchk = rp / 32;
+  const int m = a.m, rp = attend_rows(a.r), nchk = rp / 32;
   const int q = blockIdx.x * 128 + wid * 32 + l32;
   const bool qv = q < m;
   const float bl2e = a.beta_log2e;
@@ -99,13 +113,13 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
     __syncthreads();
     for (int e = tid; e < 32 * (D / 8); e += 256) {
       const int jj = e / (D / 8), k8 = e % (D / 8);
-      const size_t src = (size_t)(c * 32 + jj) * D + 8 * k8;
+      const size_t src = ks_index(c * 32 + jj, 8 * k8, D);
       *reinterpret_cast<uint4*>(sKh + jj * KP + 8 * k8) = *reinterpret_cast<const uint4*>(KSh + src);
       if (SPLIT) *reinterpret_cast<uint4*>(sKl + jj * KP + 8 * k8) = *reinterpret_cast<const uint4*>(KSl + src);
     }
     for (int e = tid; e < DV * 4; e += 256) {
       const int cc = e / 4, k8 = e % 4;
-      const size_t src = (size_t)cc * rp + c * 32 + 8 * k8;
+      const size_t src = wt_index(cc, c * 32 + 8 * k8, DV);
       *reinterpret_cast<uint4*>(sWh + cc * WP + 8 * k8) = *reinterpret_cast<const uint4*>(Wph + src);
       if (SPLIT) *reinterpret_cast<uint4*>(sWl + cc * WP + 8 * k8) = *reinterpret_cast<const uint4*>(Wpl + src);
     }
@@ -173,162 +187,199 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   }
 }
 
-// bf16 inputs: each wave takes NQ x 32 queries; coreset chunks of 64 are double-buffered in
-// LDS and the next chunk is loaded into registers while the current one is computed; one
-// barrier per chunk.
-template <int D, int DV, int NQ>
-__global__ void __launch_bounds__(256) attend_bf16_kernel(AttendArgs a) {
-  constexpr int CH = 64, KP = D + 8, WP = CH + 8, NCT = DV / 32;
-  constexpr int QPB = 4 * 32 * NQ;  // queries per workgroup
-  constexpr int KV = CH * D / 8 / 256;   // uint4 of K_S per thread per chunk
-  constexpr int WV = DV * CH / 8 / 256;  // uint4 of W^T per thread per chunk
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][CH * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 sW[2][DV * WP];
-  __shared__ float sWd[2][CH];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int h = blockIdx.y, sp = blockIdx.z;
-  const int m = a.m, rp = (a.r + 63) & ~63, nchk = rp / CH;
-  const float bl2e = a.beta_log2e;
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * m * D;
-  const int qbase = blockIdx.x * QPB + wid * 32 * NQ;
+// bf16 inputs.  Each wave takes 32 queries.  The coreset is walked in 64-row chunks held in
+// two LDS buffers: while chunk c is computed from one buffer, chunk c+1 streams into the other
+// by direct global-to-LDS loads (no staging registers, no LDS store instructions), so one
+// barrier per chunk is the only synchronisation.  A direct load writes 64 consecutive 16-byte
+// LDS units per wave instruction; with the tile-major layouts above a chunk is copied as is, and
+// the operand reads of consecutive lanes hit consecutive units (no bank conflicts).
+typedef __attribute__((address_space(3))) void* lds_void;
+typedef __attribute__((address_space(1))) const void* glb_void;
 
-  bf16x8 qb[NQ][D / 16];
+template <int D, int DV>
+struct AttendChunk {
+  uint4 k[64 * D / 8];   // K_S chunk, [D/8][64][8] bf16
+  uint4 w[DV * 64 / 8];  // W^T chunk, [8][DV][8] bf16
+  float wd[64];          // W[:, dv]
+};
+
+// One direct load: 16 bytes per lane from gptr into LDS at lds + 16 * lane.  Written as an asm
+// statement so the compiler adds no wait of its own between the load and later LDS reads of the
+// other buffer (it cannot tell the two buffers apart); the loads are waited for explicitly
+// (vmcnt(0), then a barrier) before their buffer is read.  The statement has no register
+// outputs, and its address operand is consumed when the instruction issues.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as an immediate the compiler's
+// own wait tracking understands
+constexpr int kVmcnt0 = 0x0F70;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void)const_cast<void*>(p);
+}
+
+template <int D, int DV>
+__device__ __forceinline__ void attend_issue(AttendChunk<D, DV>& b, const uint16_t* KSh, const uint16_t* Wph,
+                                             const float* Wden, int c, int wid, int lane) {
+  constexpr int KI = 64 * D / 8 / 256, WI = DV * 64 / 8 / 256;
+  const char* kbase = reinterpret_cast<const char*>(KSh) + (size_t)c * 64 * D * 2;
+  const char* wbase = reinterpret_cast<const char*>(Wph) + (size_t)c * 64 * DV * 2;
+  const uint32_t lo = 16 * (64 * wid + lane);
 #pragma unroll
-  for (int s = 0; s < NQ; ++s) {
-    const int q = qbase + 32 * s + l32;
+  for (int i = 0; i < KI; ++i) dma16(kbase + 4096 * i + lo, lds_addr(&b.k[64 * (4 * i + wid)]));
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      if (q < m) {
-        qb[s][kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
-      } else {
+  for (int i = 0; i < WI; ++i) dma16(wbase + 4096 * i + lo, lds_addr(&b.w[64 * (4 * i + wid)]));
+  if (wid == 0) dma4(Wden + c * 64 + lane, lds_addr(&b.wd[0]));
+}
+
+// One 64-row chunk for one wave of 32 queries, as two 32-row units u0, u1.  Matrix-core work
+// runs in four phases of eight MFMAs: scores of u0 | scores of u1 | values of u0 | values of
+// u1.  The exponentials of u0 are spread over the scores of u1 and those of u1 over the values
+// of u0, two per MFMA, so vector and matrix units work side by side, and every LDS operand is
+// read one phase before its MFMA.  Scheduling fences keep the compiler to this order.
+template <int D, int DV>
+__device__ __forceinline__ void attend_chunk(const AttendChunk<D, DV>& b, const bf16x8 (&qb)[D / 16],
+                                             f32x16 (&y)[DV / 32], float (&den)[4], float bl2e, int g, int l32) {
+  constexpr int NK = D / 16, NCT = DV / 32, NW = 2 * NCT;
+  static_assert(NK == 4 || NK == 8, "d = 64 or 128");
+  auto kfrag = [&](int u, int kk) { return __builtin_bit_cast(bf16x8, b.k[(2 * kk + g) * 64 + 32 * u + l32]); };
+  auto wfrag = [&](int u, int i) {  // i = 2 ct + qq
+    return __builtin_bit_cast(bf16x8, b.w[(4 * u + 2 * (i & 1) + g) * DV + 32 * (i >> 1) + l32]);
+  };
+  auto wden = [&](int u, int v4) { return *reinterpret_cast<const float4*>(&b.wd[32 * u + 8 * v4 + 4 * g]); };
+  // exponential, normaliser term and bf16 packing of scores v, v+1 of a unit
+  auto expo = [&](const f32x16& sc, const float4 (&wd)[4], bf16x8 (&pb)[2], int v) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)0.f;
-      }
+    for (int e = 0; e < 2; ++e) {
+      const int vv = v + e;
+      const float p = __builtin_amdgcn_exp2f(sc[vv] * bl2e);
+      const float4 w4 = wd[vv >> 2];
+      const float w = (vv & 3) == 0 ? w4.x : (vv & 3) == 1 ? w4.y : (vv & 3) == 2 ? w4.z : w4.w;
+      den[vv & 3] = fmaf(p, w, den[vv & 3]);
+      pb[vv >> 3][vv & 7] = (__bf16)p;
+    }
+  };
+  const f32x16 zero = {};
+  bf16x8 ka[NK], kb[NK], wa[NW], wb[NW];
+  float4 wd0[4], wd1[4];
+  bf16x8 pb0[2], pb1[2];
+  f32x16 s0 = zero, s1 = zero;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) ka[kk] = kfrag(0, kk);
+  __builtin_amdgcn_sched_barrier(0);
+  // phase A: scores of u0; K of u1 read behind them, then W[:, dv] of u0
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    s0 = mfma32(ka[kk], qb[kk], s0);
+    kb[kk] = kfrag(1, kk);
+    if (kk >= NK - 4) wd0[kk - (NK - 4)] = wden(0, kk - (NK - 4));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // phase B: scores of u1; exponentials of u0; W of u0 read, then W[:, dv] of u1
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    s1 = mfma32(kb[kk], qb[kk], s1);
+#pragma unroll
+    for (int i = kk * NW / NK; i < (kk + 1) * NW / NK; ++i) wa[i] = wfrag(0, i);
+    if (kk >= NK - 4) wd1[kk - (NK - 4)] = wden(1, kk - (NK - 4));
+#pragma unroll
+    for (int v = kk * 16 / NK; v < (kk + 1) * 16 / NK; v += 2) expo(s0, wd0, pb0, v);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // phase C: values of u0; exponentials of u1; W of u1 read
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    y[i >> 1] = mfma32(wa[i], pb0[i & 1], y[i >> 1]);
+    wb[i] = wfrag(1, i);
+#pragma unroll
+    for (int v = i * 16 / NW; v < (i + 1) * 16 / NW; v += 2) expo(s1, wd1, pb1, v);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // phase D: values of u1
+#pragma unroll
+  for (int i = 0; i < NW; ++i) y[i >> 1] = mfma32(wb[i], pb1[i & 1], y[i >> 1]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int DV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attend_bf16_kernel(AttendArgs a) {
+  constexpr int NCT = DV / 32;
+  __shared__ AttendChunk<D, DV> sb0, sb1;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y, sp = blockIdx.z;
+  const int m = a.m, rp = attend_rows(a.r);
+  const float bl2e = a.beta_log2e;
+  const int q = blockIdx.x * 128 + wid * 32 + l32;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)h * m + q) * D;
+
+  bf16x8 qb[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (q < m) {
+      qb[kk] = *reinterpret_cast<const bf16x8*>(Q + 16 * kk + 8 * g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[kk][e] = (__bf16)0.f;
     }
   }
-  f32x16 y[NQ][NCT];
+  f32x16 y[NCT];
 #pragma unroll
-  for (int s = 0; s < NQ; ++s)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) y[s][ct][v] = 0.f;
-  float den[NQ];
-#pragma unroll
-  for (int s = 0; s < NQ; ++s) den[s] = 0.f;
-  const int per = (nchk + a.nsplit - 1) / a.nsplit;
-  const int cb = sp * per, ce = min(nchk, cb + per);
+    for (int v = 0; v < 16; ++v) y[ct][v] = 0.f;
+  float den[4] = {0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the query fragments have arrived
+  // the coreset is split over blockIdx.z in blocks of 128 rows: chunk 2b in sb0, 2b+1 in sb1
+  const int nb = rp / 128, per = (nb + a.nsplit - 1) / a.nsplit;
+  const int bb = sp * per, be = min(nb, bb + per);
   const uint16_t* KSh = a.KSh + (size_t)h * rp * D;
   const uint16_t* Wph = a.Wph + (size_t)h * DV * rp;
   const float* Wden = a.Wden + (size_t)h * rp;
-  uint4 kreg[KV], wreg[WV];
-  float dreg = 0.f;
-  auto fetch = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int e = tid + 256 * i, jj = e / (D / 8), k8 = e % (D / 8);
-      kreg[i] = *reinterpret_cast<const uint4*>(KSh + (size_t)(c * CH + jj) * D + 8 * k8);
-    }
-#pragma unroll
-    for (int i = 0; i < WV; ++i) {
-      const int e = tid + 256 * i, cc = e / (CH / 8), k8 = e % (CH / 8);
-      wreg[i] = *reinterpret_cast<const uint4*>(Wph + (size_t)cc * rp + c * CH + 8 * k8);
-    }
-    if (tid < CH) dreg = Wden[c * CH + tid];
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int e = tid + 256 * i, jj = e / (D / 8), k8 = e % (D / 8);
-      *reinterpret_cast<uint4*>(&sK[buf][jj * KP + 8 * k8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < WV; ++i) {
-      const int e = tid + 256 * i, cc = e / (CH / 8), k8 = e % (CH / 8);
-      *reinterpret_cast<uint4*>(&sW[buf][cc * WP + 8 * k8]) = wreg[i];
-    }
-    if (tid < CH) sWd[buf][tid] = dreg;
-  };
-  if (cb < ce) {
-    fetch(cb);
-    store(0);
-  }
-  for (int c = cb; c < ce; ++c) {
-    const int buf = (c - cb) & 1;
+  if (bb < be) attend_issue(sb0, KSh, Wph, Wden, 2 * bb, wid, lane);
+  // Before reading a buffer every wave waits for its own loads into it and then meets the
+  // others at the barrier; the barrier also tells every wave that the other buffer's previous
+  // chunk has been read by all, so the next chunk's loads may be issued into it.
+  for (int b = bb; b < be; ++b) {
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    // both sub-chunks' score MFMAs are issued first, so the exponentials of one overlap the
-    // matrix-core work of the other
-    constexpr int NSUB = CH / 32;
-    f32x16 sc[NSUB][NQ];
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-      for (int s = 0; s < NQ; ++s)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sc[sub][s][v] = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&sK[buf][(sub * 32 + l32) * KP + 16 * kk + 8 * g]);
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) sc[sub][s] = mfma32(kh, qb[s][kk], sc[sub][s]);
-      }
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      bf16x8 pb[NQ][2];
-#pragma unroll
-      for (int s = 0; s < NQ; ++s)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(sc[sub][s][v] * bl2e);
-          den[s] = fmaf(p, sWd[buf][sub * 32 + 8 * (v >> 2) + 4 * g + (v & 3)], den[s]);
-          pb[s][v >> 3][v & 7] = (__bf16)p;
-        }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const bf16x8 wh = *reinterpret_cast<const bf16x8*>(&sW[buf][(ct * 32 + l32) * WP + sub * 32 + 16 * qq + 8 * g]);
-#pragma unroll
-          for (int s = 0; s < NQ; ++s) y[s][ct] = mfma32(wh, pb[s][qq], y[s][ct]);
-        }
-    }
-    if (c + 1 < ce) {  // the other buffer was last read before this iteration's barrier
-      fetch(c + 1);
-      store(buf ^ 1);
-    }
+    attend_issue(sb1, KSh, Wph, Wden, 2 * b + 1, wid, lane);
+    attend_chunk<D, DV>(sb0, qb, y, den, bl2e, g, l32);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    if (b + 1 < be) attend_issue(sb0, KSh, Wph, Wden, 2 * b + 2, wid, lane);
+    attend_chunk<D, DV>(sb1, qb, y, den, bl2e, g, l32);
   }
+  float dn = (den[0] + den[1]) + (den[2] + den[3]);
+  dn += __shfl_xor(dn, 32, 64);
+  if (q >= m) return;
+  if (a.nsplit == 1) {
+    if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
+    const float inv = 1.0f / dn;
+    uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
 #pragma unroll
-  for (int s = 0; s < NQ; ++s) {
-    const float dn = den[s] + __shfl_xor(den[s], 32, 64);
-    const int q = qbase + 32 * s + l32;
-    if (q >= m) continue;
-    if (a.nsplit == 1) {
-      if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
-      const float inv = 1.0f / dn;
-      uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int col = ct * 32 + 8 * v4 + 4 * g;
+        uint16_t o[4];
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int col = ct * 32 + 8 * v4 + 4 * g;
-          uint16_t o[4];
+        for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[ct][4 * v4 + e] * inv));
+        uint2 pk;
+        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *reinterpret_cast<uint2*>(O + col) = pk;
+      }
+  } else {
+    float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[s][ct][4 * v4 + e] * inv));
-          uint2 pk;
-          pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-          pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-          *reinterpret_cast<uint2*>(O + col) = pk;
-        }
-    } else {
-      float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
-      if (g == 0) Yp[DV] = dn;
-    }
+      for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[ct][v];
+    if (g == 0) Yp[DV] = dn;
   }
 }
 
@@ -353,13 +404,12 @@ __global__ void __launch_bounds__(256) attend_reduce_kernel(AttendArgs a) {
 
 template <typename T, int D, int DV>
 static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
-  static_assert(kAttendNQ == 1 || kAttendNQ == 2, "32 or 64 queries per wave");
-  const int rp = (a.r + 63) & ~63;
+  const int rp = attend_rows(a.r);
   hipLaunchKernelGGL((attend_prep_kernel<T, D, DV>), dim3(rp, a.H), dim3(128), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((attend_bf16_kernel<D, DV, kAttendNQ>), dim3((a.m + 128 * kAttendNQ - 1) / (128 * kAttendNQ), a.H, a.nsplit), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

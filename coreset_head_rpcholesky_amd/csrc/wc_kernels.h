@@ -91,17 +91,19 @@ struct AttendArgs {
   const int32_t* pivots;
   const int32_t* rank;
   const float* W;         // [H][r][dv+1]
-  uint16_t* KSh;          // ws [H][rp][d]    coreset keys, bf16 hi (rp = r rounded up to 64)
-  uint16_t* KSl;          // ws [H][rp][d]    bf16 lo (fp32 inputs only)
-  uint16_t* Wph;          // ws [H][dv][rp]   permuted W^T, bf16 hi
-  uint16_t* Wpl;          // ws [H][dv][rp]   bf16 lo (fp32 inputs only)
+  uint16_t* KSh;          // ws [H][rp*d]     coreset keys, bf16 hi, tile-major (rp = attend_rows(r))
+  uint16_t* KSl;          // ws [H][rp*d]     bf16 lo (fp32 inputs only)
+  uint16_t* Wph;          // ws [H][dv*rp]    permuted W^T, bf16 hi, tile-major
+  uint16_t* Wpl;          // ws [H][dv*rp]    bf16 lo (fp32 inputs only)
   float* Wden;            // ws [H][rp]       W[:, dv]
   float* Ypart;           // ws [H][nsplit][m][dv+1] partial sums when nsplit > 1
   int nsplit;
   void* O;                // [H][m][dv]
   uint32_t* flags;        // [H]
 };
-constexpr int kAttendNQ = 1;  // 32-query tiles per wave in the bf16 attention kernel
+// coreset rows as the attention kernels store them: r rounded up to whole 128-row blocks
+// (padding rows carry zero weight)
+__host__ __device__ inline int attend_rows(int r) { return (r + 127) & ~127; }
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
 }  // namespace wc
