@@ -23,8 +23,7 @@ ARCH = os.environ.get("WC_OFFLOAD_ARCH", "gfx950")
 # (source, object name, extra defines): the resident kernel is built once per (d, dv).
 SOURCES = [("wc_api.cpp", "wc_api", []), ("wc_stream.hip", "wc_stream", []),
            ("wc_weights.hip", "wc_weights", []),
-    # matrix-core accumulators stay in VGPRs: the attention reads them on the vector units
-    ("wc_attend.hip", "wc_attend", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"])] + [
+    ("wc_attend.hip", "wc_attend", [])] + [
     ("wc_resident.hip", f"wc_resident_{d}_{dv}", [f"-DWC_RES_D={d}", f"-DWC_RES_DV={dv}"])
     for d in (64, 128) for dv in (64, 128)]
 

@@ -44,7 +44,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int rows, nblk, nchunk, chunk_rows, nsplit, rp;
-  size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Ypart;
+  size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Wdh, Ypart;
   size_t total;
 };
 
@@ -67,11 +67,11 @@ Layout make_layout(const wc_problem& p) {
   crow = (crow + 63) & ~size_t(63);
   L.chunk_rows = (int)crow;
   L.nchunk = (int)((n + crow - 1) / crow);
-  // attention: split the coreset when the queries alone give too few workgroups (blocks of
-  // 128 coreset rows and 128 queries per workgroup for bf16, 32 and 128 for fp32)
+  // attention: split the coreset when the queries alone give too few workgroups (chunks of
+  // 64 coreset rows and 256 queries per workgroup for bf16, 32 and 128 for fp32)
   L.rp = wc::attend_rows((int)r);
-  const size_t cw = p.dtype == WC_BF16 ? 128 : 32;
-  const size_t qw = 128;
+  const size_t cw = p.dtype == WC_BF16 ? 64 : 32;
+  const size_t qw = p.dtype == WC_BF16 ? 256 : 128;
   const size_t nchk = (size_t)L.rp / cw;
   const size_t qtiles = (m + qw - 1) / qw;
   size_t nsplit = 1;
@@ -100,6 +100,7 @@ Layout make_layout(const wc_problem& p) {
   L.Wph = take(H * p.dv * L.rp * 2);
   L.Wpl = take(H * p.dv * L.rp * 2);
   L.Wden = take(H * L.rp * 4);
+  L.Wdh = take(H * L.rp * 2);
   L.Ypart = take(L.nsplit > 1 ? H * L.nsplit * m * nc * 4 : 0);
   L.total = off;
   return L;
@@ -170,6 +171,7 @@ hipError_t run_attend(const wc_problem& p, const Layout& L, void* ws, const void
   a.Wph = at<uint16_t>(ws, L.Wph);
   a.Wpl = p.dtype == WC_F32 ? at<uint16_t>(ws, L.Wpl) : nullptr;
   a.Wden = at<float>(ws, L.Wden);
+  a.Wdh = at<uint16_t>(ws, L.Wdh);
   a.Ypart = L.nsplit > 1 ? at<float>(ws, L.Ypart) : nullptr;
   a.nsplit = L.nsplit;
   a.O = O; a.flags = flags;

@@ -66,7 +66,11 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
     a.Wph[o] = bf16_bits(hi);
     if (SPLIT) a.Wpl[o] = bf16_bits(lo);
   }
-  if (tid == 0) a.Wden[(size_t)h * rp + j] = valid ? W[DV] : 0.f;
+  if (tid == 0) {
+    const float wd = valid ? W[DV] : 0.f;
+    a.Wden[(size_t)h * rp + j] = wd;
+    a.Wdh[(size_t)h * rp + p] = bf16_bits((__bf16)wd);
+  }
 }
 
 template <typename T, int D, int DV>
@@ -187,25 +191,35 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   }
 }
 
-// bf16 inputs.  Each wave takes 32 queries.  The coreset is walked in 64-row chunks held in
-// two LDS buffers: while chunk c is computed from one buffer, chunk c+1 streams into the other
-// by direct global-to-LDS loads (no staging registers, no LDS store instructions), so one
-// barrier per chunk is the only synchronisation.  A direct load writes 64 consecutive 16-byte
-// LDS units per wave instruction; with the tile-major layouts above a chunk is copied as is, and
-// the operand reads of consecutive lanes hit consecutive units (no bank conflicts).
+// bf16 inputs.  A workgroup takes 256 queries (kAttendWaves waves of kAttendNQ x 32).  The
+// coreset is walked in 64-row chunks through a ring of three LDS buffers filled by direct
+// global-to-LDS loads (no staging registers, no LDS store instructions): while chunk c is in
+// use, chunk c+1 is resident and chunk c+2 is loading, so one barrier per chunk is the only
+// synchronisation.  With the tile-major layouts above a chunk is copied as is, and the operand
+// reads of consecutive lanes hit consecutive 16-byte units (no bank conflicts).
 typedef __attribute__((address_space(3))) void* lds_void;
-typedef __attribute__((address_space(1))) const void* glb_void;
+
+#ifndef WC_ATTEND_NQ
+#define WC_ATTEND_NQ 1
+#endif
+constexpr int kAttendNQ = WC_ATTEND_NQ;          // groups of 32 queries per wave
+constexpr int kAttendWaves = 8 / kAttendNQ;      // waves per workgroup
+constexpr int kAttendQueries = 256;              // queries per workgroup
+#ifndef WC_ATTEND_PREFETCH
+#define WC_ATTEND_PREFETCH 2
+#endif
+constexpr int kAttendPrefetch = WC_ATTEND_PREFETCH;  // LDS operand reads run this many MFMAs of their kind ahead
 
 template <int D, int DV>
 struct AttendChunk {
   uint4 k[64 * D / 8];   // K_S chunk, [D/8][64][8] bf16
   uint4 w[DV * 64 / 8];  // W^T chunk, [8][DV][8] bf16
-  float wd[64];          // W[:, dv]
+  uint4 wd[8];           // W[:, dv] in bf16, permuted like the columns of W^T
 };
 
 // One direct load: 16 bytes per lane from gptr into LDS at lds + 16 * lane.  Written as an asm
-// statement so the compiler adds no wait of its own between the load and later LDS reads of the
-// other buffer (it cannot tell the two buffers apart); the loads are waited for explicitly
+// statement so the compiler adds no wait of its own between the load and later LDS reads of
+// other buffers (it cannot tell the buffers apart); the loads are waited for explicitly
 // (vmcnt(0), then a barrier) before their buffer is read.  The statement has no register
 // outputs, and its address operand is consumed when the instruction issues.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
@@ -223,163 +237,195 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 template <int D, int DV>
 __device__ __forceinline__ void attend_issue(AttendChunk<D, DV>& b, const uint16_t* KSh, const uint16_t* Wph,
-                                             const float* Wden, int c, int wid, int lane) {
-  constexpr int KI = 64 * D / 8 / 256, WI = DV * 64 / 8 / 256;
+                                             const uint16_t* Wdh, int c, int wid, int lane) {
+  constexpr int KI = D / (8 * kAttendWaves), WI = DV / (8 * kAttendWaves);  // 1 KB wave instructions per tile
   const char* kbase = reinterpret_cast<const char*>(KSh) + (size_t)c * 64 * D * 2;
   const char* wbase = reinterpret_cast<const char*>(Wph) + (size_t)c * 64 * DV * 2;
-  const uint32_t lo = 16 * (64 * wid + lane);
+  const uint32_t lo = 16 * lane;
 #pragma unroll
-  for (int i = 0; i < KI; ++i) dma16(kbase + 4096 * i + lo, lds_addr(&b.k[64 * (4 * i + wid)]));
+  for (int i = 0; i < KI; ++i)
+    dma16(kbase + 1024 * (kAttendWaves * i + wid) + lo, lds_addr(&b.k[64 * (kAttendWaves * i + wid)]));
 #pragma unroll
-  for (int i = 0; i < WI; ++i) dma16(wbase + 4096 * i + lo, lds_addr(&b.w[64 * (4 * i + wid)]));
-  if (wid == 0) dma4(Wden + c * 64 + lane, lds_addr(&b.wd[0]));
+  for (int i = 0; i < WI; ++i)
+    dma16(wbase + 1024 * (kAttendWaves * i + wid) + lo, lds_addr(&b.w[64 * (kAttendWaves * i + wid)]));
+  if (wid == 0 && lane < 32) dma4(Wdh + c * 64 + 2 * lane, lds_addr(&b.wd[0]));
 }
 
-// One 64-row chunk for one wave of 32 queries, as two 32-row units u0, u1.  Matrix-core work
-// runs in four phases of eight MFMAs: scores of u0 | scores of u1 | values of u0 | values of
-// u1.  The exponentials of u0 are spread over the scores of u1 and those of u1 over the values
-// of u0, two per MFMA, so vector and matrix units work side by side, and every LDS operand is
-// read one phase before its MFMA.  Scheduling fences keep the compiler to this order.
-template <int D, int DV>
-__device__ __forceinline__ void attend_chunk(const AttendChunk<D, DV>& b, const bf16x8 (&qb)[D / 16],
-                                             f32x16 (&y)[DV / 32], float (&den)[4], float bl2e, int g, int l32) {
-  constexpr int NK = D / 16, NCT = DV / 32, NW = 2 * NCT;
-  static_assert(NK == 4 || NK == 8, "d = 64 or 128");
-  auto kfrag = [&](int u, int kk) { return __builtin_bit_cast(bf16x8, b.k[(2 * kk + g) * 64 + 32 * u + l32]); };
-  auto wfrag = [&](int u, int i) {  // i = 2 ct + qq
-    return __builtin_bit_cast(bf16x8, b.w[(4 * u + 2 * (i & 1) + g) * DV + 32 * (i >> 1) + l32]);
+// One pipeline step of one wave (NQ groups of 32 queries) at coreset unit u (32 rows): the
+// scores of unit u+1 and the values of unit u-1 on the matrix cores, and the exponentials of
+// unit u on the vector units, one score per group per MFMA slot, so both kinds of work are
+// always available to issue.  Each LDS operand fragment feeds the NQ query groups; it is read
+// kAttendPrefetch MFMA slots of its kind ahead, and scheduling fences hold this order.
+template <int D, int DV, int NQ>
+__device__ __forceinline__ void attend_step(const AttendChunk<D, DV>& bS, int uS, const AttendChunk<D, DV>& bE,
+                                            int uE, const AttendChunk<D, DV>& bP, int uP,
+                                            const bf16x8 (&qb)[NQ][D / 16], f32x16 (&y)[NQ][DV / 32],
+                                            float (&den)[NQ][4], const f32x16 (&sc_cur)[NQ], f32x16 (&sc_next)[NQ],
+                                            const bf16x8 (&pb_prev)[NQ][2], bf16x8 (&pb_cur)[NQ][2], int g, int l32) {
+  constexpr int NK = D / 16, NW = DV / 16, NS = NK + NW;
+  auto kfrag = [&](int kk) { return __builtin_bit_cast(bf16x8, bS.k[(2 * kk + g) * 64 + 32 * uS + l32]); };
+  auto wfrag = [&](int i) {  // i = 2 ct + qq
+    return __builtin_bit_cast(bf16x8, bP.w[(4 * uP + 2 * (i & 1) + g) * DV + 32 * (i >> 1) + l32]);
   };
-  auto wden = [&](int u, int v4) { return *reinterpret_cast<const float4*>(&b.wd[32 * u + 8 * v4 + 4 * g]); };
-  // exponential, normaliser term and bf16 packing of scores v, v+1 of a unit
-  auto expo = [&](const f32x16& sc, const float4 (&wd)[4], bf16x8 (&pb)[2], int v) {
+  // W[:, dv] for the two halves of this lane's probabilities, in the same (permuted) order
+  bf16x8 wd[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int vv = v + e;
-      const float p = __builtin_amdgcn_exp2f(sc[vv] * bl2e);
-      const float4 w4 = wd[vv >> 2];
-      const float w = (vv & 3) == 0 ? w4.x : (vv & 3) == 1 ? w4.y : (vv & 3) == 2 ? w4.z : w4.w;
-      den[vv & 3] = fmaf(p, w, den[vv & 3]);
-      pb[vv >> 3][vv & 7] = (__bf16)p;
+  for (int qq = 0; qq < 2; ++qq) wd[qq] = __builtin_bit_cast(bf16x8, bE.wd[4 * uE + 2 * qq + g]);
+  bf16x8 kf[NK], wf[NW];
+#pragma unroll
+  for (int i = 0; i < kAttendPrefetch; ++i) {
+    if (i < NK) kf[i] = kfrag(i);
+    if (i < NW) wf[i] = wfrag(i);
+  }
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) sc_next[s] = f32x16{};
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int si = j * NK / NS;  // S slots before slot j
+    if ((j + 1) * NK / NS > si) {
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) sc_next[s] = mfma32(kf[si], qb[s][si], sc_next[s]);
+      if (si + kAttendPrefetch < NK) kf[si + kAttendPrefetch] = kfrag(si + kAttendPrefetch);
+    } else {
+      const int i = j - si;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) y[s][i >> 1] = mfma32(wf[i], pb_prev[s][i & 1], y[s][i >> 1]);
+      if (i + kAttendPrefetch < NW) wf[i + kAttendPrefetch] = wfrag(i + kAttendPrefetch);
     }
-  };
-  const f32x16 zero = {};
-  bf16x8 ka[NK], kb[NK], wa[NW], wb[NW];
-  float4 wd0[4], wd1[4];
-  bf16x8 pb0[2], pb1[2];
-  f32x16 s0 = zero, s1 = zero;
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) ka[kk] = kfrag(0, kk);
-  __builtin_amdgcn_sched_barrier(0);
-  // phase A: scores of u0; K of u1 read behind them, then W[:, dv] of u0
+    for (int v = j * 16 / NS; v < (j + 1) * 16 / NS; ++v)
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    s0 = mfma32(ka[kk], qb[kk], s0);
-    kb[kk] = kfrag(1, kk);
-    if (kk >= NK - 4) wd0[kk - (NK - 4)] = wden(0, kk - (NK - 4));
+      for (int s = 0; s < NQ; ++s) {
+        // the queries carry the factor beta log2(e), so the score is already a base-2 exponent
+        pb_cur[s][v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(sc_cur[s][v]);
+        if (v & 1) {  // normaliser: packed bf16 products, the same rounded P and W as the values
+          const bf16x2 pp = {pb_cur[s][v >> 3][(v & 7) - 1], pb_cur[s][v >> 3][v & 7]};
+          const bf16x2 ww = {wd[v >> 3][(v & 7) - 1], wd[v >> 3][v & 7]};
+          den[s][(v >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ww, den[s][(v >> 1) & 3], false);
+        }
+      }
     __builtin_amdgcn_sched_barrier(0);
   }
-  // phase B: scores of u1; exponentials of u0; W of u0 read, then W[:, dv] of u1
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    s1 = mfma32(kb[kk], qb[kk], s1);
-#pragma unroll
-    for (int i = kk * NW / NK; i < (kk + 1) * NW / NK; ++i) wa[i] = wfrag(0, i);
-    if (kk >= NK - 4) wd1[kk - (NK - 4)] = wden(1, kk - (NK - 4));
-#pragma unroll
-    for (int v = kk * 16 / NK; v < (kk + 1) * 16 / NK; v += 2) expo(s0, wd0, pb0, v);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // phase C: values of u0; exponentials of u1; W of u1 read
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    y[i >> 1] = mfma32(wa[i], pb0[i & 1], y[i >> 1]);
-    wb[i] = wfrag(1, i);
-#pragma unroll
-    for (int v = i * 16 / NW; v < (i + 1) * 16 / NW; v += 2) expo(s1, wd1, pb1, v);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // phase D: values of u1
-#pragma unroll
-  for (int i = 0; i < NW; ++i) y[i >> 1] = mfma32(wb[i], pb1[i & 1], y[i >> 1]);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
+// Workgroup of kAttendWaves waves (one per SIMD), each taking kAttendNQ groups of 32 queries.
 template <int D, int DV>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attend_bf16_kernel(AttendArgs a) {
-  constexpr int NCT = DV / 32;
-  __shared__ AttendChunk<D, DV> sb0, sb1;
+__global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
+attend_bf16_kernel(AttendArgs a) {
+  constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ;
+  __shared__ AttendChunk<D, DV> sb[3];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y, sp = blockIdx.z;
   const int m = a.m, rp = attend_rows(a.r);
   const float bl2e = a.beta_log2e;
-  const int q = blockIdx.x * 128 + wid * 32 + l32;
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)h * m + q) * D;
+  const int q0 = blockIdx.x * kAttendQueries + wid * 32 * NQ + l32;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * m * D;
 
-  bf16x8 qb[D / 16];
+  // query fragments scaled by beta log2(e) (one bf16 rounding, relative 2^-9 per element), so
+  // the score MFMA yields the base-2 exponent directly
+  bf16x8 qb[NQ][NK];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (q < m) {
-      qb[kk] = *reinterpret_cast<const bf16x8*>(Q + 16 * kk + 8 * g);
-    } else {
+  for (int s = 0; s < NQ; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[kk][e] = (__bf16)0.f;
+    for (int kk = 0; kk < NK; ++kk) {
+      const int q = q0 + 32 * s;
+      bf16x8 raw;
+      if (q < m) {
+        raw = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw[e] = (__bf16)0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)((float)raw[e] * bl2e);
     }
+  f32x16 y[NQ][NCT];
+  float den[NQ][4];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) y[s][ct] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) den[s][i] = 0.f;
   }
-  f32x16 y[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) y[ct][v] = 0.f;
-  float den[4] = {0.f, 0.f, 0.f, 0.f};
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the query fragments have arrived
-  // the coreset is split over blockIdx.z in blocks of 128 rows: chunk 2b in sb0, 2b+1 in sb1
-  const int nb = rp / 128, per = (nb + a.nsplit - 1) / a.nsplit;
-  const int bb = sp * per, be = min(nb, bb + per);
+  // this workgroup's share of the coreset: chunks c0 .. c0+nc-1 of 64 rows
+  const int nchk = rp / 64, per = (nchk + a.nsplit - 1) / a.nsplit;
+  const int c0 = sp * per, nc = min(nchk, c0 + per) - c0;
   const uint16_t* KSh = a.KSh + (size_t)h * rp * D;
   const uint16_t* Wph = a.Wph + (size_t)h * DV * rp;
-  const float* Wden = a.Wden + (size_t)h * rp;
-  if (bb < be) attend_issue(sb0, KSh, Wph, Wden, 2 * bb, wid, lane);
-  // Before reading a buffer every wave waits for its own loads into it and then meets the
-  // others at the barrier; the barrier also tells every wave that the other buffer's previous
-  // chunk has been read by all, so the next chunk's loads may be issued into it.
-  for (int b = bb; b < be; ++b) {
+  const uint16_t* Wdh = a.Wdh + (size_t)h * rp;
+  if (nc > 0) {
+    attend_issue(sb[0], KSh, Wph, Wdh, c0, wid, lane);
+    if (nc > 1) attend_issue(sb[1], KSh, Wph, Wdh, c0 + 1, wid, lane);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    attend_issue(sb1, KSh, Wph, Wden, 2 * b + 1, wid, lane);
-    attend_chunk<D, DV>(sb0, qb, y, den, bl2e, g, l32);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    if (b + 1 < be) attend_issue(sb0, KSh, Wph, Wden, 2 * b + 2, wid, lane);
-    attend_chunk<D, DV>(sb1, qb, y, den, bl2e, g, l32);
+    // scores of unit 0 alone; the values of the (nonexistent) unit -1 get zero probabilities
+    f32x16 scA[NQ], scB[NQ];
+    bf16x8 pbA[NQ][2], pbB[NQ][2];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      scA[s] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        scA[s] = mfma32(__builtin_bit_cast(bf16x8, sb[0].k[(2 * kk + g) * 64 + l32]), qb[s][kk], scA[s]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pbA[s][0][e] = pbA[s][1][e] = (__bf16)0.f;
+    }
+    // Unit 2c is in ring slot c % 3 (upper half of the chunk: unit 2c+1).  Chunk c's loads were
+    // issued two chunks ahead and are waited for at the barrier of chunk c-1; that barrier also
+    // frees slot (c+2) % 3, whose last reads (values of unit 2c-1) come before it.
+    for (int c = 0; c < nc; ++c) {
+      const int bc = c % 3, bn = (c + 1) % 3, bl = c == 0 ? bc : (c + 2) % 3;
+      attend_step<D, DV, NQ>(sb[bc], 1, sb[bc], 0, sb[bl], c == 0 ? 0 : 1, qb, y, den, scA, scB, pbA, pbB, g, l32);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+      if (c + 2 < nc) attend_issue(sb[(c + 2) % 3], KSh, Wph, Wdh, c0 + c + 2, wid, lane);
+      // the scores of unit 2c+2 are garbage past the last chunk and are never exponentiated
+      attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
+    }
+    // values of the last unit
+    const AttendChunk<D, DV>& bz = sb[(nc - 1) % 3];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const bf16x8 wf = __builtin_bit_cast(bf16x8, bz.w[(4 + 2 * (i & 1) + g) * DV + 32 * (i >> 1) + l32]);
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) y[s][i >> 1] = mfma32(wf, pbA[s][i & 1], y[s][i >> 1]);
+    }
   }
-  float dn = (den[0] + den[1]) + (den[2] + den[3]);
-  dn += __shfl_xor(dn, 32, 64);
-  if (q >= m) return;
-  if (a.nsplit == 1) {
-    if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
-    const float inv = 1.0f / dn;
-    uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+  for (int s = 0; s < NQ; ++s) {
+    float dn = (den[s][0] + den[s][1]) + (den[s][2] + den[s][3]);
+    dn += __shfl_xor(dn, 32, 64);
+    const int q = q0 + 32 * s;
+    if (q >= m) continue;
+    if (a.nsplit == 1) {
+      if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
+      const float inv = 1.0f / dn;
+      uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int col = ct * 32 + 8 * v4 + 4 * g;
-        uint16_t o[4];
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[ct][4 * v4 + e] * inv));
-        uint2 pk;
-        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-        *reinterpret_cast<uint2*>(O + col) = pk;
-      }
-  } else {
-    float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int col = ct * 32 + 8 * v4 + 4 * g;
+          uint16_t o[4];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+          for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[s][ct][4 * v4 + e] * inv));
+          uint2 pk;
+          pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+          pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+          *reinterpret_cast<uint2*>(O + col) = pk;
+        }
+    } else {
+      float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[ct][v];
-    if (g == 0) Yp[DV] = dn;
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
+      if (g == 0) Yp[DV] = dn;
+    }
   }
 }
 
@@ -409,7 +455,8 @@ static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((attend_bf16_kernel<D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<D, DV>), dim3((a.m + kAttendQueries - 1) / kAttendQueries, a.H, a.nsplit),
+                       dim3(64 * kAttendWaves), 0, st, a);
   else
     hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -96,6 +96,7 @@ struct AttendArgs {
   uint16_t* Wph;          // ws [H][dv*rp]    permuted W^T, bf16 hi, tile-major
   uint16_t* Wpl;          // ws [H][dv*rp]    bf16 lo (fp32 inputs only)
   float* Wden;            // ws [H][rp]       W[:, dv]
+  uint16_t* Wdh;          // ws [H][rp]       W[:, dv] in bf16, permuted like the columns of W^T
   float* Ypart;           // ws [H][nsplit][m][dv+1] partial sums when nsplit > 1
   int nsplit;
   void* O;                // [H][m][dv]
