@@ -37,7 +37,7 @@ bool req(const void* ptr) { return ptr != nullptr && aligned16(ptr); }
 bool opt(const void* ptr) { return ptr == nullptr || aligned16(ptr); }
 
 bool resident_ok(const wc_problem& p) {
-  return p.dtype == WC_BF16 && p.n <= wc::kResidentThreads && p.r <= wc::kResidentR;
+  return p.dtype == WC_BF16 && p.n <= wc::kResidentRows && p.r <= wc::kResidentR;
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }

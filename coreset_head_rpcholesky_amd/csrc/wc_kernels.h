@@ -12,7 +12,8 @@
 namespace wc {
 
 // ---- resident path: one workgroup per head (n <= 256, bf16, r <= 32) ----
-constexpr int kResidentThreads = 256;  // one key row per thread: n <= 256
+constexpr int kResidentRows = 256;     // n <= 256 keys
+constexpr int kResidentThreads = 128;  // two waves, two consecutive key rows per thread
 constexpr int kResidentR = 32;         // r <= 32 (the pivot loop is unrolled over r)
 struct ResidentArgs {
   const uint16_t* Q;

@@ -1,18 +1,25 @@
 // Resident WildCat forward: one workgroup per head, the whole head on one CU.
 //
-// For short heads (n <= 256 keys, bf16 inputs, r <= 32) every row of K and of the partial
-// Cholesky factor F lives in the registers of the thread that owns the row, so the r
-// sequential pivot steps of randomly pivoted Cholesky (gist.science/de/paper/2602.10056,
-// "Methodik" part 1) run with two workgroup barriers each and no memory traffic beyond the
-// compulsory reads of Q, K, V and the write of O.  The Nystroem weights ("Methodik" part 2)
-// and the attention over the coreset follow in the same launch on the bf16 matrix cores.
+// For short heads (n <= 256 keys, bf16 inputs, r <= 32) the r sequential pivot steps of
+// randomly pivoted Cholesky (gist.science/de/paper/2602.10056, "Methodik" part 1) run out of
+// registers and LDS with one barrier per step and no memory traffic beyond the compulsory
+// reads of Q, K, V and the write of O.  The Nystroem weights ("Methodik" part 2) and the
+// attention over the coreset follow in the same launch on the bf16 matrix cores.
 //
-// Per step t (identical arithmetic in every thread, so every thread agrees):
-//   mass p_i = max(diag_i, 0) -> wave inclusive scan (fp64) -> wave totals in LDS (barrier)
-//   T = sum of wave totals in wave order; s = min{i : C_i > u_t T} (first wave whose running
-//   total exceeds u_t T, then the first lane in it); the thread owning row s publishes k_s,
-//   F[s, :t] and g_s = H_ss - |F[s, :t]|^2 (barrier); every thread then forms
-//   g_i = exp(beta k_i.k_s) - F[i, :t].F[s, :t], F[i, t] = g_i / sqrt(g_s), diag_i -= F[i, t]^2.
+// Two waves per head; lane l of wave w owns the consecutive key rows a = 2(64w + l) and a + 1.
+// Its keys and its rows of the factor F sit in registers; copies of the keys, of the rows of
+// F (with the initial diagonal H_ii appended) and of the residual diagonal sit in LDS.  Step t,
+// after the barrier that ends step t-1 (identical arithmetic in every thread, so every thread
+// agrees without further communication):
+//   T = w0 + w1, the two wave totals of the masses max(diag, 0) (fp64, each a wave scan over
+//       the row pairs);
+//   s = min{i : C_i > u_t T}: the wave whose running total first exceeds u_t T is searched by
+//       ballot, from its own registers in that wave and from the residual diagonal in LDS
+//       (re-scanned with the same arithmetic) in the other;
+//   g_s = H_ss - |F[s, :t]|^2 from LDS, then every thread forms, for its two rows,
+//   g_i = exp(beta k_i.k_s) - F[i, :t].F[s, :t], F[i, t] = g_i / sqrt(g_s), diag_i -= F[i, t]^2,
+//   stores them to LDS, scans its wave's masses for step t+1 and meets the other wave at the
+//   barrier.
 #include "wc_device.h"
 #include "wc_kernels.h"
 
@@ -90,10 +97,15 @@ __device__ __forceinline__ int perm32(int j) {
   return jb + 16 * qq + 8 * g + e;
 }
 
+// Dynamic LDS of the resident kernel.  During the pivot loop: the keys [n][D/2] (packed bf16
+// pairs), the rows of F [n][R+1] (the last slot holds H_ii; R+1 is odd, so the column stores
+// of one step spread over the banks) and the residual diagonal double-buffered [2][256].  After
+// the loop the weights and attention buffers reuse the same bytes.
 template <int D, int DV, int R, int NT>
 struct ResidentSmem {
   static constexpr int NW = NT / 64;
-  static constexpr int CH = ((4 * R + 2 * DV) * 128 <= 32768 && NT >= 128) ? 128 : 64;
+  static constexpr int FS = R + 1;    // row stride of F in LDS
+  static constexpr int CH = 128;      // rows per staging chunk of the weights GEMM
   static constexpr int KSP = D + 8;   // padded row length of the staged coreset keys (bf16)
   static constexpr int WPP = R + 8;   // padded row length of the permuted weights (bf16)
   static constexpr int XP = DV + 1;   // row length of X (fp32)
@@ -101,115 +113,150 @@ struct ResidentSmem {
   static constexpr int STAGE_BYTES = (2 * R * CH + DV * CH) * 2;
   static constexpr int X_BYTES = R * XP * 4;
   static constexpr int A_BYTES = STAGE_BYTES > X_BYTES ? STAGE_BYTES : X_BYTES;
+  static constexpr int KS_OFF = A_BYTES;
+  static constexpr int WP_OFF = KS_OFF + R * KSP * 2;
+  static constexpr int WDEN_OFF = WP_OFF + DV * WPP * 2;
+  static constexpr int L_OFF = WDEN_OFF + R * 4;
+  static constexpr int P2_BYTES = L_OFF + R * (R + 1) * 4;
+  // pivot-loop region, for n keys
+  __host__ __device__ static constexpr int f_off(int n) { return n * D * 2; }
+  static constexpr int DGS = 2 * NT;  // row stride of each residual-diagonal buffer (all rows)
+  __host__ __device__ static constexpr int dg_off(int n) { return (f_off(n) + n * FS * 4 + 15) & ~15; }
+  __host__ __device__ static constexpr int loop_bytes(int n) { return dg_off(n) + 2 * DGS * 4; }
+  __host__ __device__ static constexpr int bytes(int n) {
+    return loop_bytes(n) > P2_BYTES ? loop_bytes(n) : P2_BYTES;
+  }
 };
+
+// Masses of a lane's row pair, their wave scan (pair sums), and the inclusive prefix of the
+// first row of the pair: xa = x - m_b.
+struct PairScan {
+  double x, xa;
+  bool pa, pb;  // rows with positive mass
+};
+__device__ __forceinline__ PairScan pair_scan(float dga, float dgb, bool va, bool vb) {
+  const double ma = va ? mass_of(dga) : 0.0, mb = vb ? mass_of(dgb) : 0.0;
+  const double x = wave_scan_fast(ma + mb);
+  return {x, x - mb, ma > 0.0, mb > 0.0};
+}
 
 template <int D, int DV, int R, int NT>
 __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
   using S = ResidentSmem<D, DV, R, NT>;
-  constexpr int NW = S::NW, D2 = D / 2, CH = S::CH;
+  constexpr int NW = S::NW, D2 = D / 2, FS = S::FS, CH = S::CH, DGS = S::DGS;
+  static_assert(NW == 2, "two waves per head");
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int n = a.n, r = a.r;
-  const bool valid = tid < n;
+  const int ra = 2 * tid;                 // own rows ra, ra + 1
+  const bool va = ra < n, vb = ra + 1 < n;
 
-  __shared__ double s_wsum[NW];
-  __shared__ int s_piv;
-  __shared__ float s_gs, s_rs;
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_u[R];
   __shared__ uint32_t s_flag;
-  __shared__ __attribute__((aligned(16))) uint32_t s_ks[D2];
-  __shared__ __attribute__((aligned(16))) float s_fs[R];
-  __shared__ float s_L[R][R + 1];
   __shared__ int s_pivots[R];
-  __shared__ __attribute__((aligned(16))) unsigned char s_A[S::A_BYTES];
-  __shared__ __attribute__((aligned(16))) __bf16 s_Ks[R * S::KSP];
-  __shared__ __attribute__((aligned(16))) __bf16 s_Wp[DV * S::WPP];
-  __shared__ float s_Wden[R];
+  uint32_t* sK = reinterpret_cast<uint32_t*>(s_dyn);                 // [n][D2]
+  float* sF = reinterpret_cast<float*>(s_dyn + S::f_off(n));         // [n][FS]
+  float* sDg = reinterpret_cast<float*>(s_dyn + S::dg_off(n));       // [2][DGS]
 
-  // ---------------- load own key row ----------------
-  uint32_t kr[D2];
+  // ---------------- load own key rows ----------------
+  uint32_t kr[2][D2];
   const uint16_t* Kh = a.K + (size_t)h * n * D;
-  if (valid) {
-    const uint4* src = reinterpret_cast<const uint4*>(Kh + (size_t)tid * D);
 #pragma unroll
-    for (int q = 0; q < D / 8; ++q) {
-      const uint4 v = src[q];
-      kr[4 * q] = v.x; kr[4 * q + 1] = v.y; kr[4 * q + 2] = v.z; kr[4 * q + 3] = v.w;
+  for (int p = 0; p < 2; ++p) {
+    const int row = ra + p;
+    if (row < n) {
+      const uint4* src = reinterpret_cast<const uint4*>(Kh + (size_t)row * D);
+#pragma unroll
+      for (int q = 0; q < D / 8; ++q) {
+        const uint4 v = src[q];
+        kr[p][4 * q] = v.x; kr[p][4 * q + 1] = v.y; kr[p][4 * q + 2] = v.z; kr[p][4 * q + 3] = v.w;
+        reinterpret_cast<uint4*>(sK + row * D2)[q] = v;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < D2; ++q) kr[p][q] = 0u;
     }
-  } else {
-#pragma unroll
-    for (int q = 0; q < D2; ++q) kr[q] = 0u;
   }
   const float bl2e = a.beta_log2e;
-  const float d0 = valid ? __builtin_amdgcn_exp2f(dot_bf16<D2>(kr, kr) * bl2e) : 0.f;
-  float dg = d0;
-  float fr[R];
+  float dg[2], fr[2][R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) fr[j] = 0.f;
-  if (tid == 0) {
-    s_flag = 0u;
-    s_piv = -1;
+  for (int p = 0; p < 2; ++p) {
+    const int row = ra + p;
+    const float d0 = row < n ? __builtin_amdgcn_exp2f(dot_bf16<D2>(kr[p], kr[p]) * bl2e) : 0.f;
+    dg[p] = d0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) fr[p][j] = 0.f;
+    if (row < n) {
+      sF[row * FS + R] = d0;
+      sDg[row] = d0;
+    }
   }
+  if (tid == 0) s_flag = 0u;
   // the r pivot uniforms, drawn once (first use is after the first barrier)
   if (tid < r) s_u[tid] = pivot_uniform(a.u_forced, a.seed, h, r, tid);
+  __syncthreads();
   int rk = r;
   uint32_t flg = 0u;
+  double T = 0.0;
 
   // ---------------- randomly pivoted Cholesky ----------------
   bool alive = true;
   static_for<0, R>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
+    constexpr int buf = t & 1;
     if (!alive || t >= r) return;
-    const double pd = valid ? mass_of(dg) : 0.0;
-    const double x = wave_scan_fast(pd);
-    if (lane == 63) s_wsum[wid] = x;
-    __syncthreads();
-    double T = 0.0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) T += s_wsum[w];
-    if (tid == 0 && a.trace) a.trace[(size_t)h * (r + 1) + t] = __builtin_isfinite(T) ? T : 0.0;
-    if (!(T > 0.0) || !__builtin_isfinite(T)) {
-      rk = t;
-      flg |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(T) ? 0u : WC_DFLAG_NONFINITE);
-      alive = false;
-      return;
-    }
+    // Both waves' row pairs at this lane position: scanned in two independent chains, so
+    // every wave holds both wave totals and the prefix sums of whichever wave is crossed.
+    const float2 d0p = reinterpret_cast<const float2*>(sDg + buf * DGS)[lane];
+    const float2 d1p = reinterpret_cast<const float2*>(sDg + buf * DGS)[64 + lane];
+    const PairScan q0 = pair_scan(d0p.x, d0p.y, 2 * lane < n, 2 * lane + 1 < n);
+    const PairScan q1 = pair_scan(d1p.x, d1p.y, 128 + 2 * lane < n, 128 + 2 * lane + 1 < n);
+    const double w0 = readlane_d(q0.x, 63), w1 = readlane_d(q1.x, 63);
+    T = w0 + w1;
+    // Breakdown (T <= 0, no row claims the draw, g_s <= 0, anything non-finite) is collected
+    // in one flag; the step's reads stay in bounds either way and its updates are skipped.
+    const bool tfin = __builtin_isfinite(T);
+    uint32_t bad = (T > 0.0 && tfin) ? 0u : (WC_DFLAG_BREAKDOWN | (tfin ? 0u : WC_DFLAG_NONFINITE));
+    // the wave holding the crossing (or, if u T rounded onto the total, the last row with
+    // positive mass), and the running total before it
     const double uT = (double)s_u[t] * T;
-    double acc = 0.0, pre = 0.0;
-    int wstar = -1, wlast = -1;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const double tw = s_wsum[w];
-      const double nxt = acc + tw;
-      if (w == wid) pre = acc;
-      if (wstar < 0 && nxt > uT) wstar = w;
-      if (tw > 0.0) wlast = w;
-      acc = nxt;
+    const bool cross = T > uT;
+    const int wsel = (w0 > uT || (!cross && !(w1 > 0.0))) ? 0 : 1;
+    const double pre = wsel == 1 ? w0 : 0.0;
+    const PairScan& q = wsel == 1 ? q1 : q0;
+    const uint64_t bx = ballot(cross ? pre + q.x > uT : (q.pa || q.pb));
+    const uint64_t bs = ballot(cross ? !(pre + q.xa > uT) : q.pb);  // second row of the pair
+    const int L = cross ? (bx ? __builtin_ctzll(bx) : 0) : (bx ? 63 - __builtin_clzll(bx) : 0);
+    int s = 2 * (64 * wsel + L) + (int)((bs >> L) & 1);
+    if (!bx || s >= n) {  // no row claimed the draw: cannot happen for finite T > 0
+      bad |= WC_DFLAG_BREAKDOWN | WC_DFLAG_NONFINITE;
+      s = 0;
     }
-    bool winner = false;
-    if (wstar >= 0) {
-      const uint64_t b = ballot(pre + x > uT);
-      if (wid == wstar) winner = lane == __builtin_ctzll(b);
-    } else {  // u T rounded onto the total: last row with positive mass
-      const uint64_t b = ballot(pd > 0.0);
-      if (wid == wlast) winner = lane == 63 - __builtin_clzll(b);
-    }
-    if (winner) {
-      s_piv = tid;
-      const float g = d0 - dot_prefix<t>(fr, fr);
-      s_gs = g;
-      s_rs = 1.0f / sqrtf(g);
+    // pivot row of F, the pivot key and everything that needs only them, side by side
+    const float* fsrow = sF + s * FS;
+    float fs[t > 0 ? t : 1];
 #pragma unroll
-      for (int q = 0; q < D2; ++q) s_ks[q] = kr[q];
+    for (int j = 0; j < t; ++j) fs[j] = fsrow[j];
+    uint32_t ks[D2];
 #pragma unroll
-      for (int j = 0; j < t; ++j) { s_fs[j] = fr[j]; s_L[t][j] = fr[j]; }
+    for (int q4 = 0; q4 < D / 8; ++q4) {
+      const uint4 v = reinterpret_cast<const uint4*>(sK + s * D2)[q4];
+      ks[4 * q4] = v.x; ks[4 * q4 + 1] = v.y; ks[4 * q4 + 2] = v.z; ks[4 * q4 + 3] = v.w;
     }
-    __syncthreads();
-    const int s = s_piv;
-    const float gs = s_gs;
-    if (s < 0 || s >= n) {  // no row claimed the draw: cannot happen for finite T > 0
+    const float gs = fsrow[R] - dot_prefix<t>(fs, fs);
+    float hk[2], corr[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      hk[p] = dot_bf16<D2>(kr[p], ks);
+      corr[p] = dot_prefix<t>(fr[p], fs);
+    }
+    if (!bad && !(gs > 0.f && __builtin_isfinite(gs)))
+      bad = WC_DFLAG_BREAKDOWN | (__builtin_isfinite(gs) ? 0u : WC_DFLAG_NONFINITE);
+    if (tid == 0 && a.trace) a.trace[(size_t)h * (r + 1) + t] = tfin ? T : 0.0;
+    if (bad) {
       rk = t;
-      flg |= WC_DFLAG_BREAKDOWN | WC_DFLAG_NONFINITE;
+      flg |= bad;
       alive = false;
       return;
     }
@@ -217,32 +264,35 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
       s_pivots[t] = s;
       if (a.pivots) a.pivots[(size_t)h * r + t] = s;
     }
-    if (!(gs > 0.f) || !__builtin_isfinite(gs)) {
-      rk = t;
-      flg |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(gs) ? 0u : WC_DFLAG_NONFINITE);
-      alive = false;
-      return;
+    const float rs = 1.0f / sqrtf(gs);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int row = ra + p;
+      const float gi = __builtin_amdgcn_exp2f(hk[p] * bl2e) - corr[p];
+      const float f = row < n ? gi * rs : 0.f;
+      fr[p][t] = f;
+      dg[p] = (row == s) ? 0.f : dg[p] - f * f;
     }
-    const float rs = s_rs;
-    const float hcol = __builtin_amdgcn_exp2f(dot_bf16<D2>(kr, s_ks) * bl2e);
-    const float gi = hcol - dot_prefix<t>(fr, s_fs);
-    const float f = valid ? gi * rs : 0.f;
-    fr[t] = f;
-    dg = (tid == s) ? 0.f : dg - f * f;
-    if (tid == s) s_L[t][t] = f;
+    if (va) {
+      sF[ra * FS + t] = fr[0][t];
+      if (vb) {
+        sF[(ra + 1) * FS + t] = fr[1][t];
+        reinterpret_cast<float2*>(sDg + (buf ^ 1) * DGS)[tid] = make_float2(dg[0], dg[1]);
+      } else {
+        sDg[(buf ^ 1) * DGS + ra] = dg[0];
+      }
+    }
+    __syncthreads();
   });
 
   // trace after the last step (reported only when all r steps completed)
   if (a.trace && rk == r) {
-    const double pd = valid ? mass_of(dg) : 0.0;
-    const double x = wave_scan_fast(pd);
-    __syncthreads();
-    if (lane == 63) s_wsum[wid] = x;
-    __syncthreads();
-    double T = 0.0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) T += s_wsum[w];
-    if (tid == 0) a.trace[(size_t)h * (r + 1) + r] = T;
+    const float2 d0p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[lane];
+    const float2 d1p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[64 + lane];
+    const PairScan q0 = pair_scan(d0p.x, d0p.y, 2 * lane < n, 2 * lane + 1 < n);
+    const PairScan q1 = pair_scan(d1p.x, d1p.y, 128 + 2 * lane < n, 128 + 2 * lane + 1 < n);
+    const double Tr = readlane_d(q0.x, 63) + readlane_d(q1.x, 63);
+    if (tid == 0) a.trace[(size_t)h * (r + 1) + r] = Tr;
   }
   if (tid == 0) {
     a.rank[h] = rk;
@@ -252,13 +302,52 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     if (a.pivots)
       for (int t = rk; t < r; ++t) a.pivots[(size_t)h * r + t] = -1;
   }
-  if (a.F && valid) {
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (j < r) a.F[((size_t)h * r + j) * n + tid] = fr[j];
+  for (int p = 0; p < 2; ++p) {
+    const int row = ra + p;
+    if (row >= n) continue;
+    if (a.F) {
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (j < r) a.F[((size_t)h * r + j) * n + row] = fr[p][j];
+    }
+    if (a.diag) a.diag[(size_t)h * n + row] = dg[p];
   }
-  if (a.diag && valid) a.diag[(size_t)h * n + tid] = dg;
   if (!a.O) return;  // pivot loop only
+
+  // ---------------- hand over to the weights and attention buffers ----------------
+  // L = F[S, :] (lower triangle) and the coreset keys K_S are read out of the loop region
+  // into registers; after the barrier the phase-2 buffers reuse those bytes.
+  float lrow[R];
+  if (tid < R) {
+    const int sp = tid < rk ? s_pivots[tid] : 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) lrow[j] = (tid < rk && j <= tid) ? sF[sp * FS + j] : 0.f;
+  }
+  constexpr int KSE = R * (D / 8);                     // uint4 of K_S
+  constexpr int KSV = (KSE + NT - 1) / NT;             // per thread
+  uint4 ksv[KSV];
+#pragma unroll
+  for (int i = 0; i < KSV; ++i) {
+    const int e = tid + NT * i, j = e / (D / 8), q = e % (D / 8);
+    ksv[i] = (e < KSE && j < rk) ? reinterpret_cast<const uint4*>(sK + s_pivots[j] * D2)[q]
+                                 : uint4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  unsigned char* s_A = s_dyn;
+  __bf16* s_Ks = reinterpret_cast<__bf16*>(s_dyn + S::KS_OFF);
+  __bf16* s_Wp = reinterpret_cast<__bf16*>(s_dyn + S::WP_OFF);
+  float* s_Wden = reinterpret_cast<float*>(s_dyn + S::WDEN_OFF);
+  float (*s_L)[R + 1] = reinterpret_cast<float (*)[R + 1]>(s_dyn + S::L_OFF);
+  if (tid < R) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) s_L[tid][j] = lrow[j];
+  }
+#pragma unroll
+  for (int i = 0; i < KSV; ++i) {
+    const int e = tid + NT * i, j = e / (D / 8), q = e % (D / 8);
+    if (e < KSE) *reinterpret_cast<uint4*>(s_Ks + j * S::KSP + 8 * q) = ksv[i];
+  }
 
   // ---------------- Nystroem weights: X = F^T [V, 1], W = L^{-T} X ----------------
   // X tiles (32 x 32) on the bf16 matrix cores; F enters as hi + lo bf16 parts, V is exact
@@ -275,32 +364,35 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
   const uint16_t* Vh = a.V + (size_t)h * n * DV;
-  for (int c0 = 0; c0 < NT; c0 += CH) {
+  for (int c0 = 0; c0 < 2 * NT; c0 += CH) {
     __syncthreads();
-    if (tid >= c0 && tid < c0 + CH) {
-      const int ii = tid - c0;
+    if (ra >= c0 && ra < c0 + CH) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        __bf16 hi, lo;
-        split_bf16(fr[j], hi, lo);
-        FtH[j * CH + ii] = hi;
-        FtL[j * CH + ii] = lo;
-      }
-      if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(Vh + (size_t)tid * DV);
+      for (int p = 0; p < 2; ++p) {
+        const int row = ra + p, ii = row - c0;
 #pragma unroll
-        for (int q = 0; q < DV / 8; ++q) {
-          const uint4 v = src[q];
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            Vt[(8 * q + 2 * e) * CH + ii] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e] & 0xffffu));
-            Vt[(8 * q + 2 * e + 1) * CH + ii] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e] >> 16));
-          }
+        for (int j = 0; j < R; ++j) {
+          __bf16 hi, lo;
+          split_bf16(fr[p][j], hi, lo);
+          FtH[j * CH + ii] = hi;
+          FtL[j * CH + ii] = lo;
         }
-      } else {
+        if (row < n) {
+          const uint4* src = reinterpret_cast<const uint4*>(Vh + (size_t)row * DV);
 #pragma unroll
-        for (int c = 0; c < DV; ++c) Vt[c * CH + ii] = (__bf16)0.f;
+          for (int q = 0; q < DV / 8; ++q) {
+            const uint4 v = src[q];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Vt[(8 * q + 2 * e) * CH + ii] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e] & 0xffffu));
+              Vt[(8 * q + 2 * e + 1) * CH + ii] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e] >> 16));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < DV; ++c) Vt[c * CH + ii] = (__bf16)0.f;
+        }
       }
     }
     __syncthreads();
@@ -359,13 +451,6 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
       if (c < DV) s_Wp[c * S::WPP + perm32(t)] = (__bf16)w;
       else s_Wden[t] = w;
     }
-  }
-  // stage the coreset keys (bf16) for the score MFMA
-  for (int e = tid; e < R * (D / 8); e += NT) {
-    const int j = e / (D / 8), q = e % (D / 8);
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (j < rk) v = reinterpret_cast<const uint4*>(Kh + (size_t)s_pivots[j] * D)[q];
-    *reinterpret_cast<uint4*>(s_Ks + j * S::KSP + 8 * q) = v;
   }
   __syncthreads();
 
@@ -456,8 +541,16 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
 #define WC_CAT(a, b, c) WC_CAT_(a, b, c)
 
 hipError_t WC_CAT(launch_resident_, WC_RES_D, WC_RES_DV)(const ResidentArgs& a, int heads, hipStream_t st) {
+  using S = ResidentSmem<WC_RES_D, WC_RES_DV, kResidentR, kResidentThreads>;
+  const int bytes = S::bytes(a.n);
+  if (bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&resident_kernel<WC_RES_D, WC_RES_DV, kResidentR, kResidentThreads>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((resident_kernel<WC_RES_D, WC_RES_DV, kResidentR, kResidentThreads>), dim3(heads),
-                     dim3(kResidentThreads), 0, st, a);
+                     dim3(kResidentThreads), bytes, st, a);
   return hipGetLastError();
 }
 
