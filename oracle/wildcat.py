@@ -11,7 +11,8 @@ Sources (the pages, cited by title and section):
 
 Where the pages leave a step open, the reading is:
   * beta = 1/sqrt(d) (softmax kernel exp(<x, y>/sqrt(d))).
-  * One bin: r sequential pivot steps over all n keys of a head.
+  * One bin: r sequential pivot steps over all n keys of a head (forward); B contiguous bins
+    with r/B steps each and per-bin weights (forward_binned, see there).
   * Step t: p = max(diag, 0); C = running sum of p (sequential, fp64); T = C[n-1];
     s = min{i : C_i > u_t T}; g = H[:, s] - F[:, :t] F[s, :t]^T; F[:, t] = g / sqrt(g[s]);
     diag -= F[:, t]^2; diag[s] = 0.  Breakdown (T <= 0, g[s] <= 0 or either not finite)
@@ -197,6 +198,60 @@ def forward(Q, K, V, r, uniforms, beta=None):
     flags = rpc["flags"] | (FLAG_DENOM if np.any(~(denom > 0.0)) else 0)
     return dict(O=O, W=W, denom=denom, kappa=kappa, pivots=rpc["pivots"], rank=rpc["rank"],
                 flags=flags, F=rpc["F"], diag=rpc["diag"], trace=rpc["trace"])
+
+
+def bin_bounds(n, r, B):
+    """Bins of the divide-and-conquer selection: bin b holds the keys [b n/B, (b+1) n/B) and the
+    pivot slots [b r/B, (b+1) r/B).  B must divide n and r."""
+    if n % B or r % B:
+        raise ValueError("the number of bins must divide n and r")
+    nb, rb = n // B, r // B
+    return [(b * nb, (b + 1) * nb, b * rb, (b + 1) * rb) for b in range(B)]
+
+
+def forward_binned(Q, K, V, r, B, uniforms, beta=None):
+    """One head of divide-and-conquer WildCat with B bins.
+
+    "Methodik" part 1 (efficiency): the input is split into B bins that are processed in
+    parallel, at O(n r^2 / B^3 + n r d / B^2), i.e. n/B keys and r/B pivots per bin.  Reading
+    taken where the pages are silent: the bins are contiguous blocks of keys; each bin runs
+    the pivot loop on its own keys with slots [b r/B, (b+1) r/B) of ``uniforms``; each bin's
+    keys get their own Nystroem weights on that bin's coreset, W_b = H_{S_b S_b}^{-1}
+    H_{S_b, bin b} [V_b, 1] ("Methodik" part 2 applied per bin); and every query attends over
+    the union of the coresets, Y = sum_b exp(beta Q K_{S_b}^T) W_b, O = Y[:, :dv] / Y[:, dv].
+    Pivots are returned as key indices of the head, bin by bin; a slot left empty by a
+    breakdown in its bin holds -1 and a zero row of W.
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    n, d = K.shape
+    dv = V.shape[1]
+    beta = beta_of(d) if beta is None else beta
+    pivots = -np.ones(r, np.int64)
+    W = np.zeros((r, dv + 1))
+    rank, flags = 0, 0
+    for k0, k1, s0, s1 in bin_bounds(n, r, B):
+        rpc = rpcholesky(K[k0:k1], s1 - s0, uniforms[s0:s1], beta)
+        rb = rpc["rank"]
+        Sb = rpc["pivots"][:rb]
+        if rb:
+            W[s0:s0 + rb] = weights(K[k0:k1], V[k0:k1], Sb, beta)
+        pivots[s0:s0 + rb] = Sb + k0
+        rank += rb
+        flags |= rpc["flags"]
+    valid = pivots >= 0
+    O, denom, kappa = attend(Q, K, pivots[valid], W[valid], beta)
+    flags |= FLAG_DENOM if np.any(~(denom > 0.0)) else 0
+    return dict(O=O, W=W, denom=denom, kappa=kappa, pivots=pivots, rank=rank, flags=flags)
+
+
+def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None):
+    """snap_uniforms applied bin by bin (bin b snaps its slots on its own keys)."""
+    K = np.asarray(K, np.float64)
+    out = np.zeros(r, np.float32)
+    for k0, k1, s0, s1 in bin_bounds(K.shape[0], r, B):
+        out[s0:s1] = snap_uniforms(K[k0:k1], s1 - s0, raw_uniforms[s0:s1], beta)[0]
+    return out
 
 
 def exact_attention(Q, K, V, beta=None):
