@@ -27,6 +27,8 @@ wc_status check_problem(const wc_problem* p) {
   if ((p->d != 64 && p->d != 128) || (p->dv != 64 && p->dv != 128)) return WC_ERR_UNSUPPORTED;
   if (p->dtype != WC_F32 && p->dtype != WC_BF16) return WC_ERR_UNSUPPORTED;
   if (p->r > kMaxR) return WC_ERR_UNSUPPORTED;
+  if (p->bins < 0) return WC_ERR_INVALID_ARG;
+  if (p->bins > 1 && (p->n % p->bins != 0 || p->r % p->bins != 0)) return WC_ERR_UNSUPPORTED;
   if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
   return WC_OK;
 }
@@ -40,6 +42,19 @@ bool resident_ok(const wc_problem& p) {
   return p.dtype == WC_BF16 && p.n <= wc::kResidentRows && p.r <= wc::kResidentR;
 }
 
+bool binned(const wc_problem& p) { return p.bins > 1; }
+
+// The per-bin view of a binned problem: heads * B sub-heads of n/B keys and r/B pivots.
+wc_problem sub_problem(const wc_problem& p) {
+  wc_problem s = p;
+  s.heads = p.heads * p.bins;
+  s.n = p.n / p.bins;
+  s.r = p.r / p.bins;
+  s.m = 0;
+  s.bins = 1;
+  return s;
+}
+
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
@@ -48,7 +63,10 @@ struct Layout {
   size_t total;
 };
 
-Layout make_layout(const wc_problem& p) {
+// parts: kSelect (pivot loop and weights) and/or kAttend (staged coreset and attention).
+constexpr int kSelect = 1, kAttend = 2;
+
+Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
   Layout L{};
   const size_t H = (size_t)p.heads, n = (size_t)p.n, r = (size_t)p.r, m = (size_t)p.m;
   const size_t nc = (size_t)p.dv + 1;
@@ -84,26 +102,61 @@ Layout make_layout(const wc_problem& p) {
   L.nsplit = (int)nsplit;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
-  L.diag0 = take(H * n * 4);
-  L.diag1 = take(H * n * 4);
-  L.part0 = take(H * L.nblk * 8);
-  L.part1 = take(H * L.nblk * 8);
-  L.unif = take(H * r * 4);
-  L.F = take(H * r * n * 4);
-  L.piv = take(H * r * 4);
-  L.L = take(H * r * r * 4);
-  L.Xpart = take(H * L.nchunk * r * nc * 4);
-  L.X = take(H * r * nc * 4);
-  L.W = take(H * r * nc * 4);
-  L.KSh = take(H * L.rp * p.d * 2);
-  L.KSl = take(H * L.rp * p.d * 2);
-  L.Wph = take(H * p.dv * L.rp * 2);
-  L.Wpl = take(H * p.dv * L.rp * 2);
-  L.Wden = take(H * L.rp * 4);
-  L.Wdh = take(H * L.rp * 2);
-  L.Ypart = take(L.nsplit > 1 ? H * L.nsplit * m * nc * 4 : 0);
+  if (parts & kSelect) {
+    L.diag0 = take(H * n * 4);
+    L.diag1 = take(H * n * 4);
+    L.part0 = take(H * L.nblk * 8);
+    L.part1 = take(H * L.nblk * 8);
+    L.unif = take(H * r * 4);
+    L.F = take(H * r * n * 4);
+    L.piv = take(H * r * 4);
+    L.L = take(H * r * r * 4);
+    L.Xpart = take(H * L.nchunk * r * nc * 4);
+    L.X = take(H * r * nc * 4);
+    L.W = take(H * r * nc * 4);
+  }
+  if (parts & kAttend) {
+    const size_t lo = p.dtype == WC_F32 ? 1 : 0;  // lo parts of the bf16 splits: fp32 only
+    L.KSh = take(H * L.rp * p.d * 2);
+    L.KSl = take(lo * H * L.rp * p.d * 2);
+    L.Wph = take(H * p.dv * L.rp * 2);
+    L.Wpl = take(lo * H * p.dv * L.rp * 2);
+    L.Wden = take(H * L.rp * 4);
+    L.Wdh = take(H * L.rp * 2);
+    L.Ypart = take(L.nsplit > 1 ? H * L.nsplit * m * nc * 4 : 0);
+  }
   L.total = off;
   return L;
+}
+
+// Workspace of a binned forward: the per-bin selection and weights (the sub-head layout, whose
+// W is the heads' W), the heads' attention buffers, and the per-bin outputs.
+struct BinnedLayout {
+  Layout sub, head;
+  size_t head_base, piv_sub, rank_sub, flags_sub, rank_slots, piv, total;
+};
+
+BinnedLayout make_binned_layout(const wc_problem& p) {
+  BinnedLayout B{};
+  wc_problem hp = p;
+  hp.bins = 1;
+  B.sub = make_layout(sub_problem(p), kSelect);
+  B.head = make_layout(hp, kAttend);
+  const size_t H = (size_t)p.heads, r = (size_t)p.r;
+  size_t off = align_up(B.sub.total);
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  B.head_base = take(B.head.total);
+  B.piv_sub = take(H * r * 4);
+  B.rank_sub = take(H * p.bins * 4);
+  B.flags_sub = take(H * p.bins * 4);
+  B.rank_slots = take(H * 4);
+  B.piv = take(H * r * 4);
+  B.total = off;
+  return B;
+}
+
+size_t workspace_total(const wc_problem& p) {
+  return binned(p) ? make_binned_layout(p).total : make_layout(p).total;
 }
 
 template <typename Tp>
@@ -178,6 +231,54 @@ hipError_t run_attend(const wc_problem& p, const Layout& L, void* ws, const void
   return wc::launch_attend(a, st);
 }
 
+// Pivot loop for every head of p (resident kernel when it fits, else the streaming loop).
+hipError_t run_select(const wc_problem& p, const Layout& L, void* ws, const void* K,
+                      const float* u_forced, uint64_t seed, int32_t* pivots, float* F,
+                      int32_t* rank, uint32_t* flags, hipStream_t st) {
+  if (resident_ok(p)) {
+    wc::ResidentArgs a{};
+    a.K = static_cast<const uint16_t*>(K);
+    a.u_forced = u_forced; a.seed = seed;
+    a.n = p.n; a.m = 0; a.r = p.r;
+    a.beta_log2e = beta_log2e(p.d);
+    a.pivots = pivots; a.F = F; a.rank = rank; a.flags = flags;
+    return wc::launch_resident(a, p.heads, p.d, p.dv, st);
+  }
+  return run_rpc_stream(p, L, ws, K, u_forced, seed, pivots, F, nullptr, nullptr, rank, flags, st);
+}
+
+// Divide-and-conquer forward: selection and weights per bin on the sub-head view (the keys,
+// values and forced uniforms of bin b of head h are those of sub-head h B + b, contiguous),
+// pivots folded back to key indices of the head, then attention over the union.
+wc_status forward_binned(const wc_problem& p, const void* Q, const void* K, const void* V,
+                         const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
+                         int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t s) {
+  const BinnedLayout B = make_binned_layout(p);
+  if (!ws || !aligned16(ws) || ws_bytes < B.total) return WC_ERR_WORKSPACE;
+  const wc_problem sp = sub_problem(p);
+  int32_t* piv_sub = at<int32_t>(ws, B.piv_sub);
+  int32_t* rank_sub = at<int32_t>(ws, B.rank_sub);
+  uint32_t* flags_sub = at<uint32_t>(ws, B.flags_sub);
+  float* F = at<float>(ws, B.sub.F);
+  float* W = at<float>(ws, B.sub.W);
+  hipError_t e = run_select(sp, B.sub, ws, K, u_forced, seed, piv_sub, F, rank_sub, flags_sub, s);
+  if (e == hipSuccess) e = run_weights(sp, B.sub, ws, V, piv_sub, rank_sub, F, W, s);
+  int32_t* piv = pivots ? pivots : at<int32_t>(ws, B.piv);
+  int32_t* slots = at<int32_t>(ws, B.rank_slots);
+  if (e == hipSuccess) {
+    wc::BinsArgs a{};
+    a.H = p.heads; a.B = p.bins; a.nb = sp.n; a.rb = sp.r;
+    a.piv_sub = piv_sub; a.rank_sub = rank_sub; a.flags_sub = flags_sub;
+    a.pivots = piv; a.rank = rank; a.flags = flags; a.rank_slots = slots;
+    e = wc::launch_bins_combine(a, s);
+  }
+  wc_problem hp = p;
+  hp.bins = 1;
+  if (e == hipSuccess && p.m > 0)
+    e = run_attend(hp, B.head, static_cast<char*>(ws) + B.head_base, Q, K, piv, slots, W, O, flags, s);
+  return dev(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,7 +300,7 @@ wc_status wc_workspace_bytes(const wc_problem* p, size_t* bytes) {
   const wc_status st = check_problem(p);
   if (st != WC_OK) return st;
   if (!bytes) return WC_ERR_INVALID_ARG;
-  *bytes = p->heads == 0 ? 0 : make_layout(*p).total;
+  *bytes = p->heads == 0 ? 0 : workspace_total(*p);
   return WC_OK;
 }
 
@@ -209,6 +310,7 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
                         void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(pivots) || !req(F) || !req(rank) || !req(flags) || !opt(u_forced) ||
       !opt(diag) || !opt(trace))
@@ -233,6 +335,7 @@ wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
                      void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(V) || !req(pivots) || !req(rank) || !req(F) || !req(W)) return WC_ERR_INVALID_ARG;
   Layout L;
@@ -245,6 +348,7 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
                     size_t ws_bytes, void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(pivots) || !req(rank) || !req(W) || !req(flags)) return WC_ERR_INVALID_ARG;
   if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
@@ -262,9 +366,10 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
   if (!req(K) || !req(V) || !req(rank) || !req(flags) || !opt(u_forced) || !opt(pivots))
     return WC_ERR_INVALID_ARG;
   if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (binned(*p)) return forward_binned(*p, Q, K, V, u_forced, seed, O, pivots, rank, flags, ws, ws_bytes, s);
   Layout L;
   if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (resident_ok(*p) && p->m > 0) {
     wc::ResidentArgs a{};
     a.Q = static_cast<const uint16_t*>(Q);

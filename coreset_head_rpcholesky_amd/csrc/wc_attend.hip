@@ -44,9 +44,11 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int rp = attend_rows(a.r);
+  // slots past the rank, and slots a bin left empty (pivot -1), carry zero weight
   const int rk = a.rank[h];
-  const bool valid = j < rk;
-  const int s = valid ? a.pivots[(size_t)h * a.r + j] : 0;
+  const int sj = j < rk ? a.pivots[(size_t)h * a.r + j] : -1;
+  const bool valid = sj >= 0;
+  const int s = valid ? sj : 0;
   const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + s) * D;
   for (int e = tid; e < D; e += 128) {
     const float v = valid ? ld_elem<T>(K + e) : 0.f;

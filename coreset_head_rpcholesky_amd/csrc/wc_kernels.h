@@ -82,6 +82,19 @@ struct WeightsArgs {
 };
 hipError_t launch_weights(const WeightsArgs& a, hipStream_t st);
 
+// ---- bins: per-bin selection and weights ran on heads * B sub-heads; fold them per head ----
+struct BinsArgs {
+  int H, B, nb, rb;              // heads, bins, keys and pivots per bin
+  const int32_t* piv_sub;        // [H*B][rb], -1 after a bin's breakdown
+  const int32_t* rank_sub;       // [H*B]
+  const uint32_t* flags_sub;     // [H*B]
+  int32_t* pivots;               // out [H][B*rb]: key index within the head, or -1
+  int32_t* rank;                 // out [H]: pivots taken over all bins
+  uint32_t* flags;               // out [H]: OR over the bins
+  int32_t* rank_slots;           // out [H]: B*rb, the slots the attention scans
+};
+hipError_t launch_bins_combine(const BinsArgs& a, hipStream_t st);
+
 // ---- attend: O = (exp(beta Q K_S^T) W)[:, :dv] / (...)[:, dv] ----
 struct AttendArgs {
   const void* Q;          // [H][m][d]

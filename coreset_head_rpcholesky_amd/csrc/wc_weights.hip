@@ -277,4 +277,32 @@ hipError_t launch_weights(const WeightsArgs& a, hipStream_t st) {
   return a.dv == 64 ? run_weights<float, 64>(a, st) : run_weights<float, 128>(a, st);
 }
 
+// Divide-and-conquer selection ran bin b of head h as sub-head h B + b; its pivots become key
+// indices of the head (offset b n/B) in slots b r/B .., empty slots keep -1, and the ranks
+// and flags of the bins are folded per head.
+__global__ void __launch_bounds__(256) bins_combine_kernel(BinsArgs a) {
+  const int h = blockIdx.x, r = a.B * a.rb;
+  int taken = 0;
+  uint32_t fl = 0u;
+  for (int j = threadIdx.x; j < r; j += 256) {
+    const int b = j / a.rb, sub = h * a.B + b;
+    const int s = a.piv_sub[(size_t)sub * a.rb + j % a.rb];
+    a.pivots[(size_t)h * r + j] = s >= 0 ? s + b * a.nb : -1;
+  }
+  if (threadIdx.x == 0) {
+    for (int b = 0; b < a.B; ++b) {
+      taken += a.rank_sub[h * a.B + b];
+      fl |= a.flags_sub[h * a.B + b];
+    }
+    a.rank[h] = taken;
+    a.flags[h] = fl;
+    a.rank_slots[h] = r;
+  }
+}
+
+hipError_t launch_bins_combine(const BinsArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bins_combine_kernel, dim3(a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace wc

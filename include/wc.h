@@ -26,7 +26,8 @@
  *    factor is contiguous); W [heads][r][dv+1] float; pivots [heads][r] int32;
  *    u_forced [heads][r] float; diag [heads][n] float; trace [heads][r+1] double;
  *    rank [heads] int32; flags [heads] uint32.
- *  - `heads` counts every (batch, head) pair.  Supported: d, dv in {64, 128};
+ *  - `heads` counts every (batch, head) pair.  `bins` selects divide-and-conquer selection in
+ *    wc_forward (see there); 0 or 1 everywhere else.  Supported: d, dv in {64, 128};
  *    dtype WC_F32 or WC_BF16; 1 <= r <= min(n, 4096); n, m >= 1 (m may be 0 for
  *    wc_attend/wc_forward: nothing is written then); heads == 0 is a no-op.
  *  - Every call validates its arguments on the host BEFORE any HIP call; on failure it
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 1
+#define WC_ABI_VERSION 2
 
 typedef enum {
   WC_OK = 0,
@@ -74,6 +75,7 @@ typedef struct {
   int32_t dv;    /* value width: 64 or 128 */
   int32_t r;     /* coreset size (pivot steps) */
   int32_t dtype; /* wc_dtype of Q, K, V and O */
+  int32_t bins;  /* 0 or 1: one bin; B > 1: divide-and-conquer selection (wc_forward only) */
 } wc_problem;
 
 /* ABI version of the loaded library (WC_ABI_VERSION it was built with). */
@@ -130,7 +132,18 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
                     size_t ws_bytes, void* stream);
 
 /* The whole forward: wc_rpcholesky, wc_weights and wc_attend in one call (the factor and the
- * weights live in the workspace).  pivots may be NULL; rank and flags are required.        */
+ * weights live in the workspace).  pivots may be NULL; rank and flags are required.
+ *
+ * bins = B > 1 (divide-and-conquer selection, gist.science/de/paper/2602.10056, "Methodik"
+ * part 1, efficiency: B bins processed in parallel at O(n r^2/B^3 + n r d/B^2)): B must divide
+ * n and r.  Bin b holds the keys [b n/B, (b+1) n/B) and the pivot slots [b r/B, (b+1) r/B);
+ * each bin runs the pivot loop on its keys (u_forced[h][slot], or Philox with counter
+ * (t, h B + b, 0, 0) for the bin's step t), each bin's keys get their own Nystroem weights on
+ * that bin's coreset, and every query attends over the union of the coresets.  pivots[h][j]
+ * is the key index within the head, or -1 for a slot its bin left empty after a breakdown
+ * (no longer only at the end); rank[h] counts the pivots taken over all bins; flags are
+ * OR-ed over the bins.  The other entry points take bins <= 1 (WC_ERR_UNSUPPORTED otherwise):
+ * their per-bin view is the problem with heads * B heads of n/B keys and r/B pivots.        */
 wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
                      const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);

@@ -37,3 +37,9 @@ def snapped(K, r):
 
 def rel(a, b):
     return ow.rel_fro(a, b)
+
+
+def snapped_binned(K, r, B):
+    """Forced uniforms snapped bin by bin (each bin on its own keys), [H, r] float32."""
+    raw = synth.raw_uniforms(K.shape[0], r)
+    return np.stack([ow.snap_uniforms_binned(K[h], r, B, raw[h]) for h in range(K.shape[0])])

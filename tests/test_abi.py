@@ -26,7 +26,7 @@ def lib():
 
 
 class Problem(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype")]
+    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype", "bins")]
 
 
 def test_exports_every_declared_symbol(lib):
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 1
+    assert lib.wc_abi_version() == 2
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -68,6 +68,10 @@ def ws_bytes(lib, p):
     ((1, 100, 10, 64, 96, 5, 1), 2),        # unsupported dv
     ((1, 100, 10, 64, 64, 5, 7), 2),        # unsupported dtype
     ((1, 10000, 10, 64, 64, 4097, 1), 2),   # r above the supported maximum
+    ((2, 4096, 64, 64, 64, 256, 1, 16), 0), # 16 bins
+    ((2, 4096, 64, 64, 64, 256, 1, -1), 1), # negative bins
+    ((2, 4004, 64, 64, 64, 256, 1, 16), 2), # bins do not divide n
+    ((2, 4096, 64, 64, 64, 200, 1, 16), 2), # bins do not divide r
 ])
 def test_workspace_bytes_validation(lib, fields, expect):
     st, nbytes = ws_bytes(lib, Problem(*fields))
@@ -132,3 +136,20 @@ def test_weights_attend_forward_argument_errors(lib):
     assert fw(ctypes.byref(p), A, A, A, None, u64, A, None, A, A, A, ctypes.c_size_t(10), None) == 3
     assert fw(ctypes.byref(Problem(2, 5000, 64, 128, 128, 0, 0)), A, A, A, None, u64, A, None, A, A, A,
               big, None) == 1
+
+
+def test_bins_only_in_forward_and_smaller_workspace(lib):
+    """A binned problem is accepted by wc_workspace_bytes and wc_forward only; its factor is
+    B times smaller (B bins of n/B keys and r/B pivots), so its workspace is smaller."""
+    plain = Problem(8, 131072, 131072, 128, 128, 2048, 1, 1)
+    binned = Problem(8, 131072, 131072, 128, 128, 2048, 1, 16)
+    st1, b1 = ws_bytes(lib, plain)
+    st2, b2 = ws_bytes(lib, binned)
+    assert st1 == 0 and st2 == 0 and b2 < b1 / 4
+    assert call_rpc(lib, binned) == 2
+    big = ctypes.c_size_t(1 << 40)
+    assert lib.wc_weights(ctypes.byref(binned), A, A, A, A, A, A, big, None) == 2
+    assert lib.wc_attend(ctypes.byref(binned), A, A, A, A, A, A, A, A, big, None) == 2
+    # the forward validates its pointers for a binned problem like for a plain one
+    assert lib.wc_forward(ctypes.byref(binned), A, None, A, None, ctypes.c_uint64(0), A, None, A, A,
+                          A, big, None) == 1

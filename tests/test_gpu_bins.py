@@ -1,0 +1,93 @@
+"""Parity of the divide-and-conquer forward (wc_forward with bins > 1) with the binned fp64
+oracle: pivots bit-exact under uniforms snapped bin by bin, outputs within the tolerances.
+Cases run the per-bin pivot loop on the resident kernel (bf16 bins of at most 256 keys and
+32 pivots) and on the streaming loop, fp32 and bf16, d and dv of 64 and 128; plus one bin
+equal to the plain forward, a breakdown confined to one bin, and the seeded mode."""
+import numpy as np
+import pytest
+
+from coreset_head_rpcholesky_amd import synth
+from oracle import philox
+from oracle import wildcat as ow
+from tests.gpu_util import TOL, dev, host, rel, snapped_binned
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wc():
+    import torch  # noqa: F401
+
+    from coreset_head_rpcholesky_amd import binding
+    return binding
+
+
+# (name, dtype, kind, H, n, m, d, dv, r, B)
+CASES = [
+    ("resident_bins", "bf16", "mixture", 2, 1024, 100, 64, 64, 32, 4),
+    ("resident_bins_d128", "bf16", "kv_outlier", 2, 2048, 64, 128, 128, 64, 16),
+    ("stream_bins_bf16", "bf16", "mixture", 2, 4096, 300, 64, 64, 128, 8),
+    ("stream_bins_f32", "f32", "iid_clip", 2, 2048, 77, 128, 64, 64, 4),
+    ("stream_bins_ragged_m", "bf16", "iid_clip", 3, 1536, 257, 64, 128, 48, 3),
+]
+
+
+def case_inputs(case):
+    name, dtype, kind, H, n, m, d, dv, r, B = case
+    return synth.random_inputs(H, n, m, d, dv, seed=700 + CASES.index(case), dtype=dtype, kind=kind,
+                               clip=2.5, clusters=8)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_binned_forward_parity(wc, case):
+    name, dtype, kind, H, n, m, d, dv, r, B = case
+    Q, K, V = case_inputs(case)
+    U = snapped_binned(K, r, B)
+    out = wc.wc_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), r, u_forced=dev(U), bins=B)
+    O, piv, rank, flags = host(out["O"]), host(out["pivots"]), host(out["rank"]), host(out["flags"])
+    for h in range(H):
+        ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h])
+        assert np.array_equal(piv[h], ref["pivots"]), (h, piv[h], ref["pivots"])
+        assert rank[h] == ref["rank"] and flags[h] == ref["flags"], (rank[h], flags[h])
+        ok = ref["kappa"] < 1e6
+        assert rel(O[h][ok], ref["O"][ok]) < TOL[dtype], (h, rel(O[h][ok], ref["O"][ok]))
+
+
+def test_one_bin_is_the_plain_forward(wc):
+    Q, K, V = synth.random_inputs(2, 600, 50, 64, 64, seed=710, dtype="bf16", kind="mixture")
+    args = (dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), 24)
+    a = wc.wc_forward(*args, seed=3, bins=1)
+    b = wc.wc_forward(*args, seed=3)
+    assert np.array_equal(host(a["pivots"]), host(b["pivots"]))
+    assert np.array_equal(host(a["O"]), host(b["O"]))
+
+
+def test_breakdown_confined_to_one_bin(wc):
+    """Bin 0 of head 0 holds only zero keys (H = 1 there exactly, rank one in any precision):
+    its other slots stay empty (-1), the head is flagged, and the output matches the oracle,
+    which skips those slots too."""
+    H, n, m, r, B = 2, 1024, 40, 32, 4
+    Q, K, V = synth.random_inputs(H, n, m, 64, 64, seed=711, dtype="bf16", kind="mixture")
+    K[0, : n // B] = 0.0
+    U = snapped_binned(K, r, B)
+    out = wc.wc_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), r, u_forced=dev(U), bins=B)
+    piv, rank, flags, O = host(out["pivots"]), host(out["rank"]), host(out["flags"]), host(out["O"])
+    ref = ow.forward_binned(Q[0], K[0], V[0], r, B, U[0])
+    assert np.array_equal(piv[0], ref["pivots"])
+    assert np.all(piv[0, 1:r // B] == -1) and rank[0] == ref["rank"] == r - r // B + 1
+    assert flags[0] & 1 and flags[1] == 0 and rank[1] == r
+    assert rel(O[0], ref["O"]) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("n,r,B", [(1024, 32, 4), (4096, 64, 8)])
+def test_binned_seeded_mode(wc, n, r, B):
+    """Seeded mode: bin b of head h draws Philox with counter (t, h B + b)."""
+    H, seed = 3, 99
+    Q, K, V = synth.random_inputs(H, n, 30, 64, 64, seed=712, dtype="bf16", kind="mixture")
+    out = wc.wc_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), r, seed=seed, bins=B)
+    piv = host(out["pivots"])
+    agree = 0
+    for h in range(H):
+        u = np.concatenate([philox.pivot_uniforms(seed, h * B + b, r // B) for b in range(B)])
+        agree += np.array_equal(piv[h], ow.forward_binned(Q[h], K[h], V[h], r, B, u)["pivots"])
+    assert agree >= H - 1, agree
