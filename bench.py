@@ -68,14 +68,17 @@ def stored_traffic(workload: str, kind: str):
         return None
 
 
-def workload_accounting(w):
-    """Algorithmic bytes and flops of one forward over all heads (per-head figures x heads)."""
+def workload_accounting(w, bins: int = 1):
+    """Algorithmic bytes and flops of one forward over all heads (per-head figures x heads).
+    With bins, the pivot loop and the weights run on heads x bins sub-heads of n/bins keys
+    and r/bins pivots; the attention still covers all r coreset rows per head."""
     b = 2 if w.dtype == "bf16" else 4
     H, n, m, d, dv, r = w.heads, w.n, w.m, w.d, w.dv, w.r
     compulsory = H * ((m * d + n * d + n * dv) * b + m * dv * b)
-    pivot_bytes = H * (n * r * d * b + 2 * n * r * (r - 1) + 12 * n * r)
-    pivot_flops = H * (2 * n * r * d + n * r * (r - 1))
-    weight_flops = H * (2 * r * n * (dv + 1) + r * r * (dv + 1))
+    Hs, ns, rs = H * bins, n // bins, r // bins
+    pivot_bytes = Hs * (ns * rs * d * b + 2 * ns * rs * (rs - 1) + 12 * ns * rs)
+    pivot_flops = Hs * (2 * ns * rs * d + ns * rs * (rs - 1))
+    weight_flops = Hs * (2 * rs * ns * (dv + 1) + rs * rs * (dv + 1))
     attend_flops = H * 2 * m * r * (d + dv + 1)
     return dict(compulsory_bytes=compulsory, pivot_bytes=pivot_bytes, pivot_flops=pivot_flops,
                 weight_flops=weight_flops, attend_flops=attend_flops)
@@ -113,7 +116,20 @@ def exact_attention_timing(w, Q, K, V, stream):
     return {"error": err}
 
 
-def cpu_baseline(w, Q, K, V, budget_s: float):
+def error_vs_exact(w, Q, K, V, O, rows: int = 256):
+    """Relative Frobenius error of the WildCat output against exact softmax attention (fp32,
+    on the GPU) over up to `rows` evenly spaced queries per head, the mean over heads."""
+    import torch
+
+    idx = torch.linspace(0, w.m - 1, min(rows, w.m), device=Q.device).round().long().unique()
+    q = Q[:, idx].float().unsqueeze(0)
+    ex = torch.nn.functional.scaled_dot_product_attention(q, K.float().unsqueeze(0), V.float().unsqueeze(0))[0]
+    got = O[:, idx].float()
+    err = torch.linalg.vector_norm(got - ex, dim=(1, 2)) / torch.linalg.vector_norm(ex, dim=(1, 2))
+    return round(float(err.mean()), 6)
+
+
+def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1):
     """The fp64 oracle on as many heads as fit in the time budget; tokens/s scaled to the
     whole workload (tokens per head = tokens / heads)."""
     import numpy as np
@@ -132,8 +148,12 @@ def cpu_baseline(w, Q, K, V, budget_s: float):
     t0 = time.perf_counter()
     done = 0
     for h in range(w.heads):
-        u = np.array(philox.pivot_uniforms(42, h, w.r))
-        ow.forward(Q[h], K[h], V[h], w.r, u)
+        if bins > 1:
+            u = np.concatenate([philox.pivot_uniforms(42, h * bins + b, w.r // bins) for b in range(bins)])
+            ow.forward_binned(Q[h], K[h], V[h], w.r, bins, u)
+        else:
+            u = np.array(philox.pivot_uniforms(42, h, w.r))
+            ow.forward(Q[h], K[h], V[h], w.r, u)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -142,8 +162,8 @@ def cpu_baseline(w, Q, K, V, budget_s: float):
         limiter.unregister()
     tokens = w.tokens * done / w.heads
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {w.heads} heads of one {w.name} forward, fp64 numpy/scipy, "
-                      f"{dt:.1f} s"}
+            "sample": f"{done} of {w.heads} heads of one {w.name} forward"
+                      f"{f' with {bins} bins' if bins > 1 else ''}, fp64 numpy/scipy, {dt:.1f} s"}
 
 
 def main():
@@ -153,6 +173,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="vit197")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--bins", type=int, default=1,
+                    help="divide-and-conquer selection with this many bins (must divide n and r)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
@@ -183,7 +205,8 @@ def main():
         return torch.from_numpy(x).to(dev, dt_t).contiguous()
 
     Q, K, V = up(Qn), up(Kn), up(Vn)
-    p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t)
+    bins = max(1, args.bins)
+    p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t, bins)
     ws = binding.workspace(p, dev)
     out = dict(O=torch.empty((w.heads, w.m, w.dv), dtype=dt_t, device=dev),
                pivots=torch.empty((w.heads, w.r), dtype=torch.int32, device=dev),
@@ -199,7 +222,7 @@ def main():
         del src, dst
 
     def fwd():
-        binding.wc_forward(Q, K, V, w.r, seed=args.seed, ws=ws, out=out)
+        binding.wc_forward(Q, K, V, w.r, seed=args.seed, bins=bins, ws=ws, out=out)
 
     # One forward is captured in a HIP graph and replayed: the host-side launch path (Python,
     # ctypes, one launch per pivot step on the streaming path) would otherwise be what is timed.
@@ -247,8 +270,8 @@ def main():
     rank = out["rank"].cpu().numpy()
     flags = out["flags"].cpu().numpy()
 
-    acc = workload_accounting(w)
-    resident = w.dtype == "bf16" and w.n <= 256 and w.r <= 32
+    acc = workload_accounting(w, bins)
+    resident = w.dtype == "bf16" and w.n <= 256 and w.r <= 32 and bins == 1
     if resident:
         # one launch per step: the resident kernel; only compulsory bytes reach HBM
         kernel_ms = float(np.mean(per))
@@ -260,9 +283,13 @@ def main():
                 "algorithmic_bytes_per_launch": acc["compulsory_bytes"],
                 "avg_launch_ms": round(kernel_ms, 5)}
     else:
-        # the pivot loop dominates: time wc_rpcholesky alone (graph replay) on the same stream
+        # the pivot loop dominates: time wc_rpcholesky alone (graph replay) on the same stream;
+        # with bins, on the per-bin view (heads x bins sub-heads), which is what the forward runs
+        Ksel = K.view(w.heads * bins, w.n // bins, w.d)
+        pws = binding.workspace(binding.problem(w.heads * bins, w.n // bins, 0, w.d, w.dv, w.r // bins, dt_t), dev)
+
         def rpc():
-            binding.wc_rpcholesky(K, w.r, seed=args.seed, ws=ws, with_diag=False, with_trace=False)
+            binding.wc_rpcholesky(Ksel, w.r // bins, seed=args.seed, ws=pws, with_diag=False, with_trace=False)
 
         rgraph = None
         if not args.no_graph:
@@ -281,7 +308,8 @@ def main():
         torch.cuda.synchronize()
         loop_ms = e0.elapsed_time(e1)
         achieved = acc["pivot_bytes"] / (loop_ms / 1e3) / 1e9
-        roof = {"kernel": f"rpc_step_kernel x {w.r} launches (streaming pivot loop)", "bound": "hbm",
+        roof = {"kernel": f"rpc_step_kernel x {w.r // bins} launches (streaming pivot loop"
+                          f"{f', {w.heads * bins} bins' if bins > 1 else ''})", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_loop": acc["pivot_bytes"], "loop_ms": round(loop_ms, 3)}
@@ -289,10 +317,11 @@ def main():
     exact = None
     if not args.no_exact:
         exact = exact_attention_timing(w, Q, K, V, stream)
+        exact["rel_err_of_wildcat"] = error_vs_exact(w, Q, K, V, out["O"])
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, Qn, Kn, Vn, args.cpu_budget)
+        cpu = cpu_baseline(w, Qn, Kn, Vn, args.cpu_budget, bins)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -300,7 +329,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "heads": w.heads, "n": w.n,
-                   "m": w.m, "d": w.d, "dv": w.dv, "r": w.r, "tokens_per_step": w.tokens,
+                   "m": w.m, "d": w.d, "dv": w.dv, "r": w.r, "bins": bins, "tokens_per_step": w.tokens,
                    "pivot_uniforms": f"Philox4x64-10 seed {args.seed}"},
         "roofline": roof,
         "cpu_baseline": cpu,
