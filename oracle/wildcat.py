@@ -12,7 +12,12 @@ Sources (the pages, cited by title and section):
 Where the pages leave a step open, the reading is:
   * beta = 1/sqrt(d) (softmax kernel exp(<x, y>/sqrt(d))).
   * One bin: r sequential pivot steps over all n keys of a head (forward); B contiguous bins
-    with r/B steps each and per-bin weights (forward_binned, see there).
+    with r/B steps each, then Nystroem weights over the union of the bins' pivots
+    (forward_binned, see there; per-bin weights as an option).
+  * The pseudo-inverse of H_SS over such a union is taken by a Cholesky in slot order that
+    leaves out every point whose residual is at most DEPENDENT_TOL times its diagonal entry
+    (numerically in the span of the earlier points; weight row zero).  For distinct keys
+    nothing is left out and it is the inverse.
   * Step t: p = max(diag, 0); C = running sum of p (sequential, fp64); T = C[n-1];
     s = min{i : C_i > u_t T}; g = H[:, s] - F[:, :t] F[s, :t]^T; F[:, t] = g / sqrt(g[s]);
     diag -= F[:, t]^2; diag[s] = 0.  Breakdown (T <= 0, g[s] <= 0 or either not finite)
@@ -34,6 +39,12 @@ from scipy.linalg import cho_factor, cho_solve
 FLAG_BREAKDOWN = 1  # rank < r: the residual vanished (T <= 0) or a pivot's g[s] <= 0
 FLAG_NONFINITE = 2  # a non-finite value reached the pivot loop
 FLAG_DENOM = 4      # some query row had a Nystroem denominator Y[:, dv] <= 0
+FLAG_DEPENDENT = 8  # union weights left out a coreset point numerically dependent on earlier ones
+
+# Relative residual g_j / H_jj at or below which a point of a union coreset counts as dependent:
+# 2^-12, above the fp32 rounding of the residual (about r 2^-24 at r = 4096) and far below the
+# residuals of distinct keys under bounded inputs.
+DEPENDENT_TOL = 2.0 ** -12
 
 
 def beta_of(d: int) -> float:
@@ -209,16 +220,66 @@ def bin_bounds(n, r, B):
     return [(b * nb, (b + 1) * nb, b * rb, (b + 1) * rb) for b in range(B)]
 
 
-def forward_binned(Q, K, V, r, B, uniforms, beta=None):
+def independent_slots(H_SS, tol=DEPENDENT_TOL):
+    """Which points of a coreset to keep for the pseudo-inverse of H_SS.
+
+    Cholesky of H_SS in slot order, one column at a time: point j's residual is
+    g_j = H_jj - sum over the kept earlier points c of L[j, c]^2.  If g_j > tol H_jj the point
+    is kept and column j of L is the residual column over sqrt(g_j); otherwise it is left out
+    (column j of L stays zero).  A slot whose diagonal entry is zero (an empty slot) is never
+    kept.  Returns a boolean mask.
+    """
+    H = np.asarray(H_SS, np.float64)
+    r = H.shape[0]
+    L = np.zeros((r, r))
+    keep = np.zeros(r, bool)
+    for j in range(r):
+        g = H[j:, j] - L[j:, :j] @ L[j, :j]
+        if g[0] > tol * H[j, j]:
+            keep[j] = True
+            L[j:, j] = g / np.sqrt(g[0])
+    return keep
+
+
+def weights_union(K, V, slots, beta=None, tol=DEPENDENT_TOL):
+    """Nystroem weights over a coreset given slot by slot, W = H_SS^+ H_{S,:} [V, 1].
+
+    "Methodik" part 2 with the union of the bins' pivots as K_S.  ``slots`` holds key indices,
+    -1 for an empty slot.  The pseudo-inverse is taken on the points independent_slots keeps:
+    W[kept] solves H[kept, kept] W = H[kept, :] [V, 1] (Cholesky), every other row is zero.
+    Returns (W [r, dv+1], kept mask [r]).
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    beta = beta_of(K.shape[1]) if beta is None else beta
+    slots = np.asarray(slots, np.int64)
+    r, dv = len(slots), V.shape[1]
+    idx = np.nonzero(slots >= 0)[0]
+    KS = K[slots[idx]]
+    keep_v = independent_slots(kernel(KS, KS, beta), tol)
+    kept = np.zeros(r, bool)
+    kept[idx[keep_v]] = True
+    W = np.zeros((r, dv + 1))
+    if kept.any():
+        S = slots[kept]
+        V1 = np.hstack([V, np.ones((V.shape[0], 1))])
+        W[kept] = cho_solve(cho_factor(kernel(K[S], K[S], beta), lower=True), kernel(K[S], K, beta) @ V1)
+    return W, kept
+
+
+def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union"):
     """One head of divide-and-conquer WildCat with B bins.
 
     "Methodik" part 1 (efficiency): the input is split into B bins that are processed in
-    parallel, at O(n r^2 / B^3 + n r d / B^2), i.e. n/B keys and r/B pivots per bin.  Reading
-    taken where the pages are silent: the bins are contiguous blocks of keys; each bin runs
-    the pivot loop on its own keys with slots [b r/B, (b+1) r/B) of ``uniforms``; each bin's
-    keys get their own Nystroem weights on that bin's coreset, W_b = H_{S_b S_b}^{-1}
-    H_{S_b, bin b} [V_b, 1] ("Methodik" part 2 applied per bin); and every query attends over
-    the union of the coresets, Y = sum_b exp(beta Q K_{S_b}^T) W_b, O = Y[:, :dv] / Y[:, dv].
+    parallel, at O(n r^2 / B^3 + n r d / B^2), i.e. n/B keys and r/B pivots per bin; part 2:
+    once the coreset K_S is chosen, its Nystroem weights.  Readings taken where the pages are
+    silent: the bins are contiguous blocks of keys; each bin runs the pivot loop on its own
+    keys with slots [b r/B, (b+1) r/B) of ``uniforms``; K_S is the union of the bins' pivots in
+    slot order, and
+      * weights_mode "union": W = H_SS^+ H_{S,:} [V, 1] over all keys (weights_union);
+      * weights_mode "bin": each bin's keys get their own weights on that bin's coreset,
+        W_b = H_{S_b S_b}^{-1} H_{S_b, bin b} [V_b, 1]  (a block-diagonal stand-in, cheaper);
+    every query attends over the union, Y = exp(beta Q K_S^T) W, O = Y[:, :dv] / Y[:, dv].
     Pivots are returned as key indices of the head, bin by bin; a slot left empty by a
     breakdown in its bin holds -1 and a zero row of W.
     """
@@ -227,6 +288,8 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None):
     n, d = K.shape
     dv = V.shape[1]
     beta = beta_of(d) if beta is None else beta
+    if weights_mode not in ("union", "bin"):
+        raise ValueError("weights_mode is 'union' or 'bin'")
     pivots = -np.ones(r, np.int64)
     W = np.zeros((r, dv + 1))
     rank, flags = 0, 0
@@ -234,15 +297,21 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None):
         rpc = rpcholesky(K[k0:k1], s1 - s0, uniforms[s0:s1], beta)
         rb = rpc["rank"]
         Sb = rpc["pivots"][:rb]
-        if rb:
+        if rb and weights_mode == "bin":
             W[s0:s0 + rb] = weights(K[k0:k1], V[k0:k1], Sb, beta)
         pivots[s0:s0 + rb] = Sb + k0
         rank += rb
         flags |= rpc["flags"]
+    kept = pivots >= 0
+    if weights_mode == "union":
+        W, kept = weights_union(K, V, pivots, beta)
+        if np.any(kept != (pivots >= 0)):
+            flags |= FLAG_DEPENDENT
     valid = pivots >= 0
     O, denom, kappa = attend(Q, K, pivots[valid], W[valid], beta)
     flags |= FLAG_DENOM if np.any(~(denom > 0.0)) else 0
-    return dict(O=O, W=W, denom=denom, kappa=kappa, pivots=pivots, rank=rank, flags=flags)
+    return dict(O=O, W=W, denom=denom, kappa=kappa, pivots=pivots, rank=rank, flags=flags,
+                kept=kept)
 
 
 def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None):

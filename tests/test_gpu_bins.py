@@ -46,7 +46,7 @@ def test_binned_forward_parity(wc, case):
     out = wc.wc_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), r, u_forced=dev(U), bins=B)
     O, piv, rank, flags = host(out["O"]), host(out["pivots"]), host(out["rank"]), host(out["flags"])
     for h in range(H):
-        ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h])
+        ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h], weights_mode="bin")
         assert np.array_equal(piv[h], ref["pivots"]), (h, piv[h], ref["pivots"])
         assert rank[h] == ref["rank"] and flags[h] == ref["flags"], (rank[h], flags[h])
         ok = ref["kappa"] < 1e6
@@ -72,7 +72,7 @@ def test_breakdown_confined_to_one_bin(wc):
     U = snapped_binned(K, r, B)
     out = wc.wc_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), r, u_forced=dev(U), bins=B)
     piv, rank, flags, O = host(out["pivots"]), host(out["rank"]), host(out["flags"]), host(out["O"])
-    ref = ow.forward_binned(Q[0], K[0], V[0], r, B, U[0])
+    ref = ow.forward_binned(Q[0], K[0], V[0], r, B, U[0], weights_mode="bin")
     assert np.array_equal(piv[0], ref["pivots"])
     assert np.all(piv[0, 1:r // B] == -1) and rank[0] == ref["rank"] == r - r // B + 1
     assert flags[0] & 1 and flags[1] == 0 and rank[1] == r
