@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(_HERE, "libwc.so")
 
 WC_OK, WC_ERR_INVALID_ARG, WC_ERR_UNSUPPORTED, WC_ERR_WORKSPACE, WC_ERR_DEVICE = range(5)
 WC_F32, WC_BF16 = 0, 1
-WC_FLAG_BREAKDOWN, WC_FLAG_NONFINITE, WC_FLAG_DENOM = 1, 2, 4
+WC_FLAG_BREAKDOWN, WC_FLAG_NONFINITE, WC_FLAG_DENOM, WC_FLAG_DEPENDENT = 1, 2, 4, 8
+WC_OPT_BIN_WEIGHTS = 1
 
 
 class WcProblem(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("n", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dv", ctypes.c_int32), ("r", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("bins", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("bins", ctypes.c_int32), ("options", ctypes.c_int32)]
 
 
 class WcError(RuntimeError):
@@ -69,10 +70,11 @@ def status_string(status: int) -> str:
 wc_status_string = status_string
 
 
-def problem(heads, n, m, d, dv, r, dtype, bins: int = 1) -> WcProblem:
+def problem(heads, n, m, d, dv, r, dtype, bins: int = 1, options: int = 0) -> WcProblem:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: WC_F32, torch.bfloat16: WC_BF16}[dtype]
-    return WcProblem(int(heads), int(n), int(m), int(d), int(dv), int(r), int(dtype), int(bins))
+    return WcProblem(int(heads), int(n), int(m), int(d), int(dv), int(r), int(dtype), int(bins),
+                     int(options))
 
 
 def wc_workspace_bytes(p: WcProblem) -> int:
@@ -174,14 +176,16 @@ def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, 
 
 
 def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_forced=None,
-               seed: int = 0, bins: int = 1, ws=None, out=None, stream=None):
+               seed: int = 0, bins: int = 1, bin_weights: bool = False, ws=None, out=None,
+               stream=None):
     """The whole WildCat forward; returns dict(O, pivots, rank, flags).  bins > 1: the
-    divide-and-conquer selection of the C entry point (bins must divide n and r)."""
+    divide-and-conquer selection of the C entry point (bins must divide n and r), with weights
+    over the union of the bins' coresets, or per bin when ``bin_weights``."""
     H, m, d = Q.shape
     n = K.shape[1]
     dv = V.shape[2]
     dev = Q.device
-    p = problem(H, n, m, d, dv, r, Q.dtype, bins)
+    p = problem(H, n, m, d, dv, r, Q.dtype, bins, WC_OPT_BIN_WEIGHTS if bin_weights else 0)
     _check_in("K", K, Q.dtype, (H, n, d), dev)
     _check_in("V", V, Q.dtype, (H, n, dv), dev)
     if u_forced is not None:

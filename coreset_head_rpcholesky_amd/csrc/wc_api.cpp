@@ -28,6 +28,7 @@ wc_status check_problem(const wc_problem* p) {
   if (p->dtype != WC_F32 && p->dtype != WC_BF16) return WC_ERR_UNSUPPORTED;
   if (p->r > kMaxR) return WC_ERR_UNSUPPORTED;
   if (p->bins < 0) return WC_ERR_INVALID_ARG;
+  if ((uint32_t)p->options & ~(uint32_t)WC_OPT_BIN_WEIGHTS) return WC_ERR_INVALID_ARG;
   if (p->bins > 1 && (p->n % p->bins != 0 || p->r % p->bins != 0)) return WC_ERR_UNSUPPORTED;
   if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
   return WC_OK;
@@ -43,6 +44,7 @@ bool resident_ok(const wc_problem& p) {
 }
 
 bool binned(const wc_problem& p) { return p.bins > 1; }
+bool union_weights(const wc_problem& p) { return binned(p) && !(p.options & WC_OPT_BIN_WEIGHTS); }
 
 // The per-bin view of a binned problem: heads * B sub-heads of n/B keys and r/B pivots.
 wc_problem sub_problem(const wc_problem& p) {
@@ -52,7 +54,27 @@ wc_problem sub_problem(const wc_problem& p) {
   s.r = p.r / p.bins;
   s.m = 0;
   s.bins = 1;
+  s.options = 0;
   return s;
+}
+
+// Coreset split of the attention: when the query tiles alone give too few workgroups, the
+// coreset rows (chunks of 64 for bf16, 32 for fp32) are shared out over nsplit workgroups
+// whose partial sums are reduced afterwards.
+int attend_split(const wc_problem& p, size_t m, size_t coreset_rows) {
+  const size_t H = (size_t)p.heads;
+  const size_t cw = p.dtype == WC_BF16 ? 64 : 32;
+  const size_t qw = p.dtype == WC_BF16 ? 256 : 128;
+  const size_t nchk = (size_t)wc::attend_rows((int)coreset_rows) / cw;
+  const size_t qtiles = (m + qw - 1) / qw;
+  size_t nsplit = 1;
+  if (qtiles * H < 512 && qtiles > 0) {
+    nsplit = (512 + qtiles * H - 1) / (qtiles * H);
+    if (nsplit > nchk) nsplit = nchk;
+    const size_t per = (nchk + nsplit - 1) / nsplit;
+    nsplit = (nchk + per - 1) / per;
+  }
+  return (int)nsplit;
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -85,21 +107,8 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
   crow = (crow + 63) & ~size_t(63);
   L.chunk_rows = (int)crow;
   L.nchunk = (int)((n + crow - 1) / crow);
-  // attention: split the coreset when the queries alone give too few workgroups (chunks of
-  // 64 coreset rows and 256 queries per workgroup for bf16, 32 and 128 for fp32)
   L.rp = wc::attend_rows((int)r);
-  const size_t cw = p.dtype == WC_BF16 ? 64 : 32;
-  const size_t qw = p.dtype == WC_BF16 ? 256 : 128;
-  const size_t nchk = (size_t)L.rp / cw;
-  const size_t qtiles = (m + qw - 1) / qw;
-  size_t nsplit = 1;
-  if (qtiles * H < 512 && qtiles > 0) {
-    nsplit = (512 + qtiles * H - 1) / (qtiles * H);
-    if (nsplit > nchk) nsplit = nchk;
-    const size_t per = (nchk + nsplit - 1) / nsplit;
-    nsplit = (nchk + per - 1) / per;
-  }
-  L.nsplit = (int)nsplit;
+  L.nsplit = attend_split(p, m, r);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   if (parts & kSelect) {
@@ -130,10 +139,14 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
 }
 
 // Workspace of a binned forward: the per-bin selection and weights (the sub-head layout, whose
-// W is the heads' W), the heads' attention buffers, and the per-bin outputs.
+// W is the heads' W), the heads' attention buffers, the per-bin outputs, and for the union
+// weights the all-keys pass X = exp(beta K_S K^T) [V, 1] and the blocked solve.
 struct BinnedLayout {
   Layout sub, head;
   size_t head_base, piv_sub, rank_sub, flags_sub, rank_slots, piv, total;
+  // union weights
+  int urp, xsplit;
+  size_t Qs, A, Hd, M, X, xKSh, xKSl, xWph, xWpl, xWden, xWdh, xYpart;
 };
 
 BinnedLayout make_binned_layout(const wc_problem& p) {
@@ -151,6 +164,25 @@ BinnedLayout make_binned_layout(const wc_problem& p) {
   B.flags_sub = take(H * p.bins * 4);
   B.rank_slots = take(H * 4);
   B.piv = take(H * r * 4);
+  if (union_weights(p)) {
+    const size_t n = (size_t)p.n, nc = (size_t)p.dv + 1, esz = p.dtype == WC_F32 ? 4 : 2;
+    const size_t lo = p.dtype == WC_F32 ? 1 : 0;
+    const size_t urp = (r + 63) & ~size_t(63), np = (size_t)wc::attend_rows(p.n);
+    B.urp = (int)urp;
+    B.xsplit = attend_split(p, r, n);
+    B.Qs = take(H * r * p.d * esz);
+    B.A = take(H * urp * urp * 4);
+    B.Hd = take(H * urp * 4);
+    B.M = take(H * urp * 64 * 4);
+    B.X = take(H * urp * nc * 4);
+    B.xKSh = take(H * np * p.d * 2);
+    B.xKSl = take(lo * H * np * p.d * 2);
+    B.xWph = take(H * p.dv * np * 2);
+    B.xWpl = take(lo * H * p.dv * np * 2);
+    B.xWden = take(H * np * 4);
+    B.xWdh = take(H * np * 2);
+    B.xYpart = take(B.xsplit > 1 ? H * B.xsplit * r * nc * 4 : 0);
+  }
   B.total = off;
   return B;
 }
@@ -262,7 +294,7 @@ wc_status forward_binned(const wc_problem& p, const void* Q, const void* K, cons
   float* F = at<float>(ws, B.sub.F);
   float* W = at<float>(ws, B.sub.W);
   hipError_t e = run_select(sp, B.sub, ws, K, u_forced, seed, piv_sub, F, rank_sub, flags_sub, s);
-  if (e == hipSuccess) e = run_weights(sp, B.sub, ws, V, piv_sub, rank_sub, F, W, s);
+  if (e == hipSuccess && !union_weights(p)) e = run_weights(sp, B.sub, ws, V, piv_sub, rank_sub, F, W, s);
   int32_t* piv = pivots ? pivots : at<int32_t>(ws, B.piv);
   int32_t* slots = at<int32_t>(ws, B.rank_slots);
   if (e == hipSuccess) {
@@ -271,6 +303,39 @@ wc_status forward_binned(const wc_problem& p, const void* Q, const void* K, cons
     a.piv_sub = piv_sub; a.rank_sub = rank_sub; a.flags_sub = flags_sub;
     a.pivots = piv; a.rank = rank; a.flags = flags; a.rank_slots = slots;
     e = wc::launch_bins_combine(a, s);
+  }
+  if (e == hipSuccess && union_weights(p)) {
+    wc::UnionArgs u{};
+    u.K = K; u.bf16 = p.dtype == WC_BF16;
+    u.H = p.heads; u.n = p.n; u.d = p.d; u.dv = p.dv; u.r = p.r; u.rp = B.urp;
+    u.beta = (float)(1.0 / std::sqrt((double)p.d));
+    u.tol = 0x1p-12f;
+    u.pivots = piv;
+    u.Qs = at<void>(ws, B.Qs);
+    u.A = at<float>(ws, B.A); u.Hd = at<float>(ws, B.Hd); u.M = at<float>(ws, B.M);
+    u.X = at<float>(ws, B.X); u.W = W; u.flags = flags;
+    e = wc::launch_union_gather(u, s);
+    if (e == hipSuccess) {
+      // X = exp(beta K_S K^T) [V, 1]: the attention kernels with the coreset keys as queries
+      // and every key as a coreset row
+      wc::AttendArgs x{};
+      x.Q = u.Qs; x.K = K; x.V = V;
+      x.bf16 = u.bf16;
+      x.H = p.heads; x.n = p.n; x.m = p.r; x.d = p.d; x.dv = p.dv; x.r = p.n;
+      x.beta_log2e = beta_log2e(p.d);
+      x.KSh = at<uint16_t>(ws, B.xKSh);
+      x.KSl = p.dtype == WC_F32 ? at<uint16_t>(ws, B.xKSl) : nullptr;
+      x.Wph = at<uint16_t>(ws, B.xWph);
+      x.Wpl = p.dtype == WC_F32 ? at<uint16_t>(ws, B.xWpl) : nullptr;
+      x.Wden = at<float>(ws, B.xWden);
+      x.Wdh = at<uint16_t>(ws, B.xWdh);
+      x.nsplit = B.xsplit;
+      x.Ypart = B.xsplit > 1 ? at<float>(ws, B.xYpart) : nullptr;
+      x.flags = flags;
+      x.Yout = u.X; x.yrows = B.urp;
+      e = wc::launch_attend_all_keys(x, s);
+    }
+    if (e == hipSuccess) e = wc::launch_union_solve(u, s);
   }
   wc_problem hp = p;
   hp.bins = 1;

@@ -75,6 +75,45 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   }
 }
 
+// Every key as a coreset row (row j = key j, rows past n zero) with W = [V, 1]: the staged
+// operands of Y = exp(beta Q K^T) [V, 1].
+template <typename T, int D, int DV>
+__global__ void __launch_bounds__(128) attend_prep_keys_kernel(AttendArgs a) {
+  constexpr bool SPLIT = sizeof(T) == 4;
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int rp = attend_rows(a.r);
+  const bool valid = j < a.n;
+  const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + (valid ? j : 0)) * D;
+  const T* V = reinterpret_cast<const T*>(a.V) + ((size_t)h * a.n + (valid ? j : 0)) * DV;
+  for (int e = tid; e < D; e += 128) {
+    const float v = valid ? ld_elem<T>(K + e) : 0.f;
+    __bf16 hi, lo;
+    split_bf16(v, hi, lo);
+    const size_t o = (size_t)h * rp * D + ks_index(j, e, D);
+    a.KSh[o] = bf16_bits(hi);
+    if (SPLIT) a.KSl[o] = bf16_bits(lo);
+  }
+  const int p = perm32_a(j);
+  for (int c = tid; c < DV; c += 128) {
+    const float w = valid ? ld_elem<T>(V + c) : 0.f;
+    __bf16 hi, lo;
+    split_bf16(w, hi, lo);
+    const size_t o = (size_t)h * DV * rp + wt_index(c, p, DV);
+    a.Wph[o] = bf16_bits(hi);
+    if (SPLIT) a.Wpl[o] = bf16_bits(lo);
+  }
+  if (tid == 0) {
+    const float wd = valid ? 1.f : 0.f;
+    a.Wden[(size_t)h * rp + j] = wd;
+    a.Wdh[(size_t)h * rp + p] = bf16_bits((__bf16)wd);
+  }
+}
+
+// Row q of head h of the unnormalised output (fp32, dv + 1 columns).
+__device__ __forceinline__ float* yout_row(const AttendArgs& a, int h, int q) {
+  return a.Yout + ((size_t)h * a.yrows + q) * (a.dv + 1);
+}
+
 template <typename T, int D, int DV>
 __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;
@@ -169,7 +208,15 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
       }
   }
   den += __shfl_xor(den, 32, 64);
-  if (a.nsplit == 1) {
+  if (a.nsplit == 1 && a.Yout) {
+    if (!qv) return;
+    float* Y = yout_row(a, h, q);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) Y[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[ct][v];
+    if (g == 0) Y[DV] = den;
+  } else if (a.nsplit == 1) {
     if (!qv) return;
     if (!(den > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
     const float inv = 1.0f / den;
@@ -403,7 +450,14 @@ attend_bf16_kernel(AttendArgs a) {
     dn += __shfl_xor(dn, 32, 64);
     const int q = q0 + 32 * s;
     if (q >= m) continue;
-    if (a.nsplit == 1) {
+    if (a.nsplit == 1 && a.Yout) {
+      float* Y = yout_row(a, h, q);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Y[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
+      if (g == 0) Y[DV] = dn;
+    } else if (a.nsplit == 1) {
       if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
       const float inv = 1.0f / dn;
       uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
@@ -440,6 +494,16 @@ __global__ void __launch_bounds__(256) attend_reduce_kernel(AttendArgs a) {
   const float* Yp = a.Ypart + ((size_t)h * a.nsplit * a.m + q) * (DV + 1);
   float den = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) den += Yp[sp * stride + DV];
+  if (a.Yout) {
+    float* Y = yout_row(a, h, q);
+    for (int c = 0; c < DV; ++c) {
+      float y = 0.f;
+      for (int sp = 0; sp < a.nsplit; ++sp) y += Yp[sp * stride + c];
+      Y[c] = y;
+    }
+    Y[DV] = den;
+    return;
+  }
   if (!(den > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
   const float inv = 1.0f / den;
   T* O = reinterpret_cast<T*>(a.O) + ((size_t)h * a.m + q) * DV;
@@ -451,11 +515,29 @@ __global__ void __launch_bounds__(256) attend_reduce_kernel(AttendArgs a) {
 }
 
 template <typename T, int D, int DV>
+static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st);
+
+template <typename T, int D, int DV>
 static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
   const int rp = attend_rows(a.r);
   hipLaunchKernelGGL((attend_prep_kernel<T, D, DV>), dim3(rp, a.H), dim3(128), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
+  return run_attend_core<T, D, DV>(a, st);
+}
+
+template <typename T, int D, int DV>
+static hipError_t run_attend_all_keys(const AttendArgs& a, hipStream_t st) {
+  const int rp = attend_rows(a.r);
+  hipLaunchKernelGGL((attend_prep_keys_kernel<T, D, DV>), dim3(rp, a.H), dim3(128), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.m == 0) return e;
+  return run_attend_core<T, D, DV>(a, st);
+}
+
+template <typename T, int D, int DV>
+static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st) {
+  hipError_t e;
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((attend_bf16_kernel<D, DV>), dim3((a.m + kAttendQueries - 1) / kAttendQueries, a.H, a.nsplit),
                        dim3(64 * kAttendWaves), 0, st, a);
@@ -476,6 +558,16 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   }
   if (a.d == 64) return a.dv == 64 ? run_attend<float, 64, 64>(a, st) : run_attend<float, 64, 128>(a, st);
   return a.dv == 64 ? run_attend<float, 128, 64>(a, st) : run_attend<float, 128, 128>(a, st);
+}
+
+hipError_t launch_attend_all_keys(const AttendArgs& a, hipStream_t st) {
+  if (a.bf16) {
+    if (a.d == 64)
+      return a.dv == 64 ? run_attend_all_keys<uint16_t, 64, 64>(a, st) : run_attend_all_keys<uint16_t, 64, 128>(a, st);
+    return a.dv == 64 ? run_attend_all_keys<uint16_t, 128, 64>(a, st) : run_attend_all_keys<uint16_t, 128, 128>(a, st);
+  }
+  if (a.d == 64) return a.dv == 64 ? run_attend_all_keys<float, 64, 64>(a, st) : run_attend_all_keys<float, 64, 128>(a, st);
+  return a.dv == 64 ? run_attend_all_keys<float, 128, 64>(a, st) : run_attend_all_keys<float, 128, 128>(a, st);
 }
 
 }  // namespace wc

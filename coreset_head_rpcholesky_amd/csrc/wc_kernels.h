@@ -8,6 +8,7 @@
 #define WC_DFLAG_BREAKDOWN 1u
 #define WC_DFLAG_NONFINITE 2u
 #define WC_DFLAG_DENOM 4u
+#define WC_DFLAG_DEPENDENT 8u
 
 namespace wc {
 
@@ -99,6 +100,7 @@ hipError_t launch_bins_combine(const BinsArgs& a, hipStream_t st);
 struct AttendArgs {
   const void* Q;          // [H][m][d]
   const void* K;          // [H][n][d]
+  const void* V;          // [H][n][dv] (the all-keys preparation only)
   int bf16;
   int H, n, m, d, dv, r;
   float beta_log2e;
@@ -115,10 +117,36 @@ struct AttendArgs {
   int nsplit;
   void* O;                // [H][m][dv]
   uint32_t* flags;        // [H]
+  float* Yout;            // NULL, or [H][yrows][dv+1]: the unnormalised Y in fp32 instead of O
+  int yrows;
 };
 // coreset rows as the attention kernels store them: r rounded up to whole 128-row blocks
 // (padding rows carry zero weight)
 __host__ __device__ inline int attend_rows(int r) { return (r + 127) & ~127; }
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+// The same attention with every key as a coreset row and W = [V, 1] (r = n): stage the keys
+// and values, then run the attention proper (normally with Yout set, giving
+// Y = exp(beta Q K^T) [V, 1]).
+hipError_t launch_attend_all_keys(const AttendArgs& a, hipStream_t st);
+
+// ---- union weights of the divide-and-conquer forward: H_SS^+ X over all bins' pivots ----
+struct UnionArgs {
+  const void* K;          // [H][n][d]
+  int bf16;
+  int H, n, d, dv, r;
+  int rp;                 // r rounded up to 64
+  float beta;             // 1/sqrt(d)
+  float tol;              // relative residual at or below which a point is left out
+  const int32_t* pivots;  // [H][r]: key index, or -1 for an empty slot
+  void* Qs;               // ws [H][r][d]  coreset keys as rows (input dtype), zero for empty slots
+  float* A;               // ws [H][rp][rp] H_SS, factored in place (lower blocks)
+  float* Hd;              // ws [H][rp]     diagonal of H_SS
+  float* M;               // ws [H][rp/64][64][64] inverses of the kept parts of the diagonal blocks
+  float* X;               // ws [H][rp][dv+1] H_{S,:}[V, 1] in (rows < r), substituted in place
+  float* W;               // out [H][r][dv+1]
+  uint32_t* flags;        // [H]: WC_DFLAG_DEPENDENT when a point of a valid slot is left out
+};
+hipError_t launch_union_gather(const UnionArgs& a, hipStream_t st);  // fills Qs
+hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st);   // A, Hd, M from Qs; X -> W
 
 }  // namespace wc

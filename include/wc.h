@@ -27,7 +27,8 @@
  *    u_forced [heads][r] float; diag [heads][n] float; trace [heads][r+1] double;
  *    rank [heads] int32; flags [heads] uint32.
  *  - `heads` counts every (batch, head) pair.  `bins` selects divide-and-conquer selection in
- *    wc_forward (see there); 0 or 1 everywhere else.  Supported: d, dv in {64, 128};
+ *    wc_forward (see there); 0 or 1 everywhere else.  `options` holds WC_OPT_* bits (any
+ *    other bit is WC_ERR_INVALID_ARG).  Supported: d, dv in {64, 128};
  *    dtype WC_F32 or WC_BF16; 1 <= r <= min(n, 4096); n, m >= 1 (m may be 0 for
  *    wc_attend/wc_forward: nothing is written then); heads == 0 is a no-op.
  *  - Every call validates its arguments on the host BEFORE any HIP call; on failure it
@@ -39,6 +40,8 @@
  *       WC_FLAG_BREAKDOWN  rank < r: the residual trace or a pivot's residual reached <= 0
  *       WC_FLAG_NONFINITE  a non-finite value reached the pivot loop
  *       WC_FLAG_DENOM      some query row had a normaliser Y[:, dv] <= 0
+ *       WC_FLAG_DEPENDENT  (bins > 1) the union weights left out a coreset point that is
+ *                          numerically dependent on earlier ones (see wc_forward)
  *    After a breakdown pivots[rank..r-1] = -1, F columns rank..r-1 = 0, and weights and
  *    attention use the first rank pivots only.
  *  - Workspace: `ws` must hold at least wc_workspace_bytes() bytes for the same problem.
@@ -53,7 +56,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 2
+#define WC_ABI_VERSION 3
 
 typedef enum {
   WC_OK = 0,
@@ -65,7 +68,12 @@ typedef enum {
 
 typedef enum { WC_F32 = 0, WC_BF16 = 1 } wc_dtype;
 
-enum { WC_FLAG_BREAKDOWN = 1u, WC_FLAG_NONFINITE = 2u, WC_FLAG_DENOM = 4u };
+enum { WC_FLAG_BREAKDOWN = 1u, WC_FLAG_NONFINITE = 2u, WC_FLAG_DENOM = 4u, WC_FLAG_DEPENDENT = 8u };
+
+/* wc_problem.options bits */
+enum {
+  WC_OPT_BIN_WEIGHTS = 1u /* bins > 1: per-bin weights instead of weights over the union */
+};
 
 typedef struct {
   int32_t heads; /* batch * heads, each an independent problem */
@@ -76,6 +84,7 @@ typedef struct {
   int32_t r;     /* coreset size (pivot steps) */
   int32_t dtype; /* wc_dtype of Q, K, V and O */
   int32_t bins;  /* 0 or 1: one bin; B > 1: divide-and-conquer selection (wc_forward only) */
+  int32_t options; /* OR of WC_OPT_* bits; 0 for the defaults */
 } wc_problem;
 
 /* ABI version of the loaded library (WC_ABI_VERSION it was built with). */
@@ -138,12 +147,20 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
  * part 1, efficiency: B bins processed in parallel at O(n r^2/B^3 + n r d/B^2)): B must divide
  * n and r.  Bin b holds the keys [b n/B, (b+1) n/B) and the pivot slots [b r/B, (b+1) r/B);
  * each bin runs the pivot loop on its keys (u_forced[h][slot], or Philox with counter
- * (t, h B + b, 0, 0) for the bin's step t), each bin's keys get their own Nystroem weights on
- * that bin's coreset, and every query attends over the union of the coresets.  pivots[h][j]
- * is the key index within the head, or -1 for a slot its bin left empty after a breakdown
- * (no longer only at the end); rank[h] counts the pivots taken over all bins; flags are
- * OR-ed over the bins.  The other entry points take bins <= 1 (WC_ERR_UNSUPPORTED otherwise):
- * their per-bin view is the problem with heads * B heads of n/B keys and r/B pivots.        */
+ * (t, h B + b, 0, 0) for the bin's step t).  The coreset K_S is the union of the bins'
+ * pivots in slot order, and its weights ("Methodik" part 2) are
+ *   default             W = H_SS^+ H_{S,:} [V, 1] over all n keys.  The pseudo-inverse is a
+ *                       Cholesky of H_SS in slot order that leaves out every point whose
+ *                       residual is at most 2^-12 H_jj (numerically in the span of the
+ *                       earlier points; its weight row is zero and WC_FLAG_DEPENDENT is set).
+ *                       For distinct keys nothing is left out and it is the inverse.
+ *   WC_OPT_BIN_WEIGHTS  each bin's keys get their own weights on that bin's coreset,
+ *                       W_b = H_{S_b S_b}^{-1} H_{S_b, bin b} [V_b, 1]: cheaper, less accurate.
+ * Every query attends over the union.  pivots[h][j] is the key index within the head, or -1
+ * for a slot its bin left empty after a breakdown (no longer only at the end); rank[h] counts
+ * the pivots taken over all bins; flags are OR-ed over the bins.  The other entry points take
+ * bins <= 1 (WC_ERR_UNSUPPORTED otherwise): their per-bin view is the problem with heads * B
+ * heads of n/B keys and r/B pivots.                                                          */
 wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
                      const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);

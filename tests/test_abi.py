@@ -26,7 +26,7 @@ def lib():
 
 
 class Problem(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype", "bins")]
+    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype", "bins", "options")]
 
 
 def test_exports_every_declared_symbol(lib):
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 2
+    assert lib.wc_abi_version() == 3
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -72,6 +72,9 @@ def ws_bytes(lib, p):
     ((2, 4096, 64, 64, 64, 256, 1, -1), 1), # negative bins
     ((2, 4004, 64, 64, 64, 256, 1, 16), 2), # bins do not divide n
     ((2, 4096, 64, 64, 64, 200, 1, 16), 2), # bins do not divide r
+    ((2, 4096, 64, 64, 64, 256, 1, 16, 1), 0),  # per-bin weights option
+    ((2, 4096, 64, 64, 64, 256, 1, 16, 2), 1),  # unknown option bit
+    ((2, 4096, 64, 64, 64, 256, 1, 1, -1), 1),  # unknown option bits
 ])
 def test_workspace_bytes_validation(lib, fields, expect):
     st, nbytes = ws_bytes(lib, Problem(*fields))
@@ -147,6 +150,10 @@ def test_bins_only_in_forward_and_smaller_workspace(lib):
     st2, b2 = ws_bytes(lib, binned)
     assert st1 == 0 and st2 == 0 and b2 < b1 / 4
     assert call_rpc(lib, binned) == 2
+    # the union weights stage every key for X = exp(beta K_S K^T) [V, 1] and hold H_SS: more
+    # workspace than the per-bin weights
+    st3, b3 = ws_bytes(lib, Problem(8, 131072, 131072, 128, 128, 2048, 1, 16, 1))
+    assert st3 == 0 and b3 < b2
     big = ctypes.c_size_t(1 << 40)
     assert lib.wc_weights(ctypes.byref(binned), A, A, A, A, A, A, big, None) == 2
     assert lib.wc_attend(ctypes.byref(binned), A, A, A, A, A, A, A, A, big, None) == 2
