@@ -75,37 +75,80 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   }
 }
 
+// Inverse of perm32_a: the coreset row stored at permuted position p.
+__device__ __forceinline__ int perm32_inv(int p) {
+  const int pb = p & ~31, pp = p & 31;
+  const int qq = pp >> 4, g = (pp >> 3) & 1, e = pp & 7;
+  return pb + 16 * qq + (((e >> 2) << 3) | (g << 2) | (e & 3));
+}
+
 // Every key as a coreset row (row j = key j, rows past n zero) with W = [V, 1]: the staged
-// operands of Y = exp(beta Q K^T) [V, 1].
+// operands of Y = exp(beta Q K^T) [V, 1].  One workgroup per 64-row chunk: the chunk's keys,
+// then its values, are read with 16-byte loads into LDS and written out in the tile-major
+// order of K_S and the permuted order of W^T, with contiguous 16-byte stores.
 template <typename T, int D, int DV>
-__global__ void __launch_bounds__(128) attend_prep_keys_kernel(AttendArgs a) {
+__global__ void __launch_bounds__(256) attend_prep_keys_kernel(AttendArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;
-  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  constexpr int E = 16 / (int)sizeof(T);           // input elements per 16-byte load
+  constexpr int W = (D > DV ? D : DV) + E;         // LDS row pitch (elements of T)
+  __shared__ __attribute__((aligned(16))) T sX[64 * W];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int rp = attend_rows(a.r);
-  const bool valid = j < a.n;
-  const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + (valid ? j : 0)) * D;
-  const T* V = reinterpret_cast<const T*>(a.V) + ((size_t)h * a.n + (valid ? j : 0)) * DV;
-  for (int e = tid; e < D; e += 128) {
-    const float v = valid ? ld_elem<T>(K + e) : 0.f;
-    __bf16 hi, lo;
-    split_bf16(v, hi, lo);
-    const size_t o = (size_t)h * rp * D + ks_index(j, e, D);
-    a.KSh[o] = bf16_bits(hi);
-    if (SPLIT) a.KSl[o] = bf16_bits(lo);
+  const int j0 = c * 64;
+  // keys
+  for (int e = tid; e < 64 * D / E; e += 256) {
+    const int row = e / (D / E), col = (e % (D / E)) * E, j = j0 + row;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (j < a.n) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + j) * D + col);
+    *reinterpret_cast<uint4*>(&sX[row * W + col]) = v;
   }
-  const int p = perm32_a(j);
-  for (int c = tid; c < DV; c += 128) {
-    const float w = valid ? ld_elem<T>(V + c) : 0.f;
-    __bf16 hi, lo;
-    split_bf16(w, hi, lo);
-    const size_t o = (size_t)h * DV * rp + wt_index(c, p, DV);
-    a.Wph[o] = bf16_bits(hi);
-    if (SPLIT) a.Wpl[o] = bf16_bits(lo);
+  __syncthreads();
+  const size_t kbase = (size_t)h * rp * D + (size_t)j0 * D;
+  for (int u = tid; u < 64 * (D / 8); u += 256) {   // output unit (column group u / 64, row u % 64)
+    const int cg = u >> 6, row = u & 63;
+    if constexpr (!SPLIT) {
+      *reinterpret_cast<uint4*>(a.KSh + kbase + 8 * (size_t)u) = *reinterpret_cast<const uint4*>(&sX[row * W + 8 * cg]);
+      continue;
+    }
+    bf16x8 hi8, lo8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 hi, lo;
+      split_bf16(ld_elem<T>(&sX[row * W + 8 * cg + e]), hi, lo);
+      hi8[e] = hi;
+      lo8[e] = lo;
+    }
+    *reinterpret_cast<bf16x8*>(a.KSh + kbase + 8 * (size_t)u) = hi8;
+    *reinterpret_cast<bf16x8*>(a.KSl + kbase + 8 * (size_t)u) = lo8;
   }
-  if (tid == 0) {
-    const float wd = valid ? 1.f : 0.f;
+  __syncthreads();
+  // values
+  for (int e = tid; e < 64 * DV / E; e += 256) {
+    const int row = e / (DV / E), col = (e % (DV / E)) * E, j = j0 + row;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (j < a.n) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.V) + ((size_t)h * a.n + j) * DV + col);
+    *reinterpret_cast<uint4*>(&sX[row * W + col]) = v;
+  }
+  __syncthreads();
+  const size_t wbase = (size_t)h * DV * rp + (size_t)c * 64 * DV;
+  for (int u = tid; u < 8 * DV; u += 256) {         // output unit (8 permuted positions, one column)
+    const int grp = u / DV, col = u % DV;
+    bf16x8 hi8, lo8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 hi, lo;
+      split_bf16(ld_elem<T>(&sX[perm32_inv(8 * grp + e) * W + col]), hi, lo);
+      hi8[e] = hi;
+      lo8[e] = lo;
+    }
+    *reinterpret_cast<bf16x8*>(a.Wph + wbase + 8 * (size_t)u) = hi8;
+    if (SPLIT) *reinterpret_cast<bf16x8*>(a.Wpl + wbase + 8 * (size_t)u) = lo8;
+  }
+  if (tid < 64) {
+    const int j = j0 + tid;
+    const float wd = j < a.n ? 1.f : 0.f;
     a.Wden[(size_t)h * rp + j] = wd;
-    a.Wdh[(size_t)h * rp + p] = bf16_bits((__bf16)wd);
+    a.Wdh[(size_t)h * rp + perm32_a(j)] = bf16_bits((__bf16)wd);
   }
 }
 
@@ -485,29 +528,28 @@ attend_bf16_kernel(AttendArgs a) {
   }
 }
 
+// Sum of the coreset-split partials: one wave per query row, lanes over the columns.
 template <typename T, int DV>
-__global__ void __launch_bounds__(256) attend_reduce_kernel(AttendArgs a) {
-  const int h = blockIdx.y;
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= a.m) return;
+__global__ void __launch_bounds__(64) attend_reduce_kernel(AttendArgs a) {
+  const int q = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const size_t stride = (size_t)a.m * (DV + 1);
   const float* Yp = a.Ypart + ((size_t)h * a.nsplit * a.m + q) * (DV + 1);
   float den = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) den += Yp[sp * stride + DV];
   if (a.Yout) {
     float* Y = yout_row(a, h, q);
-    for (int c = 0; c < DV; ++c) {
+    for (int c = lane; c < DV; c += 64) {
       float y = 0.f;
       for (int sp = 0; sp < a.nsplit; ++sp) y += Yp[sp * stride + c];
       Y[c] = y;
     }
-    Y[DV] = den;
+    if (lane == 0) Y[DV] = den;
     return;
   }
-  if (!(den > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
+  if (lane == 0 && !(den > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
   const float inv = 1.0f / den;
   T* O = reinterpret_cast<T*>(a.O) + ((size_t)h * a.m + q) * DV;
-  for (int c = 0; c < DV; ++c) {
+  for (int c = lane; c < DV; c += 64) {
     float y = 0.f;
     for (int sp = 0; sp < a.nsplit; ++sp) y += Yp[sp * stride + c];
     st_elem<T>(O + c, y * inv);
@@ -529,7 +571,7 @@ static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
 template <typename T, int D, int DV>
 static hipError_t run_attend_all_keys(const AttendArgs& a, hipStream_t st) {
   const int rp = attend_rows(a.r);
-  hipLaunchKernelGGL((attend_prep_keys_kernel<T, D, DV>), dim3(rp, a.H), dim3(128), 0, st, a);
+  hipLaunchKernelGGL((attend_prep_keys_kernel<T, D, DV>), dim3(rp / 64, a.H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
   return run_attend_core<T, D, DV>(a, st);
@@ -545,7 +587,7 @@ static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.nsplit > 1) {
-    hipLaunchKernelGGL((attend_reduce_kernel<T, DV>), dim3((a.m + 255) / 256, a.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_reduce_kernel<T, DV>), dim3(a.m, a.H), dim3(64), 0, st, a);
     e = hipGetLastError();
   }
   return e;

@@ -141,21 +141,38 @@ __global__ void __launch_bounds__(256) uniforms_kernel(StreamRpcArgs a) {
   a.uniforms[e] = philox_uniform(a.seed, (uint32_t)(e / a.r), (uint32_t)(e % a.r));
 }
 
-// Initial residual diag_i = exp(beta |k_i|^2) and per-block masses.
+// Initial residual diag_i = exp(beta |k_i|^2) and per-block masses.  Eight lanes share a key
+// row (16-byte loads, so a wave reads eight whole rows contiguously), then combine their
+// partial squared norms.
 template <typename T, int D>
 __global__ void __launch_bounds__(NT) rpc_init_kernel(StreamRpcArgs a, int rows) {
   __shared__ double red[NW];
-  const int h = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
+  constexpr int PER = D / 8;                        // elements per lane
+  constexpr int E = 16 / (int)sizeof(T);            // elements per 16-byte load
+  const int h = blockIdx.y, b = blockIdx.x, tid = threadIdx.x, sub = tid & 7, grp = tid >> 3;
   const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * a.n * D;
   double mass = 0.0;
-  for (int k = 0; k * NT < rows; ++k) {
-    const int i = b * rows + k * NT + tid;
+  for (int k = 0; k < rows; k += NT / 8) {
+    const int i = b * rows + k + grp;
+    float ss = 0.f;
     if (i < a.n) {
-      const T* kr = K + (size_t)i * D;
-      float ksq[D];
+      const T* kr = K + (size_t)i * D + sub * PER;
 #pragma unroll
-      for (int e = 0; e < D; ++e) ksq[e] = ld_elem<T>(kr + e);
-      const float d0 = __builtin_amdgcn_exp2f(row_dot<D>(kr, ksq) * a.beta_log2e);
+      for (int q = 0; q < PER / E; ++q) {
+        T x[E];
+        *reinterpret_cast<uint4*>(x) = *reinterpret_cast<const uint4*>(kr + q * E);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float v = ld_elem<T>(x + e);
+          ss = fmaf(v, v, ss);
+        }
+      }
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    if (sub == 0 && i < a.n) {
+      const float d0 = __builtin_amdgcn_exp2f(ss * a.beta_log2e);
       a.diag0[(size_t)h * a.n + i] = d0;
       mass += mass_of(d0);
     }

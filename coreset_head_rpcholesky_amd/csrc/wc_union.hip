@@ -12,7 +12,8 @@
 // so W = M^T ... M X keeps the weight rows of left-out points (and of empty slots) at zero.
 //
 // Blocked right-looking algorithm on 64 x 64 blocks of A = H_SS (fp32), per block column k:
-//   diag    one wave per head factors A_kk with the drop rule and forms M_kk;
+//   diag    one workgroup per head eliminates A_kk with the drop rule and forms M_kk (block 0
+//           in a launch of its own, block k+1 inside the update of step k);
 //   panel   L_ik = A_ik M_kk^T (i > k, in place over A_ik) and Z_k = M_kk X_k (in place);
 //   update  A_ij -= L_ik L_jk^T (k < j <= i) and X_i -= L_ik Z_k;
 // then the backward substitution, block k from the last: W_k = M_kk^T Z_k and
@@ -152,64 +153,78 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
   }
 }
 
-// ---- diag: factor A_kk with the drop rule, M_kk = inverse of the kept part ------------------
-// One wave per head; lane i holds row i of the block in registers.
-__global__ void __launch_bounds__(64) union_diag_kernel(UnionArgs a, int k) {
-  __shared__ __attribute__((aligned(16))) float sL[kUB][kLP];
-  __shared__ float sInv[kUB];
-  const int h = blockIdx.x, lane = threadIdx.x;
-  const size_t row = (size_t)k * kUB + lane;
-  const float* Ar = a.A + ((size_t)h * a.rp + row) * a.rp + (size_t)k * kUB;
-  float v[kUB];
+// ---- diag: M_kk = inverse of the Cholesky factor of the kept part of A_kk -------------------
+// Run by a whole 256-thread workgroup on the block in sA (row-major, already updated).  Right-
+// looking elimination with the drop rule, applied alongside to the identity: step j takes the
+// pivot residual p = A[j][j]; if p > tol H_jj every later row i subtracts f_i = A[i][j] / p
+// times row j, in the block and in G (G starts as the identity).  G ends as U^{-1}, U the unit
+// lower factor of A = U diag(p) U^T over the kept points, so M = diag(p)^{-1/2} G; a left-out
+// point eliminates nothing and gets a zero row of M.  Thread (i, q) holds columns 16q .. 16q+15
+// of row i of the block and of G; column j of the block and row j of G are published in LDS
+// (double-buffered by the parity of j, one barrier per step).
+__device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, const float (*sA)[kLP],
+                                           float (*sCol)[kUB], float (*sRow)[kUB]) {
+  const int tid = threadIdx.x, ri = tid >> 2, q = tid & 3, c0 = 16 * q;
+  float v[16], g[16];
 #pragma unroll
-  for (int c = 0; c < kUB; c += 4) {
-    const float4 q = *reinterpret_cast<const float4*>(Ar + c);
-    v[c] = q.x; v[c + 1] = q.y; v[c + 2] = q.z; v[c + 3] = q.w;
+  for (int e = 0; e < 16; e += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(&sA[ri][c0 + e]);
+    v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
   }
-  const float hd = a.Hd[(size_t)h * a.rp + row];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) g[e] = ri == c0 + e ? 1.f : 0.f;
+  const float* Hd = a.Hd + (size_t)h * a.rp + (size_t)k * kUB;
+  float* M = a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB;
   bool dependent = false;
+  __syncthreads();  // sA may be overwritten by the caller only after everyone has read it
 #pragma unroll
   for (int j = 0; j < kUB; ++j) {
-    const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), j));
-    const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hd), j));
-    const bool keep = g0 > a.tol * hj;
+    const int buf = j & 1;
+    // publish column j of the block (owners: q == j / 16) and row j of G (owners: ri == j)
+    if (q == j / 16) sCol[buf][ri] = v[j % 16];
+    if (ri == j) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 4)
+        *reinterpret_cast<float4*>(&sRow[buf][c0 + e]) = make_float4(g[e], g[e + 1], g[e + 2], g[e + 3]);
+    }
+    __syncthreads();
+    const float p = sCol[buf][j];
+    const float hj = Hd[j];
+    const bool keep = p > a.tol * hj;
     dependent |= !keep && hj > 0.f;
-    const float s = keep ? sqrtf(g0) : 0.f;
-    const float inv = keep ? 1.0f / s : 0.f;
-    // column j of L; rows above j keep their (unused) upper-triangle values
-    if (lane == j) v[j] = s;
-    else if (lane > j) v[j] *= inv;
-    const float lj = v[j];
+    if (ri == j) {
+      // row j of M (hardware reciprocal square root, about 1 ulp)
+      const float s = keep ? __builtin_amdgcn_rsqf(p) : 0.f;
 #pragma unroll
-    for (int c = j + 1; c < kUB; ++c) {
-      const float lc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), c));
-      v[c] = fmaf(-lj, lc, v[c]);
+      for (int e = 0; e < 16; e += 4)
+        *reinterpret_cast<float4*>(M + (size_t)j * kUB + c0 + e) = make_float4(g[e] * s, g[e + 1] * s, g[e + 2] * s, g[e + 3] * s);
     }
-    if (lane == j) sInv[j] = inv;
-  }
-  if (dependent && lane == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
+    if (keep && ri > j) {
+      const float f = sCol[buf][ri] * __builtin_amdgcn_rcpf(p);
 #pragma unroll
-  for (int c = 0; c < kUB; ++c) sL[lane][c] = c <= lane ? v[c] : 0.f;
+      for (int e = 0; e < 16; e += 4) {
+        const float4 cj = *reinterpret_cast<const float4*>(&sCol[buf][c0 + e]);
+        const float4 gj = *reinterpret_cast<const float4*>(&sRow[buf][c0 + e]);
+        v[e] = fmaf(-f, cj.x, v[e]); v[e + 1] = fmaf(-f, cj.y, v[e + 1]);
+        v[e + 2] = fmaf(-f, cj.z, v[e + 2]); v[e + 3] = fmaf(-f, cj.w, v[e + 3]);
+        g[e] = fmaf(-f, gj.x, g[e]); g[e + 1] = fmaf(-f, gj.y, g[e + 1]);
+        g[e + 2] = fmaf(-f, gj.z, g[e + 2]); g[e + 3] = fmaf(-f, gj.w, g[e + 3]);
+      }
+    }
+  }
+  if (dependent && tid == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
+}
+
+// The first diagonal block (later ones are factored by the update of the step before).
+__global__ void __launch_bounds__(256) union_diag0_kernel(UnionArgs a) {
+  __shared__ __attribute__((aligned(16))) float sA[kUB][kLP];
+  __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
+  __shared__ __attribute__((aligned(16))) float sRow[2][kUB];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float* A = a.A + (size_t)h * a.rp * a.rp;
+  stage_direct(sA, A, a.rp);
   __syncthreads();
-  // lane c: column c of M by forward substitution; a left-out row i (sInv[i] = 0) stays zero,
-  // and a left-out column of L is zero below the diagonal, so nothing flows through it
-  float m[kUB];
-#pragma unroll
-  for (int i = 0; i < kUB; ++i) {
-    float acc = i == lane ? 1.f : 0.f;
-#pragma unroll
-    for (int t = 0; t < i; t += 4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&sL[i][t]);
-      acc = fmaf(-l4.x, m[t], acc);
-      if (t + 1 < i) acc = fmaf(-l4.y, m[t + 1], acc);
-      if (t + 2 < i) acc = fmaf(-l4.z, m[t + 2], acc);
-      if (t + 3 < i) acc = fmaf(-l4.w, m[t + 3], acc);
-    }
-    m[i] = acc * sInv[i];
-  }
-  float* M = a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB;
-#pragma unroll
-  for (int i = 0; i < kUB; ++i) M[(size_t)i * kUB + lane] = m[i];
+  diag_block(a, h, 0, sA, sCol, sRow);
 }
 
 // ---- panel: L_ik = A_ik M_kk^T (i > k) and Z_k = M_kk X_k ------------------------------------
@@ -253,9 +268,13 @@ __global__ void __launch_bounds__(256) union_panel_kernel(UnionArgs a, int k) {
 }
 
 // ---- update: A_ij -= L_ik L_jk^T (k < j <= i), X_i -= L_ik Z_k --------------------------------
+// The block (k+1, k+1) has no other writer in this step, so its workgroup also factors it
+// (diag_block for block column k+1) once updated.
 __global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
   __shared__ __attribute__((aligned(16))) float sP[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sQ[kUB][kLP];
+  __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
+  __shared__ __attribute__((aligned(16))) float sRow[2][kUB];
   const int h = blockIdx.y, tid = threadIdx.x, nb = a.rp / kUB, T = nb - k - 1;
   const int nc = a.dv + 1;
   float* A = a.A + (size_t)h * a.rp * a.rp;
@@ -275,6 +294,19 @@ __global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
     __syncthreads();
     mm64(sP, sQ, acc);
     float* Aij = A + (size_t)i * kUB * a.rp + (size_t)j * kUB;
+    if (i == k + 1) {
+      // i == j == k + 1: the next diagonal block, factored here from LDS
+      __syncthreads();
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 o = *reinterpret_cast<const float4*>(Aij + (size_t)(i0 + r4) * a.rp + c0);
+        *reinterpret_cast<float4*>(&sP[i0 + r4][c0]) =
+            make_float4(o.x - acc[r4][0], o.y - acc[r4][1], o.z - acc[r4][2], o.w - acc[r4][3]);
+      }
+      __syncthreads();
+      diag_block(a, h, k + 1, sP, sCol, sRow);
+      return;
+    }
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       float4* p = reinterpret_cast<float4*>(Aij + (size_t)(i0 + r4) * a.rp + c0);
@@ -371,8 +403,8 @@ hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st) {
                         : (a.d == 64 ? run_gram<float, 64>(a, st) : run_gram<float, 128>(a, st));
   if (e != hipSuccess) return e;
   const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB;
+  hipLaunchKernelGGL(union_diag0_kernel, dim3(a.H), dim3(256), 0, st, a);
   for (int k = 0; k < nb; ++k) {
-    hipLaunchKernelGGL(union_diag_kernel, dim3(a.H), dim3(64), 0, st, a, k);
     const int T = nb - k - 1;
     hipLaunchKernelGGL(union_panel_kernel, dim3(T + nxz, a.H), dim3(256), 0, st, a, k);
     if (T > 0)
