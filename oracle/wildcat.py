@@ -323,6 +323,50 @@ def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None):
     return out
 
 
+def compress(K, V, r, uniforms, B=1, beta=None, weights_mode="union"):
+    """COMPRESSKV ("Zentrale Beitraege": the KV cache shrinks from Theta(n d) to O(r d)): the
+    rows of a compressed cache for one head, from the keys and values of a prefix.
+
+    The coreset keys K_S and their weight rows W are those of the forward (one bin) or the
+    divide-and-conquer forward (B bins); an empty slot (pivot -1) becomes a zero key with a
+    zero weight row, so that the cache always holds r rows.  Returns (KR [r, d], WR [r, dv+1],
+    pivots, rank, flags).
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    Q0 = np.zeros((0, K.shape[1]))
+    if B == 1:
+        out = forward(Q0, K, V, r, uniforms, beta)
+    else:
+        out = forward_binned(Q0, K, V, r, B, uniforms, beta, weights_mode)
+    piv = out["pivots"]
+    valid = piv >= 0
+    KR = np.zeros((r, K.shape[1]))
+    KR[valid] = K[piv[valid]]
+    WR = np.zeros((r, V.shape[1] + 1))
+    WR[: len(out["W"])] = out["W"]   # rows of empty slots are zero in W already
+    return KR, WR, piv, out["rank"], out["flags"]
+
+
+def exact_rows(K, V):
+    """Cache rows that hold keys exactly: key k_j with weight row [v_j, 1], so that its
+    contribution exp(beta q k_j) [v_j, 1] is that of exact softmax attention (numerator and
+    normaliser)."""
+    V = np.asarray(V, np.float64)
+    return np.asarray(K, np.float64), np.hstack([V, np.ones((V.shape[0], 1))])
+
+
+def decode(Q, KR, WR, beta=None):
+    """Attention of decode queries over the rows of a cache: Y = exp(beta Q KR^T) WR,
+    O = Y[:, :dv] / Y[:, dv] (compressed rows and exact rows alike)."""
+    Q = np.asarray(Q, np.float64)
+    KR = np.asarray(KR, np.float64)
+    beta = beta_of(KR.shape[1]) if beta is None else beta
+    Y = kernel(Q, KR, beta) @ np.asarray(WR, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return Y[:, :-1] / Y[:, -1:]
+
+
 def exact_attention(Q, K, V, beta=None):
     """Exact softmax attention softmax(beta Q K^T) V, with a row-max shift."""
     Q = np.asarray(Q, np.float64)
