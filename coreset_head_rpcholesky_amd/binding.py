@@ -48,6 +48,11 @@ def _load():
         "wc_weights": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_attend": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_forward": ([P, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_cache_bytes": ([P, ctypes.c_int32, ctypes.POINTER(sz)], ctypes.c_int),
+        "wc_compress": ([P, vp, vp, vp, u64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_cache_append": ([P, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int32, vp], ctypes.c_int),
+        "wc_decode_workspace_bytes": ([P, ctypes.c_int32, ctypes.POINTER(sz)], ctypes.c_int),
+        "wc_decode": ([P, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, sz, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -202,3 +207,76 @@ def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_f
     if st != WC_OK:
         raise WcError("wc_forward", st)
     return out
+
+
+def wc_cache_bytes(p: WcProblem, capacity: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = LIB.wc_cache_bytes(ctypes.byref(p), int(capacity), ctypes.byref(out))
+    if st != WC_OK:
+        raise WcError("wc_cache_bytes", st)
+    return int(out.value)
+
+
+def wc_compress(K: torch.Tensor, V: torch.Tensor, r: int, capacity: int, *, u_forced=None,
+                seed: int = 0, bins: int = 1, bin_weights: bool = False, cache=None, ws=None,
+                stream=None):
+    """Compress the prefix K, V into rows [0, r) of a cache of ``capacity`` rows per head;
+    returns dict(cache (uint8 device tensor), pivots, rank, flags)."""
+    H, n, d = K.shape
+    dv = V.shape[2]
+    dev = K.device
+    p = problem(H, n, 0, d, dv, r, K.dtype, bins, WC_OPT_BIN_WEIGHTS if bin_weights else 0)
+    _check_in("V", V, K.dtype, (H, n, dv), dev)
+    if u_forced is not None:
+        _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
+    if cache is None:
+        cache = torch.empty(max(wc_cache_bytes(p, capacity), 256), dtype=torch.uint8, device=dev)
+    out = dict(cache=cache, pivots=torch.empty((H, r), dtype=torch.int32, device=dev),
+               rank=torch.empty((H,), dtype=torch.int32, device=dev),
+               flags=torch.empty((H,), dtype=torch.int32, device=dev))
+    ws, nb = _ws(p, dev, ws)
+    st = LIB.wc_compress(ctypes.byref(p), _ptr(K), _ptr(V), _ptr(u_forced), int(seed) & (2**64 - 1),
+                         _ptr(cache), int(capacity), _ptr(out["pivots"]), _ptr(out["rank"]),
+                         _ptr(out["flags"]), _ptr(ws), nb, _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_compress", st)
+    return out
+
+
+def wc_cache_append(cache: torch.Tensor, K_new: torch.Tensor, V_new: torch.Tensor, row0: int,
+                    capacity: int, stream=None):
+    """Append K_new [H, count, d], V_new [H, count, dv] as exact rows at row0 .. row0+count-1."""
+    H, count, d = K_new.shape
+    dv = V_new.shape[2]
+    p = problem(H, max(count, 1), 0, d, dv, 1, K_new.dtype)
+    _check_in("V_new", V_new, K_new.dtype, (H, count, dv), K_new.device)
+    st = LIB.wc_cache_append(ctypes.byref(p), _ptr(K_new), _ptr(V_new), int(count), int(row0),
+                             _ptr(cache), int(capacity), _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_cache_append", st)
+
+
+def wc_decode_workspace_bytes(p: WcProblem, rows: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = LIB.wc_decode_workspace_bytes(ctypes.byref(p), int(rows), ctypes.byref(out))
+    if st != WC_OK:
+        raise WcError("wc_decode_workspace_bytes", st)
+    return int(out.value)
+
+
+def wc_decode(Q: torch.Tensor, cache: torch.Tensor, capacity: int, rows: int, dv: int, *,
+              flags=None, ws=None, out=None, stream=None):
+    """Attention of Q [H, m, d] over rows [0, rows) of the cache; returns (O [H, m, dv], flags)."""
+    H, m, d = Q.shape
+    dev = Q.device
+    p = problem(H, 1, m, d, dv, 1, Q.dtype)
+    if flags is None:
+        flags = torch.zeros((H,), dtype=torch.int32, device=dev)
+    O = torch.empty((H, m, dv), dtype=Q.dtype, device=dev) if out is None else out
+    if ws is None:
+        ws = torch.empty(max(wc_decode_workspace_bytes(p, rows), 256), dtype=torch.uint8, device=dev)
+    st = LIB.wc_decode(ctypes.byref(p), _ptr(Q), _ptr(cache), int(capacity), int(rows), _ptr(O),
+                       _ptr(flags), _ptr(ws), ws.numel(), _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_decode", st)
+    return O, flags

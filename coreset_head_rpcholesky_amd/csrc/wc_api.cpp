@@ -344,6 +344,52 @@ wc_status forward_binned(const wc_problem& p, const void* Q, const void* K, cons
   return dev(e);
 }
 
+// Compressed KV cache: per head, capacity rows (rounded up to whole 128-row blocks) in the
+// staged layout of the attention kernels (keys tile-major, weights transposed and permuted).
+struct CacheLayout {
+  int cp;
+  size_t KSh, KSl, Wph, Wpl, Wden, Wdh, total;
+};
+
+CacheLayout make_cache_layout(const wc_problem& p, int capacity) {
+  CacheLayout C{};
+  const size_t H = (size_t)p.heads, lo = p.dtype == WC_F32 ? 1 : 0;
+  C.cp = wc::attend_rows(capacity);
+  const size_t cp = (size_t)C.cp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  C.KSh = take(H * cp * p.d * 2);
+  C.KSl = take(lo * H * cp * p.d * 2);
+  C.Wph = take(H * p.dv * cp * 2);
+  C.Wpl = take(lo * H * p.dv * cp * 2);
+  C.Wden = take(H * cp * 4);
+  C.Wdh = take(H * cp * 2);
+  C.total = off;
+  return C;
+}
+
+// The attention arguments that address a cache.
+wc::AttendArgs cache_args(const wc_problem& p, const CacheLayout& C, const void* cache, int capacity) {
+  wc::AttendArgs a{};
+  char* c = static_cast<char*>(const_cast<void*>(cache));
+  a.bf16 = p.dtype == WC_BF16;
+  a.H = p.heads; a.d = p.d; a.dv = p.dv; a.r = capacity;
+  a.beta_log2e = beta_log2e(p.d);
+  a.ldrows = C.cp;
+  a.KSh = reinterpret_cast<uint16_t*>(c + C.KSh);
+  a.KSl = p.dtype == WC_F32 ? reinterpret_cast<uint16_t*>(c + C.KSl) : nullptr;
+  a.Wph = reinterpret_cast<uint16_t*>(c + C.Wph);
+  a.Wpl = p.dtype == WC_F32 ? reinterpret_cast<uint16_t*>(c + C.Wpl) : nullptr;
+  a.Wden = reinterpret_cast<float*>(c + C.Wden);
+  a.Wdh = reinterpret_cast<uint16_t*>(c + C.Wdh);
+  return a;
+}
+
+size_t decode_ws_bytes(const wc_problem& p, int rows) {
+  const int ns = attend_split(p, (size_t)p.m, (size_t)rows);
+  return ns > 1 ? align_up((size_t)p.heads * ns * p.m * (p.dv + 1) * 4) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -454,6 +500,94 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
   if (e == hipSuccess) e = run_weights(*p, L, ws, V, piv, rank, F, W, s);
   if (e == hipSuccess) e = run_attend(*p, L, ws, Q, K, piv, rank, W, O, flags, s);
   return dev(e);
+}
+
+wc_status wc_cache_bytes(const wc_problem* p, int32_t capacity, size_t* bytes) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (!bytes || capacity < 1) return WC_ERR_INVALID_ARG;
+  *bytes = p->heads == 0 ? 0 : make_cache_layout(*p, capacity).total;
+  return WC_OK;
+}
+
+wc_status wc_compress(const wc_problem* p, const void* K, const void* V, const float* u_forced,
+                      uint64_t seed, void* cache, int32_t capacity, int32_t* pivots, int32_t* rank,
+                      uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (capacity < p->r) return WC_ERR_INVALID_ARG;
+  if (p->heads == 0) return WC_OK;
+  if (!req(K) || !req(V) || !req(cache) || !req(rank) || !req(flags) || !opt(u_forced) || !opt(pivots))
+    return WC_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  wc_problem q = *p;
+  q.m = 0;
+  const CacheLayout C = make_cache_layout(q, capacity);
+  wc::AttendArgs a = cache_args(q, C, cache, capacity);
+  a.K = K; a.n = q.n; a.r = q.r;
+  hipError_t e;
+  if (binned(q)) {
+    // selection and weights as in the forward (no queries); the weights and the head's
+    // pivots are left in the workspace
+    if ((st = forward_binned(q, nullptr, K, V, u_forced, seed, nullptr, pivots, rank, flags, ws, ws_bytes, s)) != WC_OK)
+      return st;
+    const BinnedLayout B = make_binned_layout(q);
+    a.pivots = pivots ? pivots : at<int32_t>(ws, B.piv);
+    a.rank = at<int32_t>(ws, B.rank_slots);
+    a.W = at<float>(ws, B.sub.W);
+  } else {
+    Layout L;
+    if ((st = check_ws(q, ws, ws_bytes, &L)) != WC_OK) return st;
+    int32_t* piv = pivots ? pivots : at<int32_t>(ws, L.piv);
+    float* F = at<float>(ws, L.F);
+    float* W = at<float>(ws, L.W);
+    e = run_select(q, L, ws, K, u_forced, seed, piv, F, rank, flags, s);
+    if (e == hipSuccess) e = run_weights(q, L, ws, V, piv, rank, F, W, s);
+    if (e != hipSuccess) return dev(e);
+    a.pivots = piv; a.rank = rank; a.W = W;
+  }
+  // every staged row is written: the coreset rows, then zeros up to the capacity
+  a.ldrows = C.cp;
+  return dev(wc::launch_attend_prep(a, s));
+}
+
+wc_status wc_cache_append(const wc_problem* p, const void* K_new, const void* V_new, int32_t count,
+                          int32_t row0, void* cache, int32_t capacity, void* stream) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (count < 0 || row0 < 0 || capacity < 1 || (int64_t)row0 + count > capacity) return WC_ERR_INVALID_ARG;
+  if (p->heads == 0 || count == 0) return WC_OK;
+  if (!req(K_new) || !req(V_new) || !req(cache)) return WC_ERR_INVALID_ARG;
+  const CacheLayout C = make_cache_layout(*p, capacity);
+  wc::AttendArgs a = cache_args(*p, C, cache, capacity);
+  a.K = K_new; a.V = V_new; a.n = count; a.row0 = row0;
+  return dev(wc::launch_attend_append(a, static_cast<hipStream_t>(stream)));
+}
+
+wc_status wc_decode_workspace_bytes(const wc_problem* p, int32_t rows, size_t* bytes) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (!bytes || rows < 1) return WC_ERR_INVALID_ARG;
+  *bytes = p->heads == 0 ? 0 : decode_ws_bytes(*p, rows);
+  return WC_OK;
+}
+
+wc_status wc_decode(const wc_problem* p, const void* Q, const void* cache, int32_t capacity,
+                    int32_t rows, void* O, uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (rows < 1 || capacity < rows) return WC_ERR_INVALID_ARG;
+  if (p->heads == 0 || p->m == 0) return WC_OK;
+  if (!req(Q) || !req(cache) || !req(O) || !req(flags)) return WC_ERR_INVALID_ARG;
+  const size_t need = decode_ws_bytes(*p, rows);
+  if (need > 0 && (!ws || !aligned16(ws) || ws_bytes < need)) return WC_ERR_WORKSPACE;
+  const CacheLayout C = make_cache_layout(*p, capacity);
+  wc::AttendArgs a = cache_args(*p, C, cache, capacity);
+  a.Q = Q; a.m = p->m; a.scan_rows = rows;
+  a.nsplit = attend_split(*p, (size_t)p->m, (size_t)rows);
+  a.Ypart = a.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
+  a.O = O; a.flags = flags;
+  return dev(wc::launch_attend_core(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -43,7 +43,7 @@ template <typename T, int D, int DV>
 __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int rp = attend_rows(a.r);
+  const int rp = staged_rows(a);
   // slots past the rank, and slots a bin left empty (pivot -1), carry zero weight
   const int rk = a.rank[h];
   const int sj = j < rk ? a.pivots[(size_t)h * a.r + j] : -1;
@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256) attend_prep_keys_kernel(AttendArgs a) {
   constexpr int W = (D > DV ? D : DV) + E;         // LDS row pitch (elements of T)
   __shared__ __attribute__((aligned(16))) T sX[64 * W];
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int rp = attend_rows(a.r);
+  const int rp = staged_rows(a);
   const int j0 = c * 64;
   // keys
   for (int e = tid; e < 64 * D / E; e += 256) {
@@ -152,6 +152,36 @@ __global__ void __launch_bounds__(256) attend_prep_keys_kernel(AttendArgs a) {
   }
 }
 
+// Exact rows: row row0 + j of the staged layout holds key j of K with weights [v_j, 1]
+// (j < n), so that its contribution is that of exact softmax attention.
+template <typename T, int D, int DV>
+__global__ void __launch_bounds__(128) attend_append_kernel(AttendArgs a) {
+  constexpr bool SPLIT = sizeof(T) == 4;
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int rp = staged_rows(a), row = a.row0 + j;
+  const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + j) * D;
+  const T* V = reinterpret_cast<const T*>(a.V) + ((size_t)h * a.n + j) * DV;
+  for (int e = tid; e < D; e += 128) {
+    __bf16 hi, lo;
+    split_bf16(ld_elem<T>(K + e), hi, lo);
+    const size_t o = (size_t)h * rp * D + ks_index(row, e, D);
+    a.KSh[o] = bf16_bits(hi);
+    if (SPLIT) a.KSl[o] = bf16_bits(lo);
+  }
+  const int p = perm32_a(row);
+  for (int c = tid; c < DV; c += 128) {
+    __bf16 hi, lo;
+    split_bf16(ld_elem<T>(V + c), hi, lo);
+    const size_t o = (size_t)h * DV * rp + wt_index(c, p, DV);
+    a.Wph[o] = bf16_bits(hi);
+    if (SPLIT) a.Wpl[o] = bf16_bits(lo);
+  }
+  if (tid == 0) {
+    a.Wden[(size_t)h * rp + row] = 1.f;
+    a.Wdh[(size_t)h * rp + p] = bf16_bits((__bf16)1.f);
+  }
+}
+
 // Row q of head h of the unnormalised output (fp32, dv + 1 columns).
 __device__ __forceinline__ float* yout_row(const AttendArgs& a, int h, int q) {
   return a.Yout + ((size_t)h * a.yrows + q) * (a.dv + 1);
@@ -168,7 +198,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   __shared__ float sWd[32];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y, sp = blockIdx.z;
-  const int m = a.m, rp = attend_rows(a.r), nchk = rp / 32;
+  const int m = a.m, rp = staged_rows(a), nchk = scanned_rows(a) / 32;
   const int q = blockIdx.x * 128 + wid * 32 + l32;
   const bool qv = q < m;
   const float bl2e = a.beta_log2e;
@@ -410,7 +440,7 @@ attend_bf16_kernel(AttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y, sp = blockIdx.z;
-  const int m = a.m, rp = attend_rows(a.r);
+  const int m = a.m, rp = staged_rows(a);
   const float bl2e = a.beta_log2e;
   const int q0 = blockIdx.x * kAttendQueries + wid * 32 * NQ + l32;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * m * D;
@@ -444,7 +474,7 @@ attend_bf16_kernel(AttendArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the query fragments have arrived
   // this workgroup's share of the coreset: chunks c0 .. c0+nc-1 of 64 rows
-  const int nchk = rp / 64, per = (nchk + a.nsplit - 1) / a.nsplit;
+  const int nchk = scanned_rows(a) / 64, per = (nchk + a.nsplit - 1) / a.nsplit;
   const int c0 = sp * per, nc = min(nchk, c0 + per) - c0;
   const uint16_t* KSh = a.KSh + (size_t)h * rp * D;
   const uint16_t* Wph = a.Wph + (size_t)h * DV * rp;
@@ -561,7 +591,7 @@ static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st);
 
 template <typename T, int D, int DV>
 static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
-  const int rp = attend_rows(a.r);
+  const int rp = staged_rows(a);
   hipLaunchKernelGGL((attend_prep_kernel<T, D, DV>), dim3(rp, a.H), dim3(128), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
@@ -569,8 +599,21 @@ static hipError_t run_attend(const AttendArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D, int DV>
+static hipError_t run_attend_prep(const AttendArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((attend_prep_kernel<T, D, DV>), dim3(staged_rows(a), a.H), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DV>
+static hipError_t run_attend_append(const AttendArgs& a, hipStream_t st) {
+  if (a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL((attend_append_kernel<T, D, DV>), dim3(a.n, a.H), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DV>
 static hipError_t run_attend_all_keys(const AttendArgs& a, hipStream_t st) {
-  const int rp = attend_rows(a.r);
+  const int rp = staged_rows(a);
   hipLaunchKernelGGL((attend_prep_keys_kernel<T, D, DV>), dim3(rp / 64, a.H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.m == 0) return e;
@@ -600,6 +643,21 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   }
   if (a.d == 64) return a.dv == 64 ? run_attend<float, 64, 64>(a, st) : run_attend<float, 64, 128>(a, st);
   return a.dv == 64 ? run_attend<float, 128, 64>(a, st) : run_attend<float, 128, 128>(a, st);
+}
+
+#define WC_ATTEND_DISPATCH(FN)                                                                \
+  if (a.bf16) {                                                                               \
+    if (a.d == 64) return a.dv == 64 ? FN<uint16_t, 64, 64>(a, st) : FN<uint16_t, 64, 128>(a, st); \
+    return a.dv == 64 ? FN<uint16_t, 128, 64>(a, st) : FN<uint16_t, 128, 128>(a, st);         \
+  }                                                                                           \
+  if (a.d == 64) return a.dv == 64 ? FN<float, 64, 64>(a, st) : FN<float, 64, 128>(a, st);     \
+  return a.dv == 64 ? FN<float, 128, 64>(a, st) : FN<float, 128, 128>(a, st);
+
+hipError_t launch_attend_prep(const AttendArgs& a, hipStream_t st) { WC_ATTEND_DISPATCH(run_attend_prep) }
+hipError_t launch_attend_append(const AttendArgs& a, hipStream_t st) { WC_ATTEND_DISPATCH(run_attend_append) }
+hipError_t launch_attend_core(const AttendArgs& a, hipStream_t st) {
+  if (a.m == 0) return hipSuccess;
+  WC_ATTEND_DISPATCH(run_attend_core)
 }
 
 hipError_t launch_attend_all_keys(const AttendArgs& a, hipStream_t st) {

@@ -119,15 +119,28 @@ struct AttendArgs {
   uint32_t* flags;        // [H]
   float* Yout;            // NULL, or [H][yrows][dv+1]: the unnormalised Y in fp32 instead of O
   int yrows;
+  int ldrows;             // staged rows per head (0: attend_rows(r)); a cache uses its capacity
+  int scan_rows;          // rows the attention scans (0: all staged rows); rows past it are zero
+  int row0;               // first row written by the append staging
 };
 // coreset rows as the attention kernels store them: r rounded up to whole 128-row blocks
 // (padding rows carry zero weight)
 __host__ __device__ inline int attend_rows(int r) { return (r + 127) & ~127; }
+__host__ __device__ inline int staged_rows(const AttendArgs& a) { return a.ldrows ? a.ldrows : attend_rows(a.r); }
+__host__ __device__ inline int scanned_rows(const AttendArgs& a) {
+  return a.scan_rows ? attend_rows(a.scan_rows) : staged_rows(a);
+}
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 // The same attention with every key as a coreset row and W = [V, 1] (r = n): stage the keys
 // and values, then run the attention proper (normally with Yout set, giving
 // Y = exp(beta Q K^T) [V, 1]).
 hipError_t launch_attend_all_keys(const AttendArgs& a, hipStream_t st);
+// Staging only (the coreset rows into the staged layout, every staged row written).
+hipError_t launch_attend_prep(const AttendArgs& a, hipStream_t st);
+// Exact rows: key j of K with weight row [v_j, 1], written at staged row row0 + j (n rows).
+hipError_t launch_attend_append(const AttendArgs& a, hipStream_t st);
+// The attention proper over already staged rows (no staging).
+hipError_t launch_attend_core(const AttendArgs& a, hipStream_t st);
 
 // ---- union weights of the divide-and-conquer forward: H_SS^+ X over all bins' pivots ----
 struct UnionArgs {

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 3
+#define WC_ABI_VERSION 4
 
 typedef enum {
   WC_OK = 0,
@@ -164,6 +164,48 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
 wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
                      const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- COMPRESSKV: a compressed KV cache and decode over it ----------------------------------
+ * gist.science/de/paper/2602.10056, "Zentrale Beitraege": a COMPRESSKV module shrinks the KV
+ * cache from Theta(n d) to O(r d).  A cache holds, per head, up to `capacity` rows; a row is a
+ * key with a weight row of dv+1 floats.  wc_compress fills rows [0, r) with the coreset of a
+ * prefix (K_S and the weights W of wc_forward, same pivots, bins and options) and zeroes the
+ * rest.  Tokens that come later are appended as exact rows (key k, weights [v, 1]), a reading
+ * the pages leave open: their contribution exp(beta q k) [v, 1] is exactly that of softmax
+ * attention.  wc_decode attends queries over rows [0, rows):
+ *     Y = sum over rows of exp(beta q k_row) w_row,   O = Y[:dv] / Y[dv].
+ * The cache is opaque device memory of wc_cache_bytes() bytes (16-byte aligned), laid out for
+ * the attention kernels: keys as bf16 (hi and lo parts for fp32 problems), weights as bf16
+ * (hi and lo for fp32) with the normaliser column also in fp32.  `p` gives heads, d, dv and
+ * dtype for every cache call, n and r for wc_compress, m for wc_decode; the same capacity
+ * must be passed to every call on one cache.  Rows past the last written one must be zero
+ * (wc_compress leaves them so; append in order).                                             */
+
+/* Bytes of a cache with `capacity` rows per head (capacity >= 1). */
+wc_status wc_cache_bytes(const wc_problem* p, int32_t capacity, size_t* bytes);
+
+/* Compress the prefix K, V ([heads][n][d], [heads][n][dv]) into rows [0, r) of `cache`
+ * (capacity >= r).  u_forced, seed, pivots, rank, flags and the workspace are those of
+ * wc_forward for the same problem (wc_workspace_bytes); m is ignored.  A slot left empty
+ * (pivot -1) or a point left out of the union weights is a row of weight zero.             */
+wc_status wc_compress(const wc_problem* p, const void* K, const void* V, const float* u_forced,
+                      uint64_t seed, void* cache, int32_t capacity, int32_t* pivots,
+                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);
+
+/* Append `count` exact rows per head: key j of K_new [heads][count][d] with weights
+ * [V_new[j], 1] ([heads][count][dv]) at row row0 + j; row0 + count <= capacity.           */
+wc_status wc_cache_append(const wc_problem* p, const void* K_new, const void* V_new,
+                          int32_t count, int32_t row0, void* cache, int32_t capacity,
+                          void* stream);
+
+/* Workspace of wc_decode for p->m queries per head over `rows` rows (may be 0 bytes). */
+wc_status wc_decode_workspace_bytes(const wc_problem* p, int32_t rows, size_t* bytes);
+
+/* Attention of Q [heads][m][d] over rows [0, rows) of the cache (1 <= rows <= capacity);
+ * O [heads][m][dv] in the problem's dtype; WC_FLAG_DENOM is OR-ed into flags [heads].      */
+wc_status wc_decode(const wc_problem* p, const void* Q, const void* cache, int32_t capacity,
+                    int32_t rows, void* O, uint32_t* flags, void* ws, size_t ws_bytes,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,14 +32,16 @@ class Problem(ctypes.Structure):
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"wc_rpcholesky", "wc_weights", "wc_attend", "wc_forward",
-                          "wc_workspace_bytes", "wc_status_string", "wc_abi_version"}
+                          "wc_workspace_bytes", "wc_status_string", "wc_abi_version",
+                          "wc_cache_bytes", "wc_compress", "wc_cache_append",
+                          "wc_decode_workspace_bytes", "wc_decode"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 3
+    assert lib.wc_abi_version() == 4
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -160,3 +162,53 @@ def test_bins_only_in_forward_and_smaller_workspace(lib):
     # the forward validates its pointers for a binned problem like for a plain one
     assert lib.wc_forward(ctypes.byref(binned), A, None, A, None, ctypes.c_uint64(0), A, None, A, A,
                           A, big, None) == 1
+
+
+def cache_bytes(lib, p, capacity):
+    out = ctypes.c_size_t(0)
+    st = lib.wc_cache_bytes(ctypes.byref(p), ctypes.c_int32(capacity), ctypes.byref(out))
+    return st, out.value
+
+
+def test_cache_bytes_scale_with_capacity_not_prefix(lib):
+    """The cache holds capacity rows per head whatever the prefix length (the O(r d) memory of
+    the compressed cache); fp32 problems keep hi and lo parts, so they need more."""
+    a = Problem(32, 32768, 64, 128, 128, 1024, 1)
+    b = Problem(32, 4096, 64, 128, 128, 1024, 1)
+    st1, n1 = cache_bytes(lib, a, 1024)
+    st2, n2 = cache_bytes(lib, b, 1024)
+    st3, n3 = cache_bytes(lib, a, 2048)
+    st4, n4 = cache_bytes(lib, Problem(32, 32768, 64, 128, 128, 1024, 0), 1024)
+    assert st1 == st2 == st3 == st4 == 0
+    assert n1 == n2 and n3 > 1.9 * n1 and n4 > 1.9 * n1
+    # bf16: keys and weights in bf16 plus the fp32 normaliser column, rounded to 256 bytes
+    assert n1 >= 32 * 1024 * (128 + 128 + 1) * 2 and n1 < 32 * 1024 * (128 + 128 + 4) * 2
+    assert cache_bytes(lib, a, 0)[0] == 1
+
+
+def test_cache_calls_validate_before_any_device_work(lib):
+    A = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation first
+    u64 = ctypes.c_uint64(0)
+    big = ctypes.c_size_t(1 << 40)
+    p = Problem(2, 4096, 1, 64, 64, 256, 1)
+    i32 = ctypes.c_int32
+    # capacity below r
+    assert lib.wc_compress(ctypes.byref(p), A, A, None, u64, A, i32(255), None, A, A, A, big, None) == 1
+    # missing cache / rank
+    assert lib.wc_compress(ctypes.byref(p), A, A, None, u64, None, i32(256), None, A, A, A, big, None) == 1
+    assert lib.wc_compress(ctypes.byref(p), A, A, None, u64, A, i32(256), None, None, A, A, big, None) == 1
+    # append past the capacity, negative counts
+    assert lib.wc_cache_append(ctypes.byref(p), A, A, i32(10), i32(250), A, i32(256), None) == 1
+    assert lib.wc_cache_append(ctypes.byref(p), A, A, i32(-1), i32(0), A, i32(256), None) == 1
+    assert lib.wc_cache_append(ctypes.byref(p), A, A, i32(0), i32(0), A, i32(256), None) == 0  # nothing
+    # decode: rows outside [1, capacity], workspace too small for the coreset split
+    assert lib.wc_decode(ctypes.byref(p), A, A, i32(256), i32(300), A, A, A, big, None) == 1
+    assert lib.wc_decode(ctypes.byref(p), A, A, i32(256), i32(0), A, A, A, big, None) == 1
+    out = ctypes.c_size_t(0)
+    assert lib.wc_decode_workspace_bytes(ctypes.byref(p), i32(256), ctypes.byref(out)) == 0
+    assert out.value > 0  # 2 heads x 1 query: the rows are split over workgroups
+    assert lib.wc_decode(ctypes.byref(p), A, A, i32(256), i32(256), A, A, None, 0, None) == 3
+    # unsupported problem
+    assert lib.wc_decode(ctypes.byref(Problem(2, 4096, 1, 80, 64, 256, 1)), A, A, i32(256), i32(256),
+                         A, A, A, big, None) == 2
+
