@@ -170,6 +170,99 @@ def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1):
                       f"{f' with {bins} bins' if bins > 1 else ''}, fp64 numpy/scipy, {dt:.1f} s"}
 
 
+def run_decode(args, w, Q, K, V, dt_t, dev):
+    """COMPRESSKV measurement: compress the workload's keys and values into a cache once, then
+    time decode steps over it (queries_per_head queries per head per step, the first ones of
+    the workload), beside exact decode attention over the full key/value cache (SDPA)."""
+    import torch
+
+    from coreset_head_rpcholesky_amd import binding
+
+    bins = max(1, args.bins)
+    m = max(1, min(args.decode_queries, w.m))
+    rows = w.r
+    Qd = Q[:, :m].contiguous()
+    stream = torch.cuda.current_stream()
+    p = binding.problem(w.heads, w.n, m, w.d, w.dv, w.r, dt_t, bins)
+    ws = binding.workspace(p, dev)
+    cache = torch.empty(binding.wc_cache_bytes(p, rows), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(binding.wc_decode_workspace_bytes(p, rows), 256), dtype=torch.uint8, device=dev)
+    O = torch.empty((w.heads, m, w.dv), dtype=dt_t, device=dev)
+    flags = torch.zeros((w.heads,), dtype=torch.int32, device=dev)
+
+    def compress():
+        return binding.wc_compress(K, V, w.r, rows, seed=args.seed, bins=bins, cache=cache, ws=ws)
+
+    def decode():
+        binding.wc_decode(Qd, cache, rows, rows, w.dv, flags=flags, ws=dws, out=O)
+
+    def timed(fn, reps, per_graph):
+        fn()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(per_graph):
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per_graph)
+
+    compress_ms = timed(compress, 3, 1)
+    c = compress()
+    torch.cuda.synchronize()
+    per = 10
+    ms = timed(decode, max(1, args.steps // per), per)
+    decode()
+    torch.cuda.synchronize()
+    # exact decode attention over the full cache
+    q, k, v = Qd.unsqueeze(0), K.unsqueeze(0), V.unsqueeze(0)
+    ex = torch.nn.functional.scaled_dot_product_attention(q.float(), k.float(), v.float())[0]
+    err = torch.linalg.vector_norm(O.float() - ex, dim=(1, 2)) / torch.linalg.vector_norm(ex, dim=(1, 2))
+
+    def sdpa():
+        torch.nn.functional.scaled_dot_product_attention(q, k, v)
+
+    exact_ms = timed(sdpa, max(1, args.steps // per), per)
+    esz = 2 if w.dtype == "bf16" else 4
+    # bytes one decode step must move: the cache rows (keys, weights and the bf16 normaliser
+    # column; hi and lo parts for fp32), the queries and the outputs
+    row_bytes = (w.d + w.dv) * 2 * (1 if w.dtype == "bf16" else 2) + 2
+    step_bytes = w.heads * (rows * row_bytes + m * (w.d + w.dv) * esz)
+    achieved = step_bytes / (ms / 1e3) / 1e9
+    exact_bytes = w.heads * (w.n * (w.d + w.dv) * esz + m * (w.d + w.dv) * esz)
+    line = {
+        "metric": "WildCat COMPRESSKV decode queries/sec over the compressed cache",
+        "value": round(w.heads * m / (ms / 1e3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "prefix_keys": w.n, "cache_rows": rows,
+                   "d": w.d, "dv": w.dv, "bins": bins, "queries_per_head": m,
+                   "pivot_uniforms": f"Philox4x64-10 seed {args.seed}"},
+        "roofline": {"kernel": "attend kernels over the cache (decode step)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": step_bytes},
+        "compress_ms": round(compress_ms, 4),
+        "cache_bytes": int(cache.numel()),
+        "full_kv_bytes": int(w.heads * w.n * (w.d + w.dv) * esz),
+        "exact_decode": {"ms_per_step": round(exact_ms, 5), "bytes_per_step": exact_bytes,
+                         "op": "torch.nn.functional.scaled_dot_product_attention over the full cache"},
+        "rel_err_vs_exact": round(float(err.mean()), 6),
+        "checks": {"rank_min": int(c["rank"].min()), "flags_max": int(c["flags"].max())},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +276,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--decode", action="store_true",
+                    help="COMPRESSKV: compress the workload once, then time decode steps over the cache")
+    ap.add_argument("--decode-queries", type=int, default=1, help="queries per head per decode step")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run a plain copy kernel of this size first (for counter scaling)")
     args = ap.parse_args()
@@ -209,6 +305,9 @@ def main():
         return torch.from_numpy(x).to(dev, dt_t).contiguous()
 
     Q, K, V = up(Qn), up(Kn), up(Vn)
+    if args.decode:
+        run_decode(args, w, Q, K, V, dt_t, dev)
+        return
     bins = max(1, args.bins)
     p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t, bins)
     ws = binding.workspace(p, dev)
