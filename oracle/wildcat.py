@@ -27,6 +27,7 @@ Where the pages leave a step open, the reading is:
     Cholesky (it is positive definite for distinct keys, so the pseudo-inverse the pages
     write coincides with the inverse).
   * Output O = Y[:, :dv] / Y[:, dv] with Y = exp(beta Q K_S^T) W; no shift is applied.
+  * Key centring, when asked for, replaces K by center_keys(K) before every step.
 
 Every function here is plain numpy/scipy in float64.  Inputs given in fp32 or bf16 are
 upcast exactly.  Nothing in this package is shared with, or imported by, the HIP path.
@@ -321,6 +322,25 @@ def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None):
     for k0, k1, s0, s1 in bin_bounds(K.shape[0], r, B):
         out[s0:s1] = snap_uniforms(K[k0:k1], s1 - s0, raw_uniforms[s0:s1], beta)[0]
     return out
+
+
+def round_bf16(x):
+    """fp32 -> bf16 with round-to-nearest-even (finite inputs), returned as float32."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def center_keys(K, dtype="f32"):
+    """Key centring ("Methodik" part 3: softmax attention is invariant under a global shift of
+    the keys, K <- K - mean of the keys).  Reading for the stored precision: the shifted keys
+    are formed in fp64 and stored in the input precision, fp32 (round to nearest) or bf16 by
+    way of fp32 (round to nearest even each time).  Returns them as float64 values."""
+    K = np.asarray(K, np.float64)
+    Kc = (K - K.mean(axis=0)).astype(np.float32)
+    if dtype == "bf16":
+        Kc = round_bf16(Kc)
+    return Kc.astype(np.float64)
 
 
 def compress(K, V, r, uniforms, B=1, beta=None, weights_mode="union"):
