@@ -19,6 +19,7 @@ WC_OK, WC_ERR_INVALID_ARG, WC_ERR_UNSUPPORTED, WC_ERR_WORKSPACE, WC_ERR_DEVICE =
 WC_F32, WC_BF16 = 0, 1
 WC_FLAG_BREAKDOWN, WC_FLAG_NONFINITE, WC_FLAG_DENOM, WC_FLAG_DEPENDENT = 1, 2, 4, 8
 WC_OPT_BIN_WEIGHTS = 1
+WC_OPT_CENTER_KEYS = 2
 
 
 class WcProblem(ctypes.Structure):
@@ -181,8 +182,8 @@ def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, 
 
 
 def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_forced=None,
-               seed: int = 0, bins: int = 1, bin_weights: bool = False, ws=None, out=None,
-               stream=None):
+               seed: int = 0, bins: int = 1, bin_weights: bool = False, center_keys: bool = False,
+               ws=None, out=None, stream=None):
     """The whole WildCat forward; returns dict(O, pivots, rank, flags).  bins > 1: the
     divide-and-conquer selection of the C entry point (bins must divide n and r), with weights
     over the union of the bins' coresets, or per bin when ``bin_weights``."""
@@ -190,7 +191,8 @@ def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_f
     n = K.shape[1]
     dv = V.shape[2]
     dev = Q.device
-    p = problem(H, n, m, d, dv, r, Q.dtype, bins, WC_OPT_BIN_WEIGHTS if bin_weights else 0)
+    opts = (WC_OPT_BIN_WEIGHTS if bin_weights else 0) | (WC_OPT_CENTER_KEYS if center_keys else 0)
+    p = problem(H, n, m, d, dv, r, Q.dtype, bins, opts)
     _check_in("K", K, Q.dtype, (H, n, d), dev)
     _check_in("V", V, Q.dtype, (H, n, dv), dev)
     if u_forced is not None:

@@ -23,6 +23,7 @@ ARCH = os.environ.get("WC_OFFLOAD_ARCH", "gfx950")
 # (source, object name, extra defines): the resident kernel is built once per (d, dv).
 SOURCES = [("wc_api.cpp", "wc_api", []), ("wc_stream.hip", "wc_stream", []),
            ("wc_weights.hip", "wc_weights", []), ("wc_union.hip", "wc_union", []),
+           ("wc_center.hip", "wc_center", []),
            ("wc_attend.hip", "wc_attend", [])] + [
     ("wc_resident.hip", f"wc_resident_{d}_{dv}", [f"-DWC_RES_D={d}", f"-DWC_RES_DV={dv}"])
     for d in (64, 128) for dv in (64, 128)]

@@ -28,7 +28,7 @@ wc_status check_problem(const wc_problem* p) {
   if (p->dtype != WC_F32 && p->dtype != WC_BF16) return WC_ERR_UNSUPPORTED;
   if (p->r > kMaxR) return WC_ERR_UNSUPPORTED;
   if (p->bins < 0) return WC_ERR_INVALID_ARG;
-  if ((uint32_t)p->options & ~(uint32_t)WC_OPT_BIN_WEIGHTS) return WC_ERR_INVALID_ARG;
+  if ((uint32_t)p->options & ~(uint32_t)(WC_OPT_BIN_WEIGHTS | WC_OPT_CENTER_KEYS)) return WC_ERR_INVALID_ARG;
   if (p->bins > 1 && (p->n % p->bins != 0 || p->r % p->bins != 0)) return WC_ERR_UNSUPPORTED;
   if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
   return WC_OK;
@@ -45,6 +45,7 @@ bool resident_ok(const wc_problem& p) {
 
 bool binned(const wc_problem& p) { return p.bins > 1; }
 bool union_weights(const wc_problem& p) { return binned(p) && !(p.options & WC_OPT_BIN_WEIGHTS); }
+bool centred(const wc_problem& p) { return (p.options & WC_OPT_CENTER_KEYS) != 0; }
 
 // The per-bin view of a binned problem: heads * B sub-heads of n/B keys and r/B pivots.
 wc_problem sub_problem(const wc_problem& p) {
@@ -187,8 +188,27 @@ BinnedLayout make_binned_layout(const wc_problem& p) {
   return B;
 }
 
+// Key centring keeps its buffers after everything else: the centred keys, the per-block fp64
+// column sums and the mean.
+struct CenterLayout {
+  size_t Kc, part, mean, total;
+};
+
+CenterLayout make_center_layout(const wc_problem& p, size_t base) {
+  CenterLayout C{};
+  const size_t H = (size_t)p.heads, esz = p.dtype == WC_F32 ? 4 : 2;
+  size_t off = align_up(base);
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  C.Kc = take(H * p.n * p.d * esz);
+  C.part = take(H * wc::center_blocks(p.n) * p.d * 8);
+  C.mean = take(H * p.d * 8);
+  C.total = off;
+  return C;
+}
+
 size_t workspace_total(const wc_problem& p) {
-  return binned(p) ? make_binned_layout(p).total : make_layout(p).total;
+  const size_t base = binned(p) ? make_binned_layout(p).total : make_layout(p).total;
+  return centred(p) ? make_center_layout(p, base).total : base;
 }
 
 template <typename Tp>
@@ -421,6 +441,7 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
                         void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
   if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(pivots) || !req(F) || !req(rank) || !req(flags) || !opt(u_forced) ||
@@ -446,6 +467,7 @@ wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
                      void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
   if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(V) || !req(pivots) || !req(rank) || !req(F) || !req(W)) return WC_ERR_INVALID_ARG;
@@ -459,6 +481,7 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
                     size_t ws_bytes, void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
   if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(pivots) || !req(rank) || !req(W) || !req(flags)) return WC_ERR_INVALID_ARG;
@@ -478,6 +501,19 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
     return WC_ERR_INVALID_ARG;
   if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (centred(*p)) {
+    // every step below runs on the centred keys, kept after the forward's own workspace
+    if (!ws || !aligned16(ws) || ws_bytes < workspace_total(*p)) return WC_ERR_WORKSPACE;
+    const size_t base = binned(*p) ? make_binned_layout(*p).total : make_layout(*p).total;
+    const CenterLayout C = make_center_layout(*p, base);
+    wc::CenterArgs c{};
+    c.K = K; c.bf16 = p->dtype == WC_BF16;
+    c.H = p->heads; c.n = p->n; c.d = p->d; c.nblk = wc::center_blocks(p->n);
+    c.part = at<double>(ws, C.part); c.mean = at<double>(ws, C.mean); c.Kc = at<void>(ws, C.Kc);
+    const hipError_t e = wc::launch_center(c, s);
+    if (e != hipSuccess) return dev(e);
+    K = c.Kc;
+  }
   if (binned(*p)) return forward_binned(*p, Q, K, V, u_forced, seed, O, pivots, rank, flags, ws, ws_bytes, s);
   Layout L;
   if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
@@ -515,6 +551,7 @@ wc_status wc_compress(const wc_problem* p, const void* K, const void* V, const f
                       uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
   if (capacity < p->r) return WC_ERR_INVALID_ARG;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(V) || !req(cache) || !req(rank) || !req(flags) || !opt(u_forced) || !opt(pivots))
@@ -555,6 +592,7 @@ wc_status wc_cache_append(const wc_problem* p, const void* K_new, const void* V_
                           int32_t row0, void* cache, int32_t capacity, void* stream) {
   const wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
   if (count < 0 || row0 < 0 || capacity < 1 || (int64_t)row0 + count > capacity) return WC_ERR_INVALID_ARG;
   if (p->heads == 0 || count == 0) return WC_OK;
   if (!req(K_new) || !req(V_new) || !req(cache)) return WC_ERR_INVALID_ARG;
@@ -576,6 +614,7 @@ wc_status wc_decode(const wc_problem* p, const void* Q, const void* cache, int32
                     int32_t rows, void* O, uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
   const wc_status st = check_problem(p);
   if (st != WC_OK) return st;
+  if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
   if (rows < 1 || capacity < rows) return WC_ERR_INVALID_ARG;
   if (p->heads == 0 || p->m == 0) return WC_OK;
   if (!req(Q) || !req(cache) || !req(O) || !req(flags)) return WC_ERR_INVALID_ARG;

@@ -162,4 +162,17 @@ struct UnionArgs {
 hipError_t launch_union_gather(const UnionArgs& a, hipStream_t st);  // fills Qs
 hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st);   // A, Hd, M from Qs; X -> W
 
+// ---- key centring: Kc = K - mean of the head's keys (fp64 mean, input-precision result) ----
+struct CenterArgs {
+  const void* K;          // [H][n][d]
+  int bf16;
+  int H, n, d;
+  int nblk;               // center_blocks(n)
+  double* part;           // ws [H][nblk][d]
+  double* mean;           // ws [H][d]
+  void* Kc;               // ws [H][n][d], input dtype
+};
+int center_blocks(int n);
+hipError_t launch_center(const CenterArgs& a, hipStream_t st);
+
 }  // namespace wc

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 4
+#define WC_ABI_VERSION 5
 
 typedef enum {
   WC_OK = 0,
@@ -72,7 +72,8 @@ enum { WC_FLAG_BREAKDOWN = 1u, WC_FLAG_NONFINITE = 2u, WC_FLAG_DENOM = 4u, WC_FL
 
 /* wc_problem.options bits */
 enum {
-  WC_OPT_BIN_WEIGHTS = 1u /* bins > 1: per-bin weights instead of weights over the union */
+  WC_OPT_BIN_WEIGHTS = 1u, /* bins > 1: per-bin weights instead of weights over the union */
+  WC_OPT_CENTER_KEYS = 2u  /* wc_forward only: run on the centred keys (see wc_forward) */
 };
 
 typedef struct {
@@ -160,7 +161,15 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
  * for a slot its bin left empty after a breakdown (no longer only at the end); rank[h] counts
  * the pivots taken over all bins; flags are OR-ed over the bins.  The other entry points take
  * bins <= 1 (WC_ERR_UNSUPPORTED otherwise): their per-bin view is the problem with heads * B
- * heads of n/B keys and r/B pivots.                                                          */
+ * heads of n/B keys and r/B pivots.
+ *
+ * WC_OPT_CENTER_KEYS ("Methodik" part 3: softmax attention is invariant under a global shift
+ * of the keys, which are re-centred by their mean): every step runs on Kc = K - mean of the
+ * head's keys, the mean a fixed-order fp64 sum, Kc formed in fp64 and stored in the input
+ * precision (bf16 through fp32, round to nearest even).  Queries are not shifted: the factor
+ * exp(-beta q.mean) is common to a query's numerator and normaliser.  The pivots then refer
+ * to the centred keys (same indices).  Needs wc_workspace_bytes() of the problem with the
+ * option set.  The other entry points return WC_ERR_UNSUPPORTED for it.                      */
 wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
                      const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 4
+    assert lib.wc_abi_version() == 5
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -75,7 +75,7 @@ def ws_bytes(lib, p):
     ((2, 4004, 64, 64, 64, 256, 1, 16), 2), # bins do not divide n
     ((2, 4096, 64, 64, 64, 200, 1, 16), 2), # bins do not divide r
     ((2, 4096, 64, 64, 64, 256, 1, 16, 1), 0),  # per-bin weights option
-    ((2, 4096, 64, 64, 64, 256, 1, 16, 2), 1),  # unknown option bit
+    ((2, 4096, 64, 64, 64, 256, 1, 16, 4), 1),  # unknown option bit
     ((2, 4096, 64, 64, 64, 256, 1, 1, -1), 1),  # unknown option bits
 ])
 def test_workspace_bytes_validation(lib, fields, expect):
@@ -212,3 +212,29 @@ def test_cache_calls_validate_before_any_device_work(lib):
     assert lib.wc_decode(ctypes.byref(Problem(2, 4096, 1, 80, 64, 256, 1)), A, A, i32(256), i32(256),
                          A, A, A, big, None) == 2
 
+
+
+def test_key_centring_only_in_the_forward(lib):
+    """WC_OPT_CENTER_KEYS (2) is accepted by wc_workspace_bytes and wc_forward (whose
+    workspace grows by the centred keys) and refused by every other entry point."""
+    A = ctypes.c_void_p(256)
+    u64 = ctypes.c_uint64(0)
+    big = ctypes.c_size_t(1 << 40)
+    i32 = ctypes.c_int32
+    plain = Problem(2, 5000, 64, 128, 128, 256, 1, 1, 0)
+    cent = Problem(2, 5000, 64, 128, 128, 256, 1, 1, 2)
+    st1, b1 = ws_bytes(lib, plain)
+    st2, b2 = ws_bytes(lib, cent)
+    assert st1 == st2 == 0 and b2 >= b1 + 2 * 5000 * 128 * 2
+    st3, b3 = ws_bytes(lib, Problem(2, 5000, 64, 128, 128, 250, 1, 5, 3))  # with bins and per-bin weights
+    assert st3 == 0 and b3 > 0
+    assert call_rpc(lib, cent) == 2
+    assert lib.wc_weights(ctypes.byref(cent), A, A, A, A, A, A, big, None) == 2
+    assert lib.wc_attend(ctypes.byref(cent), A, A, A, A, A, A, A, A, big, None) == 2
+    assert lib.wc_compress(ctypes.byref(cent), A, A, None, u64, A, i32(256), None, A, A, A, big, None) == 2
+    assert lib.wc_cache_append(ctypes.byref(cent), A, A, i32(1), i32(0), A, i32(256), None) == 2
+    assert lib.wc_decode(ctypes.byref(cent), A, A, i32(256), i32(256), A, A, A, big, None) == 2
+    # the forward validates its pointers and workspace with the option like without it
+    assert lib.wc_forward(ctypes.byref(cent), A, None, A, None, u64, A, None, A, A, A, big, None) == 1
+    assert lib.wc_forward(ctypes.byref(cent), A, A, A, None, u64, A, None, A, A, A,
+                          ctypes.c_size_t(b1), None) == 3
