@@ -122,6 +122,89 @@ def rpcholesky(K, r, uniforms, beta=None):
     return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
 
 
+def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
+    """Randomly pivoted Cholesky with b candidate pivots per round.
+
+    The pages name the sequential pivot selection as a limitation that oversampling could
+    lift (future work, gist.science/de/paper/2602.10056, "Bedeutung und Ansprueche").  Reading
+    taken: the block variant of randomly pivoted Cholesky.  Round k draws b candidates, all
+    from the residual diagonal at the start of the round (s_j = min{i : C_i > u T} with
+    u = uniforms[k b + j]); their kernel columns minus what the factor already explains are
+    formed together, G = H[:, S] - F F[S, :]^T; then the candidates are eliminated in order,
+    like single pivots: candidate j's residual column g removes the accepted earlier
+    candidates of the round, and it is accepted into slot k b + j when g[s] > tol H_ss (else
+    the slot stays empty, pivot -1, zero column; an index drawn a second time in a round has
+    residual zero and is left out this way).  After
+    the round diag = diag - sum of the new columns squared, 0 at the accepted indices.  A
+    round that finds no mass stops the loop (breakdown).  b must divide r.  Returns the dict
+    of rpcholesky (rank counts accepted pivots; trace[k b] is the total before round k).
+    """
+    K = np.asarray(K, np.float64)
+    n, d = K.shape
+    beta = beta_of(d) if beta is None else beta
+    if not 1 <= r <= n or r % b:
+        raise ValueError("need 1 <= r <= n and b dividing r")
+    Hd = initial_residual(K, beta)
+    diag = Hd.copy()
+    F = np.zeros((n, r))
+    pivots = -np.ones(r, np.int64)
+    trace = np.zeros(r + 1)
+    rank, flags = 0, 0
+    if not np.all(np.isfinite(K)):
+        flags |= FLAG_NONFINITE
+    for k in range(r // b):
+        t0 = k * b
+        S = []
+        for j in range(b):
+            s, T, _ = sample_pivot(diag, uniforms[t0 + j])
+            S.append(s)
+        trace[t0] = T if np.isfinite(T) else 0.0
+        if S[0] < 0:
+            flags |= FLAG_BREAKDOWN | (0 if np.isfinite(T) else FLAG_NONFINITE)
+            break
+        G = kernel(K, K[S], beta) - F[:, :t0] @ F[S, :t0].T
+        taken = []
+        for j, s in enumerate(S):
+            g = G[:, j] - F[:, t0:t0 + j] @ F[s, t0:t0 + j]
+            if not (np.isfinite(g[s]) and g[s] > tol * Hd[s]):
+                continue
+            F[:, t0 + j] = g / np.sqrt(g[s])
+            pivots[t0 + j] = s
+            taken.append(s)
+            rank += 1
+        diag = diag - np.sum(F[:, t0:t0 + b] ** 2, axis=1)
+        diag[taken] = 0.0
+    else:
+        trace[r] = np.cumsum(np.maximum(diag, 0.0))[-1]
+    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
+
+
+def snap_uniforms_block(K, r, b, raw_uniforms, beta=None, tol=DEPENDENT_TOL):
+    """Forced-uniform mode of rpcholesky_block: each candidate's u moves to the centre of the
+    interval of the round-start running sum it selects (as snap_uniforms does per step)."""
+    K = np.asarray(K, np.float64)
+    out = np.zeros(r, np.float32)
+    u = np.asarray(raw_uniforms, np.float64).copy()
+    for k in range(r // b):
+        # the round-start diagonal is that of the loop run with the already snapped rounds
+        if k:
+            diag = rpcholesky_block(K, k * b, u[:k * b], b, beta, tol)["diag"]
+        else:
+            diag = initial_residual(K, beta_of(K.shape[1]) if beta is None else beta)
+        for j in range(b):
+            s, T, C = sample_pivot(diag, u[k * b + j])
+            if s < 0:
+                return out
+            lo = C[s - 1] if s > 0 else 0.0
+            v = np.round((lo + 0.5 * (C[s] - lo)) / T * 2.0 ** 24) * 2.0 ** -24
+            v = min(max(v, 0.0), 1.0 - 2.0 ** -24)
+            if sample_pivot(diag, v)[0] != s:
+                raise RuntimeError("snapping moved a candidate")
+            u[k * b + j] = v
+            out[k * b + j] = v
+    return out
+
+
 def snap_uniforms(K, r, raw_uniforms, beta=None):
     """Forced-uniform mode: move each u_t to the middle of the CDF interval it selects.
 
@@ -268,7 +351,7 @@ def weights_union(K, V, slots, beta=None, tol=DEPENDENT_TOL):
     return W, kept
 
 
-def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union"):
+def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union", pivot_block=1):
     """One head of divide-and-conquer WildCat with B bins.
 
     "Methodik" part 1 (efficiency): the input is split into B bins that are processed in
@@ -282,7 +365,9 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union"):
         W_b = H_{S_b S_b}^{-1} H_{S_b, bin b} [V_b, 1]  (a block-diagonal stand-in, cheaper);
     every query attends over the union, Y = exp(beta Q K_S^T) W, O = Y[:, :dv] / Y[:, dv].
     Pivots are returned as key indices of the head, bin by bin; a slot left empty by a
-    breakdown in its bin holds -1 and a zero row of W.
+    breakdown in its bin holds -1 and a zero row of W.  pivot_block = b > 1: each bin selects
+    with rpcholesky_block (b candidates per round; union weights only); B = 1 then gives the
+    block-pivoted forward of a whole head.
     """
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -291,10 +376,19 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union"):
     beta = beta_of(d) if beta is None else beta
     if weights_mode not in ("union", "bin"):
         raise ValueError("weights_mode is 'union' or 'bin'")
+    if pivot_block > 1 and weights_mode != "union":
+        raise ValueError("block pivoting leaves slots empty inside a bin: union weights only")
     pivots = -np.ones(r, np.int64)
     W = np.zeros((r, dv + 1))
     rank, flags = 0, 0
     for k0, k1, s0, s1 in bin_bounds(n, r, B):
+        if pivot_block > 1:
+            rpc = rpcholesky_block(K[k0:k1], s1 - s0, uniforms[s0:s1], pivot_block, beta)
+            pb = rpc["pivots"]
+            pivots[s0:s1] = np.where(pb >= 0, pb + k0, -1)
+            rank += rpc["rank"]
+            flags |= rpc["flags"]
+            continue
         rpc = rpcholesky(K[k0:k1], s1 - s0, uniforms[s0:s1], beta)
         rb = rpc["rank"]
         Sb = rpc["pivots"][:rb]
@@ -315,12 +409,16 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union"):
                 kept=kept)
 
 
-def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None):
-    """snap_uniforms applied bin by bin (bin b snaps its slots on its own keys)."""
+def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None, pivot_block=1):
+    """snap_uniforms (or snap_uniforms_block) applied bin by bin (bin b snaps its slots on its
+    own keys)."""
     K = np.asarray(K, np.float64)
     out = np.zeros(r, np.float32)
     for k0, k1, s0, s1 in bin_bounds(K.shape[0], r, B):
-        out[s0:s1] = snap_uniforms(K[k0:k1], s1 - s0, raw_uniforms[s0:s1], beta)[0]
+        if pivot_block > 1:
+            out[s0:s1] = snap_uniforms_block(K[k0:k1], s1 - s0, pivot_block, raw_uniforms[s0:s1], beta)
+        else:
+            out[s0:s1] = snap_uniforms(K[k0:k1], s1 - s0, raw_uniforms[s0:s1], beta)[0]
     return out
 
 
