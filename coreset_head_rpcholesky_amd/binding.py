@@ -25,7 +25,8 @@ WC_OPT_CENTER_KEYS = 2
 class WcProblem(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("n", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dv", ctypes.c_int32), ("r", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("bins", ctypes.c_int32), ("options", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("bins", ctypes.c_int32), ("options", ctypes.c_int32),
+                ("pivot_block", ctypes.c_int32)]
 
 
 class WcError(RuntimeError):
@@ -76,11 +77,12 @@ def status_string(status: int) -> str:
 wc_status_string = status_string
 
 
-def problem(heads, n, m, d, dv, r, dtype, bins: int = 1, options: int = 0) -> WcProblem:
+def problem(heads, n, m, d, dv, r, dtype, bins: int = 1, options: int = 0,
+            pivot_block: int = 1) -> WcProblem:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: WC_F32, torch.bfloat16: WC_BF16}[dtype]
     return WcProblem(int(heads), int(n), int(m), int(d), int(dv), int(r), int(dtype), int(bins),
-                     int(options))
+                     int(options), int(pivot_block))
 
 
 def wc_workspace_bytes(p: WcProblem) -> int:
@@ -119,11 +121,12 @@ def _ws(p, device, ws):
 
 
 def wc_rpcholesky(K: torch.Tensor, r: int, *, u_forced=None, seed: int = 0, ws=None,
-                  with_diag: bool = True, with_trace: bool = True, stream=None):
+                  with_diag: bool = True, with_trace: bool = True, pivot_block: int = 1,
+                  stream=None):
     """Randomly pivoted Cholesky of exp(beta K K^T) per head.  K: [H, n, d] f32 or bf16."""
     H, n, d = K.shape
     dev = K.device
-    p = problem(H, n, 0, d, 64, r, K.dtype)
+    p = problem(H, n, 0, d, 64, r, K.dtype, pivot_block=pivot_block)
     if u_forced is not None:
         _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
     pivots = torch.empty((H, r), dtype=torch.int32, device=dev)
@@ -183,7 +186,7 @@ def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, 
 
 def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_forced=None,
                seed: int = 0, bins: int = 1, bin_weights: bool = False, center_keys: bool = False,
-               ws=None, out=None, stream=None):
+               pivot_block: int = 1, ws=None, out=None, stream=None):
     """The whole WildCat forward; returns dict(O, pivots, rank, flags).  bins > 1: the
     divide-and-conquer selection of the C entry point (bins must divide n and r), with weights
     over the union of the bins' coresets, or per bin when ``bin_weights``."""
@@ -192,7 +195,7 @@ def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_f
     dv = V.shape[2]
     dev = Q.device
     opts = (WC_OPT_BIN_WEIGHTS if bin_weights else 0) | (WC_OPT_CENTER_KEYS if center_keys else 0)
-    p = problem(H, n, m, d, dv, r, Q.dtype, bins, opts)
+    p = problem(H, n, m, d, dv, r, Q.dtype, bins, opts, pivot_block)
     _check_in("K", K, Q.dtype, (H, n, d), dev)
     _check_in("V", V, Q.dtype, (H, n, dv), dev)
     if u_forced is not None:
@@ -220,14 +223,15 @@ def wc_cache_bytes(p: WcProblem, capacity: int) -> int:
 
 
 def wc_compress(K: torch.Tensor, V: torch.Tensor, r: int, capacity: int, *, u_forced=None,
-                seed: int = 0, bins: int = 1, bin_weights: bool = False, cache=None, ws=None,
-                stream=None):
+                seed: int = 0, bins: int = 1, bin_weights: bool = False, pivot_block: int = 1,
+                cache=None, ws=None, stream=None):
     """Compress the prefix K, V into rows [0, r) of a cache of ``capacity`` rows per head;
     returns dict(cache (uint8 device tensor), pivots, rank, flags)."""
     H, n, d = K.shape
     dv = V.shape[2]
     dev = K.device
-    p = problem(H, n, 0, d, dv, r, K.dtype, bins, WC_OPT_BIN_WEIGHTS if bin_weights else 0)
+    p = problem(H, n, 0, d, dv, r, K.dtype, bins, WC_OPT_BIN_WEIGHTS if bin_weights else 0,
+                pivot_block)
     _check_in("V", V, K.dtype, (H, n, dv), dev)
     if u_forced is not None:
         _check_in("u_forced", u_forced, torch.float32, (H, r), dev)

@@ -29,6 +29,13 @@ wc_status check_problem(const wc_problem* p) {
   if (p->r > kMaxR) return WC_ERR_UNSUPPORTED;
   if (p->bins < 0) return WC_ERR_INVALID_ARG;
   if ((uint32_t)p->options & ~(uint32_t)(WC_OPT_BIN_WEIGHTS | WC_OPT_CENTER_KEYS)) return WC_ERR_INVALID_ARG;
+  if (p->pivot_block < 0) return WC_ERR_INVALID_ARG;
+  if (p->pivot_block > 1) {
+    const int B = p->bins > 1 ? p->bins : 1;
+    if (p->pivot_block != 16 && p->pivot_block != 32 && p->pivot_block != 64) return WC_ERR_UNSUPPORTED;
+    if ((p->r / B) % p->pivot_block != 0) return WC_ERR_UNSUPPORTED;
+    if (p->options & WC_OPT_BIN_WEIGHTS) return WC_ERR_UNSUPPORTED;  // empty slots inside a bin
+  }
   if (p->bins > 1 && (p->n % p->bins != 0 || p->r % p->bins != 0)) return WC_ERR_UNSUPPORTED;
   if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
   return WC_OK;
@@ -44,15 +51,21 @@ bool resident_ok(const wc_problem& p) {
 }
 
 bool binned(const wc_problem& p) { return p.bins > 1; }
-bool union_weights(const wc_problem& p) { return binned(p) && !(p.options & WC_OPT_BIN_WEIGHTS); }
+bool blocked(const wc_problem& p) { return p.pivot_block > 1; }
+// Bins, or block pivots (whose empty slots the factor-based weights cannot take), go through
+// the per-bin selection, the fold of the pivots and weights over the union.
+bool union_path(const wc_problem& p) { return binned(p) || blocked(p); }
+bool union_weights(const wc_problem& p) { return union_path(p) && !(p.options & WC_OPT_BIN_WEIGHTS); }
 bool centred(const wc_problem& p) { return (p.options & WC_OPT_CENTER_KEYS) != 0; }
 
-// The per-bin view of a binned problem: heads * B sub-heads of n/B keys and r/B pivots.
+// The per-bin view of a binned problem: heads * B sub-heads of n/B keys and r/B pivots (a
+// problem with one bin is its own view).
 wc_problem sub_problem(const wc_problem& p) {
   wc_problem s = p;
-  s.heads = p.heads * p.bins;
-  s.n = p.n / p.bins;
-  s.r = p.r / p.bins;
+  const int B = p.bins > 1 ? p.bins : 1;
+  s.heads = p.heads * B;
+  s.n = p.n / B;
+  s.r = p.r / B;
   s.m = 0;
   s.bins = 1;
   s.options = 0;
@@ -83,6 +96,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   int rows, nblk, nchunk, chunk_rows, nsplit, rp;
   size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Wdh, Ypart;
+  size_t bcand, bG, bM, bstop;  // block pivot selection
   size_t total;
 };
 
@@ -124,6 +138,13 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
     L.Xpart = take(H * L.nchunk * r * nc * 4);
     L.X = take(H * r * nc * 4);
     L.W = take(H * r * nc * 4);
+    if (blocked(p)) {
+      const size_t b = (size_t)p.pivot_block;
+      L.bcand = take(H * b * 4);
+      L.bG = take(H * b * n * 4);
+      L.bM = take(H * b * b * 4);
+      L.bstop = take(H * 4);
+    }
   }
   if (parts & kAttend) {
     const size_t lo = p.dtype == WC_F32 ? 1 : 0;  // lo parts of the bf16 splits: fp32 only
@@ -207,7 +228,7 @@ CenterLayout make_center_layout(const wc_problem& p, size_t base) {
 }
 
 size_t workspace_total(const wc_problem& p) {
-  const size_t base = binned(p) ? make_binned_layout(p).total : make_layout(p).total;
+  const size_t base = union_path(p) ? make_binned_layout(p).total : make_layout(p).total;
   return centred(p) ? make_center_layout(p, base).total : base;
 }
 
@@ -284,9 +305,38 @@ hipError_t run_attend(const wc_problem& p, const Layout& L, void* ws, const void
 }
 
 // Pivot loop for every head of p (resident kernel when it fits, else the streaming loop).
+hipError_t run_rpc_block(const wc_problem& p, const Layout& L, void* ws, const void* K,
+                         const float* u_forced, uint64_t seed, int32_t* pivots, float* F,
+                         float* diag, double* trace, int32_t* rank, uint32_t* flags, hipStream_t st) {
+  wc::BlockRpcArgs a{};
+  wc::StreamRpcArgs& s = a.s;
+  s.K = K;
+  s.bf16 = p.dtype == WC_BF16;
+  s.u_forced = u_forced;
+  s.seed = seed;
+  s.uniforms = u_forced ? const_cast<float*>(u_forced) : at<float>(ws, L.unif);
+  s.H = p.heads; s.n = p.n; s.d = p.d; s.r = p.r;
+  s.rows = L.rows; s.nblk = L.nblk;
+  s.beta_log2e = beta_log2e(p.d);
+  s.F = F;
+  s.diag0 = at<float>(ws, L.diag0);
+  s.diag1 = at<float>(ws, L.diag1);
+  s.part0 = at<double>(ws, L.part0);
+  s.part1 = at<double>(ws, L.part1);
+  s.pivots = pivots; s.trace = trace; s.rank = rank; s.flags = flags; s.diag_out = diag;
+  a.b = p.pivot_block;
+  a.tol = 0x1p-12f;
+  a.cand = at<int32_t>(ws, L.bcand);
+  a.G = at<float>(ws, L.bG);
+  a.M = at<float>(ws, L.bM);
+  a.stop = at<int32_t>(ws, L.bstop);
+  return wc::launch_rpc_block(a, st);
+}
+
 hipError_t run_select(const wc_problem& p, const Layout& L, void* ws, const void* K,
                       const float* u_forced, uint64_t seed, int32_t* pivots, float* F,
                       int32_t* rank, uint32_t* flags, hipStream_t st) {
+  if (blocked(p)) return run_rpc_block(p, L, ws, K, u_forced, seed, pivots, F, nullptr, nullptr, rank, flags, st);
   if (resident_ok(p)) {
     wc::ResidentArgs a{};
     a.K = static_cast<const uint16_t*>(K);
@@ -450,6 +500,8 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
   Layout L;
   if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (blocked(*p))
+    return dev(run_rpc_block(*p, L, ws, K, u_forced, seed, pivots, F, diag, trace, rank, flags, s));
   if (resident_ok(*p)) {
     wc::ResidentArgs a{};
     a.K = static_cast<const uint16_t*>(K);
@@ -468,7 +520,7 @@ wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
   if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
-  if (binned(*p)) return WC_ERR_UNSUPPORTED;
+  if (binned(*p) || blocked(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(V) || !req(pivots) || !req(rank) || !req(F) || !req(W)) return WC_ERR_INVALID_ARG;
   Layout L;
@@ -482,7 +534,7 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
   if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
-  if (binned(*p)) return WC_ERR_UNSUPPORTED;
+  if (binned(*p) || blocked(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(pivots) || !req(rank) || !req(W) || !req(flags)) return WC_ERR_INVALID_ARG;
   if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
@@ -514,7 +566,7 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
     if (e != hipSuccess) return dev(e);
     K = c.Kc;
   }
-  if (binned(*p)) return forward_binned(*p, Q, K, V, u_forced, seed, O, pivots, rank, flags, ws, ws_bytes, s);
+  if (union_path(*p)) return forward_binned(*p, Q, K, V, u_forced, seed, O, pivots, rank, flags, ws, ws_bytes, s);
   Layout L;
   if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
   if (resident_ok(*p) && p->m > 0) {
@@ -563,7 +615,7 @@ wc_status wc_compress(const wc_problem* p, const void* K, const void* V, const f
   wc::AttendArgs a = cache_args(q, C, cache, capacity);
   a.K = K; a.n = q.n; a.r = q.r;
   hipError_t e;
-  if (binned(q)) {
+  if (union_path(q)) {
     // selection and weights as in the forward (no queries); the weights and the head's
     // pivots are left in the workspace
     if ((st = forward_binned(q, nullptr, K, V, u_forced, seed, nullptr, pivots, rank, flags, ws, ws_bytes, s)) != WC_OK)

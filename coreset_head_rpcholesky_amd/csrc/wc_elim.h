@@ -1,0 +1,71 @@
+// Elimination of a small symmetric block with the leave-out rule, shared by the union weights
+// and the block pivot selection.
+#pragma once
+#include "wc_device.h"
+
+namespace wc {
+
+// M = inverse of the Cholesky factor of the kept part of the B x B block in sA (row-major,
+// pitch P floats), for a workgroup of 4 B threads.  Right-looking elimination applied
+// alongside to the identity: step j takes the pivot residual p = A[j][j]; if p > tol hd[j]
+// every later row i subtracts f_i = A[i][j] / p times row j, in the block and in G (G starts
+// as the identity).  G ends as U^{-1}, U the unit lower factor of A = U diag(p) U^T over the
+// kept points, so M = diag(p)^{-1/2} G; a left-out point eliminates nothing and gets a zero
+// row of M (M[j][j] > 0 exactly for the kept ones).  Thread (i, q) holds columns
+// q B/4 .. (q+1) B/4 - 1 of row i of the block and of G; column j of the block and row j of G
+// are published in LDS (double-buffered by the parity of j, one barrier per step).  M is
+// written row-major with leading dimension B.  Returns, in every thread, whether a point with
+// hd > 0 was left out.
+template <int B, int P>
+__device__ __forceinline__ bool elim_block(const float* sA, const float* hd, float tol, float* M,
+                                           float (*sCol)[B], float (*sRow)[B]) {
+  constexpr int CB = B / 4;
+  const int tid = threadIdx.x, ri = tid >> 2, q = tid & 3, c0 = CB * q;
+  float v[CB], g[CB];
+#pragma unroll
+  for (int e = 0; e < CB; e += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(sA + ri * P + c0 + e);
+    v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
+  }
+#pragma unroll
+  for (int e = 0; e < CB; ++e) g[e] = ri == c0 + e ? 1.f : 0.f;
+  bool dependent = false;
+  __syncthreads();  // sA may be overwritten by the caller only after everyone has read it
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int buf = j & 1;
+    if (q == j / CB) sCol[buf][ri] = v[j % CB];
+    if (ri == j) {
+#pragma unroll
+      for (int e = 0; e < CB; e += 4)
+        *reinterpret_cast<float4*>(&sRow[buf][c0 + e]) = make_float4(g[e], g[e + 1], g[e + 2], g[e + 3]);
+    }
+    __syncthreads();
+    const float p = sCol[buf][j];
+    const float hj = hd[j];
+    const bool keep = p > tol * hj;
+    dependent |= !keep && hj > 0.f;
+    if (ri == j) {
+      // row j of M (hardware reciprocal square root, about 1 ulp)
+      const float s = keep ? __builtin_amdgcn_rsqf(p) : 0.f;
+#pragma unroll
+      for (int e = 0; e < CB; e += 4)
+        *reinterpret_cast<float4*>(M + (size_t)j * B + c0 + e) = make_float4(g[e] * s, g[e + 1] * s, g[e + 2] * s, g[e + 3] * s);
+    }
+    if (keep && ri > j) {
+      const float f = sCol[buf][ri] * __builtin_amdgcn_rcpf(p);
+#pragma unroll
+      for (int e = 0; e < CB; e += 4) {
+        const float4 cj = *reinterpret_cast<const float4*>(&sCol[buf][c0 + e]);
+        const float4 gj = *reinterpret_cast<const float4*>(&sRow[buf][c0 + e]);
+        v[e] = fmaf(-f, cj.x, v[e]); v[e + 1] = fmaf(-f, cj.y, v[e + 1]);
+        v[e + 2] = fmaf(-f, cj.z, v[e + 2]); v[e + 3] = fmaf(-f, cj.w, v[e + 3]);
+        g[e] = fmaf(-f, gj.x, g[e]); g[e + 1] = fmaf(-f, gj.y, g[e + 1]);
+        g[e + 2] = fmaf(-f, gj.z, g[e + 2]); g[e + 3] = fmaf(-f, gj.w, g[e + 3]);
+      }
+    }
+  }
+  return dependent;
+}
+
+}  // namespace wc

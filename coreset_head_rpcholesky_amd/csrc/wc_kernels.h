@@ -67,6 +67,18 @@ struct StreamRpcArgs {
 constexpr int kStreamThreads = 256;
 hipError_t launch_rpc_stream(const StreamRpcArgs& a, hipStream_t st);
 
+// ---- block pivot selection: b candidates per round (the fields of the streaming loop plus) ----
+struct BlockRpcArgs {
+  StreamRpcArgs s;      // K, uniforms, residual and block masses (rows, nblk), F, pivots, ...
+  int b;                // candidates per round: 16, 32 or 64, dividing r
+  float tol;            // relative residual at or below which a candidate is left out
+  int32_t* cand;        // ws [H][b]
+  float* G;             // ws [H][b][n]  candidate columns minus what F explains
+  float* M;             // ws [H][b][b]  inverse factor of the kept part of the candidate block
+  int32_t* stop;        // ws [H]        round at which the loop stopped (r / b: it did not)
+};
+hipError_t launch_rpc_block(const BlockRpcArgs& a, hipStream_t st);
+
 // ---- weights: W = L^{-T} F^T [V, 1] ----
 struct WeightsArgs {
   const void* V;          // [H][n][dv]

@@ -14,6 +14,7 @@
 // what step t-1 wrote.  Column t of F is a contiguous run of n floats (F is [r][n]), so the
 // correction F[i, :t].F[s, :t] streams F column by column with coalesced loads.
 #include "wc_device.h"
+#include "wc_elim.h"
 #include "wc_kernels.h"
 
 namespace wc {
@@ -417,6 +418,330 @@ static hipError_t run_rpc(StreamRpcArgs a, int rows, hipStream_t st) {
   }
   hipLaunchKernelGGL((rpc_final_kernel<0>), dim3(a.H), dim3(NT), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block pivot selection (b candidates per round; the pages leave the mechanism that would lift
+// the sequential pivot selection to future work, gist.science/de/paper/2602.10056, "Bedeutung
+// und Ansprueche"; read here as the block variant of randomly pivoted Cholesky).  Round k,
+// slots t0 = k b .. t0 + b - 1, reads the residual and block masses written by round k - 1:
+//   sample  one workgroup per candidate resolves s_j = min{i : C_i > u T} on that residual;
+//   column  G[:, j] = exp(beta K k_{s_j}) - F[:, :t0] F[s_j, :t0]^T for all rows (F is read
+//           once per round instead of once per pivot);
+//   factor  the b x b block G[S, :] is eliminated in candidate order with the leave-out rule
+//           (elim_block, relative to H_ss); kept candidates fill their slots, the others -1;
+//   apply   F[:, t0 + j] = G M^T (zero columns for the left-out ones), residual update, masses.
+// ---------------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(64) blk_init_kernel(BlockRpcArgs A) {
+  const int h = blockIdx.x;
+  if (threadIdx.x == 0) {
+    A.s.rank[h] = 0;
+    A.stop[h] = A.s.r / A.b;
+  }
+}
+
+__global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int t0) {
+  __shared__ double red[NW];
+  __shared__ int ired[NW];
+  extern __shared__ __attribute__((aligned(16))) double s_part[];  // [nblk]
+  const StreamRpcArgs& a = A.s;
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int n = a.n, nblk = a.nblk, rows = a.rows, k = t0 / A.b;
+  int32_t* cand = A.cand + (size_t)h * A.b + j;
+  if (a.flags[h] & WC_DFLAG_BREAKDOWN) {
+    if (tid == 0) *cand = -1;
+    return;
+  }
+  const double* part = (k & 1) ? a.part1 : a.part0;
+  const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
+  const int per = (nblk + NT - 1) / NT;
+  double mine = 0.0;
+  for (int e = 0; e < per; ++e) {
+    const int bb = tid * per + e;
+    if (bb < nblk) {
+      const double v = part[(size_t)h * nblk + bb];
+      s_part[bb] = v;
+      mine += v;
+    }
+  }
+  double Ttot;
+  const double excl = block_excl_scan(mine, red, &Ttot);
+  if (!(Ttot > 0.0) || !__builtin_isfinite(Ttot)) {
+    if (tid == 0) {
+      *cand = -1;
+      if (j == 0) {
+        a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(Ttot) ? 0u : WC_DFLAG_NONFINITE);
+        A.stop[h] = k;
+        if (a.trace) a.trace[(size_t)h * (a.r + 1) + t0] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
+      }
+    }
+    return;
+  }
+  if (j == 0 && a.trace)
+    for (int t = tid; t < A.b; t += NT) a.trace[(size_t)h * (a.r + 1) + t0 + t] = t == 0 ? Ttot : 0.0;
+  const double uT = (double)a.uniforms[(size_t)h * a.r + t0 + j] * Ttot;
+  int bc = 0x7fffffff, lastpos = -1;
+  double run = excl;
+  for (int e = 0; e < per; ++e) {
+    const int bb = tid * per + e;
+    if (bb < nblk) {
+      const double v = s_part[bb];
+      run += v;
+      if (bc == 0x7fffffff && v > 0.0 && run > uT) bc = bb;
+      if (v > 0.0) lastpos = bb;
+    }
+  }
+  int bstar = block_min_int(bc, ired);
+  if (bstar == 0x7fffffff) bstar = block_max_int(lastpos, ired);
+  __syncthreads();
+  if (tid == bstar / per) {
+    double o = excl;
+    for (int e = 0; e < bstar - tid * per; ++e) o += s_part[tid * per + e];
+    red[0] = o;
+  }
+  __syncthreads();
+  const double boff = red[0];
+  const int rpt = rows / NT, r0 = bstar * rows;
+  double pm[4];
+  double tmass = 0.0;
+  for (int e = 0; e < rpt; ++e) {
+    const int i = r0 + tid * rpt + e;
+    pm[e] = (i < n) ? mass_of(dg_in[i]) : 0.0;
+    tmass += pm[e];
+  }
+  double btot;
+  __syncthreads();
+  const double rexcl = block_excl_scan(tmass, red, &btot);
+  int scand = 0x7fffffff, slast = -1;
+  double c = boff + rexcl;
+  for (int e = 0; e < rpt; ++e) {
+    c += pm[e];
+    const int i = r0 + tid * rpt + e;
+    if (scand == 0x7fffffff && c > uT && pm[e] > 0.0) scand = i;
+    if (pm[e] > 0.0) slast = i;
+  }
+  int s = block_min_int(scand, ired);
+  if (s == 0x7fffffff) s = block_max_int(slast, ired);
+  if (tid == 0) *cand = (s >= 0 && s < n) ? s : -1;
+}
+
+// One thread per row (256 rows per workgroup): the candidate keys and, chunk by chunk, the
+// candidate rows of F sit in LDS; F is read once, column by column (coalesced).
+template <typename T, int D, int B>
+__global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A, int t0) {
+  __shared__ __attribute__((aligned(16))) float sKS[D][B];
+  __shared__ __attribute__((aligned(16))) float sFS[64][B];
+  __shared__ int sC[B];
+  const StreamRpcArgs& a = A.s;
+  const int h = blockIdx.y, tid = threadIdx.x, n = a.n;
+  if (a.flags[h] & WC_DFLAG_BREAKDOWN) return;
+  const int i = blockIdx.x * NT + tid;
+  const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * n * D;
+  const float* F = a.F + (size_t)h * a.r * n;
+  if (tid < B) sC[tid] = A.cand[(size_t)h * B + tid];
+  __syncthreads();
+  for (int e = tid; e < D * B; e += NT) {
+    const int jj = e / D, ee = e % D, sj = sC[jj];
+    sKS[ee][jj] = sj >= 0 ? ld_elem<T>(K + (size_t)sj * D + ee) : 0.f;
+  }
+  float acc[B];
+#pragma unroll
+  for (int jj = 0; jj < B; ++jj) acc[jj] = 0.f;
+  for (int c0 = 0; c0 < t0; c0 += 64) {
+    const int cc = min(64, t0 - c0);
+    __syncthreads();
+    for (int e = tid; e < cc * B; e += NT) {
+      const int c = e / B, jj = e % B, sj = sC[jj];
+      sFS[c][jj] = sj >= 0 ? F[(size_t)(c0 + c) * n + sj] : 0.f;
+    }
+    __syncthreads();
+    if (i < n) {
+      for (int c = 0; c < cc; ++c) {
+        const float f = F[(size_t)(c0 + c) * n + i];
+#pragma unroll
+        for (int jj = 0; jj < B; jj += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(&sFS[c][jj]);
+          acc[jj] = fmaf(f, q.x, acc[jj]); acc[jj + 1] = fmaf(f, q.y, acc[jj + 1]);
+          acc[jj + 2] = fmaf(f, q.z, acc[jj + 2]); acc[jj + 3] = fmaf(f, q.w, acc[jj + 3]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (i >= n) return;
+  float hk[B];
+#pragma unroll
+  for (int jj = 0; jj < B; ++jj) hk[jj] = 0.f;
+  const T* kr = K + (size_t)i * D;
+  for (int e = 0; e < D; ++e) {
+    const float x = ld_elem<T>(kr + e);
+#pragma unroll
+    for (int jj = 0; jj < B; jj += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(&sKS[e][jj]);
+      hk[jj] = fmaf(x, q.x, hk[jj]); hk[jj + 1] = fmaf(x, q.y, hk[jj + 1]);
+      hk[jj + 2] = fmaf(x, q.z, hk[jj + 2]); hk[jj + 3] = fmaf(x, q.w, hk[jj + 3]);
+    }
+  }
+  float* G = A.G + (size_t)h * B * n;
+#pragma unroll
+  for (int jj = 0; jj < B; ++jj) G[(size_t)jj * n + i] = __builtin_amdgcn_exp2f(hk[jj] * a.beta_log2e) - acc[jj];
+}
+
+template <typename T, int D, int B>
+__global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int t0) {
+  constexpr int P = B + 4;
+  __shared__ __attribute__((aligned(16))) float sA[B * P];
+  __shared__ __attribute__((aligned(16))) float sCol[2][B];
+  __shared__ __attribute__((aligned(16))) float sRow[2][B];
+  __shared__ float sHd[B];
+  __shared__ int sC[B];
+  const StreamRpcArgs& a = A.s;
+  const int h = blockIdx.x, tid = threadIdx.x, n = a.n;
+  if (a.flags[h] & WC_DFLAG_BREAKDOWN) return;
+  const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * n * D;
+  if (tid < B) {
+    const int sj = A.cand[(size_t)h * B + tid];
+    sC[tid] = sj;
+    // kernel diagonal at the candidate, the scale of the leave-out test
+    float q = 0.f;
+    if (sj >= 0)
+      for (int e = 0; e < D; ++e) {
+        const float x = ld_elem<T>(K + (size_t)sj * D + e);
+        q = fmaf(x, x, q);
+      }
+    sHd[tid] = sj >= 0 ? __builtin_amdgcn_exp2f(q * a.beta_log2e) : 0.f;
+  }
+  __syncthreads();
+  const float* G = A.G + (size_t)h * B * n;
+  for (int e = tid; e < B * B; e += 4 * B) {
+    const int ii = e / B, jj = e % B, si = sC[ii];
+    sA[ii * P + jj] = si >= 0 ? G[(size_t)jj * n + si] : 0.f;
+  }
+  __syncthreads();
+  float* M = A.M + (size_t)h * B * B;
+  elim_block<B, P>(sA, sHd, A.tol, M, sCol, sRow);
+  __syncthreads();
+  if (tid < B) {
+    const bool keep = M[(size_t)tid * B + tid] > 0.f;
+    a.pivots[(size_t)h * a.r + t0 + tid] = keep ? sC[tid] : -1;
+    if (keep) atomicAdd(&a.rank[h], 1);
+  }
+}
+
+// New columns of F, residual update and block masses; `rows` rows per workgroup as the
+// streaming loop, so that the masses line up with the blocks the sampler reads.
+template <int B>
+__global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int t0) {
+  __shared__ __attribute__((aligned(16))) float sMt[B][B];
+  __shared__ int sP[B];
+  __shared__ double red[NW];
+  const StreamRpcArgs& a = A.s;
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, n = a.n, k = t0 / B;
+  if (a.flags[h] & WC_DFLAG_BREAKDOWN) return;
+  const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
+  float* dg_out = ((k & 1) ? a.diag0 : a.diag1) + (size_t)h * n;
+  double* part_out = (k & 1) ? a.part0 : a.part1;
+  const float* M = A.M + (size_t)h * B * B;
+  for (int e = tid; e < B * B; e += NT) sMt[e % B][e / B] = M[e];
+  if (tid < B) sP[tid] = a.pivots[(size_t)h * a.r + t0 + tid];
+  __syncthreads();
+  const float* G = A.G + (size_t)h * B * n;
+  float* F = a.F + (size_t)h * a.r * n;
+  double mass = 0.0;
+  for (int i = b * a.rows + tid; i < min(n, (b + 1) * a.rows); i += NT) {
+    float g[B];
+#pragma unroll
+    for (int c = 0; c < B; ++c) g[c] = G[(size_t)c * n + i];
+    float dsum = 0.f;
+    bool piv = false;
+#pragma unroll 4
+    for (int jj = 0; jj < B; ++jj) {
+      float f = 0.f;
+#pragma unroll
+      for (int c = 0; c < B; ++c) f = fmaf(g[c], sMt[c][jj], f);
+      F[(size_t)(t0 + jj) * n + i] = f;
+      dsum = fmaf(f, f, dsum);
+      piv |= sP[jj] == i;
+    }
+    const float d = piv ? 0.f : dg_in[i] - dsum;
+    dg_out[i] = d;
+    mass += mass_of(d);
+  }
+  const double tot = block_sum(mass, red);
+  if (tid == 0) part_out[(size_t)h * a.nblk + b] = tot;
+}
+
+// After the last round: the trace after it, and for a head that stopped early the empty slots,
+// zero columns of F and zero trace entries past the stop; the final residual if asked for.
+__global__ void __launch_bounds__(NT) blk_final_kernel(BlockRpcArgs A) {
+  __shared__ double red[NW];
+  const StreamRpcArgs& a = A.s;
+  const int h = blockIdx.x, tid = threadIdx.x, n = a.n, nblk = a.nblk;
+  const int ks = A.stop[h], rounds = a.r / A.b, t1 = ks * A.b;
+  const double* part = (ks & 1) ? a.part1 : a.part0;
+  const float* dg = ((ks & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
+  if (ks == rounds && a.trace) {
+    const int per = (nblk + NT - 1) / NT;
+    double mine = 0.0;
+    for (int e = 0; e < per; ++e) {
+      const int bb = tid * per + e;
+      if (bb < nblk) mine += part[(size_t)h * nblk + bb];
+    }
+    double T;
+    block_excl_scan(mine, red, &T);
+    if (tid == 0) a.trace[(size_t)h * (a.r + 1) + a.r] = T;
+  }
+  if (ks < rounds) {
+    if (a.trace)
+      for (int t = t1 + 1 + tid; t <= a.r; t += NT) a.trace[(size_t)h * (a.r + 1) + t] = 0.0;
+    for (int t = t1 + tid; t < a.r; t += NT) a.pivots[(size_t)h * a.r + t] = -1;
+    for (size_t e = (size_t)t1 * n + tid; e < (size_t)a.r * n; e += NT) a.F[(size_t)h * a.r * n + e] = 0.f;
+  }
+  if (a.diag_out)
+    for (int i = tid; i < n; i += NT) a.diag_out[(size_t)h * n + i] = dg[i];
+}
+
+template <typename T, int D, int B>
+static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
+  StreamRpcArgs& a = A.s;
+  const dim3 grid(a.nblk, a.H);
+  hipError_t e;
+  if (!a.u_forced) {
+    const size_t nu = (size_t)a.H * a.r;
+    hipLaunchKernelGGL(uniforms_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((rpc_init_kernel<T, D>), grid, dim3(NT), 0, st, a, a.rows);
+  hipLaunchKernelGGL(blk_init_kernel, dim3(a.H), dim3(64), 0, st, A);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t lds = (size_t)a.nblk * sizeof(double);
+  const int colgrid = (a.n + NT - 1) / NT;
+  for (int t0 = 0; t0 < a.r; t0 += B) {
+    hipLaunchKernelGGL(blk_sample_kernel, dim3(B, a.H), dim3(NT), lds, st, A, t0);
+    hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A, t0);
+    hipLaunchKernelGGL((blk_factor_kernel<T, D, B>), dim3(a.H), dim3(4 * B), 0, st, A, t0);
+    hipLaunchKernelGGL((blk_apply_kernel<B>), grid, dim3(NT), 0, st, A, t0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(blk_final_kernel, dim3(a.H), dim3(NT), 0, st, A);
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t run_block_b(const BlockRpcArgs& A, hipStream_t st) {
+  const StreamRpcArgs& a = A.s;
+  if (a.bf16) return a.d == 64 ? run_block<uint16_t, 64, B>(A, st) : run_block<uint16_t, 128, B>(A, st);
+  return a.d == 64 ? run_block<float, 64, B>(A, st) : run_block<float, 128, B>(A, st);
+}
+
+hipError_t launch_rpc_block(const BlockRpcArgs& A, hipStream_t st) {
+  switch (A.b) {
+    case 16: return run_block_b<16>(A, st);
+    case 32: return run_block_b<32>(A, st);
+    case 64: return run_block_b<64>(A, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rpc_stream(const StreamRpcArgs& a, hipStream_t st) {

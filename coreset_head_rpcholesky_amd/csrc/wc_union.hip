@@ -19,6 +19,7 @@
 // then the backward substitution, block k from the last: W_k = M_kk^T Z_k and
 // Z_j -= L_kj^T W_k for j < k.  All heads run in each launch.
 #include "wc_device.h"
+#include "wc_elim.h"
 #include "wc_kernels.h"
 
 namespace wc {
@@ -154,65 +155,14 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
 }
 
 // ---- diag: M_kk = inverse of the Cholesky factor of the kept part of A_kk -------------------
-// Run by a whole 256-thread workgroup on the block in sA (row-major, already updated).  Right-
-// looking elimination with the drop rule, applied alongside to the identity: step j takes the
-// pivot residual p = A[j][j]; if p > tol H_jj every later row i subtracts f_i = A[i][j] / p
-// times row j, in the block and in G (G starts as the identity).  G ends as U^{-1}, U the unit
-// lower factor of A = U diag(p) U^T over the kept points, so M = diag(p)^{-1/2} G; a left-out
-// point eliminates nothing and gets a zero row of M.  Thread (i, q) holds columns 16q .. 16q+15
-// of row i of the block and of G; column j of the block and row j of G are published in LDS
-// (double-buffered by the parity of j, one barrier per step).
+// A whole 256-thread workgroup eliminates the (already updated) block in sA with the leave-out
+// rule (elim_block); left-out points of valid slots set WC_DFLAG_DEPENDENT.
 __device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, const float (*sA)[kLP],
                                            float (*sCol)[kUB], float (*sRow)[kUB]) {
-  const int tid = threadIdx.x, ri = tid >> 2, q = tid & 3, c0 = 16 * q;
-  float v[16], g[16];
-#pragma unroll
-  for (int e = 0; e < 16; e += 4) {
-    const float4 x = *reinterpret_cast<const float4*>(&sA[ri][c0 + e]);
-    v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
-  }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) g[e] = ri == c0 + e ? 1.f : 0.f;
   const float* Hd = a.Hd + (size_t)h * a.rp + (size_t)k * kUB;
   float* M = a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB;
-  bool dependent = false;
-  __syncthreads();  // sA may be overwritten by the caller only after everyone has read it
-#pragma unroll
-  for (int j = 0; j < kUB; ++j) {
-    const int buf = j & 1;
-    // publish column j of the block (owners: q == j / 16) and row j of G (owners: ri == j)
-    if (q == j / 16) sCol[buf][ri] = v[j % 16];
-    if (ri == j) {
-#pragma unroll
-      for (int e = 0; e < 16; e += 4)
-        *reinterpret_cast<float4*>(&sRow[buf][c0 + e]) = make_float4(g[e], g[e + 1], g[e + 2], g[e + 3]);
-    }
-    __syncthreads();
-    const float p = sCol[buf][j];
-    const float hj = Hd[j];
-    const bool keep = p > a.tol * hj;
-    dependent |= !keep && hj > 0.f;
-    if (ri == j) {
-      // row j of M (hardware reciprocal square root, about 1 ulp)
-      const float s = keep ? __builtin_amdgcn_rsqf(p) : 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4)
-        *reinterpret_cast<float4*>(M + (size_t)j * kUB + c0 + e) = make_float4(g[e] * s, g[e + 1] * s, g[e + 2] * s, g[e + 3] * s);
-    }
-    if (keep && ri > j) {
-      const float f = sCol[buf][ri] * __builtin_amdgcn_rcpf(p);
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const float4 cj = *reinterpret_cast<const float4*>(&sCol[buf][c0 + e]);
-        const float4 gj = *reinterpret_cast<const float4*>(&sRow[buf][c0 + e]);
-        v[e] = fmaf(-f, cj.x, v[e]); v[e + 1] = fmaf(-f, cj.y, v[e + 1]);
-        v[e + 2] = fmaf(-f, cj.z, v[e + 2]); v[e + 3] = fmaf(-f, cj.w, v[e + 3]);
-        g[e] = fmaf(-f, gj.x, g[e]); g[e + 1] = fmaf(-f, gj.y, g[e + 1]);
-        g[e + 2] = fmaf(-f, gj.z, g[e + 2]); g[e + 3] = fmaf(-f, gj.w, g[e + 3]);
-      }
-    }
-  }
-  if (dependent && tid == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
+  const bool dependent = elim_block<kUB, kLP>(&sA[0][0], Hd, a.tol, M, sCol, sRow);
+  if (dependent && threadIdx.x == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
 }
 
 // The first diagonal block (later ones are factored by the update of the step before).

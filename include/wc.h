@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 5
+#define WC_ABI_VERSION 6
 
 typedef enum {
   WC_OK = 0,
@@ -86,6 +86,8 @@ typedef struct {
   int32_t dtype; /* wc_dtype of Q, K, V and O */
   int32_t bins;  /* 0 or 1: one bin; B > 1: divide-and-conquer selection (wc_forward only) */
   int32_t options; /* OR of WC_OPT_* bits; 0 for the defaults */
+  int32_t pivot_block; /* 0 or 1: one pivot per step; b in {16, 32, 64}: b candidates per round
+                          (wc_rpcholesky, wc_forward, wc_compress; see wc_rpcholesky) */
 } wc_problem;
 
 /* ABI version of the loaded library (WC_ABI_VERSION it was built with). */
@@ -113,6 +115,18 @@ wc_status wc_workspace_bytes(const wc_problem* p, size_t* bytes);
  *   diag     out  [heads][n] final residual diagonal, or NULL
  *   trace    out  [heads][r+1]: trace[t] = T before step t, trace[r] after the last, or NULL
  *   rank, flags out [heads]                                                              */
+/* pivot_block = b > 1 (b in {16, 32, 64} dividing r, or r / bins with bins): b candidate
+ * pivots per round.  The pages leave a remedy for the sequential pivot selection (an
+ * oversampling mechanism) to future work (gist.science/de/paper/2602.10056, "Bedeutung und
+ * Ansprueche"); this is the block variant of randomly pivoted Cholesky.  Round k draws its b
+ * candidates from the residual at the start of the round (u_forced[h][k b + j], or Philox with
+ * counter (k b + j, head)), forms their columns together, G = H[:, S] - F F[S, :]^T (F read
+ * once per round), then takes them in order: candidate j enters slot k b + j when its residual
+ * after the round's earlier accepted candidates exceeds 2^-12 H_ss; otherwise the slot is
+ * empty (pivot -1, zero column of F).  rank counts the accepted pivots, so slots past rank are
+ * not the empty ones; trace[k b] is the total mass before round k (other entries 0).  Weights
+ * over such pivots are the union weights (see wc_forward); wc_weights and wc_attend refuse
+ * pivot_block > 1.  With bins, each bin does this on its own keys.                          */
 wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_forced,
                         uint64_t seed, int32_t* pivots, float* F, float* diag, double* trace,
                         int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes,

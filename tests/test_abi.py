@@ -26,7 +26,8 @@ def lib():
 
 
 class Problem(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype", "bins", "options")]
+    _fields_ = [(f, ctypes.c_int32) for f in ("heads", "n", "m", "d", "dv", "r", "dtype", "bins", "options",
+                                              "pivot_block")]
 
 
 def test_exports_every_declared_symbol(lib):
@@ -41,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 5
+    assert lib.wc_abi_version() == 6
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -238,3 +239,24 @@ def test_key_centring_only_in_the_forward(lib):
     assert lib.wc_forward(ctypes.byref(cent), A, None, A, None, u64, A, None, A, A, A, big, None) == 1
     assert lib.wc_forward(ctypes.byref(cent), A, A, A, None, u64, A, None, A, A, A,
                           ctypes.c_size_t(b1), None) == 3
+
+
+def test_pivot_block_validation(lib):
+    """pivot_block: 0/1 (one pivot per step) or 16, 32, 64 dividing r (r / bins with bins);
+    not with per-bin weights; refused by wc_weights and wc_attend."""
+    ok = [Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 32), Problem(2, 4096, 64, 64, 64, 256, 1, 4, 0, 64),
+          Problem(2, 4096, 64, 64, 64, 256, 1, 16, 0, 16), Problem(2, 4096, 64, 64, 64, 256, 1, 1, 2, 16)]
+    for p in ok:
+        assert ws_bytes(lib, p)[0] == 0
+    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, -1))[0] == 1
+    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 24))[0] == 2    # not 16/32/64
+    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 240, 1, 1, 0, 32))[0] == 2    # 32 does not divide r
+    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 16, 0, 32))[0] == 2   # r / bins = 16
+    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 4, 1, 32))[0] == 2    # per-bin weights
+    A = ctypes.c_void_p(256)
+    big = ctypes.c_size_t(1 << 40)
+    blk = Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 32)
+    assert lib.wc_weights(ctypes.byref(blk), A, A, A, A, A, A, big, None) == 2
+    assert lib.wc_attend(ctypes.byref(blk), A, A, A, A, A, A, A, A, big, None) == 2
+    # the selection holds the candidate columns G [b][n]: more workspace than one pivot a step
+    assert ws_bytes(lib, blk)[1] > ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 0))[1]

@@ -1,0 +1,83 @@
+"""Parity of block pivot selection (pivot_block = b candidates per round) with the oracle's
+rpcholesky_block and the block-pivoted forward: pivots (with empty slots), rank and flags
+bit-exact under uniforms snapped on each round's start residual; F, the residual and the
+round-start traces within fp32 rounding; outputs within the tolerances.  Block sizes 16, 32
+and 64, fp32 and bf16, d of 64 and 128, ragged n, with and without bins; plus the seeded mode."""
+import numpy as np
+import pytest
+
+from coreset_head_rpcholesky_amd import synth
+from oracle import philox
+from oracle import wildcat as ow
+from tests.gpu_util import TOL, dev, host, rel, snapped_block
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wc():
+    import torch  # noqa: F401
+
+    from coreset_head_rpcholesky_amd import binding
+    return binding
+
+
+# (name, dtype, kind, H, n, m, d, dv, r, b, B)
+CASES = [
+    ("b16_bf16", "bf16", "mixture", 2, 2000, 90, 64, 64, 64, 16, 1),
+    ("b32_f32", "f32", "iid_clip", 2, 1500, 60, 128, 64, 64, 32, 1),
+    ("b64_bf16_d128", "bf16", "kv_outlier", 2, 5000, 64, 128, 128, 128, 64, 1),
+    ("b16_bins", "bf16", "mixture", 2, 4096, 100, 64, 128, 128, 16, 4),
+]
+
+
+def case_inputs(case):
+    name, dtype, kind, H, n, m, d, dv, r, b, B = case
+    return synth.random_inputs(H, n, m, d, dv, seed=950 + CASES.index(case), dtype=dtype, kind=kind,
+                               clip=2.5, clusters=8)
+
+
+@pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_block_selection_parity(wc, case):
+    name, dtype, kind, H, n, m, d, dv, r, b, B = case
+    Q, K, V = case_inputs(case)
+    U = snapped_block(K, r, b)
+    out = wc.wc_rpcholesky(dev(K, dtype), r, u_forced=dev(U), pivot_block=b)
+    piv, F, diag = host(out["pivots"]), host(out["F"]), host(out["diag"])
+    trace, rank, flags = host(out["trace"]), host(out["rank"]), host(out["flags"])
+    for h in range(H):
+        ref = ow.rpcholesky_block(K[h], r, U[h], b)
+        assert np.array_equal(piv[h], ref["pivots"]), (h, piv[h], ref["pivots"])
+        assert rank[h] == ref["rank"] and flags[h] == ref["flags"]
+        assert rel(F[h].T, ref["F"]) < 1e-4, rel(F[h].T, ref["F"])
+        assert np.all(F[h][ref["pivots"] < 0] == 0.0)
+        assert np.allclose(diag[h], ref["diag"], rtol=1e-4, atol=1e-4 * ref["diag"].max())
+        starts = np.arange(0, r + 1, b)
+        assert np.allclose(trace[h][starts], ref["trace"][starts], rtol=1e-5)
+        assert np.all(trace[h][np.setdiff1d(np.arange(r + 1), starts)] == 0.0)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_block_forward_parity(wc, case):
+    name, dtype, kind, H, n, m, d, dv, r, b, B = case
+    Q, K, V = case_inputs(case)
+    U = snapped_block(K, r, b, B)
+    out = wc.wc_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), r, u_forced=dev(U), bins=B, pivot_block=b)
+    O, piv, rank, flags = host(out["O"]), host(out["pivots"]), host(out["rank"]), host(out["flags"])
+    for h in range(H):
+        ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h], pivot_block=b)
+        assert np.array_equal(piv[h], ref["pivots"]), h
+        assert rank[h] == ref["rank"] and flags[h] == ref["flags"], (rank[h], flags[h], ref["rank"], ref["flags"])
+        ok = ref["kappa"] < 1e6
+        assert rel(O[h][ok], ref["O"][ok]) < TOL[dtype], (h, rel(O[h][ok], ref["O"][ok]))
+
+
+def test_block_seeded_mode(wc):
+    """Seeded mode: candidate j of round k of head h draws Philox with counter (k b + j, h)."""
+    H, n, r, b = 3, 3000, 64, 32
+    _, K, _ = synth.random_inputs(H, n, 1, 64, 64, seed=960, dtype="bf16", kind="mixture")
+    out = wc.wc_rpcholesky(dev(K, "bf16"), r, seed=77, pivot_block=b)
+    piv = host(out["pivots"])
+    agree = sum(np.array_equal(piv[h], ow.rpcholesky_block(K[h], r, np.array(philox.pivot_uniforms(77, h, r)), b)["pivots"])
+                for h in range(H))
+    assert agree >= H - 1, agree
