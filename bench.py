@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "WildCat forward tokens/sec (coreset+weights+attend); % HBM/MFMA roofline"
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -133,7 +134,7 @@ def error_vs_exact(w, Q, K, V, O, rows: int = 256):
     return round(float(err.mean()), 6)
 
 
-def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1):
+def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1, pivot_block: int = 1):
     """The fp64 oracle on as many heads as fit in the time budget; tokens/s scaled to the
     whole workload (tokens per head = tokens / heads)."""
     import numpy as np
@@ -152,9 +153,9 @@ def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1):
     t0 = time.perf_counter()
     done = 0
     for h in range(w.heads):
-        if bins > 1:
+        if bins > 1 or pivot_block > 1:
             u = np.concatenate([philox.pivot_uniforms(42, h * bins + b, w.r // bins) for b in range(bins)])
-            ow.forward_binned(Q[h], K[h], V[h], w.r, bins, u)
+            ow.forward_binned(Q[h], K[h], V[h], w.r, bins, u, pivot_block=pivot_block)
         else:
             u = np.array(philox.pivot_uniforms(42, h, w.r))
             ow.forward(Q[h], K[h], V[h], w.r, u)
@@ -183,7 +184,8 @@ def run_decode(args, w, Q, K, V, dt_t, dev):
     rows = w.r
     Qd = Q[:, :m].contiguous()
     stream = torch.cuda.current_stream()
-    p = binding.problem(w.heads, w.n, m, w.d, w.dv, w.r, dt_t, bins)
+    pb = max(1, args.pivot_block)
+    p = binding.problem(w.heads, w.n, m, w.d, w.dv, w.r, dt_t, bins, 0, pb)
     ws = binding.workspace(p, dev)
     cache = torch.empty(binding.wc_cache_bytes(p, rows), dtype=torch.uint8, device=dev)
     dws = torch.empty(max(binding.wc_decode_workspace_bytes(p, rows), 256), dtype=torch.uint8, device=dev)
@@ -191,7 +193,7 @@ def run_decode(args, w, Q, K, V, dt_t, dev):
     flags = torch.zeros((w.heads,), dtype=torch.int32, device=dev)
 
     def compress():
-        return binding.wc_compress(K, V, w.r, rows, seed=args.seed, bins=bins, cache=cache, ws=ws)
+        return binding.wc_compress(K, V, w.r, rows, seed=args.seed, bins=bins, pivot_block=pb, cache=cache, ws=ws)
 
     def decode():
         binding.wc_decode(Qd, cache, rows, rows, w.dv, flags=flags, ws=dws, out=O)
@@ -246,7 +248,7 @@ def run_decode(args, w, Q, K, V, dt_t, dev):
         "steps": args.steps, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "heads": w.heads, "prefix_keys": w.n, "cache_rows": rows,
-                   "d": w.d, "dv": w.dv, "bins": bins, "queries_per_head": m,
+                   "d": w.d, "dv": w.dv, "bins": bins, "pivot_block": pb, "queries_per_head": m,
                    "pivot_uniforms": f"Philox4x64-10 seed {args.seed}"},
         "roofline": {"kernel": "attend kernels over the cache (decode step)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -272,6 +274,8 @@ def main():
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--bins", type=int, default=1,
                     help="divide-and-conquer selection with this many bins (must divide n and r)")
+    ap.add_argument("--pivot-block", type=int, default=1,
+                    help="block pivot selection: 16, 32 or 64 candidates per round (1: one pivot per step)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
@@ -309,7 +313,8 @@ def main():
         run_decode(args, w, Q, K, V, dt_t, dev)
         return
     bins = max(1, args.bins)
-    p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t, bins)
+    pb = max(1, args.pivot_block)
+    p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t, bins, 0, pb)
     ws = binding.workspace(p, dev)
     out = dict(O=torch.empty((w.heads, w.m, w.dv), dtype=dt_t, device=dev),
                pivots=torch.empty((w.heads, w.r), dtype=torch.int32, device=dev),
@@ -325,7 +330,7 @@ def main():
         del src, dst
 
     def fwd():
-        binding.wc_forward(Q, K, V, w.r, seed=args.seed, bins=bins, ws=ws, out=out)
+        binding.wc_forward(Q, K, V, w.r, seed=args.seed, bins=bins, pivot_block=pb, ws=ws, out=out)
 
     # One forward is captured in a HIP graph and replayed: the host-side launch path (Python,
     # ctypes, one launch per pivot step on the streaming path) would otherwise be what is timed.
@@ -374,7 +379,7 @@ def main():
     flags = out["flags"].cpu().numpy()
 
     acc = workload_accounting(w, bins)
-    resident = w.dtype == "bf16" and w.n <= 256 and w.r <= 32 and bins == 1
+    resident = w.dtype == "bf16" and w.n <= 256 and w.r <= 32 and bins == 1 and pb == 1
     if resident:
         # one launch per step: the resident kernel; only compulsory bytes reach HBM
         kernel_ms = float(np.mean(per))
@@ -389,10 +394,12 @@ def main():
         # the pivot loop dominates: time wc_rpcholesky alone (graph replay) on the same stream;
         # with bins, on the per-bin view (heads x bins sub-heads), which is what the forward runs
         Ksel = K.view(w.heads * bins, w.n // bins, w.d)
-        pws = binding.workspace(binding.problem(w.heads * bins, w.n // bins, 0, w.d, w.dv, w.r // bins, dt_t), dev)
+        pws = binding.workspace(binding.problem(w.heads * bins, w.n // bins, 0, w.d, w.dv, w.r // bins, dt_t,
+                                                1, 0, pb), dev)
 
         def rpc():
-            binding.wc_rpcholesky(Ksel, w.r // bins, seed=args.seed, ws=pws, with_diag=False, with_trace=False)
+            binding.wc_rpcholesky(Ksel, w.r // bins, seed=args.seed, ws=pws, with_diag=False, with_trace=False,
+                                  pivot_block=pb)
 
         rgraph = None
         if not args.no_graph:
@@ -410,19 +417,33 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         loop_ms = e0.elapsed_time(e1)
-        sub_resident = w.dtype == "bf16" and w.n // bins <= 256 and w.r // bins <= 32
-        if sub_resident:
+        sub_resident = w.dtype == "bf16" and w.n // bins <= 256 and w.r // bins <= 32 and pb == 1
+        if pb > 1:
+            name = (f"blk_column_kernel x {w.r // bins // pb} rounds (block pivots, {pb} candidates per round"
+                    f"{f', {w.heads * bins} bins' if bins > 1 else ''}; fp32 vector)")
+            loop_bytes = None
+        elif sub_resident:
             name = f"resident_kernel (pivot loop only, {w.heads * bins} sub-heads, factor on chip)"
             loop_bytes = acc["pivot_resident_bytes"]
         else:
             name = (f"rpc_step_kernel x {w.r // bins} launches (streaming pivot loop"
                     f"{f', {w.heads * bins} bins' if bins > 1 else ''})")
             loop_bytes = acc["pivot_bytes"]
-        achieved = loop_bytes / (loop_ms / 1e3) / 1e9
-        roof = {"kernel": name, "bound": "hbm",
-                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes_per_loop": loop_bytes, "loop_ms": round(loop_ms, 3)}
+        if pb > 1:
+            # candidate columns G = exp(beta K K_S^T) - F F_S^T and F_new = G M^T, per sub-head
+            Hs, ns, rs = w.heads * bins, w.n // bins, w.r // bins
+            rounds = rs // pb
+            flops = Hs * (2 * ns * rs * w.d + ns * rs * (rs - pb) + 2 * ns * pb * rs)
+            achieved = flops / (loop_ms / 1e3) / 1e12
+            roof = {"kernel": name, "bound": "alu", "achieved": round(achieved, 2), "peak": FP32_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4), "traffic": None,
+                    "algorithmic_flops_per_loop": flops, "rounds": rounds, "loop_ms": round(loop_ms, 3)}
+        else:
+            achieved = loop_bytes / (loop_ms / 1e3) / 1e9
+            roof = {"kernel": name, "bound": "hbm",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_loop": loop_bytes, "loop_ms": round(loop_ms, 3)}
 
     exact = None
     if not args.no_exact:
@@ -431,7 +452,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, Qn, Kn, Vn, args.cpu_budget, bins)
+        cpu = cpu_baseline(w, Qn, Kn, Vn, args.cpu_budget, bins, pb)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -439,7 +460,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "heads": w.heads, "n": w.n,
-                   "m": w.m, "d": w.d, "dv": w.dv, "r": w.r, "bins": bins, "tokens_per_step": w.tokens,
+                   "m": w.m, "d": w.d, "dv": w.dv, "r": w.r, "bins": bins, "pivot_block": pb,
+                   "tokens_per_step": w.tokens,
                    "pivot_uniforms": f"Philox4x64-10 seed {args.seed}"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -102,6 +102,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+BLOCK_DRAWS = 4  # forced uniforms per pivot slot with pivot_block > 1
+
+
+def _draws(r, pivot_block):
+    return BLOCK_DRAWS * r if pivot_block > 1 else r
+
+
 def _check_in(name, t, dtype, shape, device):
     if t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
@@ -128,7 +135,7 @@ def wc_rpcholesky(K: torch.Tensor, r: int, *, u_forced=None, seed: int = 0, ws=N
     dev = K.device
     p = problem(H, n, 0, d, 64, r, K.dtype, pivot_block=pivot_block)
     if u_forced is not None:
-        _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
+        _check_in("u_forced", u_forced, torch.float32, (H, _draws(r, pivot_block)), dev)
     pivots = torch.empty((H, r), dtype=torch.int32, device=dev)
     F = torch.empty((H, r, n), dtype=torch.float32, device=dev)
     diag = torch.empty((H, n), dtype=torch.float32, device=dev) if with_diag else None
@@ -199,7 +206,7 @@ def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_f
     _check_in("K", K, Q.dtype, (H, n, d), dev)
     _check_in("V", V, Q.dtype, (H, n, dv), dev)
     if u_forced is not None:
-        _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
+        _check_in("u_forced", u_forced, torch.float32, (H, _draws(r, pivot_block)), dev)
     if out is None:
         out = dict(O=torch.empty((H, m, dv), dtype=Q.dtype, device=dev),
                    pivots=torch.empty((H, r), dtype=torch.int32, device=dev),
@@ -234,7 +241,7 @@ def wc_compress(K: torch.Tensor, V: torch.Tensor, r: int, capacity: int, *, u_fo
                 pivot_block)
     _check_in("V", V, K.dtype, (H, n, dv), dev)
     if u_forced is not None:
-        _check_in("u_forced", u_forced, torch.float32, (H, r), dev)
+        _check_in("u_forced", u_forced, torch.float32, (H, _draws(r, pivot_block)), dev)
     if cache is None:
         cache = torch.empty(max(wc_cache_bytes(p, capacity), 256), dtype=torch.uint8, device=dev)
     out = dict(cache=cache, pivots=torch.empty((H, r), dtype=torch.int32, device=dev),

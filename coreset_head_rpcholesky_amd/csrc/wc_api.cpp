@@ -34,7 +34,6 @@ wc_status check_problem(const wc_problem* p) {
     const int B = p->bins > 1 ? p->bins : 1;
     if (p->pivot_block != 16 && p->pivot_block != 32 && p->pivot_block != 64) return WC_ERR_UNSUPPORTED;
     if ((p->r / B) % p->pivot_block != 0) return WC_ERR_UNSUPPORTED;
-    if (p->options & WC_OPT_BIN_WEIGHTS) return WC_ERR_UNSUPPORTED;  // empty slots inside a bin
   }
   if (p->bins > 1 && (p->n % p->bins != 0 || p->r % p->bins != 0)) return WC_ERR_UNSUPPORTED;
   if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
@@ -47,14 +46,13 @@ bool req(const void* ptr) { return ptr != nullptr && aligned16(ptr); }
 bool opt(const void* ptr) { return ptr == nullptr || aligned16(ptr); }
 
 bool resident_ok(const wc_problem& p) {
-  return p.dtype == WC_BF16 && p.n <= wc::kResidentRows && p.r <= wc::kResidentR;
+  return p.dtype == WC_BF16 && p.n <= wc::kResidentRows && p.r <= wc::kResidentR && p.pivot_block <= 1;
 }
 
 bool binned(const wc_problem& p) { return p.bins > 1; }
 bool blocked(const wc_problem& p) { return p.pivot_block > 1; }
-// Bins, or block pivots (whose empty slots the factor-based weights cannot take), go through
-// the per-bin selection, the fold of the pivots and weights over the union.
-bool union_path(const wc_problem& p) { return binned(p) || blocked(p); }
+// Bins go through the per-bin selection, the fold of the pivots and weights over the union.
+bool union_path(const wc_problem& p) { return binned(p); }
 bool union_weights(const wc_problem& p) { return union_path(p) && !(p.options & WC_OPT_BIN_WEIGHTS); }
 bool centred(const wc_problem& p) { return (p.options & WC_OPT_CENTER_KEYS) != 0; }
 
@@ -96,7 +94,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   int rows, nblk, nchunk, chunk_rows, nsplit, rp;
   size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Wdh, Ypart;
-  size_t bcand, bG, bM, bstop;  // block pivot selection
+  size_t bcand, bslot, bG, bM, brounds;  // block pivot selection
   size_t total;
 };
 
@@ -131,7 +129,7 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
     L.diag1 = take(H * n * 4);
     L.part0 = take(H * L.nblk * 8);
     L.part1 = take(H * L.nblk * 8);
-    L.unif = take(H * r * 4);
+    L.unif = take(H * r * 4 * (blocked(p) ? wc::kBlockDraws : 1));
     L.F = take(H * r * n * 4);
     L.piv = take(H * r * 4);
     L.L = take(H * r * r * 4);
@@ -141,9 +139,10 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
     if (blocked(p)) {
       const size_t b = (size_t)p.pivot_block;
       L.bcand = take(H * b * 4);
+      L.bslot = take(H * b * 4);
       L.bG = take(H * b * n * 4);
       L.bM = take(H * b * b * 4);
-      L.bstop = take(H * 4);
+      L.brounds = take(H * 4);
     }
   }
   if (parts & kAttend) {
@@ -327,9 +326,10 @@ hipError_t run_rpc_block(const wc_problem& p, const Layout& L, void* ws, const v
   a.b = p.pivot_block;
   a.tol = 0x1p-12f;
   a.cand = at<int32_t>(ws, L.bcand);
+  a.slot = at<int32_t>(ws, L.bslot);
   a.G = at<float>(ws, L.bG);
   a.M = at<float>(ws, L.bM);
-  a.stop = at<int32_t>(ws, L.bstop);
+  a.rounds = at<int32_t>(ws, L.brounds);
   return wc::launch_rpc_block(a, st);
 }
 
@@ -520,7 +520,7 @@ wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
   if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
-  if (binned(*p) || blocked(*p)) return WC_ERR_UNSUPPORTED;
+  if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(V) || !req(pivots) || !req(rank) || !req(F) || !req(W)) return WC_ERR_INVALID_ARG;
   Layout L;
@@ -534,7 +534,7 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
   wc_status st = check_problem(p);
   if (st != WC_OK) return st;
   if (centred(*p)) return WC_ERR_UNSUPPORTED;  // wc_forward only
-  if (binned(*p) || blocked(*p)) return WC_ERR_UNSUPPORTED;
+  if (binned(*p)) return WC_ERR_UNSUPPORTED;
   if (p->heads == 0) return WC_OK;
   if (!req(K) || !req(pivots) || !req(rank) || !req(W) || !req(flags)) return WC_ERR_INVALID_ARG;
   if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
@@ -584,7 +584,7 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
   int32_t* piv = pivots ? pivots : at<int32_t>(ws, L.piv);
   float* F = at<float>(ws, L.F);
   float* W = at<float>(ws, L.W);
-  hipError_t e = run_rpc_stream(*p, L, ws, K, u_forced, seed, piv, F, nullptr, nullptr, rank, flags, s);
+  hipError_t e = run_select(*p, L, ws, K, u_forced, seed, piv, F, rank, flags, s);
   if (e == hipSuccess) e = run_weights(*p, L, ws, V, piv, rank, F, W, s);
   if (e == hipSuccess) e = run_attend(*p, L, ws, Q, K, piv, rank, W, O, flags, s);
   return dev(e);

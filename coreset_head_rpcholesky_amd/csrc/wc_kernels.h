@@ -68,14 +68,17 @@ constexpr int kStreamThreads = 256;
 hipError_t launch_rpc_stream(const StreamRpcArgs& a, hipStream_t st);
 
 // ---- block pivot selection: b candidates per round (the fields of the streaming loop plus) ----
+constexpr int kBlockDraws = 4;  // candidates drawn per pivot slot at most
 struct BlockRpcArgs {
-  StreamRpcArgs s;      // K, uniforms, residual and block masses (rows, nblk), F, pivots, ...
+  StreamRpcArgs s;      // K, residual and block masses (rows, nblk), F, pivots, rank (slots
+                        // filled so far), ...; s.uniforms holds kBlockDraws r per head
   int b;                // candidates per round: 16, 32 or 64, dividing r
-  float tol;            // relative residual at or below which a candidate is left out
+  float tol;            // relative residual at or below which a candidate is passed over
   int32_t* cand;        // ws [H][b]
+  int32_t* slot;        // ws [H][b]     slot a candidate fills, or -1
   float* G;             // ws [H][b][n]  candidate columns minus what F explains
   float* M;             // ws [H][b][b]  inverse factor of the kept part of the candidate block
-  int32_t* stop;        // ws [H]        round at which the loop stopped (r / b: it did not)
+  int32_t* rounds;      // ws [H]        rounds applied so far (the residual's buffer parity)
 };
 hipError_t launch_rpc_block(const BlockRpcArgs& a, hipStream_t st);
 

@@ -423,36 +423,53 @@ static hipError_t run_rpc(StreamRpcArgs a, int rows, hipStream_t st) {
 // ---------------------------------------------------------------------------------------------
 // Block pivot selection (b candidates per round; the pages leave the mechanism that would lift
 // the sequential pivot selection to future work, gist.science/de/paper/2602.10056, "Bedeutung
-// und Ansprueche"; read here as the block variant of randomly pivoted Cholesky).  Round k,
-// slots t0 = k b .. t0 + b - 1, reads the residual and block masses written by round k - 1:
-//   sample  one workgroup per candidate resolves s_j = min{i : C_i > u T} on that residual;
-//   column  G[:, j] = exp(beta K k_{s_j}) - F[:, :t0] F[s_j, :t0]^T for all rows (F is read
+// und Ansprueche"; read here as the block variant of randomly pivoted Cholesky, oversampled
+// until the r slots are full).  Round k reads the residual and block masses its predecessor
+// wrote; f0 slots are full when it starts:
+//   sample  one workgroup per candidate resolves s_j = min{i : C_i > u T} on that residual,
+//           u = uniforms[k b + j];
+//   column  G[:, j] = exp(beta K k_{s_j}) - F[:, :f0] F[s_j, :f0]^T for all rows (F is read
 //           once per round instead of once per pivot);
 //   factor  the b x b block G[S, :] is eliminated in candidate order with the leave-out rule
-//           (elim_block, relative to H_ss); kept candidates fill their slots, the others -1;
-//   apply   F[:, t0 + j] = G M^T (zero columns for the left-out ones), residual update, masses.
+//           (elim_block, relative to H_ss); the kept candidates take slots f0, f0 + 1, ...
+//           while slots remain;
+//   apply   F[:, slot_j] = (G M^T)[:, j] for the candidates with a slot, residual, masses.
+// Rounds run until the slots are full or kBlockDraws r candidates are drawn; every kernel of
+// a head that is full, or has stopped, returns at once.
 // ---------------------------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(64) blk_init_kernel(BlockRpcArgs A) {
-  const int h = blockIdx.x;
-  if (threadIdx.x == 0) {
-    A.s.rank[h] = 0;
-    A.stop[h] = A.s.r / A.b;
-  }
+__global__ void __launch_bounds__(256) blk_uniforms_kernel(BlockRpcArgs A) {
+  const StreamRpcArgs& a = A.s;
+  const size_t per = (size_t)kBlockDraws * a.r;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (size_t)a.H * per) return;
+  a.uniforms[e] = philox_uniform(a.seed, (uint32_t)(e / per), (uint32_t)(e % per));
 }
 
-__global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int t0) {
+__global__ void __launch_bounds__(NT) blk_init_kernel(BlockRpcArgs A) {
+  const StreamRpcArgs& a = A.s;
+  const int h = blockIdx.x;
+  if (threadIdx.x == 0) {
+    a.rank[h] = 0;
+    A.rounds[h] = 0;
+  }
+  if (a.trace)
+    for (int t = threadIdx.x; t <= a.r; t += NT) a.trace[(size_t)h * (a.r + 1) + t] = 0.0;
+}
+
+__device__ __forceinline__ bool blk_done(const BlockRpcArgs& A, int h) {
+  return A.s.rank[h] >= A.s.r || (A.s.flags[h] & WC_DFLAG_BREAKDOWN);
+}
+
+__global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int k) {
   __shared__ double red[NW];
   __shared__ int ired[NW];
   extern __shared__ __attribute__((aligned(16))) double s_part[];  // [nblk]
   const StreamRpcArgs& a = A.s;
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int n = a.n, nblk = a.nblk, rows = a.rows, k = t0 / A.b;
+  const int n = a.n, nblk = a.nblk, rows = a.rows;
   int32_t* cand = A.cand + (size_t)h * A.b + j;
-  if (a.flags[h] & WC_DFLAG_BREAKDOWN) {
-    if (tid == 0) *cand = -1;
-    return;
-  }
+  if (blk_done(A, h)) return;
   const double* part = (k & 1) ? a.part1 : a.part0;
   const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
   const int per = (nblk + NT - 1) / NT;
@@ -467,20 +484,20 @@ __global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int t0) 
   }
   double Ttot;
   const double excl = block_excl_scan(mine, red, &Ttot);
+  const int f0 = a.rank[h];
   if (!(Ttot > 0.0) || !__builtin_isfinite(Ttot)) {
+    // no mass left: the loop stops (every later kernel of the head sees the flag or cand -1)
     if (tid == 0) {
       *cand = -1;
       if (j == 0) {
         a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(Ttot) ? 0u : WC_DFLAG_NONFINITE);
-        A.stop[h] = k;
-        if (a.trace) a.trace[(size_t)h * (a.r + 1) + t0] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
+        if (a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
       }
     }
     return;
   }
-  if (j == 0 && a.trace)
-    for (int t = tid; t < A.b; t += NT) a.trace[(size_t)h * (a.r + 1) + t0 + t] = t == 0 ? Ttot : 0.0;
-  const double uT = (double)a.uniforms[(size_t)h * a.r + t0 + j] * Ttot;
+  if (j == 0 && tid == 0 && a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = Ttot;
+  const double uT = (double)a.uniforms[(size_t)h * kBlockDraws * a.r + (size_t)k * A.b + j] * Ttot;
   int bc = 0x7fffffff, lastpos = -1;
   double run = excl;
   for (int e = 0; e < per; ++e) {
@@ -529,13 +546,14 @@ __global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int t0) 
 // One thread per row (256 rows per workgroup): the candidate keys and, chunk by chunk, the
 // candidate rows of F sit in LDS; F is read once, column by column (coalesced).
 template <typename T, int D, int B>
-__global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A, int t0) {
+__global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A) {
   __shared__ __attribute__((aligned(16))) float sKS[D][B];
   __shared__ __attribute__((aligned(16))) float sFS[64][B];
   __shared__ int sC[B];
   const StreamRpcArgs& a = A.s;
   const int h = blockIdx.y, tid = threadIdx.x, n = a.n;
-  if (a.flags[h] & WC_DFLAG_BREAKDOWN) return;
+  if (blk_done(A, h) || A.cand[(size_t)h * B] < 0) return;
+  const int f0 = a.rank[h];
   const int i = blockIdx.x * NT + tid;
   const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * n * D;
   const float* F = a.F + (size_t)h * a.r * n;
@@ -548,8 +566,8 @@ __global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A, int t0) 
   float acc[B];
 #pragma unroll
   for (int jj = 0; jj < B; ++jj) acc[jj] = 0.f;
-  for (int c0 = 0; c0 < t0; c0 += 64) {
-    const int cc = min(64, t0 - c0);
+  for (int c0 = 0; c0 < f0; c0 += 64) {
+    const int cc = min(64, f0 - c0);
     __syncthreads();
     for (int e = tid; e < cc * B; e += NT) {
       const int c = e / B, jj = e % B, sj = sC[jj];
@@ -589,7 +607,7 @@ __global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A, int t0) 
 }
 
 template <typename T, int D, int B>
-__global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int t0) {
+__global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int k) {
   constexpr int P = B + 4;
   __shared__ __attribute__((aligned(16))) float sA[B * P];
   __shared__ __attribute__((aligned(16))) float sCol[2][B];
@@ -598,7 +616,11 @@ __global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int t
   __shared__ int sC[B];
   const StreamRpcArgs& a = A.s;
   const int h = blockIdx.x, tid = threadIdx.x, n = a.n;
-  if (a.flags[h] & WC_DFLAG_BREAKDOWN) return;
+  if (blk_done(A, h)) return;
+  if (A.cand[(size_t)h * B] < 0) {  // no mass left: the loop stops
+    if (tid == 0) a.flags[h] |= WC_DFLAG_BREAKDOWN;
+    return;
+  }
   const T* K = reinterpret_cast<const T*>(a.K) + (size_t)h * n * D;
   if (tid < B) {
     const int sj = A.cand[(size_t)h * B + tid];
@@ -622,29 +644,44 @@ __global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int t
   float* M = A.M + (size_t)h * B * B;
   elim_block<B, P>(sA, sHd, A.tol, M, sCol, sRow);
   __syncthreads();
-  if (tid < B) {
-    const bool keep = M[(size_t)tid * B + tid] > 0.f;
-    a.pivots[(size_t)h * a.r + t0 + tid] = keep ? sC[tid] : -1;
-    if (keep) atomicAdd(&a.rank[h], 1);
+  if (tid == 0) {
+    // kept candidates take the next free slots in order; once the slots are full the rest of
+    // the round is dropped (later candidates were eliminated only against earlier ones)
+    const int f0 = a.rank[h];
+    int f = f0;
+    for (int jj = 0; jj < B; ++jj) {
+      int sl = -1;
+      if (f < a.r && M[(size_t)jj * B + jj] > 0.f) {
+        sl = f++;
+        a.pivots[(size_t)h * a.r + sl] = sC[jj];
+      }
+      A.slot[(size_t)h * B + jj] = sl;
+    }
+    a.rank[h] = f;
+    A.rounds[h] = k + 1;
   }
 }
 
 // New columns of F, residual update and block masses; `rows` rows per workgroup as the
 // streaming loop, so that the masses line up with the blocks the sampler reads.
 template <int B>
-__global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int t0) {
+__global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int k) {
   __shared__ __attribute__((aligned(16))) float sMt[B][B];
-  __shared__ int sP[B];
+  __shared__ int sSl[B], sP[B];
   __shared__ double red[NW];
   const StreamRpcArgs& a = A.s;
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, n = a.n, k = t0 / B;
-  if (a.flags[h] & WC_DFLAG_BREAKDOWN) return;
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, n = a.n;
+  if ((a.flags[h] & WC_DFLAG_BREAKDOWN) || A.rounds[h] != k + 1) return;  // this round did not run
   const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
   float* dg_out = ((k & 1) ? a.diag0 : a.diag1) + (size_t)h * n;
   double* part_out = (k & 1) ? a.part0 : a.part1;
   const float* M = A.M + (size_t)h * B * B;
   for (int e = tid; e < B * B; e += NT) sMt[e % B][e / B] = M[e];
-  if (tid < B) sP[tid] = a.pivots[(size_t)h * a.r + t0 + tid];
+  if (tid < B) {
+    const int sl = A.slot[(size_t)h * B + tid];
+    sSl[tid] = sl;
+    sP[tid] = sl >= 0 ? A.cand[(size_t)h * B + tid] : -1;
+  }
   __syncthreads();
   const float* G = A.G + (size_t)h * B * n;
   float* F = a.F + (size_t)h * a.r * n;
@@ -657,10 +694,12 @@ __global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int t0) {
     bool piv = false;
 #pragma unroll 4
     for (int jj = 0; jj < B; ++jj) {
+      const int sl = sSl[jj];
+      if (sl < 0) continue;
       float f = 0.f;
 #pragma unroll
       for (int c = 0; c < B; ++c) f = fmaf(g[c], sMt[c][jj], f);
-      F[(size_t)(t0 + jj) * n + i] = f;
+      F[(size_t)sl * n + i] = f;
       dsum = fmaf(f, f, dsum);
       piv |= sP[jj] == i;
     }
@@ -672,31 +711,31 @@ __global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int t0) {
   if (tid == 0) part_out[(size_t)h * a.nblk + b] = tot;
 }
 
-// After the last round: the trace after it, and for a head that stopped early the empty slots,
-// zero columns of F and zero trace entries past the stop; the final residual if asked for.
+// After the last round: a head with slots left over breaks down (empty slots, zero columns of
+// F); a full one gets the trace after its last round; the final residual if asked for.
 __global__ void __launch_bounds__(NT) blk_final_kernel(BlockRpcArgs A) {
   __shared__ double red[NW];
   const StreamRpcArgs& a = A.s;
   const int h = blockIdx.x, tid = threadIdx.x, n = a.n, nblk = a.nblk;
-  const int ks = A.stop[h], rounds = a.r / A.b, t1 = ks * A.b;
-  const double* part = (ks & 1) ? a.part1 : a.part0;
-  const float* dg = ((ks & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
-  if (ks == rounds && a.trace) {
-    const int per = (nblk + NT - 1) / NT;
-    double mine = 0.0;
-    for (int e = 0; e < per; ++e) {
-      const int bb = tid * per + e;
-      if (bb < nblk) mine += part[(size_t)h * nblk + bb];
+  const int rk = a.rank[h], kr = A.rounds[h];
+  const double* part = (kr & 1) ? a.part1 : a.part0;
+  const float* dg = ((kr & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
+  if (rk == a.r) {
+    if (a.trace) {
+      const int per = (nblk + NT - 1) / NT;
+      double mine = 0.0;
+      for (int e = 0; e < per; ++e) {
+        const int bb = tid * per + e;
+        if (bb < nblk) mine += part[(size_t)h * nblk + bb];
+      }
+      double T;
+      block_excl_scan(mine, red, &T);
+      if (tid == 0) a.trace[(size_t)h * (a.r + 1) + a.r] = T;
     }
-    double T;
-    block_excl_scan(mine, red, &T);
-    if (tid == 0) a.trace[(size_t)h * (a.r + 1) + a.r] = T;
-  }
-  if (ks < rounds) {
-    if (a.trace)
-      for (int t = t1 + 1 + tid; t <= a.r; t += NT) a.trace[(size_t)h * (a.r + 1) + t] = 0.0;
-    for (int t = t1 + tid; t < a.r; t += NT) a.pivots[(size_t)h * a.r + t] = -1;
-    for (size_t e = (size_t)t1 * n + tid; e < (size_t)a.r * n; e += NT) a.F[(size_t)h * a.r * n + e] = 0.f;
+  } else {
+    if (tid == 0) a.flags[h] |= WC_DFLAG_BREAKDOWN;
+    for (int t = rk + tid; t < a.r; t += NT) a.pivots[(size_t)h * a.r + t] = -1;
+    for (size_t e = (size_t)rk * n + tid; e < (size_t)a.r * n; e += NT) a.F[(size_t)h * a.r * n + e] = 0.f;
   }
   if (a.diag_out)
     for (int i = tid; i < n; i += NT) a.diag_out[(size_t)h * n + i] = dg[i];
@@ -708,20 +747,21 @@ static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
   const dim3 grid(a.nblk, a.H);
   hipError_t e;
   if (!a.u_forced) {
-    const size_t nu = (size_t)a.H * a.r;
-    hipLaunchKernelGGL(uniforms_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, a);
+    const size_t nu = (size_t)a.H * kBlockDraws * a.r;
+    hipLaunchKernelGGL(blk_uniforms_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((rpc_init_kernel<T, D>), grid, dim3(NT), 0, st, a, a.rows);
-  hipLaunchKernelGGL(blk_init_kernel, dim3(a.H), dim3(64), 0, st, A);
+  hipLaunchKernelGGL(blk_init_kernel, dim3(a.H), dim3(NT), 0, st, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t lds = (size_t)a.nblk * sizeof(double);
   const int colgrid = (a.n + NT - 1) / NT;
-  for (int t0 = 0; t0 < a.r; t0 += B) {
-    hipLaunchKernelGGL(blk_sample_kernel, dim3(B, a.H), dim3(NT), lds, st, A, t0);
-    hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A, t0);
-    hipLaunchKernelGGL((blk_factor_kernel<T, D, B>), dim3(a.H), dim3(4 * B), 0, st, A, t0);
-    hipLaunchKernelGGL((blk_apply_kernel<B>), grid, dim3(NT), 0, st, A, t0);
+  const int rounds = kBlockDraws * a.r / B;
+  for (int k = 0; k < rounds; ++k) {
+    hipLaunchKernelGGL(blk_sample_kernel, dim3(B, a.H), dim3(NT), lds, st, A, k);
+    hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A);
+    hipLaunchKernelGGL((blk_factor_kernel<T, D, B>), dim3(a.H), dim3(4 * B), 0, st, A, k);
+    hipLaunchKernelGGL((blk_apply_kernel<B>), grid, dim3(NT), 0, st, A, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(blk_final_kernel, dim3(a.H), dim3(NT), 0, st, A);

@@ -118,15 +118,19 @@ wc_status wc_workspace_bytes(const wc_problem* p, size_t* bytes);
 /* pivot_block = b > 1 (b in {16, 32, 64} dividing r, or r / bins with bins): b candidate
  * pivots per round.  The pages leave a remedy for the sequential pivot selection (an
  * oversampling mechanism) to future work (gist.science/de/paper/2602.10056, "Bedeutung und
- * Ansprueche"); this is the block variant of randomly pivoted Cholesky.  Round k draws its b
- * candidates from the residual at the start of the round (u_forced[h][k b + j], or Philox with
- * counter (k b + j, head)), forms their columns together, G = H[:, S] - F F[S, :]^T (F read
- * once per round), then takes them in order: candidate j enters slot k b + j when its residual
- * after the round's earlier accepted candidates exceeds 2^-12 H_ss; otherwise the slot is
- * empty (pivot -1, zero column of F).  rank counts the accepted pivots, so slots past rank are
- * not the empty ones; trace[k b] is the total mass before round k (other entries 0).  Weights
- * over such pivots are the union weights (see wc_forward); wc_weights and wc_attend refuse
- * pivot_block > 1.  With bins, each bin does this on its own keys.                          */
+ * Ansprueche"); this is the block variant of randomly pivoted Cholesky, oversampled until the
+ * slots are full.  Round k draws its b candidates from the residual at the start of the round
+ * (u_forced[h][k b + j], or Philox with counter (k b + j, head)), forms their columns
+ * together, G = H[:, S] - F F[S, :]^T (F read once per round), then takes them in order:
+ * candidate j enters the next free slot when its residual after the round's earlier accepted
+ * candidates exceeds 2^-12 H_ss, and is passed over otherwise (an index drawn again, or one
+ * dependent on them).  Rounds go on until the r slots are full or 4 r candidates are drawn,
+ * so u_forced holds 4 r values per head ([heads][4 r]); running out of draws (or of mass) is a
+ * breakdown with rank < r.  The pivots fill slots 0 .. rank-1 as in the one-pivot loop, and
+ * F[S, :] is lower triangular, so wc_weights and wc_attend take them as they are.  trace[t]
+ * holds the total mass before the round that started with t slots full, trace[r] the total
+ * after the last round, other entries 0.  With bins, each bin does this on its own keys and
+ * draws u_forced[h][4 s0 .. 4 s1) for its slots [s0, s1).                                  */
 wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_forced,
                         uint64_t seed, int32_t* pivots, float* F, float* diag, double* trace,
                         int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes,

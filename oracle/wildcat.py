@@ -122,75 +122,90 @@ def rpcholesky(K, r, uniforms, beta=None):
     return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
 
 
+BLOCK_DRAWS = 4  # candidates drawn per pivot slot at most, in block pivot selection
+
+
 def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
     """Randomly pivoted Cholesky with b candidate pivots per round.
 
     The pages name the sequential pivot selection as a limitation that oversampling could
     lift (future work, gist.science/de/paper/2602.10056, "Bedeutung und Ansprueche").  Reading
-    taken: the block variant of randomly pivoted Cholesky.  Round k draws b candidates, all
-    from the residual diagonal at the start of the round (s_j = min{i : C_i > u T} with
-    u = uniforms[k b + j]); their kernel columns minus what the factor already explains are
-    formed together, G = H[:, S] - F F[S, :]^T; then the candidates are eliminated in order,
-    like single pivots: candidate j's residual column g removes the accepted earlier
-    candidates of the round, and it is accepted into slot k b + j when g[s] > tol H_ss (else
-    the slot stays empty, pivot -1, zero column; an index drawn a second time in a round has
-    residual zero and is left out this way).  After
-    the round diag = diag - sum of the new columns squared, 0 at the accepted indices.  A
-    round that finds no mass stops the loop (breakdown).  b must divide r.  Returns the dict
-    of rpcholesky (rank counts accepted pivots; trace[k b] is the total before round k).
+    taken: the block variant of randomly pivoted Cholesky, oversampled until the slots are
+    full.  Round k draws b candidates, all from the residual diagonal at the start of the
+    round (s_j = min{i : C_i > u T}, u = uniforms[k b + j]); their kernel columns minus what the
+    factor already explains are formed together, G = H[:, S] - F F[S, :]^T; then the
+    candidates are taken in order like single pivots: candidate j's residual column g removes
+    the round's earlier accepted candidates, and it is accepted into the next free slot when
+    g[s] > tol H_ss (an index drawn again, or one dependent on the accepted ones, has a
+    negligible residual and is passed over).  After the round diag = diag - sum of the new
+    columns squared, 0 at the accepted indices.  Rounds go on until the r slots are full or
+    BLOCK_DRAWS r candidates are drawn (``uniforms`` holds that many); a round that finds no
+    mass, or running out of draws, stops the loop with rank < r (breakdown).  Pivots fill
+    slots 0 .. rank-1 in order, so F[S, :] is lower triangular as for single pivots; trace[t]
+    is the total before the round that started with t slots full (other entries zero), and
+    trace[r] the total after the last one.
     """
     K = np.asarray(K, np.float64)
     n, d = K.shape
     beta = beta_of(d) if beta is None else beta
-    if not 1 <= r <= n or r % b:
-        raise ValueError("need 1 <= r <= n and b dividing r")
+    if not 1 <= r <= n:
+        raise ValueError("need 1 <= r <= n")
     Hd = initial_residual(K, beta)
     diag = Hd.copy()
     F = np.zeros((n, r))
     pivots = -np.ones(r, np.int64)
     trace = np.zeros(r + 1)
-    rank, flags = 0, 0
+    filled, flags = 0, 0
     if not np.all(np.isfinite(K)):
         flags |= FLAG_NONFINITE
-    for k in range(r // b):
-        t0 = k * b
+    for k in range(BLOCK_DRAWS * r // b):
+        if filled == r:
+            break
         S = []
         for j in range(b):
-            s, T, _ = sample_pivot(diag, uniforms[t0 + j])
+            s, T, _ = sample_pivot(diag, uniforms[k * b + j])
             S.append(s)
-        trace[t0] = T if np.isfinite(T) else 0.0
+        trace[filled] = T if np.isfinite(T) else 0.0
         if S[0] < 0:
             flags |= FLAG_BREAKDOWN | (0 if np.isfinite(T) else FLAG_NONFINITE)
             break
-        G = kernel(K, K[S], beta) - F[:, :t0] @ F[S, :t0].T
-        taken = []
+        f0 = filled
+        G = kernel(K, K[S], beta) - F[:, :f0] @ F[S, :f0].T
         for j, s in enumerate(S):
-            g = G[:, j] - F[:, t0:t0 + j] @ F[s, t0:t0 + j]
+            if filled == r:
+                break
+            g = G[:, j] - F[:, f0:filled] @ F[s, f0:filled]
             if not (np.isfinite(g[s]) and g[s] > tol * Hd[s]):
                 continue
-            F[:, t0 + j] = g / np.sqrt(g[s])
-            pivots[t0 + j] = s
-            taken.append(s)
-            rank += 1
-        diag = diag - np.sum(F[:, t0:t0 + b] ** 2, axis=1)
-        diag[taken] = 0.0
-    else:
+            F[:, filled] = g / np.sqrt(g[s])
+            pivots[filled] = s
+            filled += 1
+        diag = diag - np.sum(F[:, f0:filled] ** 2, axis=1)
+        diag[pivots[f0:filled]] = 0.0
+    if filled == r:
         trace[r] = np.cumsum(np.maximum(diag, 0.0))[-1]
-    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
+    else:
+        flags |= FLAG_BREAKDOWN
+    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=filled, flags=flags)
 
 
 def snap_uniforms_block(K, r, b, raw_uniforms, beta=None, tol=DEPENDENT_TOL):
     """Forced-uniform mode of rpcholesky_block: each candidate's u moves to the centre of the
-    interval of the round-start running sum it selects (as snap_uniforms does per step)."""
+    interval of the round-start running sum it selects (as snap_uniforms does per step).
+    ``raw_uniforms`` and the result hold BLOCK_DRAWS r values; draws of rounds that never run
+    stay as they are."""
     K = np.asarray(K, np.float64)
-    out = np.zeros(r, np.float32)
+    beta = beta_of(K.shape[1]) if beta is None else beta
     u = np.asarray(raw_uniforms, np.float64).copy()
-    for k in range(r // b):
-        # the round-start diagonal is that of the loop run with the already snapped rounds
-        if k:
-            diag = rpcholesky_block(K, k * b, u[:k * b], b, beta, tol)["diag"]
-        else:
-            diag = initial_residual(K, beta_of(K.shape[1]) if beta is None else beta)
+    out = u.astype(np.float32)
+    Hd = initial_residual(K, beta)
+    diag = Hd.copy()
+    F = np.zeros((K.shape[0], r))
+    filled = 0
+    for k in range(BLOCK_DRAWS * r // b):
+        if filled == r:
+            break
+        S = []
         for j in range(b):
             s, T, C = sample_pivot(diag, u[k * b + j])
             if s < 0:
@@ -200,8 +215,23 @@ def snap_uniforms_block(K, r, b, raw_uniforms, beta=None, tol=DEPENDENT_TOL):
             v = min(max(v, 0.0), 1.0 - 2.0 ** -24)
             if sample_pivot(diag, v)[0] != s:
                 raise RuntimeError("snapping moved a candidate")
-            u[k * b + j] = v
             out[k * b + j] = v
+            S.append(s)
+        # the round itself, as rpcholesky_block runs it
+        f0 = filled
+        G = kernel(K, K[S], beta) - F[:, :f0] @ F[S, :f0].T
+        piv = []
+        for j, s in enumerate(S):
+            if filled == r:
+                break
+            g = G[:, j] - F[:, f0:filled] @ F[s, f0:filled]
+            if not (np.isfinite(g[s]) and g[s] > tol * Hd[s]):
+                continue
+            F[:, filled] = g / np.sqrt(g[s])
+            piv.append(s)
+            filled += 1
+        diag = diag - np.sum(F[:, f0:filled] ** 2, axis=1)
+        diag[piv] = 0.0
     return out
 
 
@@ -366,8 +396,8 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union", piv
     every query attends over the union, Y = exp(beta Q K_S^T) W, O = Y[:, :dv] / Y[:, dv].
     Pivots are returned as key indices of the head, bin by bin; a slot left empty by a
     breakdown in its bin holds -1 and a zero row of W.  pivot_block = b > 1: each bin selects
-    with rpcholesky_block (b candidates per round; union weights only); B = 1 then gives the
-    block-pivoted forward of a whole head.
+    with rpcholesky_block (b candidates per round), bin b drawing from uniforms
+    [BLOCK_DRAWS s0, BLOCK_DRAWS s1) for its slots [s0, s1).
     """
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -376,20 +406,16 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union", piv
     beta = beta_of(d) if beta is None else beta
     if weights_mode not in ("union", "bin"):
         raise ValueError("weights_mode is 'union' or 'bin'")
-    if pivot_block > 1 and weights_mode != "union":
-        raise ValueError("block pivoting leaves slots empty inside a bin: union weights only")
     pivots = -np.ones(r, np.int64)
     W = np.zeros((r, dv + 1))
     rank, flags = 0, 0
     for k0, k1, s0, s1 in bin_bounds(n, r, B):
         if pivot_block > 1:
-            rpc = rpcholesky_block(K[k0:k1], s1 - s0, uniforms[s0:s1], pivot_block, beta)
-            pb = rpc["pivots"]
-            pivots[s0:s1] = np.where(pb >= 0, pb + k0, -1)
-            rank += rpc["rank"]
-            flags |= rpc["flags"]
-            continue
-        rpc = rpcholesky(K[k0:k1], s1 - s0, uniforms[s0:s1], beta)
+            # bin b draws from its own stretch of BLOCK_DRAWS r / B uniforms
+            ub = uniforms[BLOCK_DRAWS * s0:BLOCK_DRAWS * s1]
+            rpc = rpcholesky_block(K[k0:k1], s1 - s0, ub, pivot_block, beta)
+        else:
+            rpc = rpcholesky(K[k0:k1], s1 - s0, uniforms[s0:s1], beta)
         rb = rpc["rank"]
         Sb = rpc["pivots"][:rb]
         if rb and weights_mode == "bin":
@@ -411,14 +437,17 @@ def forward_binned(Q, K, V, r, B, uniforms, beta=None, weights_mode="union", piv
 
 def snap_uniforms_binned(K, r, B, raw_uniforms, beta=None, pivot_block=1):
     """snap_uniforms (or snap_uniforms_block) applied bin by bin (bin b snaps its slots on its
-    own keys)."""
+    own keys).  With pivot_block > 1 the uniforms are BLOCK_DRAWS r long."""
     K = np.asarray(K, np.float64)
+    if pivot_block > 1:
+        out = np.zeros(BLOCK_DRAWS * r, np.float32)
+        for k0, k1, s0, s1 in bin_bounds(K.shape[0], r, B):
+            c0, c1 = BLOCK_DRAWS * s0, BLOCK_DRAWS * s1
+            out[c0:c1] = snap_uniforms_block(K[k0:k1], s1 - s0, pivot_block, raw_uniforms[c0:c1], beta)
+        return out
     out = np.zeros(r, np.float32)
     for k0, k1, s0, s1 in bin_bounds(K.shape[0], r, B):
-        if pivot_block > 1:
-            out[s0:s1] = snap_uniforms_block(K[k0:k1], s1 - s0, pivot_block, raw_uniforms[s0:s1], beta)
-        else:
-            out[s0:s1] = snap_uniforms(K[k0:k1], s1 - s0, raw_uniforms[s0:s1], beta)[0]
+        out[s0:s1] = snap_uniforms(K[k0:k1], s1 - s0, raw_uniforms[s0:s1], beta)[0]
     return out
 
 

@@ -47,8 +47,8 @@ def snapped_binned(K, r, B):
 
 def snapped_block(K, r, b, B=1):
     """Forced uniforms for block pivots (b candidates per round), snapped on each round's
-    start residual by the oracle, bin by bin when B > 1; [H, r] float32."""
-    raw = synth.raw_uniforms(K.shape[0], r)
+    start residual by the oracle, bin by bin when B > 1; [H, BLOCK_DRAWS r] float32."""
+    raw = synth.raw_uniforms(K.shape[0], ow.BLOCK_DRAWS * r)
     if B == 1:
         return np.stack([ow.snap_uniforms_block(K[h], r, b, raw[h]) for h in range(K.shape[0])])
     return np.stack([ow.snap_uniforms_binned(K[h], r, B, raw[h], pivot_block=b) for h in range(K.shape[0])])

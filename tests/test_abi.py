@@ -243,7 +243,7 @@ def test_key_centring_only_in_the_forward(lib):
 
 def test_pivot_block_validation(lib):
     """pivot_block: 0/1 (one pivot per step) or 16, 32, 64 dividing r (r / bins with bins);
-    not with per-bin weights; refused by wc_weights and wc_attend."""
+    accepted with per-bin weights and by wc_weights (the slots fill in order)."""
     ok = [Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 32), Problem(2, 4096, 64, 64, 64, 256, 1, 4, 0, 64),
           Problem(2, 4096, 64, 64, 64, 256, 1, 16, 0, 16), Problem(2, 4096, 64, 64, 64, 256, 1, 1, 2, 16)]
     for p in ok:
@@ -252,11 +252,11 @@ def test_pivot_block_validation(lib):
     assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 24))[0] == 2    # not 16/32/64
     assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 240, 1, 1, 0, 32))[0] == 2    # 32 does not divide r
     assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 16, 0, 32))[0] == 2   # r / bins = 16
-    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 4, 1, 32))[0] == 2    # per-bin weights
+    assert ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 4, 1, 32))[0] == 0    # per-bin weights
     A = ctypes.c_void_p(256)
     big = ctypes.c_size_t(1 << 40)
     blk = Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 32)
-    assert lib.wc_weights(ctypes.byref(blk), A, A, A, A, A, A, big, None) == 2
-    assert lib.wc_attend(ctypes.byref(blk), A, A, A, A, A, A, A, A, big, None) == 2
+    # the component entry points validate block problems like the others (missing pointers)
+    assert lib.wc_weights(ctypes.byref(blk), A, None, A, A, A, big, big, None) == 1
     # the selection holds the candidate columns G [b][n]: more workspace than one pivot a step
     assert ws_bytes(lib, blk)[1] > ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 0))[1]

@@ -1,8 +1,9 @@
-"""Parity of block pivot selection (pivot_block = b candidates per round) with the oracle's
-rpcholesky_block and the block-pivoted forward: pivots (with empty slots), rank and flags
-bit-exact under uniforms snapped on each round's start residual; F, the residual and the
-round-start traces within fp32 rounding; outputs within the tolerances.  Block sizes 16, 32
-and 64, fp32 and bf16, d of 64 and 128, ragged n, with and without bins; plus the seeded mode."""
+"""Parity of block pivot selection (pivot_block = b candidates per round, rounds until the
+slots are full) with the oracle's rpcholesky_block and the block-pivoted forward: pivots, rank
+and flags bit-exact under uniforms snapped on each round's start residual; F, the residual and
+the round-start traces within fp32 rounding; outputs within the tolerances.  Block sizes 16,
+32 and 64, fp32 and bf16, d of 64 and 128, ragged n, keys whose mass sits on a few outliers
+(later rounds fill the slots), with and without bins, both weight modes; the seeded mode."""
 import numpy as np
 import pytest
 
@@ -22,24 +23,26 @@ def wc():
     return binding
 
 
-# (name, dtype, kind, H, n, m, d, dv, r, b, B)
+# (name, dtype, kind, H, n, m, d, dv, r, b, B, mode)
 CASES = [
-    ("b16_bf16", "bf16", "mixture", 2, 2000, 90, 64, 64, 64, 16, 1),
-    ("b32_f32", "f32", "iid_clip", 2, 1500, 60, 128, 64, 64, 32, 1),
-    ("b64_bf16_d128", "bf16", "kv_outlier", 2, 5000, 64, 128, 128, 128, 64, 1),
-    ("b16_bins", "bf16", "mixture", 2, 4096, 100, 64, 128, 128, 16, 4),
+    ("b16_bf16", "bf16", "mixture", 2, 2000, 90, 64, 64, 64, 16, 1, "union"),
+    ("b32_f32", "f32", "iid_clip", 2, 1500, 60, 128, 64, 64, 32, 1, "union"),
+    ("b64_bf16_d128", "bf16", "kv_outlier", 2, 5000, 64, 128, 128, 128, 64, 1, "union"),
+    ("b16_bins", "bf16", "mixture", 2, 4096, 100, 64, 128, 128, 16, 4, "union"),
+    ("b32_bins_outliers", "bf16", "kv_outlier", 2, 8192, 64, 128, 128, 128, 32, 4, "union"),
+    ("b16_bins_perbin", "bf16", "mixture", 2, 2048, 50, 64, 64, 64, 16, 2, "bin"),
 ]
 
 
 def case_inputs(case):
-    name, dtype, kind, H, n, m, d, dv, r, b, B = case
+    name, dtype, kind, H, n, m, d, dv, r, b, B, mode = case
     return synth.random_inputs(H, n, m, d, dv, seed=950 + CASES.index(case), dtype=dtype, kind=kind,
                                clip=2.5, clusters=8)
 
 
 @pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
 def test_block_selection_parity(wc, case):
-    name, dtype, kind, H, n, m, d, dv, r, b, B = case
+    name, dtype, kind, H, n, m, d, dv, r, b, B, mode = case
     Q, K, V = case_inputs(case)
     U = snapped_block(K, r, b)
     out = wc.wc_rpcholesky(dev(K, dtype), r, u_forced=dev(U), pivot_block=b)
@@ -50,22 +53,22 @@ def test_block_selection_parity(wc, case):
         assert np.array_equal(piv[h], ref["pivots"]), (h, piv[h], ref["pivots"])
         assert rank[h] == ref["rank"] and flags[h] == ref["flags"]
         assert rel(F[h].T, ref["F"]) < 1e-4, rel(F[h].T, ref["F"])
-        assert np.all(F[h][ref["pivots"] < 0] == 0.0)
         assert np.allclose(diag[h], ref["diag"], rtol=1e-4, atol=1e-4 * ref["diag"].max())
-        starts = np.arange(0, r + 1, b)
-        assert np.allclose(trace[h][starts], ref["trace"][starts], rtol=1e-5)
-        assert np.all(trace[h][np.setdiff1d(np.arange(r + 1), starts)] == 0.0)
+        nz = ref["trace"] != 0.0
+        assert np.array_equal(trace[h] != 0.0, nz)
+        assert np.allclose(trace[h][nz], ref["trace"][nz], rtol=1e-5)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_block_forward_parity(wc, case):
-    name, dtype, kind, H, n, m, d, dv, r, b, B = case
+    name, dtype, kind, H, n, m, d, dv, r, b, B, mode = case
     Q, K, V = case_inputs(case)
     U = snapped_block(K, r, b, B)
-    out = wc.wc_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), r, u_forced=dev(U), bins=B, pivot_block=b)
+    out = wc.wc_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), r, u_forced=dev(U), bins=B, pivot_block=b,
+                        bin_weights=mode == "bin")
     O, piv, rank, flags = host(out["O"]), host(out["pivots"]), host(out["rank"]), host(out["flags"])
     for h in range(H):
-        ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h], pivot_block=b)
+        ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h], weights_mode=mode, pivot_block=b)
         assert np.array_equal(piv[h], ref["pivots"]), h
         assert rank[h] == ref["rank"] and flags[h] == ref["flags"], (rank[h], flags[h], ref["rank"], ref["flags"])
         ok = ref["kappa"] < 1e6
@@ -78,6 +81,19 @@ def test_block_seeded_mode(wc):
     _, K, _ = synth.random_inputs(H, n, 1, 64, 64, seed=960, dtype="bf16", kind="mixture")
     out = wc.wc_rpcholesky(dev(K, "bf16"), r, seed=77, pivot_block=b)
     piv = host(out["pivots"])
-    agree = sum(np.array_equal(piv[h], ow.rpcholesky_block(K[h], r, np.array(philox.pivot_uniforms(77, h, r)), b)["pivots"])
-                for h in range(H))
+    agree = sum(np.array_equal(piv[h], ow.rpcholesky_block(
+        K[h], r, np.array(philox.pivot_uniforms(77, h, ow.BLOCK_DRAWS * r)), b)["pivots"]) for h in range(H))
     assert agree >= H - 1, agree
+
+
+def test_block_on_outlier_keys_fills_every_slot_and_matches_exact(wc):
+    """kv32k-like keys (1 % of rows four times longer, holding nearly all the mass): rounds
+    after the first fill the slots, and the forward stays close to exact attention."""
+    H, n, m, r, b = 2, 8192, 64, 256, 64
+    Q, K, V = synth.random_inputs(H, n, m, 128, 128, seed=961, dtype="bf16", kind="kv_outlier")
+    out = wc.wc_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), r, seed=3, pivot_block=b)
+    plain = wc.wc_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), r, seed=3)
+    assert np.all(host(out["rank"]) == r)
+    eb = np.mean([rel(host(out["O"])[h], ow.exact_attention(Q[h], K[h], V[h])) for h in range(H)])
+    ep = np.mean([rel(host(plain["O"])[h], ow.exact_attention(Q[h], K[h], V[h])) for h in range(H)])
+    assert eb < 2 * ep + 0.01, (eb, ep)

@@ -1,9 +1,11 @@
 """Pins of block pivoting (rpcholesky_block): one candidate per round is the plain loop; at any
-block size the factor satisfies the Nystroem identity for its accepted pivots (F F^T =
-H_{:,S} H_SS^{-1} H_{S,:}, written with a linear solve) and the rows of F at the pivots are
-lower triangular in slot order; full rank (every index accepted) reproduces H; an index drawn
-twice in a round is left out once; the candidates of a round are draws from the round-start
-diagonal (a brute-force linear scan); the trace never grows; snapped uniforms keep the pivots."""
+block size the factor satisfies the Nystroem identity for its pivots (F F^T =
+H_{:,S} H_SS^{-1} H_{S,:}, written with a linear solve), the rows of F at the pivots are lower
+triangular and the pivots fill slots 0 .. rank-1; full rank reproduces H; an index drawn twice
+in a round is passed over and the round's later draws fill the slot; a skewed residual (a few
+keys holding nearly all the mass) is filled by later rounds; the candidates of a round are
+draws from the round-start diagonal (a brute-force linear scan); snapped uniforms keep the
+pivots; the block-pivoted forward is close to the plain one."""
 import numpy as np
 import pytest
 
@@ -19,7 +21,7 @@ def keys(n=40, d=5, seed=0):
 @pytest.mark.parametrize("seed", range(4))
 def test_one_candidate_per_round_is_the_plain_loop(seed):
     K = keys(seed=seed)
-    u = np.random.default_rng(seed).random(12)
+    u = np.random.default_rng(seed).random(48)
     a = ow.rpcholesky_block(K, 12, u, 1)
     b = ow.rpcholesky(K, 12, u)
     assert np.array_equal(a["pivots"], b["pivots"]) and a["rank"] == b["rank"] == 12
@@ -31,10 +33,11 @@ def test_one_candidate_per_round_is_the_plain_loop(seed):
 def test_nystroem_identity_and_triangular_pivot_rows(b):
     K = keys(n=60, seed=10 + b)
     beta = ow.beta_of(5)
-    u = np.random.default_rng(b).random(16)
+    u = np.random.default_rng(b).random(64)
     out = ow.rpcholesky_block(K, 16, u, b)
     piv, F = out["pivots"], out["F"]
     valid = piv >= 0
+    assert out["rank"] == 16 and np.all(valid)
     S = piv[valid]
     Fv = F[:, valid]
     H = ow.kernel(K, K, beta)
@@ -46,37 +49,52 @@ def test_nystroem_identity_and_triangular_pivot_rows(b):
     expect = np.diag(H) - np.sum(Fv ** 2, 1)
     expect[S] = 0.0
     assert np.allclose(out["diag"], expect, rtol=1e-9, atol=1e-10)
-    assert np.all(np.diff(out["trace"][: 16 // b * b + 1 : b]) <= 1e-12)
+    nz = np.nonzero(out["trace"])[0]
+    assert nz[0] == 0 and nz[-1] == 16 and np.all(np.diff(out["trace"][nz]) <= 1e-12)
 
 
 def test_full_rank_reproduces_h():
     """Every index accepted (r = n, forced uniforms walking the remaining mass): F F^T = H."""
     K = keys(n=12, seed=3)
     beta = ow.beta_of(5)
-    u = np.zeros(12)
+    u = np.zeros(48)
     out = ow.rpcholesky_block(K, 12, u, 1)
     assert out["rank"] == 12
     assert np.allclose(out["F"] @ out["F"].T, ow.kernel(K, K, beta), rtol=1e-10, atol=1e-12)
-    # blocks of 3: the same keys, r = n; indices drawn twice are left out, so take the rank
-    out3 = ow.rpcholesky_block(K, 12, np.random.default_rng(4).random(12), 3)
-    v = out3["pivots"] >= 0
-    Fv = out3["F"][:, v]
-    S = out3["pivots"][v]
-    assert np.allclose(Fv[S] @ Fv[S].T, ow.kernel(K[S], K[S], beta), rtol=1e-10, atol=1e-12)
+    # blocks of 3, r = n: repeated draws are passed over, later rounds fill every slot
+    out3 = ow.rpcholesky_block(K, 12, np.random.default_rng(4).random(48), 3)
+    assert out3["rank"] == 12 and sorted(out3["pivots"]) == list(range(12))
+    assert np.allclose(out3["F"] @ out3["F"].T, ow.kernel(K, K, beta), rtol=1e-9, atol=1e-11)
 
 
-def test_index_drawn_twice_is_left_out_once():
+def test_index_drawn_twice_is_passed_over():
     K = keys(n=30, seed=5)
-    u = np.array([0.3, 0.3, 0.8, 0.1])   # the first two candidates are the same draw
+    u = np.array([0.3, 0.3, 0.8, 0.1] + [0.55, 0.2, 0.9, 0.6] + [0.5] * 8)
     out = ow.rpcholesky_block(K, 4, u, 4)
-    assert out["pivots"][0] >= 0 and out["pivots"][1] == -1
-    assert out["rank"] == 3 and np.all(out["F"][:, 1] == 0.0)
+    first = ow.rpcholesky_block(K, 1, u[:1], 1)["pivots"][0]
+    assert out["pivots"][0] == first and out["rank"] == 4
+    assert out["pivots"][1] != first                    # the repeated draw took no slot
+    assert len(set(out["pivots"])) == 4                 # the second round filled the last slot
+
+
+def test_skewed_residual_is_filled_by_later_rounds():
+    """Three keys hold nearly all the mass: the first round's eight draws hit only them, the
+    next rounds, drawn from the updated residual, fill the remaining slots."""
+    rng = np.random.default_rng(18)
+    K = rng.standard_normal((200, 6)) * 0.3
+    K[[5, 70, 150]] *= 12.0
+    out = ow.rpcholesky_block(K, 16, rng.random(64), 8)
+    assert out["rank"] == 16
+    assert set(out["pivots"][:3]) == {5, 70, 150}
 
 
 def test_candidates_are_draws_from_the_round_start_diagonal():
+    """Distinct draws (well spread keys, two rounds of four): the pivots are, in order, the
+    brute-force inverse-CDF draws on each round's start residual."""
     K = keys(n=50, seed=6)
-    u = np.random.default_rng(7).random(8)
+    u = np.random.default_rng(7).random(32)
     out = ow.rpcholesky_block(K, 8, u, 4)
+    assert out["rank"] == 8
     beta = ow.beta_of(5)
     diag = ow.initial_residual(K, beta)
     for k in range(2):
@@ -89,16 +107,15 @@ def test_candidates_are_draws_from_the_round_start_diagonal():
                 if acc > u[4 * k + j] * T:
                     s = i
                     break
-            if out["pivots"][4 * k + j] >= 0:
-                assert out["pivots"][4 * k + j] == s
+            assert out["pivots"][4 * k + j] == s
         Fk = out["F"][:, 4 * k: 4 * k + 4]
         diag = diag - np.sum(Fk ** 2, 1)
-        diag[out["pivots"][4 * k: 4 * k + 4][out["pivots"][4 * k: 4 * k + 4] >= 0]] = 0.0
+        diag[out["pivots"][4 * k: 4 * k + 4]] = 0.0
 
 
 def test_snapping_keeps_the_pivots():
     K = keys(n=80, seed=8)
-    raw = np.random.default_rng(9).random(16)
+    raw = np.random.default_rng(9).random(64)
     U = ow.snap_uniforms_block(K, 16, 4, raw)
     a = ow.rpcholesky_block(K, 16, raw, 4)
     c = ow.rpcholesky_block(K, 16, U.astype(np.float64), 4)
@@ -116,9 +133,9 @@ def test_block_forward_is_close_to_exact_and_to_the_plain_forward():
     ex = ow.exact_attention(Q, K, V)
     eb, ep = [], []
     for r in (16, 48):
-        u = np.random.default_rng(r).random(r)
+        u = np.random.default_rng(r).random(4 * r)
         eb.append(ow.rel_fro(ow.forward_binned(Q, K, V, r, 1, u, pivot_block=8)["O"], ex))
-        ep.append(ow.rel_fro(ow.forward(Q, K, V, r, u)["O"], ex))
+        ep.append(ow.rel_fro(ow.forward(Q, K, V, r, u[:r])["O"], ex))
     assert eb[1] < eb[0] and ep[1] < ep[0]
     assert eb[0] < 3 * ep[0] and eb[1] < 3 * ep[1], (eb, ep)
 
@@ -127,12 +144,32 @@ def test_block_forward_with_bins_keeps_pivots_in_their_bins():
     K = keys(n=64, seed=14)
     Q = keys(n=5, seed=15)
     V = np.random.default_rng(16).standard_normal((64, 2))
-    u = np.random.default_rng(17).random(16)
-    out = ow.forward_binned(Q, K, V, 16, 4, u, pivot_block=2)
-    for k0, k1, s0, s1 in ow.bin_bounds(64, 16, 4):
-        S = out["pivots"][s0:s1]
-        assert np.all((S == -1) | ((S >= k0) & (S < k1)))
-        ref = ow.rpcholesky_block(K[k0:k1], 4, u[s0:s1], 2)["pivots"]
-        assert np.array_equal(np.where(ref >= 0, ref + k0, -1), S)
-    with pytest.raises(ValueError):
-        ow.forward_binned(Q, K, V, 16, 4, u, weights_mode="bin", pivot_block=2)
+    u = np.random.default_rng(17).random(64)
+    for mode in ("union", "bin"):
+        out = ow.forward_binned(Q, K, V, 16, 4, u, weights_mode=mode, pivot_block=2)
+        for k0, k1, s0, s1 in ow.bin_bounds(64, 16, 4):
+            S = out["pivots"][s0:s1]
+            assert np.all((S >= k0) & (S < k1))
+            ref = ow.rpcholesky_block(K[k0:k1], 4, u[4 * s0:4 * s1], 2)["pivots"]
+            assert np.array_equal(ref + k0, S)
+
+
+def test_near_copy_of_a_long_key_is_passed_over():
+    """A long key (H_ss ~ 1e8) and a near copy of it hold nearly all the mass: the copy's
+    residual after the key is accepted is about 1 in absolute terms but ~1e-8 of H_ss, so the
+    relative test passes over it and the slot goes to a later draw."""
+    rng = np.random.default_rng(19)
+    K = rng.standard_normal((100, 3)) * 0.3
+    K[10] = rng.standard_normal(3)
+    K[10] *= 5.5 / np.linalg.norm(K[10])
+    K[60] = K[10] + 1e-4 * rng.standard_normal(3)
+    beta = 0.6
+    u = rng.random(32)
+    out = ow.rpcholesky_block(K, 4, u, 4, beta=beta)
+    piv = list(out["pivots"])
+    assert out["rank"] == 4
+    assert (10 in piv) != (60 in piv)   # exactly one of the pair
+    first = piv[0]
+    other = 60 if first == 10 else 10
+    g = ow.kernel(K[[other]], K[[other]], beta)[0, 0] - ow.kernel(K[[other]], K[[first]], beta)[0, 0] ** 2 / ow.kernel(K[[first]], K[[first]], beta)[0, 0]
+    assert 1e-3 < g < ow.DEPENDENT_TOL * ow.kernel(K[[other]], K[[other]], beta)[0, 0]
