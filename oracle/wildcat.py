@@ -125,19 +125,36 @@ def rpcholesky(K, r, uniforms, beta=None):
 BLOCK_DRAWS = 4  # candidates drawn per pivot slot at most, in block pivot selection
 
 
+def round_candidates(diag, uniforms):
+    """Candidates of one round of block pivot selection: drawn one after the other from the
+    residual diagonal at the start of the round without replacement, i.e. candidate j is the
+    inverse-CDF draw (sample_pivot) from the masses with the round's earlier candidates set to
+    zero.  Stops early when no mass is left."""
+    p = np.maximum(np.asarray(diag, np.float64), 0.0)
+    S = []
+    for u in uniforms:
+        q = p.copy()
+        q[S] = 0.0
+        s, _, _ = sample_pivot(q, u)
+        if s < 0:
+            break
+        S.append(s)
+    return S
+
+
 def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
     """Randomly pivoted Cholesky with b candidate pivots per round.
 
     The pages name the sequential pivot selection as a limitation that oversampling could
     lift (future work, gist.science/de/paper/2602.10056, "Bedeutung und Ansprueche").  Reading
     taken: the block variant of randomly pivoted Cholesky, oversampled until the slots are
-    full.  Round k draws b candidates, all from the residual diagonal at the start of the
-    round (s_j = min{i : C_i > u T}, u = uniforms[k b + j]); their kernel columns minus what the
+    full.  Round k draws b candidates from the residual diagonal at the start of the round,
+    without replacement (round_candidates, u = uniforms[k b + j]); their kernel columns minus what the
     factor already explains are formed together, G = H[:, S] - F F[S, :]^T; then the
     candidates are taken in order like single pivots: candidate j's residual column g removes
     the round's earlier accepted candidates, and it is accepted into the next free slot when
-    g[s] > tol H_ss (an index drawn again, or one dependent on the accepted ones, has a
-    negligible residual and is passed over).  After the round diag = diag - sum of the new
+    g[s] > tol H_ss (one dependent on the accepted ones has a negligible residual and is
+    passed over).  After the round diag = diag - sum of the new
     columns squared, 0 at the accepted indices.  Rounds go on until the r slots are full or
     BLOCK_DRAWS r candidates are drawn (``uniforms`` holds that many); a round that finds no
     mass, or running out of draws, stops the loop with rank < r (breakdown).  Pivots fill
@@ -161,12 +178,10 @@ def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
     for k in range(BLOCK_DRAWS * r // b):
         if filled == r:
             break
-        S = []
-        for j in range(b):
-            s, T, _ = sample_pivot(diag, uniforms[k * b + j])
-            S.append(s)
+        S = round_candidates(diag, uniforms[k * b:(k + 1) * b])
+        T = np.cumsum(np.maximum(diag, 0.0))[-1]
         trace[filled] = T if np.isfinite(T) else 0.0
-        if S[0] < 0:
+        if not S:
             flags |= FLAG_BREAKDOWN | (0 if np.isfinite(T) else FLAG_NONFINITE)
             break
         f0 = filled
@@ -206,17 +221,22 @@ def snap_uniforms_block(K, r, b, raw_uniforms, beta=None, tol=DEPENDENT_TOL):
         if filled == r:
             break
         S = []
+        p = np.maximum(diag, 0.0)
         for j in range(b):
-            s, T, C = sample_pivot(diag, u[k * b + j])
+            q = p.copy()
+            q[S] = 0.0
+            s, T, C = sample_pivot(q, u[k * b + j])
             if s < 0:
-                return out
+                break
             lo = C[s - 1] if s > 0 else 0.0
             v = np.round((lo + 0.5 * (C[s] - lo)) / T * 2.0 ** 24) * 2.0 ** -24
             v = min(max(v, 0.0), 1.0 - 2.0 ** -24)
-            if sample_pivot(diag, v)[0] != s:
+            if sample_pivot(q, v)[0] != s:
                 raise RuntimeError("snapping moved a candidate")
             out[k * b + j] = v
             S.append(s)
+        if not S:
+            return out
         # the round itself, as rpcholesky_block runs it
         f0 = filled
         G = kernel(K, K[S], beta) - F[:, :f0] @ F[S, :f0].T

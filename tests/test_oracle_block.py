@@ -2,10 +2,10 @@
 block size the factor satisfies the Nystroem identity for its pivots (F F^T =
 H_{:,S} H_SS^{-1} H_{S,:}, written with a linear solve), the rows of F at the pivots are lower
 triangular and the pivots fill slots 0 .. rank-1; full rank reproduces H; an index drawn twice
-in a round is passed over and the round's later draws fill the slot; a skewed residual (a few
-keys holding nearly all the mass) is filled by later rounds; the candidates of a round are
-draws from the round-start diagonal (a brute-force linear scan); snapped uniforms keep the
-pivots; the block-pivoted forward is close to the plain one."""
+never happens (a round's draws are without replacement: a brute-force scan of the masses with
+the earlier draws removed); a skewed residual (a few keys holding nearly all the mass) fills in
+one round; snapped uniforms keep the pivots; the block-pivoted forward is close to the plain
+one; a near copy of a long key is passed over (relative leave-out test)."""
 import numpy as np
 import pytest
 
@@ -67,30 +67,31 @@ def test_full_rank_reproduces_h():
     assert np.allclose(out3["F"] @ out3["F"].T, ow.kernel(K, K, beta), rtol=1e-9, atol=1e-11)
 
 
-def test_index_drawn_twice_is_passed_over():
+def test_draws_of_a_round_are_distinct():
+    """The same uniform twice in a round: the second draw skips the first's index."""
     K = keys(n=30, seed=5)
-    u = np.array([0.3, 0.3, 0.8, 0.1] + [0.55, 0.2, 0.9, 0.6] + [0.5] * 8)
+    u = np.array([0.3, 0.3, 0.8, 0.1] + [0.5] * 12)
     out = ow.rpcholesky_block(K, 4, u, 4)
-    first = ow.rpcholesky_block(K, 1, u[:1], 1)["pivots"][0]
-    assert out["pivots"][0] == first and out["rank"] == 4
-    assert out["pivots"][1] != first                    # the repeated draw took no slot
-    assert len(set(out["pivots"])) == 4                 # the second round filled the last slot
+    assert out["rank"] == 4 and len(set(out["pivots"])) == 4
+    first = ow.rpcholesky_block(K, 1, u[:4], 1)["pivots"][0]
+    assert out["pivots"][0] == first
 
 
-def test_skewed_residual_is_filled_by_later_rounds():
-    """Three keys hold nearly all the mass: the first round's eight draws hit only them, the
-    next rounds, drawn from the updated residual, fill the remaining slots."""
+def test_skewed_residual_fills_in_one_round():
+    """Three keys hold nearly all the mass: the round's first draws take them, the later ones
+    (without replacement) spread over the rest, and one round fills the eight slots."""
     rng = np.random.default_rng(18)
     K = rng.standard_normal((200, 6)) * 0.3
     K[[5, 70, 150]] *= 12.0
-    out = ow.rpcholesky_block(K, 16, rng.random(64), 8)
-    assert out["rank"] == 16
+    out = ow.rpcholesky_block(K, 8, rng.random(32), 8)
+    assert out["rank"] == 8
     assert set(out["pivots"][:3]) == {5, 70, 150}
+    assert np.count_nonzero(out["trace"]) == 2      # one round: totals before it and after
 
 
 def test_candidates_are_draws_from_the_round_start_diagonal():
-    """Distinct draws (well spread keys, two rounds of four): the pivots are, in order, the
-    brute-force inverse-CDF draws on each round's start residual."""
+    """Well spread keys, two rounds of four: the pivots are, in order, brute-force inverse-CDF
+    draws on each round's start residual with the round's earlier draws removed."""
     K = keys(n=50, seed=6)
     u = np.random.default_rng(7).random(32)
     out = ow.rpcholesky_block(K, 8, u, 4)
@@ -98,15 +99,18 @@ def test_candidates_are_draws_from_the_round_start_diagonal():
     beta = ow.beta_of(5)
     diag = ow.initial_residual(K, beta)
     for k in range(2):
-        p = np.maximum(diag, 0)
-        T = p.sum()
+        drawn = []
         for j in range(4):
+            p = np.maximum(diag, 0)
+            p[drawn] = 0.0
+            T = p.sum()
             acc, s = 0.0, None
             for i in range(50):       # brute force: first index whose running sum passes u T
                 acc += p[i]
                 if acc > u[4 * k + j] * T:
                     s = i
                     break
+            drawn.append(s)
             assert out["pivots"][4 * k + j] == s
         Fk = out["F"][:, 4 * k: 4 * k + 4]
         diag = diag - np.sum(Fk ** 2, 1)
