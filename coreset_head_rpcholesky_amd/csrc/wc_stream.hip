@@ -461,14 +461,24 @@ __device__ __forceinline__ bool blk_done(const BlockRpcArgs& A, int h) {
   return A.s.rank[h] >= A.s.r || (A.s.flags[h] & WC_DFLAG_BREAKDOWN);
 }
 
+// One workgroup per head draws the round's b candidates one after the other, without
+// replacement: candidate j is the inverse-CDF draw on the round-start masses with the earlier
+// candidates' masses removed.  The running sums are not rebuilt: the target u T' (T' the mass
+// left) is moved past the intervals [C_{d-1}, C_d) of the earlier candidates d, taken in index
+// order, and then searched on the unchanged block masses and rows.
 __global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int k) {
   __shared__ double red[NW];
   __shared__ int ired[NW];
-  extern __shared__ __attribute__((aligned(16))) double s_part[];  // [nblk]
+  __shared__ double s_x;
+  __shared__ int s_idx[64];     // candidates drawn so far, by index
+  __shared__ double s_lo[64];   // their running sum before them
+  __shared__ double s_m[64];    // their mass
+  __shared__ double s_flo, s_fm;
+  extern __shared__ __attribute__((aligned(16))) double s_pre[];  // [nblk] exclusive block sums
   const StreamRpcArgs& a = A.s;
-  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int n = a.n, nblk = a.nblk, rows = a.rows;
-  int32_t* cand = A.cand + (size_t)h * A.b + j;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int n = a.n, nblk = a.nblk, rows = a.rows, B = A.b;
+  int32_t* cand = A.cand + (size_t)h * B;
   if (blk_done(A, h)) return;
   const double* part = (k & 1) ? a.part1 : a.part0;
   const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
@@ -476,71 +486,105 @@ __global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int k) {
   double mine = 0.0;
   for (int e = 0; e < per; ++e) {
     const int bb = tid * per + e;
-    if (bb < nblk) {
-      const double v = part[(size_t)h * nblk + bb];
-      s_part[bb] = v;
-      mine += v;
-    }
+    if (bb < nblk) mine += part[(size_t)h * nblk + bb];
   }
   double Ttot;
-  const double excl = block_excl_scan(mine, red, &Ttot);
+  {
+    double run = block_excl_scan(mine, red, &Ttot);
+    for (int e = 0; e < per; ++e) {
+      const int bb = tid * per + e;
+      if (bb < nblk) {
+        s_pre[bb] = run;
+        run += part[(size_t)h * nblk + bb];
+      }
+    }
+  }
   const int f0 = a.rank[h];
   if (!(Ttot > 0.0) || !__builtin_isfinite(Ttot)) {
     // no mass left: the loop stops (every later kernel of the head sees the flag or cand -1)
     if (tid == 0) {
-      *cand = -1;
-      if (j == 0) {
-        a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(Ttot) ? 0u : WC_DFLAG_NONFINITE);
-        if (a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
-      }
+      a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(Ttot) ? 0u : WC_DFLAG_NONFINITE);
+      if (a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
     }
+    for (int j = tid; j < B; j += NT) cand[j] = -1;
     return;
   }
-  if (j == 0 && tid == 0 && a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = Ttot;
-  const double uT = (double)a.uniforms[(size_t)h * kBlockDraws * a.r + (size_t)k * A.b + j] * Ttot;
-  int bc = 0x7fffffff, lastpos = -1;
-  double run = excl;
-  for (int e = 0; e < per; ++e) {
-    const int bb = tid * per + e;
-    if (bb < nblk) {
-      const double v = s_part[bb];
-      run += v;
-      if (bc == 0x7fffffff && v > 0.0 && run > uT) bc = bb;
-      if (v > 0.0) lastpos = bb;
+  if (tid == 0 && a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = Ttot;
+  const float* u = a.uniforms + (size_t)h * kBlockDraws * a.r + (size_t)k * B;
+  double removed = 0.0;
+  int nd = 0;
+  for (int j = 0; j < B; ++j) {
+    const double Tl = Ttot - removed;
+    if (!(Tl > 0.0)) {  // every index with mass is drawn: the round has fewer candidates
+      for (int jj = j + tid; jj < B; jj += NT) cand[jj] = -1;
+      break;
     }
+    __syncthreads();
+    if (tid == 0) {
+      double x = (double)u[j] * Tl;
+      for (int q = 0; q < nd; ++q)  // in index order, so later intervals see the shifted target
+        if (x >= s_lo[q]) x += s_m[q];
+      s_x = x;
+    }
+    __syncthreads();
+    const double x = s_x;
+    // block holding x (the last block with mass if rounding put x at or past the total)
+    int bc = 0x7fffffff, lastpos = -1;
+    for (int e = 0; e < per; ++e) {
+      const int bb = tid * per + e;
+      if (bb < nblk) {
+        const double v = part[(size_t)h * nblk + bb];
+        if (bc == 0x7fffffff && v > 0.0 && s_pre[bb] + v > x) bc = bb;
+        if (v > 0.0) lastpos = bb;
+      }
+    }
+    int bstar = block_min_int(bc, ired);
+    if (bstar == 0x7fffffff) bstar = block_max_int(lastpos, ired);
+    // row inside it
+    const int rpt = rows / NT, r0 = bstar * rows;
+    double pm[4];
+    double tmass = 0.0;
+    for (int e = 0; e < rpt; ++e) {
+      const int i = r0 + tid * rpt + e;
+      pm[e] = (i < n) ? mass_of(dg_in[i]) : 0.0;
+      tmass += pm[e];
+    }
+    double btot;
+    __syncthreads();
+    const double rexcl = block_excl_scan(tmass, red, &btot);
+    int scand = 0x7fffffff;
+    double c = s_pre[bstar] + rexcl;
+    for (int e = 0; e < rpt; ++e) {
+      c += pm[e];
+      const int i = r0 + tid * rpt + e;
+      if (scand == 0x7fffffff && c > x && pm[e] > 0.0) scand = i;
+    }
+    const int s = block_min_int(scand, ired);
+    if (s != 0x7fffffff && tid == (s - r0) / rpt) {
+      // the thread holding row s records its interval [C_{s-1}, C_s) of the running sum
+      double lo = s_pre[bstar] + rexcl;
+      for (int e = 0; e < s - r0 - tid * rpt; ++e) lo += pm[e];
+      s_flo = lo;
+      s_fm = pm[s - r0 - tid * rpt];
+    }
+    __syncthreads();
+    if (s == 0x7fffffff || s >= n) {  // rounding left no row to claim x: no more candidates
+      for (int jj = j + tid; jj < B; jj += NT) cand[jj] = -1;
+      break;
+    }
+    if (tid == 0) {
+      cand[j] = s;
+      // insert into the index-ordered list of drawn candidates
+      int q = nd;
+      while (q > 0 && s_idx[q - 1] > s) {
+        s_idx[q] = s_idx[q - 1]; s_lo[q] = s_lo[q - 1]; s_m[q] = s_m[q - 1];
+        --q;
+      }
+      s_idx[q] = s; s_lo[q] = s_flo; s_m[q] = s_fm;
+    }
+    removed += s_fm;
+    ++nd;
   }
-  int bstar = block_min_int(bc, ired);
-  if (bstar == 0x7fffffff) bstar = block_max_int(lastpos, ired);
-  __syncthreads();
-  if (tid == bstar / per) {
-    double o = excl;
-    for (int e = 0; e < bstar - tid * per; ++e) o += s_part[tid * per + e];
-    red[0] = o;
-  }
-  __syncthreads();
-  const double boff = red[0];
-  const int rpt = rows / NT, r0 = bstar * rows;
-  double pm[4];
-  double tmass = 0.0;
-  for (int e = 0; e < rpt; ++e) {
-    const int i = r0 + tid * rpt + e;
-    pm[e] = (i < n) ? mass_of(dg_in[i]) : 0.0;
-    tmass += pm[e];
-  }
-  double btot;
-  __syncthreads();
-  const double rexcl = block_excl_scan(tmass, red, &btot);
-  int scand = 0x7fffffff, slast = -1;
-  double c = boff + rexcl;
-  for (int e = 0; e < rpt; ++e) {
-    c += pm[e];
-    const int i = r0 + tid * rpt + e;
-    if (scand == 0x7fffffff && c > uT && pm[e] > 0.0) scand = i;
-    if (pm[e] > 0.0) slast = i;
-  }
-  int s = block_min_int(scand, ired);
-  if (s == 0x7fffffff) s = block_max_int(slast, ired);
-  if (tid == 0) *cand = (s >= 0 && s < n) ? s : -1;
 }
 
 // One thread per row (256 rows per workgroup): the candidate keys and, chunk by chunk, the
@@ -758,7 +802,7 @@ static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
   const int colgrid = (a.n + NT - 1) / NT;
   const int rounds = kBlockDraws * a.r / B;
   for (int k = 0; k < rounds; ++k) {
-    hipLaunchKernelGGL(blk_sample_kernel, dim3(B, a.H), dim3(NT), lds, st, A, k);
+    hipLaunchKernelGGL(blk_sample_kernel, dim3(a.H), dim3(NT), lds, st, A, k);
     hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A);
     hipLaunchKernelGGL((blk_factor_kernel<T, D, B>), dim3(a.H), dim3(4 * B), 0, st, A, k);
     hipLaunchKernelGGL((blk_apply_kernel<B>), grid, dim3(NT), 0, st, A, k);
