@@ -432,6 +432,28 @@ __device__ __forceinline__ void attend_step(const AttendChunk<D, DV>& bS, int uS
 }
 
 // Workgroup of kAttendWaves waves (one per SIMD), each taking kAttendNQ groups of 32 queries.
+#ifndef WC_ATTEND_XCD
+#define WC_ATTEND_XCD 1
+#endif
+// Workgroups are dealt to the 8 XCDs round-robin by linear id.  The id is remapped so that each
+// XCD takes a contiguous run of (head, coreset split, query tile) triples, head-major: a head's
+// coreset is then read through one or two XCDs' L2 instead of all eight.
+__device__ __forceinline__ void attend_tile(int& qt, int& h, int& sp) {
+  const int QT = gridDim.x, NH = gridDim.y, NS = gridDim.z;
+  qt = blockIdx.x; h = blockIdx.y; sp = blockIdx.z;
+#if WC_ATTEND_XCD
+  const int T = QT * NH * NS;
+  if (T % 8 == 0) {
+    const int L = blockIdx.x + QT * (blockIdx.y + NH * blockIdx.z);
+    const int p = (L % 8) * (T / 8) + L / 8;
+    qt = p % QT;
+    const int hs = p / QT;
+    h = hs / NS;
+    sp = hs % NS;
+  }
+#endif
+}
+
 template <int D, int DV>
 __global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
 attend_bf16_kernel(AttendArgs a) {
@@ -439,10 +461,11 @@ attend_bf16_kernel(AttendArgs a) {
   __shared__ AttendChunk<D, DV> sb[3];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, sp = blockIdx.z;
+  int qt, h, sp;
+  attend_tile(qt, h, sp);
   const int m = a.m, rp = staged_rows(a);
   const float bl2e = a.beta_log2e;
-  const int q0 = blockIdx.x * kAttendQueries + wid * 32 * NQ + l32;
+  const int q0 = qt * kAttendQueries + wid * 32 * NQ + l32;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * m * D;
 
   // query fragments scaled by beta log2(e) (one bf16 rounding, relative 2^-9 per element), so

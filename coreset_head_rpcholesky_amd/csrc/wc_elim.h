@@ -6,18 +6,18 @@
 namespace wc {
 
 // M = inverse of the Cholesky factor of the kept part of the B x B block in sA (row-major,
-// pitch P floats), for a workgroup of 4 B threads.  Right-looking elimination applied
+// pitch P floats), for a workgroup of 4 B threads; M replaces the block in sA (same pitch).  Right-looking elimination applied
 // alongside to the identity: step j takes the pivot residual p = A[j][j]; if p > tol hd[j]
 // every later row i subtracts f_i = A[i][j] / p times row j, in the block and in G (G starts
 // as the identity).  G ends as U^{-1}, U the unit lower factor of A = U diag(p) U^T over the
 // kept points, so M = diag(p)^{-1/2} G; a left-out point eliminates nothing and gets a zero
 // row of M (M[j][j] > 0 exactly for the kept ones).  Thread (i, q) holds columns
 // q B/4 .. (q+1) B/4 - 1 of row i of the block and of G; column j of the block and row j of G
-// are published in LDS (double-buffered by the parity of j, one barrier per step).  M is
-// written row-major with leading dimension B.  Returns, in every thread, whether a point with
-// hd > 0 was left out.
+// are published in LDS (double-buffered by the parity of j, one barrier per step).  hd (B
+// entries) should sit in LDS: it is read at every step.  Ends with a barrier.  Returns, in
+// every thread, whether a point with hd > 0 was left out.
 template <int B, int P>
-__device__ __forceinline__ bool elim_block(const float* sA, const float* hd, float tol, float* M,
+__device__ __forceinline__ bool elim_block(float* sA, const float* hd, float tol,
                                            float (*sCol)[B], float (*sRow)[B]) {
   constexpr int CB = B / 4;
   const int tid = threadIdx.x, ri = tid >> 2, q = tid & 3, c0 = CB * q;
@@ -46,11 +46,13 @@ __device__ __forceinline__ bool elim_block(const float* sA, const float* hd, flo
     const bool keep = p > tol * hj;
     dependent |= !keep && hj > 0.f;
     if (ri == j) {
-      // row j of M (hardware reciprocal square root, about 1 ulp)
+      // row j of M, into the block's own LDS rows (read once at the start; a global store
+      // here would hold up every later barrier until it completes); hardware reciprocal
+      // square root, about 1 ulp
       const float s = keep ? __builtin_amdgcn_rsqf(p) : 0.f;
 #pragma unroll
       for (int e = 0; e < CB; e += 4)
-        *reinterpret_cast<float4*>(M + (size_t)j * B + c0 + e) = make_float4(g[e] * s, g[e + 1] * s, g[e + 2] * s, g[e + 3] * s);
+        *reinterpret_cast<float4*>(sA + j * P + c0 + e) = make_float4(g[e] * s, g[e + 1] * s, g[e + 2] * s, g[e + 3] * s);
     }
     if (keep && ri > j) {
       const float f = sCol[buf][ri] * __builtin_amdgcn_rcpf(p);
@@ -65,7 +67,18 @@ __device__ __forceinline__ bool elim_block(const float* sA, const float* hd, flo
       }
     }
   }
+  __syncthreads();
   return dependent;
+}
+
+// Copy M (B x B, pitch P in LDS, as elim_block leaves it) to global memory, row-major with
+// leading dimension B, by the 4 B threads of the workgroup.
+template <int B, int P>
+__device__ __forceinline__ void store_block(const float* sM, float* M) {
+  for (int e = threadIdx.x; e < B * B / 4; e += 4 * B) {
+    const int row = (4 * e) / B, col = (4 * e) % B;
+    *reinterpret_cast<float4*>(M + (size_t)row * B + col) = *reinterpret_cast<const float4*>(sM + row * P + col);
+  }
 }
 
 }  // namespace wc

@@ -686,8 +686,8 @@ __global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int k
   }
   __syncthreads();
   float* M = A.M + (size_t)h * B * B;
-  elim_block<B, P>(sA, sHd, A.tol, M, sCol, sRow);
-  __syncthreads();
+  elim_block<B, P>(sA, sHd, A.tol, sCol, sRow);
+  store_block<B, P>(sA, M);
   if (tid == 0) {
     // kept candidates take the next free slots in order; once the slots are full the rest of
     // the round is dropped (later candidates were eliminated only against earlier ones)
@@ -695,7 +695,7 @@ __global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int k
     int f = f0;
     for (int jj = 0; jj < B; ++jj) {
       int sl = -1;
-      if (f < a.r && M[(size_t)jj * B + jj] > 0.f) {
+      if (f < a.r && sA[jj * P + jj] > 0.f) {
         sl = f++;
         a.pivots[(size_t)h * a.r + sl] = sC[jj];
       }

@@ -157,11 +157,13 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
 // ---- diag: M_kk = inverse of the Cholesky factor of the kept part of A_kk -------------------
 // A whole 256-thread workgroup eliminates the (already updated) block in sA with the leave-out
 // rule (elim_block); left-out points of valid slots set WC_DFLAG_DEPENDENT.
-__device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, const float (*sA)[kLP],
-                                           float (*sCol)[kUB], float (*sRow)[kUB]) {
-  const float* Hd = a.Hd + (size_t)h * a.rp + (size_t)k * kUB;
-  float* M = a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB;
-  const bool dependent = elim_block<kUB, kLP>(&sA[0][0], Hd, a.tol, M, sCol, sRow);
+// The diagonal entries H_jj (the scale of the leave-out test) are staged in LDS first: read
+// from global memory inside the pivot loop, each step would wait for one load.
+__device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, float (*sA)[kLP],
+                                           float (*sCol)[kUB], float (*sRow)[kUB], float* sHd) {
+  if (threadIdx.x < kUB) sHd[threadIdx.x] = a.Hd[(size_t)h * a.rp + (size_t)k * kUB + threadIdx.x];
+  const bool dependent = elim_block<kUB, kLP>(&sA[0][0], sHd, a.tol, sCol, sRow);
+  store_block<kUB, kLP>(&sA[0][0], a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB);
   if (dependent && threadIdx.x == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
 }
 
@@ -170,11 +172,12 @@ __global__ void __launch_bounds__(256) union_diag0_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(16))) float sA[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
   __shared__ __attribute__((aligned(16))) float sRow[2][kUB];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ float sHd[kUB];
+  const int h = blockIdx.x;
   const float* A = a.A + (size_t)h * a.rp * a.rp;
   stage_direct(sA, A, a.rp);
   __syncthreads();
-  diag_block(a, h, 0, sA, sCol, sRow);
+  diag_block(a, h, 0, sA, sCol, sRow, sHd);
 }
 
 // ---- panel: L_ik = A_ik M_kk^T (i > k) and Z_k = M_kk X_k ------------------------------------
@@ -225,6 +228,7 @@ __global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
   __shared__ __attribute__((aligned(16))) float sQ[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
   __shared__ __attribute__((aligned(16))) float sRow[2][kUB];
+  __shared__ float sHd[kUB];
   const int h = blockIdx.y, tid = threadIdx.x, nb = a.rp / kUB, T = nb - k - 1;
   const int nc = a.dv + 1;
   float* A = a.A + (size_t)h * a.rp * a.rp;
@@ -254,7 +258,7 @@ __global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
             make_float4(o.x - acc[r4][0], o.y - acc[r4][1], o.z - acc[r4][2], o.w - acc[r4][3]);
       }
       __syncthreads();
-      diag_block(a, h, k + 1, sP, sCol, sRow);
+      diag_block(a, h, k + 1, sP, sCol, sRow, sHd);
       return;
     }
 #pragma unroll
