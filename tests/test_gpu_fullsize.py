@@ -9,7 +9,11 @@ compute one by one:
   * factor rows F[i, :] for sampled rows i, which are fixed once the pivots are
     (F[i, :] = L^{-1} H[S, i] with L the Cholesky factor of H_SS);
   * W and O for sampled queries from the GPU's pivots (given the pivots, W and O are unique);
-  * properties at any size: distinct pivots, full rank, non-increasing trace, no flags."""
+  * properties at any size: distinct pivots, full rank, non-increasing trace, no flags.
+The divide-and-conquer forward at the same two sizes (64 and 16 bins, one pivot per step and
+block pivots) is checked the same way: pivots distinct and inside their bins, the first bin's
+pivots from the same Philox draws, the union weights and sampled outputs from the GPU's
+pivots."""
 import numpy as np
 import pytest
 
@@ -29,21 +33,22 @@ def wc():
     return binding
 
 
-def forward_graph(wc, Q, K, V, r, u_forced=None, seed=42):
+def forward_graph(wc, Q, K, V, r, u_forced=None, seed=42, bins=1, pivot_block=1):
     """wc_forward captured in a HIP graph and replayed, as bench.py launches it."""
     import torch
 
     H, m, d = Q.shape
-    p = wc.problem(H, K.shape[1], m, d, V.shape[2], r, Q.dtype)
+    p = wc.problem(H, K.shape[1], m, d, V.shape[2], r, Q.dtype, bins, 0, pivot_block)
     ws = wc.workspace(p, Q.device)
-    out = wc.wc_forward(Q, K, V, r, u_forced=u_forced, seed=seed, ws=ws)
+    kw = dict(u_forced=u_forced, seed=seed, bins=bins, pivot_block=pivot_block, ws=ws)
+    out = wc.wc_forward(Q, K, V, r, **kw)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            wc.wc_forward(Q, K, V, r, u_forced=u_forced, seed=seed, ws=ws, out=out)
+            wc.wc_forward(Q, K, V, r, out=out, **kw)
     torch.cuda.current_stream().wait_stream(side)
     g.replay()
     torch.cuda.synchronize()
@@ -119,3 +124,38 @@ def test_sampled_full(wc, name, check_heads, nq):
         Oo, den, kappa = ow.attend(Q[h][qs], K[h], S, Wo, beta)
         ok = kappa < 1e6
         assert rel(O[h][qs][ok], Oo[ok]) < TOL["bf16"], rel(O[h][qs][ok], Oo[ok])
+
+
+@pytest.mark.parametrize("name,B,pb,h,nq", [("long128k", 64, 1, 0, 256), ("long128k", 64, 32, 5, 256),
+                                           ("kv32k", 16, 1, 3, None), ("kv32k", 16, 64, 30, None)])
+def test_binned_full(wc, name, B, pb, h, nq):
+    import torch
+
+    w = synth.WORKLOADS[name]
+    Q, K, V = synth.make_inputs(name)
+    out = forward_graph(wc, dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), w.r, seed=42, bins=B, pivot_block=pb)
+    O, piv = host(out["O"]), host(out["pivots"])
+    assert np.all(host(out["rank"]) == w.r) and np.all(host(out["flags"]) == 0)
+    del out
+    torch.cuda.empty_cache()
+    nb, rb = w.n // B, w.r // B
+    S = piv[h]
+    assert len(set(S.tolist())) == w.r
+    for b in range(B):
+        assert np.all((S[b * rb:(b + 1) * rb] >= b * nb) & (S[b * rb:(b + 1) * rb] < (b + 1) * nb))
+    beta = 1.0 / np.sqrt(w.d)
+    # the first bin from the same Philox draws (sub-head h B of the per-bin view)
+    if pb > 1:
+        ref = ow.rpcholesky_block(K[h][:nb], rb, np.array(philox.pivot_uniforms(42, h * B, ow.BLOCK_DRAWS * rb)), pb, beta)
+        assert np.array_equal(S[:rb], ref["pivots"])
+    else:
+        ref = ow.rpcholesky(K[h][:nb], 3, philox.pivot_uniforms(42, h * B, 3), beta)
+        assert np.array_equal(S[:3], ref["pivots"])
+    # union weights and sampled outputs from the GPU's pivots
+    W, kept = ow.weights_union(K[h], V[h], S, beta)
+    assert kept.all()
+    rng = np.random.default_rng(1)
+    qs = np.arange(w.m) if nq is None else rng.choice(w.m, nq, replace=False)
+    Oo, den, kappa = ow.attend(Q[h][qs], K[h], S, W, beta)
+    ok = kappa < 1e6
+    assert rel(O[h][qs][ok], Oo[ok]) < TOL["bf16"], rel(O[h][qs][ok], Oo[ok])
