@@ -314,10 +314,10 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
 }
 
 // bf16 inputs.  A workgroup takes 256 queries (kAttendWaves waves of kAttendNQ x 32).  The
-// coreset is walked in 64-row chunks through a ring of three LDS buffers filled by direct
+// coreset is walked in 64-row chunks through a ring of LDS buffers filled by direct
 // global-to-LDS loads (no staging registers, no LDS store instructions): while chunk c is in
-// use, chunk c+1 is resident and chunk c+2 is loading, so one barrier per chunk is the only
-// synchronisation.  With the tile-major layouts above a chunk is copied as is, and the operand
+// use, chunk c+1 is resident and the next ones are loading, so one barrier per chunk is the
+// only synchronisation.  With the tile-major layouts above a chunk is copied as is, and the operand
 // reads of consecutive lanes hit consecutive 16-byte units (no bank conflicts).
 typedef __attribute__((address_space(3))) void* lds_void;
 
@@ -353,8 +353,31 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as an immediate the compiler's
 // own wait tracking understands
 constexpr int kVmcnt0 = 0x0F70;
+#ifndef WC_ATTEND_RING
+#define WC_ATTEND_RING 4
+#endif
+constexpr int kAttendRing = WC_ATTEND_RING;  // LDS chunk buffers: chunks in use, resident, loading
+static_assert(kAttendRing == 3 || kAttendRing == 4, "ring of three or four chunks");
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void)const_cast<void*>(p);
+}
+
+// Wait until at most `pending` chunks of this wave's direct loads are still in flight (loads
+// complete in order, so every older chunk has landed).  A chunk is KI + WI load instructions
+// per wave, plus the normaliser column's on wave 0.
+template <int D, int DV>
+__device__ __forceinline__ void attend_wait(int pending, int wid) {
+  constexpr int per = D / (8 * kAttendWaves) + DV / (8 * kAttendWaves);
+  static_assert(2 * per + 2 < 16, "vmcnt field");
+  if (pending <= 0) {
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  } else if (pending == 1) {
+    if (wid == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0 | (per + 1));
+    else __builtin_amdgcn_s_waitcnt(kVmcnt0 | per);
+  } else {
+    if (wid == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0 | (2 * per + 2));
+    else __builtin_amdgcn_s_waitcnt(kVmcnt0 | (2 * per));
+  }
 }
 
 template <int D, int DV>
@@ -458,7 +481,7 @@ template <int D, int DV>
 __global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
 attend_bf16_kernel(AttendArgs a) {
   constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ;
-  __shared__ AttendChunk<D, DV> sb[3];
+  __shared__ AttendChunk<D, DV> sb[kAttendRing];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   int qt, h, sp;
@@ -503,9 +526,9 @@ attend_bf16_kernel(AttendArgs a) {
   const uint16_t* Wph = a.Wph + (size_t)h * DV * rp;
   const uint16_t* Wdh = a.Wdh + (size_t)h * rp;
   if (nc > 0) {
-    attend_issue(sb[0], KSh, Wph, Wdh, c0, wid, lane);
-    if (nc > 1) attend_issue(sb[1], KSh, Wph, Wdh, c0 + 1, wid, lane);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    // chunks 0 .. kAttendRing-2 in flight; chunk 0 waited for
+    for (int i = 0; i < kAttendRing - 1 && i < nc; ++i) attend_issue(sb[i], KSh, Wph, Wdh, c0 + i, wid, lane);
+    attend_wait<D, DV>(min(nc, kAttendRing - 1) - 1, wid);
     __syncthreads();
     // scores of unit 0 alone; the values of the (nonexistent) unit -1 get zero probabilities
     f32x16 scA[NQ], scB[NQ];
@@ -519,20 +542,23 @@ attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pbA[s][0][e] = pbA[s][1][e] = (__bf16)0.f;
     }
-    // Unit 2c is in ring slot c % 3 (upper half of the chunk: unit 2c+1).  Chunk c's loads were
-    // issued two chunks ahead and are waited for at the barrier of chunk c-1; that barrier also
-    // frees slot (c+2) % 3, whose last reads (values of unit 2c-1) come before it.
+    // Unit 2c is in ring slot c % R (upper half of the chunk: unit 2c+1), R = kAttendRing.
+    // Chunk c's loads were issued R-1 chunks ahead and are waited for at the barrier of chunk
+    // c-1, with the chunks after it still in flight; that barrier also frees slot
+    // (c+R-1) % R = (c-1) % R, whose last reads (values of unit 2c-1) come before it.
+    constexpr int R = kAttendRing;
     for (int c = 0; c < nc; ++c) {
-      const int bc = c % 3, bn = (c + 1) % 3, bl = c == 0 ? bc : (c + 2) % 3;
+      const int bc = c % R, bn = (c + 1) % R, bl = c == 0 ? bc : (c + R - 1) % R;
       attend_step<D, DV, NQ>(sb[bc], 1, sb[bc], 0, sb[bl], c == 0 ? 0 : 1, qb, y, den, scA, scB, pbA, pbB, g, l32);
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      // chunk c+1 landed; chunks c+2 .. c+R-2 (those issued) may still be loading
+      attend_wait<D, DV>(min(nc, c + R - 1) - (c + 2), wid);
       __syncthreads();
-      if (c + 2 < nc) attend_issue(sb[(c + 2) % 3], KSh, Wph, Wdh, c0 + c + 2, wid, lane);
+      if (c + R - 1 < nc) attend_issue(sb[(c + R - 1) % R], KSh, Wph, Wdh, c0 + c + R - 1, wid, lane);
       // the scores of unit 2c+2 are garbage past the last chunk and are never exponentiated
       attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
     }
     // values of the last unit
-    const AttendChunk<D, DV>& bz = sb[(nc - 1) % 3];
+    const AttendChunk<D, DV>& bz = sb[(nc - 1) % R];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const bf16x8 wf = __builtin_bit_cast(bf16x8, bz.w[(4 + 2 * (i & 1) + g) * DV + 32 * (i >> 1) + l32]);

@@ -27,10 +27,11 @@
 
 namespace wc {
 
+// Lane movement of an fp64 value; lanes with no source lane read zero (bound_ctrl).
 template <int CTRL>
 __device__ __forceinline__ double dpp_d(double x) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, 0xf, 0xf, true);
   return __hiloint2double(hi, lo);
 }
 __device__ __forceinline__ double readlane_d(double x, int lane) {
@@ -38,19 +39,26 @@ __device__ __forceinline__ double readlane_d(double x, int lane) {
   const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
   return __hiloint2double(hi, lo);
 }
-// Inclusive fp64 scan over the wave: row_shr within 16-lane rows, then row offsets.
-__device__ __forceinline__ double wave_scan_fast(double x) {
+// Two independent inclusive fp64 scans over the wave, level by level side by side (the step is
+// latency-bound, so the two dependency chains overlap): row_shr within 16-lane rows, then the
+// row offsets.  Each scan adds in the same order as a scan of its own.
+__device__ __forceinline__ void wave_scan2(double& x, double& y) {
   x += dpp_d<0x111>(x);
+  y += dpp_d<0x111>(y);
   x += dpp_d<0x112>(x);
+  y += dpp_d<0x112>(y);
   x += dpp_d<0x114>(x);
+  y += dpp_d<0x114>(y);
   x += dpp_d<0x118>(x);
-  const double r0 = readlane_d(x, 15), r1 = readlane_d(x, 31), r2 = readlane_d(x, 47);
-  const double o2 = r0 + r1, o3 = o2 + r2;
+  y += dpp_d<0x118>(y);
+  const double rx0 = readlane_d(x, 15), rx1 = readlane_d(x, 31), rx2 = readlane_d(x, 47);
+  const double ry0 = readlane_d(y, 15), ry1 = readlane_d(y, 31), ry2 = readlane_d(y, 47);
+  const double ox2 = rx0 + rx1, oy2 = ry0 + ry1;
+  const double ox3 = ox2 + rx2, oy3 = oy2 + ry2;
+  // row offsets by selection (adding +0 leaves row 0's non-negative sums unchanged)
   const int row = (threadIdx.x & 63) >> 4;
-  if (row == 1) x += r0;
-  if (row == 2) x += o2;
-  if (row == 3) x += o3;
-  return x;
+  x += row == 0 ? 0.0 : row == 1 ? rx0 : row == 2 ? ox2 : ox3;
+  y += row == 0 ? 0.0 : row == 1 ? ry0 : row == 2 ? oy2 : oy3;
 }
 
 // dot(k_a, k_b) of two keys held as packed bf16 pairs; fixed association order.
@@ -117,8 +125,12 @@ struct ResidentSmem {
   static constexpr int WP_OFF = KS_OFF + R * KSP * 2;
   static constexpr int WDEN_OFF = WP_OFF + DV * WPP * 2;
   static constexpr int L_OFF = WDEN_OFF + R * 4;
-  static constexpr int P2_BYTES = L_OFF + R * (R + 1) * 4;
-  // pivot-loop region, for n keys
+  static constexpr int LS = R + 4;    // row stride of L (16-byte rows; column R holds 1 / L_tt)
+  static constexpr int P2_BYTES = L_OFF + R * LS * 4;
+  static_assert(L_OFF % 16 == 0, "16-byte rows of L");
+  // pivot-loop region, for n keys.  At n = 197 (d = 64) this region plus the kernel's ~270
+  // bytes of static arrays just lets three workgroups share a CU; 256 more bytes of static LDS
+  // were measured to drop that to two (1.5x slower at 768 heads).
   __host__ __device__ static constexpr int f_off(int n) { return n * D * 2; }
   static constexpr int DGS = 2 * NT;  // row stride of each residual-diagonal buffer (all rows)
   __host__ __device__ static constexpr int dg_off(int n) { return (f_off(n) + n * FS * 4 + 15) & ~15; }
@@ -134,10 +146,14 @@ struct PairScan {
   double x, xa;
   bool pa, pb;  // rows with positive mass
 };
-__device__ __forceinline__ PairScan pair_scan(float dga, float dgb, bool va, bool vb) {
-  const double ma = va ? mass_of(dga) : 0.0, mb = vb ? mass_of(dgb) : 0.0;
-  const double x = wave_scan_fast(ma + mb);
-  return {x, x - mb, ma > 0.0, mb > 0.0};
+// Both waves' row pairs at this lane position (rows 2l, 2l+1 and 128 + 2l, 128 + 2l + 1).
+__device__ __forceinline__ void pair_scan2(float2 d0, float2 d1, int lane, int n, PairScan& q0, PairScan& q1) {
+  const double m0a = 2 * lane < n ? mass_of(d0.x) : 0.0, m0b = 2 * lane + 1 < n ? mass_of(d0.y) : 0.0;
+  const double m1a = 128 + 2 * lane < n ? mass_of(d1.x) : 0.0, m1b = 129 + 2 * lane < n ? mass_of(d1.y) : 0.0;
+  double x0 = m0a + m0b, x1 = m1a + m1b;
+  wave_scan2(x0, x1);
+  q0 = {x0, x0 - m0b, m0a > 0.0, m0b > 0.0};
+  q1 = {x1, x1 - m1b, m1a > 0.0, m1b > 0.0};
 }
 
 template <int D, int DV, int R, int NT>
@@ -210,8 +226,8 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     // every wave holds both wave totals and the prefix sums of whichever wave is crossed.
     const float2 d0p = reinterpret_cast<const float2*>(sDg + buf * DGS)[lane];
     const float2 d1p = reinterpret_cast<const float2*>(sDg + buf * DGS)[64 + lane];
-    const PairScan q0 = pair_scan(d0p.x, d0p.y, 2 * lane < n, 2 * lane + 1 < n);
-    const PairScan q1 = pair_scan(d1p.x, d1p.y, 128 + 2 * lane < n, 128 + 2 * lane + 1 < n);
+    PairScan q0, q1;
+    pair_scan2(d0p, d1p, lane, n, q0, q1);
     const double w0 = readlane_d(q0.x, 63), w1 = readlane_d(q1.x, 63);
     T = w0 + w1;
     // Breakdown (T <= 0, no row claims the draw, g_s <= 0, anything non-finite) is collected
@@ -260,11 +276,9 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
       alive = false;
       return;
     }
-    if (tid == 0) {
-      s_pivots[t] = s;
-      if (a.pivots) a.pivots[(size_t)h * r + t] = s;
-    }
-    const float rs = 1.0f / sqrtf(gs);
+    if (tid == 0) s_pivots[t] = s;
+    // reciprocal square root of the pivot's residual (hardware rsq, within an ulp or so)
+    const float rs = __builtin_amdgcn_rsqf(gs);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int row = ra + p;
@@ -284,23 +298,25 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     }
     __syncthreads();
   });
+  __syncthreads();  // a breakdown step leaves the loop before its barrier
 
-  // trace after the last step (reported only when all r steps completed)
-  if (a.trace && rk == r) {
-    const float2 d0p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[lane];
-    const float2 d1p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[64 + lane];
-    const PairScan q0 = pair_scan(d0p.x, d0p.y, 2 * lane < n, 2 * lane + 1 < n);
-    const PairScan q1 = pair_scan(d1p.x, d1p.y, 128 + 2 * lane < n, 128 + 2 * lane + 1 < n);
-    const double Tr = readlane_d(q0.x, 63) + readlane_d(q1.x, 63);
-    if (tid == 0) a.trace[(size_t)h * (r + 1) + r] = Tr;
+  // the trace after the last step when all r steps completed, zero past a breakdown step (the
+  // steps taken stored theirs in the loop); pivots, -1 past the rank
+  if (a.trace) {
+    double Tr = 0.0;
+    if (rk == r) {
+      const float2 d0p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[lane];
+      const float2 d1p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[64 + lane];
+      PairScan q0, q1;
+      pair_scan2(d0p, d1p, lane, n, q0, q1);
+      Tr = readlane_d(q0.x, 63) + readlane_d(q1.x, 63);
+    }
+    if (tid <= r && (tid > rk || tid == r)) a.trace[(size_t)h * (r + 1) + tid] = tid < r ? 0.0 : Tr;
   }
+  if (a.pivots && tid < r) a.pivots[(size_t)h * r + tid] = tid < rk ? s_pivots[tid] : -1;
   if (tid == 0) {
     a.rank[h] = rk;
     a.flags[h] = flg;
-    if (a.trace)
-      for (int t = rk + 1; t <= r; ++t) a.trace[(size_t)h * (r + 1) + t] = 0.0;
-    if (a.pivots)
-      for (int t = rk; t < r; ++t) a.pivots[(size_t)h * r + t] = -1;
   }
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -338,10 +354,11 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
   __bf16* s_Ks = reinterpret_cast<__bf16*>(s_dyn + S::KS_OFF);
   __bf16* s_Wp = reinterpret_cast<__bf16*>(s_dyn + S::WP_OFF);
   float* s_Wden = reinterpret_cast<float*>(s_dyn + S::WDEN_OFF);
-  float (*s_L)[R + 1] = reinterpret_cast<float (*)[R + 1]>(s_dyn + S::L_OFF);
+  float (*s_L)[S::LS] = reinterpret_cast<float (*)[S::LS]>(s_dyn + S::L_OFF);
   if (tid < R) {
 #pragma unroll
     for (int j = 0; j < R; ++j) s_L[tid][j] = lrow[j];
+    s_L[tid][R] = tid < rk ? 1.0f / lrow[tid] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < KSV; ++i) {
@@ -367,31 +384,29 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
   for (int c0 = 0; c0 < 2 * NT; c0 += CH) {
     __syncthreads();
     if (ra >= c0 && ra < c0 + CH) {
+      // the thread's two rows are adjacent columns of F^T and V^T: one 32-bit store per pair
+      const int ii = ra - c0;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int row = ra + p, ii = row - c0;
+      for (int j = 0; j < R; ++j) {
+        __bf16 ha, la, hb, lb;
+        split_bf16(fr[0][j], ha, la);
+        split_bf16(fr[1][j], hb, lb);
+        *reinterpret_cast<uint32_t*>(FtH + j * CH + ii) =
+            (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+        *reinterpret_cast<uint32_t*>(FtL + j * CH + ii) =
+            (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+      }
+      const uint4* srca = reinterpret_cast<const uint4*>(Vh + (size_t)ra * DV);
+      const uint4* srcb = reinterpret_cast<const uint4*>(Vh + (size_t)(ra + 1) * DV);
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          __bf16 hi, lo;
-          split_bf16(fr[p][j], hi, lo);
-          FtH[j * CH + ii] = hi;
-          FtL[j * CH + ii] = lo;
-        }
-        if (row < n) {
-          const uint4* src = reinterpret_cast<const uint4*>(Vh + (size_t)row * DV);
+      for (int q = 0; q < DV / 8; ++q) {
+        const uint4 va4 = va ? srca[q] : uint4{0u, 0u, 0u, 0u};
+        const uint4 vb4 = vb ? srcb[q] : uint4{0u, 0u, 0u, 0u};
+        const uint32_t wa[4] = {va4.x, va4.y, va4.z, va4.w}, wb[4] = {vb4.x, vb4.y, vb4.z, vb4.w};
 #pragma unroll
-          for (int q = 0; q < DV / 8; ++q) {
-            const uint4 v = src[q];
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              Vt[(8 * q + 2 * e) * CH + ii] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e] & 0xffffu));
-              Vt[(8 * q + 2 * e + 1) * CH + ii] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e] >> 16));
-            }
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < DV; ++c) Vt[c * CH + ii] = (__bf16)0.f;
+        for (int e = 0; e < 4; ++e) {
+          *reinterpret_cast<uint32_t*>(Vt + (8 * q + 2 * e) * CH + ii) = (wa[e] & 0xffffu) | (wb[e] << 16);
+          *reinterpret_cast<uint32_t*>(Vt + (8 * q + 2 * e + 1) * CH + ii) = (wa[e] >> 16) | (wb[e] & 0xffff0000u);
         }
       }
     }
@@ -443,7 +458,7 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     for (int t = R - 1; t >= 0; --t) {
       float w = 0.f;
       if (t < rk) {
-        w = xv[t] / s_L[t][t];
+        w = xv[t] * s_L[t][R];
 #pragma unroll
         for (int j = 0; j < t; ++j) xv[j] = fmaf(-s_L[t][j], w, xv[j]);
       }
