@@ -156,8 +156,10 @@ __device__ __forceinline__ void pair_scan2(float2 d0, float2 d1, int lane, int n
   q1 = {x1, x1 - m1b, m1a > 0.0, m1b > 0.0};
 }
 
+// d = dv = 64 keeps to 256 registers, so that two waves fit a SIMD and three workgroups a CU
+// (the short heads run 768 at a time at n = 197).
 template <int D, int DV, int R, int NT>
-__global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
+__global__ void __launch_bounds__(NT, (D == 64 && DV == 64) ? 2 : 1) resident_kernel(ResidentArgs a) {
   using S = ResidentSmem<D, DV, R, NT>;
   constexpr int NW = S::NW, D2 = D / 2, FS = S::FS, CH = S::CH, DGS = S::DGS;
   static_assert(NW == 2, "two waves per head");
@@ -299,6 +301,18 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     __syncthreads();
   });
   __syncthreads();  // a breakdown step leaves the loop before its barrier
+  // the thread's two value rows, requested now (the key registers are free) so that their
+  // latency overlaps the hand-over; zero past the last key
+  uint4 vra[DV / 8], vrb[DV / 8];
+  if (a.O) {
+    const uint4* srca = reinterpret_cast<const uint4*>(a.V + ((size_t)h * n + ra) * DV);
+    const uint4* srcb = reinterpret_cast<const uint4*>(a.V + ((size_t)h * n + ra + 1) * DV);
+#pragma unroll
+    for (int q = 0; q < DV / 8; ++q) {
+      vra[q] = va ? srca[q] : uint4{0u, 0u, 0u, 0u};
+      vrb[q] = vb ? srcb[q] : uint4{0u, 0u, 0u, 0u};
+    }
+  }
 
   // the trace after the last step when all r steps completed, zero past a breakdown step (the
   // steps taken stored theirs in the loop); pivots, -1 past the rank
@@ -380,7 +394,6 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
   for (int k = 0; k < TPW; ++k)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
-  const uint16_t* Vh = a.V + (size_t)h * n * DV;
   for (int c0 = 0; c0 < 2 * NT; c0 += CH) {
     __syncthreads();
     if (ra >= c0 && ra < c0 + CH) {
@@ -396,13 +409,10 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
         *reinterpret_cast<uint32_t*>(FtL + j * CH + ii) =
             (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
       }
-      const uint4* srca = reinterpret_cast<const uint4*>(Vh + (size_t)ra * DV);
-      const uint4* srcb = reinterpret_cast<const uint4*>(Vh + (size_t)(ra + 1) * DV);
 #pragma unroll
       for (int q = 0; q < DV / 8; ++q) {
-        const uint4 va4 = va ? srca[q] : uint4{0u, 0u, 0u, 0u};
-        const uint4 vb4 = vb ? srcb[q] : uint4{0u, 0u, 0u, 0u};
-        const uint32_t wa[4] = {va4.x, va4.y, va4.z, va4.w}, wb[4] = {vb4.x, vb4.y, vb4.z, vb4.w};
+        const uint32_t wa[4] = {vra[q].x, vra[q].y, vra[q].z, vra[q].w};
+        const uint32_t wb[4] = {vrb[q].x, vrb[q].y, vrb[q].z, vrb[q].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           *reinterpret_cast<uint32_t*>(Vt + (8 * q + 2 * e) * CH + ii) = (wa[e] & 0xffffu) | (wb[e] << 16);
@@ -449,22 +459,31 @@ __global__ void __launch_bounds__(NT) resident_kernel(ResidentArgs a) {
     }
   }
   __syncthreads();
-  // backward substitution L^T W = X, one column per thread
+  // backward substitution L^T W = X, one column per thread, W in place of X.  Rows at and past
+  // the rank need no test: their L rows, reciprocal diagonals and X rows are all zero, so
+  // they solve to zero and subtract nothing.
   for (int c = tid; c <= DV; c += NT) {
     float xv[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) xv[j] = Xs[j * S::XP + c];
 #pragma unroll
     for (int t = R - 1; t >= 0; --t) {
-      float w = 0.f;
-      if (t < rk) {
-        w = xv[t] * s_L[t][R];
+      xv[t] *= s_L[t][R];
 #pragma unroll
-        for (int j = 0; j < t; ++j) xv[j] = fmaf(-s_L[t][j], w, xv[j]);
-      }
-      if (a.W && t < r) a.W[((size_t)h * r + t) * (DV + 1) + c] = w;
-      if (c < DV) s_Wp[c * S::WPP + perm32(t)] = (__bf16)w;
-      else s_Wden[t] = w;
+      for (int j = 0; j < t; ++j) xv[j] = fmaf(-s_L[t][j], xv[t], xv[j]);
+    }
+    if (a.W) {
+      float* Wc = a.W + (size_t)h * r * (DV + 1) + c;
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+        if (t < r) Wc[(size_t)t * (DV + 1)] = xv[t];
+    }
+    if (c < DV) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) s_Wp[c * S::WPP + perm32(t)] = (__bf16)xv[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < R; ++t) s_Wden[t] = xv[t];
     }
   }
   __syncthreads();
