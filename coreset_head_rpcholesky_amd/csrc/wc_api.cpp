@@ -455,8 +455,12 @@ wc::AttendArgs cache_args(const wc_problem& p, const CacheLayout& C, const void*
   return a;
 }
 
+// A few bf16 queries per head take the decode kernel; more queries, or fp32, the attention
+// kernels with the coreset split.
+bool decode_kernel_path(const wc_problem& p) { return p.dtype == WC_BF16 && p.m <= wc::kDecodeMaxQueries; }
+
 size_t decode_ws_bytes(const wc_problem& p, int rows) {
-  const int ns = attend_split(p, (size_t)p.m, (size_t)rows);
+  const int ns = decode_kernel_path(p) ? wc::decode_splits(rows) : attend_split(p, (size_t)p.m, (size_t)rows);
   return ns > 1 ? align_up((size_t)p.heads * ns * p.m * (p.dv + 1) * 4) : 0;
 }
 
@@ -675,9 +679,13 @@ wc_status wc_decode(const wc_problem* p, const void* Q, const void* cache, int32
   const CacheLayout C = make_cache_layout(*p, capacity);
   wc::AttendArgs a = cache_args(*p, C, cache, capacity);
   a.Q = Q; a.m = p->m; a.scan_rows = rows;
+  a.O = O; a.flags = flags;
+  if (decode_kernel_path(*p)) {
+    a.Ypart = need > 0 ? static_cast<float*>(ws) : nullptr;
+    return dev(wc::launch_decode(a, static_cast<hipStream_t>(stream)));
+  }
   a.nsplit = attend_split(*p, (size_t)p->m, (size_t)rows);
   a.Ypart = a.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
-  a.O = O; a.flags = flags;
   return dev(wc::launch_attend_core(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -635,6 +635,117 @@ __global__ void __launch_bounds__(64) attend_reduce_kernel(AttendArgs a) {
   }
 }
 
+// A few queries per head over a bf16 staged coreset (the compressed cache's decode step).  Each
+// wave takes one 64-row chunk (a workgroup of 16 covers a 1024-row cache alone): lanes over the rows for the scores (the chunk's key pieces are
+// 64 consecutive 16-byte units per column group) and over the value columns for
+// Y = sum_j p_j W[j, :] (a 16-byte unit of W^T holds 8 permuted positions of one column, whose
+// probabilities sit side by side in LDS).  The normaliser uses the fp32 W[:, dv].  The waves
+// of a workgroup are summed in LDS; one workgroup per (chunk group, head, query) writes either
+// O (when it covers every row in use) or an fp32 partial for the split reduction.
+template <int D, int DV>
+__global__ void __launch_bounds__(64 * kDecodeWaves) decode_kernel(AttendArgs a) {
+  constexpr int NCOL = DV / 64;  // value columns per lane
+  const int sp = blockIdx.x, h = blockIdx.y, q = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int rp = staged_rows(a), rows = a.scan_rows;
+  const int ch = sp * kDecodeWaves + wid, row = ch * 64 + lane;
+  const bool live = ch * 64 < rows;  // wave-uniform
+  __shared__ __attribute__((aligned(16))) float s_p[kDecodeWaves][64];
+  __shared__ float s_y[kDecodeWaves][DV + 1];
+  // the chunk's W^T units are requested first, so that their latency overlaps the key loads
+  const uint4* wt = reinterpret_cast<const uint4*>(a.Wph + (size_t)h * DV * rp) + (size_t)ch * 8 * DV;
+  uint4 wv[8][NCOL];
+  if (live) {
+#pragma unroll
+    for (int G = 0; G < 8; ++G)
+#pragma unroll
+      for (int i = 0; i < NCOL; ++i) wv[G][i] = wt[G * DV + lane + 64 * i];
+  }
+  // score as a base-2 exponent: the query is scaled by beta log2(e) and rounded to bf16, as in
+  // the attention kernels
+  float sc = 0.f;
+  if (live) {
+    const uint4* Qv = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)h * a.m + q) * D);
+    const uint4* kc = reinterpret_cast<const uint4*>(a.KSh + (size_t)h * rp * D) + (size_t)ch * 8 * D;
+    const float bl2e = a.beta_log2e;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int dg = 0; dg < D / 8; ++dg) {
+      const uint4 qr = Qv[dg];
+      const uint4 kv = kc[dg * 64 + lane];
+      const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w}, kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 lo = (__bf16)(__uint_as_float(qw[e] << 16) * bl2e);
+        const __bf16 hi = (__bf16)(__uint_as_float(qw[e] & 0xffff0000u) * bl2e);
+        const bf16x2 qq = {lo, hi};
+        if (e & 1) s1 = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf16x2, kw[e]), s1, false);
+        else s0 = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf16x2, kw[e]), s0, false);
+      }
+    }
+    sc = s0 + s1;
+  }
+  const bool in = row < rows;
+  const float p = in ? __builtin_amdgcn_exp2f(sc) : 0.f;
+  float dn = in ? p * a.Wden[(size_t)h * rp + row] : 0.f;
+  s_p[wid][perm32_a(lane)] = p;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dn += __shfl_xor(dn, o, 64);
+  __syncthreads();
+  float y[NCOL];
+#pragma unroll
+  for (int i = 0; i < NCOL; ++i) y[i] = 0.f;
+  if (live) {
+#pragma unroll
+    for (int G = 0; G < 8; ++G) {
+      const float4 pa = *reinterpret_cast<const float4*>(&s_p[wid][8 * G]);
+      const float4 pb = *reinterpret_cast<const float4*>(&s_p[wid][8 * G + 4]);
+#pragma unroll
+      for (int i = 0; i < NCOL; ++i) {
+        const uint4 w = wv[G][i];
+        float acc = y[i];
+        acc = fmaf(pa.x, __uint_as_float(w.x << 16), acc);
+        acc = fmaf(pa.y, __uint_as_float(w.x & 0xffff0000u), acc);
+        acc = fmaf(pa.z, __uint_as_float(w.y << 16), acc);
+        acc = fmaf(pa.w, __uint_as_float(w.y & 0xffff0000u), acc);
+        acc = fmaf(pb.x, __uint_as_float(w.z << 16), acc);
+        acc = fmaf(pb.y, __uint_as_float(w.z & 0xffff0000u), acc);
+        acc = fmaf(pb.z, __uint_as_float(w.w << 16), acc);
+        acc = fmaf(pb.w, __uint_as_float(w.w & 0xffff0000u), acc);
+        y[i] = acc;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NCOL; ++i) s_y[wid][lane + 64 * i] = y[i];
+  if (lane == 0) s_y[wid][DV] = dn;
+  __syncthreads();
+  if (wid != 0) return;
+  float yt[NCOL];
+#pragma unroll
+  for (int i = 0; i < NCOL; ++i) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) t += s_y[w][lane + 64 * i];
+    yt[i] = t;
+  }
+  float dt = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves; ++w) dt += s_y[w][DV];
+  if (gridDim.x == 1) {
+    if (lane == 0 && !(dt > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
+    const float inv = 1.0f / dt;
+    uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * a.m + q) * DV;
+#pragma unroll
+    for (int i = 0; i < NCOL; ++i) O[lane + 64 * i] = bf16_bits((__bf16)(yt[i] * inv));
+  } else {
+    float* Yp = a.Ypart + (((size_t)h * gridDim.x + sp) * a.m + q) * (DV + 1);
+#pragma unroll
+    for (int i = 0; i < NCOL; ++i) Yp[lane + 64 * i] = yt[i];
+    if (lane == 0) Yp[DV] = dt;
+  }
+}
+
 template <typename T, int D, int DV>
 static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st);
 
@@ -707,6 +818,31 @@ hipError_t launch_attend_append(const AttendArgs& a, hipStream_t st) { WC_ATTEND
 hipError_t launch_attend_core(const AttendArgs& a, hipStream_t st) {
   if (a.m == 0) return hipSuccess;
   WC_ATTEND_DISPATCH(run_attend_core)
+}
+
+template <typename T, int D, int DV>
+static hipError_t run_decode(const AttendArgs& a, hipStream_t st) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;
+  } else {
+    const int ns = decode_splits(a.scan_rows);
+    hipLaunchKernelGGL((decode_kernel<D, DV>), dim3(ns, a.H, a.m), dim3(64 * kDecodeWaves), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1) return e;
+    AttendArgs r = a;
+    r.nsplit = ns;
+    r.Yout = nullptr;
+    hipLaunchKernelGGL((attend_reduce_kernel<T, DV>), dim3(a.m, a.H), dim3(64), 0, st, r);
+    return hipGetLastError();
+  }
+}
+
+hipError_t launch_decode(const AttendArgs& a, hipStream_t st) {
+  if (a.m == 0) return hipSuccess;
+  if (!a.bf16 || a.m > kDecodeMaxQueries || a.scan_rows < 1 || a.scan_rows > staged_rows(a) || !a.Q || !a.O ||
+      (decode_splits(a.scan_rows) > 1 && !a.Ypart))
+    return hipErrorInvalidValue;
+  WC_ATTEND_DISPATCH(run_decode)
 }
 
 hipError_t launch_attend_all_keys(const AttendArgs& a, hipStream_t st) {

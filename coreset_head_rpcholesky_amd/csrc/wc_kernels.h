@@ -156,6 +156,16 @@ hipError_t launch_attend_prep(const AttendArgs& a, hipStream_t st);
 hipError_t launch_attend_append(const AttendArgs& a, hipStream_t st);
 // The attention proper over already staged rows (no staging).
 hipError_t launch_attend_core(const AttendArgs& a, hipStream_t st);
+// Decode: at most kDecodeMaxQueries bf16 queries per head over staged rows [0, scan_rows),
+// kDecodeWaves 64-row chunks per workgroup; with more than one workgroup per head the fp32
+// partials go to Ypart [H][decode_splits(scan_rows)][m][dv+1] and a reduction writes O.
+constexpr int kDecodeWaves = 16;
+constexpr int kDecodeMaxQueries = 8;
+__host__ __device__ inline int decode_splits(int rows) {
+  const int chunks = (rows + 63) / 64;
+  return (chunks + kDecodeWaves - 1) / kDecodeWaves;
+}
+hipError_t launch_decode(const AttendArgs& a, hipStream_t st);
 
 // ---- union weights of the divide-and-conquer forward: H_SS^+ X over all bins' pivots ----
 struct UnionArgs {

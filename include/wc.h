@@ -229,7 +229,10 @@ wc_status wc_cache_append(const wc_problem* p, const void* K_new, const void* V_
 wc_status wc_decode_workspace_bytes(const wc_problem* p, int32_t rows, size_t* bytes);
 
 /* Attention of Q [heads][m][d] over rows [0, rows) of the cache (1 <= rows <= capacity);
- * O [heads][m][dv] in the problem's dtype; WC_FLAG_DENOM is OR-ed into flags [heads].      */
+ * O [heads][m][dv] in the problem's dtype; WC_FLAG_DENOM is OR-ed into flags [heads].
+ * bf16 problems with m <= 8 run a decode kernel (one workgroup per 1024 rows per head and
+ * query, fp32 probabilities and normaliser, a split reduction past 1024 rows); others run the
+ * attention kernels with the rows split over workgroups.                                    */
 wc_status wc_decode(const wc_problem* p, const void* Q, const void* cache, int32_t capacity,
                     int32_t rows, void* O, uint32_t* flags, void* ws, size_t ws_bytes,
                     void* stream);

@@ -118,3 +118,27 @@ def test_decode_matches_forward(wc, B):
     O = host(wc.wc_decode(dev(Q, "bf16"), c["cache"], r, r, 64)[0])
     assert np.array_equal(host(f["pivots"]), host(c["pivots"]))
     assert rel(O, host(f["O"])) < 5e-3
+
+
+@pytest.mark.parametrize("d,dv,n,m", [(128, 128, 1000, 1), (64, 128, 300, 8), (128, 64, 2500, 3),
+                                      (64, 64, 64, 2), (64, 64, 257, 1)])
+def test_decode_kernel_few_queries(wc, d, dv, n, m):
+    """At most 8 bf16 queries per head take the decode kernel: one workgroup when the rows fit
+    (up to 1024), split partials and a reduction beyond.  Exact rows only, so the oracle is exact
+    attention; the same queries padded to 9 (the attention kernels' path) agree closely."""
+    import torch
+
+    H = 3
+    Q, K, V = synth.random_inputs(H, n, 9, d, dv, seed=840 + n + m, dtype="bf16", kind="iid_clip", clip=2.0)
+    cap = n + 70
+    p = wc.problem(H, n, 9, d, dv, 1, wc.WC_BF16)
+    cache = torch.zeros(wc.wc_cache_bytes(p, cap), dtype=torch.uint8, device="cuda")
+    wc.wc_cache_append(cache, dev(K, "bf16"), dev(V, "bf16"), 0, cap)
+    Qd = dev(Q, "bf16")
+    O, flags = wc.wc_decode(Qd[:, :m].contiguous(), cache, cap, n, dv)
+    O = host(O)
+    assert np.all(host(flags) == 0)
+    for h in range(H):
+        assert rel(O[h], ow.exact_attention(Q[h][:m], K[h], V[h])) < TOL["bf16"]
+    O9 = host(wc.wc_decode(Qd, cache, cap, n, dv)[0])
+    assert rel(O, O9[:, :m]) < 5e-3, rel(O, O9[:, :m])
