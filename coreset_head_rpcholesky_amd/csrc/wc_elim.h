@@ -71,6 +71,66 @@ __device__ __forceinline__ bool elim_block(float* sA, const float* hd, float tol
   return dependent;
 }
 
+// The same elimination of a 64 x 64 block by one wave, without barriers (same results up to
+// rounding order).  Called by every thread of the workgroup; wave 0 works and the others wait at
+// the final barrier.  Lane i holds row i of the block and column i of G.  Step j reads column j
+// of the block (every lane's A[i][j], written to LDS at the end of step j-1) and takes the
+// pivot p = A[j][j] and the leave-out scale hd[j] by readlane; rows i > j subtract
+// f_i = A[i][j] / p times row j, whose entries past j equal column j's (the block is
+// symmetric); column c of G subtracts f_i G[j][c] from its rows i > j.  Row j of
+// M = G[j][:] rsq(p) (G's row j is final once step j begins) goes into row j of sA, which was
+// read into registers at the start.  One wave's LDS accesses complete in order, so no barrier
+// separates a column's write from its reads; the two column buffers alternate.  Returns, in
+// thread 0, whether a point with hd > 0 was left out.
+template <int P>
+__device__ __forceinline__ bool elim_block64_wave(float* sA, const float* hd, float tol, float (*sCol)[64]) {
+  constexpr int B = 64;
+  bool dependent = false;
+  __syncthreads();  // the block and hd are complete in LDS
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const float hdl = hd[lane];  // leave-out scale of the lane's point, broadcast by readlane
+    float v[B], g[B];
+#pragma unroll
+    for (int e = 0; e < B; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(sA + lane * P + e);
+      v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
+    }
+#pragma unroll
+    for (int e = 0; e < B; ++e) g[e] = e == lane ? 1.f : 0.f;
+    sCol[0][lane] = v[0];
+    static_for<0, B>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const float* col = sCol[j & 1];
+      const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), j));
+      const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hdl), j));
+      const bool keep = p > tol * hj;
+      dependent |= !keep && hj > 0.f;
+      sA[j * P + lane] = g[j] * (keep ? __builtin_amdgcn_rsqf(p) : 0.f);
+      if (keep) {
+        const float rp = __builtin_amdgcn_rcpf(p);
+        const float f = v[j] * rp, t = g[j] * rp;
+        constexpr int k0 = (j + 1) & ~3;
+#pragma unroll
+        for (int k4 = k0; k4 < B; k4 += 4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(col + k4);
+          const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (k4 + e > j) {
+              v[k4 + e] = fmaf(-f, c[e], v[k4 + e]);
+              g[k4 + e] = fmaf(-c[e], t, g[k4 + e]);
+            }
+          }
+        }
+      }
+      if constexpr (j + 1 < B) sCol[(j + 1) & 1][lane] = v[j + 1];
+    });
+  }
+  __syncthreads();
+  return dependent;
+}
+
 // Copy M (B x B, pitch P in LDS, as elim_block leaves it) to global memory, row-major with
 // leading dimension B, by the 4 B threads of the workgroup.
 template <int B, int P>

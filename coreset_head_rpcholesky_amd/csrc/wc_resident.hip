@@ -88,13 +88,6 @@ __device__ __forceinline__ float dot_prefix(const PA& a, const PB& b) {
   return c0 + c1;
 }
 
-template <int I, int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-  if constexpr (I < N) {
-    fn(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(fn);
-  }
-}
 
 // Position of coreset index j inside a permuted 32-chunk, so that the accumulator layout
 // of the score MFMA feeds the value MFMA directly (see the attention phase below).

@@ -155,14 +155,13 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
 }
 
 // ---- diag: M_kk = inverse of the Cholesky factor of the kept part of A_kk -------------------
-// A whole 256-thread workgroup eliminates the (already updated) block in sA with the leave-out
-// rule (elim_block); left-out points of valid slots set WC_DFLAG_DEPENDENT.
-// The diagonal entries H_jj (the scale of the leave-out test) are staged in LDS first: read
-// from global memory inside the pivot loop, each step would wait for one load.
+// Wave 0 of the workgroup eliminates the (already updated) block in sA with the leave-out rule
+// (elim_block64_wave); left-out points of valid slots set WC_DFLAG_DEPENDENT.  The diagonal
+// entries H_jj (the scale of the leave-out test) are staged in LDS first.
 __device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, float (*sA)[kLP],
                                            float (*sCol)[kUB], float (*sRow)[kUB], float* sHd) {
   if (threadIdx.x < kUB) sHd[threadIdx.x] = a.Hd[(size_t)h * a.rp + (size_t)k * kUB + threadIdx.x];
-  const bool dependent = elim_block<kUB, kLP>(&sA[0][0], sHd, a.tol, sCol, sRow);
+  const bool dependent = elim_block64_wave<kLP>(&sA[0][0], sHd, a.tol, sCol);
   store_block<kUB, kLP>(&sA[0][0], a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB);
   if (dependent && threadIdx.x == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
 }
