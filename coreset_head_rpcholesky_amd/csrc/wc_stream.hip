@@ -650,6 +650,96 @@ __global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A) {
   for (int jj = 0; jj < B; ++jj) G[(size_t)jj * n + i] = __builtin_amdgcn_exp2f(hk[jj] * a.beta_log2e) - acc[jj];
 }
 
+// The same candidate columns for bf16 keys on the matrix cores.  A workgroup takes 128 rows (32
+// per wave); the candidates are the M dimension and the rows the N dimension of 32 x 32 tiles,
+// so that a lane holds one row and every store of G is 32 consecutive rows.
+//   kernel part: bf16 MFMAs, candidate keys from LDS, the wave's own key rows straight from
+//                memory (the products of bf16 values are exact, the sums fp32);
+//   exp2 in place, then the factor part on fp32 MFMAs (32 x 32 x 2): the candidates' factor
+//   rows, negated, staged in LDS 64 columns at a time, the rows' factor columns from memory,
+//   accumulated onto the exponentials.
+template <int D, int B>
+__global__ void __launch_bounds__(256) blk_column_mfma_kernel(BlockRpcArgs A) {
+  constexpr int NC = (B + 31) / 32, BP = 32 * NC;  // candidate tiles (16 candidates use half of one)
+  constexpr int KP = D + 8;                         // padded candidate-key row (bf16)
+  constexpr int FP = BP + 1;                        // padded factor-chunk row (fp32)
+  __shared__ __attribute__((aligned(16))) uint16_t sKS[BP * KP];
+  __shared__ __attribute__((aligned(16))) float sFS[64 * FP];
+  __shared__ int sC[BP];
+  const StreamRpcArgs& a = A.s;
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int n = a.n;
+  if (blk_done(A, h) || A.cand[(size_t)h * B] < 0) return;
+  const int f0 = a.rank[h];
+  const int row = blockIdx.x * 128 + (tid >> 6) * 32 + l32;
+  const bool rv = row < n;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.K) + (size_t)h * n * D;
+  const float* F = a.F + (size_t)h * a.r * n;
+  if (tid < BP) sC[tid] = tid < B ? A.cand[(size_t)h * B + tid] : -1;
+  // the wave's key rows, requested before the staging barrier
+  bf16x8 kb[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (rv) kb[kk] = *reinterpret_cast<const bf16x8*>(K + (size_t)row * D + 16 * kk + 8 * g);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kb[kk][e] = (__bf16)0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < BP * D / 8; e += 256) {
+    const int jj = e / (D / 8), q = e % (D / 8), sj = sC[jj];
+    const uint4 v = sj >= 0 ? reinterpret_cast<const uint4*>(K + (size_t)sj * D)[q] : uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(sKS + jj * KP + 8 * q) = v;
+  }
+  __syncthreads();
+  f32x16 acc[NC];
+#pragma unroll
+  for (int t = 0; t < NC; ++t) acc[t] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int t = 0; t < NC; ++t)
+      acc[t] = mfma32(*reinterpret_cast<const bf16x8*>(sKS + (32 * t + l32) * KP + 16 * kk + 8 * g), kb[kk], acc[t]);
+  const float bl2e = a.beta_log2e;
+#pragma unroll
+  for (int t = 0; t < NC; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = __builtin_amdgcn_exp2f(acc[t][v] * bl2e);
+  for (int c0 = 0; c0 < f0; c0 += 64) {
+    const int cc = min(64, f0 - c0);
+    __syncthreads();
+    for (int e = tid; e < 64 * BP; e += 256) {
+      const int c = e / BP, jj = e % BP, sj = sC[jj];
+      sFS[c * FP + jj] = (c < cc && sj >= 0) ? -F[(size_t)(c0 + c) * n + sj] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < cc; c += 16) {
+      float fb[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int ck = c + 2 * m + g;
+        fb[m] = (rv && ck < cc) ? F[(size_t)(c0 + ck) * n + row] : 0.f;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int ck = c + 2 * m + g;
+#pragma unroll
+        for (int t = 0; t < NC; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(sFS[ck * FP + 32 * t + l32], fb[m], acc[t], 0, 0, 0);
+      }
+    }
+  }
+  if (!rv) return;
+  float* G = A.G + (size_t)h * B * n;
+#pragma unroll
+  for (int t = 0; t < NC; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int jj = 32 * t + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (jj < B) G[(size_t)jj * n + row] = acc[t][v];
+    }
+}
+
 template <typename T, int D, int B>
 __global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int k) {
   constexpr int P = B + 4;
@@ -803,7 +893,10 @@ static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
   const int rounds = kBlockDraws * a.r / B;
   for (int k = 0; k < rounds; ++k) {
     hipLaunchKernelGGL(blk_sample_kernel, dim3(a.H), dim3(NT), lds, st, A, k);
-    hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((blk_column_mfma_kernel<D, B>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, A);
+    else
+      hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A);
     hipLaunchKernelGGL((blk_factor_kernel<T, D, B>), dim3(a.H), dim3(4 * B), 0, st, A, k);
     hipLaunchKernelGGL((blk_apply_kernel<B>), grid, dim3(NT), 0, st, A, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;

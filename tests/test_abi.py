@@ -206,9 +206,13 @@ def test_cache_calls_validate_before_any_device_work(lib):
     assert lib.wc_decode(ctypes.byref(p), A, A, i32(256), i32(300), A, A, A, big, None) == 1
     assert lib.wc_decode(ctypes.byref(p), A, A, i32(256), i32(0), A, A, A, big, None) == 1
     out = ctypes.c_size_t(0)
+    # a few bf16 queries: up to 1024 rows in one workgroup (no workspace), more split over
+    # workgroups with fp32 partials: heads x splits x m x (dv + 1) floats
     assert lib.wc_decode_workspace_bytes(ctypes.byref(p), i32(256), ctypes.byref(out)) == 0
-    assert out.value > 0  # 2 heads x 1 query: the rows are split over workgroups
-    assert lib.wc_decode(ctypes.byref(p), A, A, i32(256), i32(256), A, A, None, 0, None) == 3
+    assert out.value == 0
+    assert lib.wc_decode_workspace_bytes(ctypes.byref(p), i32(2000), ctypes.byref(out)) == 0
+    assert out.value >= 2 * 2 * 1 * 65 * 4
+    assert lib.wc_decode(ctypes.byref(p), A, A, i32(2048), i32(2000), A, A, None, 0, None) == 3
     # unsupported problem
     assert lib.wc_decode(ctypes.byref(Problem(2, 4096, 1, 80, 64, 256, 1)), A, A, i32(256), i32(256),
                          A, A, A, big, None) == 2
