@@ -13,7 +13,7 @@ compute one by one:
 The divide-and-conquer forward at the same two sizes (64 and 16 bins, one pivot per step and
 block pivots) is checked the same way: pivots distinct and inside their bins, the first bin's
 pivots from the same Philox draws, the union weights and sampled outputs from the GPU's
-pivots."""
+pivots.  The largest supported coreset (r = 4096) is checked the same way on 8192 keys."""
 import numpy as np
 import pytest
 
@@ -159,3 +159,38 @@ def test_binned_full(wc, name, B, pb, h, nq):
     Oo, den, kappa = ow.attend(Q[h][qs], K[h], S, W, beta)
     ok = kappa < 1e6
     assert rel(O[h][qs][ok], Oo[ok]) < TOL["bf16"], rel(O[h][qs][ok], Oo[ok])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_max_r(wc, dtype):
+    """The largest supported coreset, r = 4096, on n = 8192 keys shaped like the KV-cache workload
+    (a well-conditioned kernel matrix, so the full rank is reached in fp32): the streaming pivot
+    loop over 4096 steps, the blocked solve over 64 blocks and the attention over 4096 rows,
+    checked as at full size: rank, flags, distinct pivots, non-increasing trace, the first
+    pivots from Philox, sampled factor rows, and the weights and outputs from the GPU's
+    pivots."""
+    import torch
+
+    H, n, m, d, dv, r = 1, 8192, 200, 128, 64, 4096
+    Q, K, V = synth.random_inputs(H, n, m, d, dv, seed=860, dtype=dtype, kind="kv_outlier")
+    Qd, Kd, Vd = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    out = forward_graph(wc, Qd, Kd, Vd, r, seed=7)
+    O, piv = host(out["O"]), host(out["pivots"])
+    assert np.all(host(out["rank"]) == r) and np.all(host(out["flags"]) == 0), (host(out["rank"]), host(out["flags"]))
+    del out
+    rpc = wc.wc_rpcholesky(Kd, r, seed=7, with_diag=False)
+    assert np.array_equal(host(rpc["pivots"]), piv)
+    S, trace = piv[0], host(rpc["trace"])[0]
+    beta = 1.0 / np.sqrt(d)
+    assert len(set(S.tolist())) == r and S.min() >= 0 and S.max() < n
+    assert np.all(np.diff(trace) <= 1e-6 * trace[0])
+    assert np.array_equal(S[:3], ow.rpcholesky(K[0], 3, philox.pivot_uniforms(7, 0, 3), beta)["pivots"])
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([rng.choice(n, 40, replace=False), S[[0, 1, r // 2, r - 1]]])
+    Fr, _ = ow.factor_rows_given_pivots(K[0], S, rows, beta)
+    Fg = host(rpc["F"][0][:, torch.as_tensor(rows, device="cuda")]).T
+    assert rel(Fg, Fr) < 1e-3, rel(Fg, Fr)
+    Wo = ow.weights(K[0], V[0], S, beta)
+    Oo, den, kappa = ow.attend(Q[0], K[0], S, Wo, beta)
+    ok = kappa < 1e6
+    assert rel(O[0][ok], Oo[ok]) < TOL[dtype], rel(O[0][ok], Oo[ok])
