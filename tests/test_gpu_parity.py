@@ -215,3 +215,23 @@ def test_graph_replay_matches_eager(wc, n, dtype):
             assert torch.equal(out[k], ref[k]), (rep, k)
         wc.wc_forward(Qd, Kd, Vd, 32, seed=5, ws=ws)  # unrelated eager work in between
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,r", [(1, 1), (2, 1), (2, 2), (3, 3), (5, 2)])
+def test_tiny_heads(wc, dtype, n, r):
+    """Heads of one to five keys (bf16 on the resident kernel, fp32 on the streaming loop):
+    pivots and rank as the oracle's, O within the tolerance, and at r = n exact attention
+    (a single key gives O = its value row)."""
+    H, m = 3, 7
+    Q, K, V = synth.random_inputs(H, n, m, 64, 64, seed=870 + 10 * n + r, dtype=dtype, kind="iid_clip")
+    U = snapped(K, r)
+    out = wc.wc_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), r, u_forced=dev(U))
+    O, piv, rank, flags = host(out["O"]), host(out["pivots"]), host(out["rank"]), host(out["flags"])
+    for h in range(H):
+        ref = ow.forward(Q[h], K[h], V[h], r, U[h])
+        assert np.array_equal(piv[h], ref["pivots"]) and rank[h] == ref["rank"] == r
+        assert flags[h] == 0
+        assert rel(O[h], ref["O"]) < TOL[dtype], (h, rel(O[h], ref["O"]))
+        if r == n:
+            assert rel(O[h], ow.exact_attention(Q[h], K[h], V[h])) < TOL[dtype]
