@@ -94,7 +94,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   int rows, nblk, nchunk, chunk_rows, nsplit, rp;
   size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Wdh, Ypart;
-  size_t bcand, bslot, bG, bM, brounds;  // block pivot selection
+  size_t bcand, bslot, bG, bM, brounds, bFS;  // block pivot selection
   size_t total;
 };
 
@@ -143,6 +143,7 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
       L.bG = take(H * b * n * 4);
       L.bM = take(H * b * b * 4);
       L.brounds = take(H * 4);
+      L.bFS = take(H * r * b * 4);
     }
   }
   if (parts & kAttend) {
@@ -330,6 +331,7 @@ hipError_t run_rpc_block(const wc_problem& p, const Layout& L, void* ws, const v
   a.G = at<float>(ws, L.bG);
   a.M = at<float>(ws, L.bM);
   a.rounds = at<int32_t>(ws, L.brounds);
+  a.FS = at<float>(ws, L.bFS);
   return wc::launch_rpc_block(a, st);
 }
 

@@ -79,6 +79,7 @@ struct BlockRpcArgs {
   float* G;             // ws [H][b][n]  candidate columns minus what F explains
   float* M;             // ws [H][b][b]  inverse factor of the kept part of the candidate block
   int32_t* rounds;      // ws [H]        rounds applied so far (the residual's buffer parity)
+  float* FS;            // ws [H][r][b]  factor rows at the round's candidates, by factor column
 };
 hipError_t launch_rpc_block(const BlockRpcArgs& a, hipStream_t st);
 

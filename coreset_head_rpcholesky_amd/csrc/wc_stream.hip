@@ -650,21 +650,34 @@ __global__ void __launch_bounds__(NT) blk_column_kernel(BlockRpcArgs A) {
   for (int jj = 0; jj < B; ++jj) G[(size_t)jj * n + i] = __builtin_amdgcn_exp2f(hk[jj] * a.beta_log2e) - acc[jj];
 }
 
+// The factor rows at the round's candidates, negated, -F[S, :f0], into FS [f0][b] (by factor
+// column), so that the column kernel reads them with coalesced loads and accumulates them onto
+// the exponentials as they are.  Grid (blocks of 256 entries, heads).
+template <int B>
+__global__ void __launch_bounds__(256) blk_gather_kernel(BlockRpcArgs A) {
+  const StreamRpcArgs& a = A.s;
+  const int h = blockIdx.y;
+  if (blk_done(A, h) || A.cand[(size_t)h * B] < 0) return;
+  const int f0 = a.rank[h];
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= f0 * B) return;
+  const int c = e / B, jj = e % B, sj = A.cand[(size_t)h * B + jj];
+  A.FS[(size_t)h * a.r * B + e] = sj >= 0 ? -a.F[((size_t)h * a.r + c) * a.n + sj] : 0.f;
+}
+
 // The same candidate columns for bf16 keys on the matrix cores.  A workgroup takes 128 rows (32
 // per wave); the candidates are the M dimension and the rows the N dimension of 32 x 32 tiles,
 // so that a lane holds one row and every store of G is 32 consecutive rows.
 //   kernel part: bf16 MFMAs, candidate keys from LDS, the wave's own key rows straight from
 //                memory (the products of bf16 values are exact, the sums fp32);
 //   exp2 in place, then the factor part on fp32 MFMAs (32 x 32 x 2): the candidates' factor
-//   rows, negated, staged in LDS 64 columns at a time, the rows' factor columns from memory,
-//   accumulated onto the exponentials.
+//   rows (gathered for the round by blk_gather_kernel), negated, and the rows' factor columns,
+//   both read straight from memory, accumulated onto the exponentials.
 template <int D, int B>
 __global__ void __launch_bounds__(256) blk_column_mfma_kernel(BlockRpcArgs A) {
   constexpr int NC = (B + 31) / 32, BP = 32 * NC;  // candidate tiles (16 candidates use half of one)
   constexpr int KP = D + 8;                         // padded candidate-key row (bf16)
-  constexpr int FP = BP + 1;                        // padded factor-chunk row (fp32)
   __shared__ __attribute__((aligned(16))) uint16_t sKS[BP * KP];
-  __shared__ __attribute__((aligned(16))) float sFS[64 * FP];
   __shared__ int sC[BP];
   const StreamRpcArgs& a = A.s;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -705,29 +718,33 @@ __global__ void __launch_bounds__(256) blk_column_mfma_kernel(BlockRpcArgs A) {
   for (int t = 0; t < NC; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t][v] = __builtin_amdgcn_exp2f(acc[t][v] * bl2e);
-  for (int c0 = 0; c0 < f0; c0 += 64) {
-    const int cc = min(64, f0 - c0);
-    __syncthreads();
-    for (int e = tid; e < 64 * BP; e += 256) {
-      const int c = e / BP, jj = e % BP, sj = sC[jj];
-      sFS[c * FP + jj] = (c < cc && sj >= 0) ? -F[(size_t)(c0 + c) * n + sj] : 0.f;
+  // factor part: 16 factor columns per batch; the candidates' rows from FS and this lane's
+  // row from F, both coalesced, no LDS and no barrier
+  // Loads use clamped indices and no conditions (a masked load compiles to a branch and a wait
+  // per load); factor columns past f0 are zeroed afterwards, and the lanes of rows past n or of
+  // candidate slots past b feed only outputs that are never stored.
+  const float* FSh = A.FS + (size_t)h * a.r * B;
+  const int rowc = rv ? row : n - 1;
+  int jc[NC];  // candidate slot of each tile's lane, clamped into [0, b)
+#pragma unroll
+  for (int t = 0; t < NC; ++t) jc[t] = 32 * t + l32 < B ? 32 * t + l32 : 0;
+  for (int c = 0; c < f0; c += 16) {
+    float fa[8][NC], fb[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int ck = min(c + 2 * m + g, f0 - 1);
+      fb[m] = F[(size_t)ck * n + rowc];
+#pragma unroll
+      for (int t = 0; t < NC; ++t) fa[m][t] = FSh[(size_t)ck * B + jc[t]];
     }
-    __syncthreads();
-    for (int c = 0; c < cc; c += 16) {
-      float fb[8];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int ck = c + 2 * m + g;
-        fb[m] = (rv && ck < cc) ? F[(size_t)(c0 + ck) * n + row] : 0.f;
-      }
+    for (int m = 0; m < 8; ++m)
+      if (c + 2 * m + g >= f0) fb[m] = 0.f;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int ck = c + 2 * m + g;
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int t = 0; t < NC; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(sFS[ck * FP + 32 * t + l32], fb[m], acc[t], 0, 0, 0);
-      }
-    }
+      for (int t = 0; t < NC; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[m][t], fb[m], acc[t], 0, 0, 0);
   }
   if (!rv) return;
   float* G = A.G + (size_t)h * B * n;
@@ -893,8 +910,10 @@ static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
   const int rounds = kBlockDraws * a.r / B;
   for (int k = 0; k < rounds; ++k) {
     hipLaunchKernelGGL(blk_sample_kernel, dim3(a.H), dim3(NT), lds, st, A, k);
-    if constexpr (sizeof(T) == 2)
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((blk_gather_kernel<B>), dim3((a.r * B + 255) / 256, a.H), dim3(256), 0, st, A);
       hipLaunchKernelGGL((blk_column_mfma_kernel<D, B>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, A);
+    }
     else
       hipLaunchKernelGGL((blk_column_kernel<T, D, B>), dim3(colgrid, a.H), dim3(NT), 0, st, A);
     hipLaunchKernelGGL((blk_factor_kernel<T, D, B>), dim3(a.H), dim3(4 * B), 0, st, A, k);
