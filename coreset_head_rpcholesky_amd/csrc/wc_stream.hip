@@ -461,128 +461,155 @@ __device__ __forceinline__ bool blk_done(const BlockRpcArgs& A, int h) {
   return A.s.rank[h] >= A.s.r || (A.s.flags[h] & WC_DFLAG_BREAKDOWN);
 }
 
-// One workgroup per head draws the round's b candidates one after the other, without
-// replacement: candidate j is the inverse-CDF draw on the round-start masses with the earlier
-// candidates' masses removed.  The running sums are not rebuilt: the target u T' (T' the mass
-// left) is moved past the intervals [C_{d-1}, C_d) of the earlier candidates d, taken in index
-// order, and then searched on the unchanged block masses and rows.
-__global__ void __launch_bounds__(NT) blk_sample_kernel(BlockRpcArgs A, int k) {
-  __shared__ double red[NW];
-  __shared__ int ired[NW];
-  __shared__ double s_x;
-  __shared__ int s_idx[64];     // candidates drawn so far, by index
-  __shared__ double s_lo[64];   // their running sum before them
-  __shared__ double s_m[64];    // their mass
-  __shared__ double s_flo, s_fm;
-  extern __shared__ __attribute__((aligned(16))) double s_pre[];  // [nblk] exclusive block sums
+__device__ __forceinline__ double lane_d(double x, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// One wave per head draws the round's b candidates one after the other, without replacement:
+// candidate j is the inverse-CDF draw on the round-start masses with the earlier candidates'
+// masses removed.  The running sums are not rebuilt: the target u T' (T' the mass left) is
+// moved past the intervals [C_{d-1}, C_d) of the earlier candidates d, taken in index order,
+// and then searched on the unchanged block masses and rows.  The block masses and their
+// exclusive sums sit in LDS for the round and the drawn candidates in registers (lane q the
+// q-th in index order); a draw is a wave scan for the shifted target, a wave search over the
+// blocks, one load of the chosen block's rows (RPT per lane), a wave scan and a shuffle to
+// insert the new candidate, with no barrier.
+template <int RPT>
+__global__ void __launch_bounds__(64) blk_sample_kernel(BlockRpcArgs A, int k) {
+  extern __shared__ __attribute__((aligned(16))) double s_blk[];  // [nblk] masses, [nblk] exclusive sums
   const StreamRpcArgs& a = A.s;
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const int n = a.n, nblk = a.nblk, rows = a.rows, B = A.b;
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const int n = a.n, nblk = a.nblk, B = A.b;
   int32_t* cand = A.cand + (size_t)h * B;
   if (blk_done(A, h)) return;
-  const double* part = (k & 1) ? a.part1 : a.part0;
+  double* s_part = s_blk;
+  double* s_pre = s_blk + nblk;
+  const double* part = ((k & 1) ? a.part1 : a.part0) + (size_t)h * nblk;
   const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
-  const int per = (nblk + NT - 1) / NT;
+  const int per = (nblk + 63) / 64;
   double mine = 0.0;
   for (int e = 0; e < per; ++e) {
-    const int bb = tid * per + e;
-    if (bb < nblk) mine += part[(size_t)h * nblk + bb];
+    const int bb = lane * per + e;
+    if (bb < nblk) {
+      const double v = part[bb];
+      s_part[bb] = v;
+      mine += v;
+    }
   }
-  double Ttot;
+  const double incl = wave_incl_scan(mine);
+  const double Ttot = lane_d(incl, 63);
   {
-    double run = block_excl_scan(mine, red, &Ttot);
+    double run = incl - mine;
     for (int e = 0; e < per; ++e) {
-      const int bb = tid * per + e;
+      const int bb = lane * per + e;
       if (bb < nblk) {
         s_pre[bb] = run;
-        run += part[(size_t)h * nblk + bb];
+        run += s_part[bb];
       }
     }
   }
   const int f0 = a.rank[h];
   if (!(Ttot > 0.0) || !__builtin_isfinite(Ttot)) {
     // no mass left: the loop stops (every later kernel of the head sees the flag or cand -1)
-    if (tid == 0) {
+    if (lane == 0) {
       a.flags[h] |= WC_DFLAG_BREAKDOWN | (__builtin_isfinite(Ttot) ? 0u : WC_DFLAG_NONFINITE);
       if (a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = __builtin_isfinite(Ttot) ? Ttot : 0.0;
     }
-    for (int j = tid; j < B; j += NT) cand[j] = -1;
+    for (int j = lane; j < B; j += 64) cand[j] = -1;
     return;
   }
-  if (tid == 0 && a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = Ttot;
+  if (lane == 0 && a.trace) a.trace[(size_t)h * (a.r + 1) + f0] = Ttot;
   const float* u = a.uniforms + (size_t)h * kBlockDraws * a.r + (size_t)k * B;
   double removed = 0.0;
   int nd = 0;
+  // the drawn candidates in index order, lane q holding the q-th: index, running sum before
+  // it and its mass
+  int c_idx = 0x7fffffff;
+  double c_lo = 0.0, c_m = 0.0;
   for (int j = 0; j < B; ++j) {
     const double Tl = Ttot - removed;
     if (!(Tl > 0.0)) {  // every index with mass is drawn: the round has fewer candidates
-      for (int jj = j + tid; jj < B; jj += NT) cand[jj] = -1;
+      for (int jj = j + lane; jj < B; jj += 64) cand[jj] = -1;
       break;
     }
-    __syncthreads();
-    if (tid == 0) {
-      double x = (double)u[j] * Tl;
-      for (int q = 0; q < nd; ++q)  // in index order, so later intervals see the shifted target
-        if (x >= s_lo[q]) x += s_m[q];
-      s_x = x;
-    }
-    __syncthreads();
-    const double x = s_x;
+    // Move the target past the earlier candidates' intervals in index order: with M_q the
+    // masses of the first q of them, the target ends at x + M_Q for the first Q whose interval
+    // x + M_Q does not reach (intervals in index order start in increasing order).
+    const double x0 = (double)u[j] * Tl;
+    const double mq = lane < nd ? c_m : 0.0;
+    const double Mx = wave_incl_scan(mq) - mq;  // M_lane
+    const uint64_t stop = __ballot(lane < nd && !(x0 + Mx >= c_lo)) | (nd < 64 ? (1ull << nd) : 0ull);
+    const int Q = stop ? __builtin_ctzll(stop) : 64;
+    const double x = Q == 0 ? x0 : x0 + lane_d(Mx + mq, Q - 1);
     // block holding x (the last block with mass if rounding put x at or past the total)
     int bc = 0x7fffffff, lastpos = -1;
     for (int e = 0; e < per; ++e) {
-      const int bb = tid * per + e;
+      const int bb = lane * per + e;
       if (bb < nblk) {
-        const double v = part[(size_t)h * nblk + bb];
+        const double v = s_part[bb];
         if (bc == 0x7fffffff && v > 0.0 && s_pre[bb] + v > x) bc = bb;
         if (v > 0.0) lastpos = bb;
       }
     }
-    int bstar = block_min_int(bc, ired);
-    if (bstar == 0x7fffffff) bstar = block_max_int(lastpos, ired);
-    // row inside it
-    const int rpt = rows / NT, r0 = bstar * rows;
-    double pm[4];
-    double tmass = 0.0;
-    for (int e = 0; e < rpt; ++e) {
-      const int i = r0 + tid * rpt + e;
-      pm[e] = (i < n) ? mass_of(dg_in[i]) : 0.0;
-      tmass += pm[e];
-    }
-    double btot;
-    __syncthreads();
-    const double rexcl = block_excl_scan(tmass, red, &btot);
-    int scand = 0x7fffffff;
-    double c = s_pre[bstar] + rexcl;
-    for (int e = 0; e < rpt; ++e) {
-      c += pm[e];
-      const int i = r0 + tid * rpt + e;
-      if (scand == 0x7fffffff && c > x && pm[e] > 0.0) scand = i;
-    }
-    const int s = block_min_int(scand, ired);
-    if (s != 0x7fffffff && tid == (s - r0) / rpt) {
-      // the thread holding row s records its interval [C_{s-1}, C_s) of the running sum
-      double lo = s_pre[bstar] + rexcl;
-      for (int e = 0; e < s - r0 - tid * rpt; ++e) lo += pm[e];
-      s_flo = lo;
-      s_fm = pm[s - r0 - tid * rpt];
-    }
-    __syncthreads();
-    if (s == 0x7fffffff || s >= n) {  // rounding left no row to claim x: no more candidates
-      for (int jj = j + tid; jj < B; jj += NT) cand[jj] = -1;
+    int bstar = wave_min_int(bc);
+    if (bstar == 0x7fffffff) bstar = -wave_min_int(-lastpos);
+    if (bstar < 0) {  // no block with mass (excluded by T > 0; kept as a guard)
+      for (int jj = j + lane; jj < B; jj += 64) cand[jj] = -1;
       break;
     }
-    if (tid == 0) {
-      cand[j] = s;
-      // insert into the index-ordered list of drawn candidates
-      int q = nd;
-      while (q > 0 && s_idx[q - 1] > s) {
-        s_idx[q] = s_idx[q - 1]; s_lo[q] = s_lo[q - 1]; s_m[q] = s_m[q - 1];
-        --q;
-      }
-      s_idx[q] = s; s_lo[q] = s_flo; s_m[q] = s_fm;
+    // row inside it: unconditional loads (clamped indices), rows past n weigh nothing
+    const int r0 = bstar * 64 * RPT;
+    float dv[RPT];
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) dv[e] = dg_in[min(r0 + lane * RPT + e, n - 1)];
+    double pm[RPT];
+    double tmass = 0.0;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      pm[e] = (r0 + lane * RPT + e < n) ? mass_of(dv[e]) : 0.0;
+      tmass += pm[e];
     }
-    removed += s_fm;
+    const double rincl = wave_incl_scan(tmass);
+    const double base = s_pre[bstar] + (rincl - tmass);
+    int scand = 0x7fffffff;
+    double c = base;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      c += pm[e];
+      if (scand == 0x7fffffff && c > x && pm[e] > 0.0) scand = r0 + lane * RPT + e;
+    }
+    const int s = wave_min_int(scand);
+    if (s == 0x7fffffff || s >= n) {  // rounding left no row to claim x: no more candidates
+      for (int jj = j + lane; jj < B; jj += 64) cand[jj] = -1;
+      break;
+    }
+    // the lane holding row s records its interval [C_{s-1}, C_s) of the running sum
+    const int owner = (s - r0) / RPT, loc = s - r0 - owner * RPT;
+    double lo = base, ms = 0.0;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      if (e < loc) lo += pm[e];
+      if (e == loc) ms = pm[e];
+    }
+    const double flo = lane_d(lo, owner), fm = lane_d(ms, owner);
+    if (lane == 0) cand[j] = s;
+    // insert into the index-ordered list: lanes at and past the new position move up by one
+    const int pos = __popcll(__ballot(lane < nd && c_idx < s));
+    const int up_idx = __shfl_up(c_idx, 1, 64);
+    const double up_lo = __shfl_up(c_lo, 1, 64), up_m = __shfl_up(c_m, 1, 64);
+    if (lane == pos) {
+      c_idx = s; c_lo = flo; c_m = fm;
+    } else if (lane > pos) {
+      c_idx = up_idx; c_lo = up_lo; c_m = up_m;
+    }
+    removed += fm;
     ++nd;
   }
 }
@@ -905,11 +932,18 @@ static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
   hipLaunchKernelGGL((rpc_init_kernel<T, D>), grid, dim3(NT), 0, st, a, a.rows);
   hipLaunchKernelGGL(blk_init_kernel, dim3(a.H), dim3(NT), 0, st, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t lds = (size_t)a.nblk * sizeof(double);
+  const size_t lds = 2 * (size_t)a.nblk * sizeof(double);
+  const bool wide = a.rows == 1024;  // rows per block: 1024 (16 per lane) or 256 (4 per lane)
+  if (lds > 48 * 1024) {
+    const void* fn = wide ? reinterpret_cast<const void*>(&blk_sample_kernel<16>)
+                          : reinterpret_cast<const void*>(&blk_sample_kernel<4>);
+    if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) return e;
+  }
   const int colgrid = (a.n + NT - 1) / NT;
   const int rounds = kBlockDraws * a.r / B;
   for (int k = 0; k < rounds; ++k) {
-    hipLaunchKernelGGL(blk_sample_kernel, dim3(a.H), dim3(NT), lds, st, A, k);
+    if (wide) hipLaunchKernelGGL(blk_sample_kernel<16>, dim3(a.H), dim3(64), lds, st, A, k);
+    else hipLaunchKernelGGL(blk_sample_kernel<4>, dim3(a.H), dim3(64), lds, st, A, k);
     if constexpr (sizeof(T) == 2) {
       hipLaunchKernelGGL((blk_gather_kernel<B>), dim3((a.r * B + 255) / 256, a.H), dim3(256), 0, st, A);
       hipLaunchKernelGGL((blk_column_mfma_kernel<D, B>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, A);
