@@ -844,7 +844,7 @@ __global__ void __launch_bounds__(4 * B) blk_factor_kernel(BlockRpcArgs A, int k
 // streaming loop, so that the masses line up with the blocks the sampler reads.
 template <int B>
 __global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int k) {
-  __shared__ __attribute__((aligned(16))) float sMt[B][B];
+  __shared__ __attribute__((aligned(16))) float sM[B][B];  // sM[jj][c] = M[jj][c]
   __shared__ int sSl[B], sP[B];
   __shared__ double red[NW];
   const StreamRpcArgs& a = A.s;
@@ -854,7 +854,7 @@ __global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int k) {
   float* dg_out = ((k & 1) ? a.diag0 : a.diag1) + (size_t)h * n;
   double* part_out = (k & 1) ? a.part0 : a.part1;
   const float* M = A.M + (size_t)h * B * B;
-  for (int e = tid; e < B * B; e += NT) sMt[e % B][e / B] = M[e];
+  for (int e = tid; e < B * B; e += NT) sM[e / B][e % B] = M[e];
   if (tid < B) {
     const int sl = A.slot[(size_t)h * B + tid];
     sSl[tid] = sl;
@@ -876,7 +876,13 @@ __global__ void __launch_bounds__(NT) blk_apply_kernel(BlockRpcArgs A, int k) {
       if (sl < 0) continue;
       float f = 0.f;
 #pragma unroll
-      for (int c = 0; c < B; ++c) f = fmaf(g[c], sMt[c][jj], f);
+      for (int c = 0; c < B; c += 4) {  // row jj of M, four entries per LDS read (broadcast)
+        const float4 m4 = *reinterpret_cast<const float4*>(&sM[jj][c]);
+        f = fmaf(g[c], m4.x, f);
+        f = fmaf(g[c + 1], m4.y, f);
+        f = fmaf(g[c + 2], m4.z, f);
+        f = fmaf(g[c + 3], m4.w, f);
+      }
       F[(size_t)sl * n + i] = f;
       dsum = fmaf(f, f, dsum);
       piv |= sP[jj] == i;
