@@ -50,6 +50,9 @@ bool resident_ok(const wc_problem& p) {
 }
 
 bool binned(const wc_problem& p) { return p.bins > 1; }
+// Weights solve: blocked back substitution over 64-row blocks (one launch per block, all blocks
+// of the update in parallel) for large coresets, the one-pass trisolve otherwise.
+bool blocked_solve(const wc_problem& p) { return p.r % 64 == 0 && p.r >= 512; }
 bool blocked(const wc_problem& p) { return p.pivot_block > 1; }
 // Bins go through the per-bin selection, the fold of the pivots and weights over the union.
 bool union_path(const wc_problem& p) { return binned(p); }
@@ -93,7 +96,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int rows, nblk, nchunk, chunk_rows, nsplit, rp;
-  size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, KSh, KSl, Wph, Wpl, Wden, Wdh, Ypart;
+  size_t diag0, diag1, part0, part1, unif, F, piv, L, Xpart, X, W, Minv, KSh, KSl, Wph, Wpl, Wden, Wdh, Ypart;
   size_t bcand, bslot, bG, bM, brounds, bFS;  // block pivot selection
   size_t total;
 };
@@ -136,6 +139,7 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
     L.Xpart = take(H * L.nchunk * r * nc * 4);
     L.X = take(H * r * nc * 4);
     L.W = take(H * r * nc * 4);
+    L.Minv = blocked_solve(p) ? take(H * r * 64 * 4) : 0;
     if (blocked(p)) {
       const size_t b = (size_t)p.pivot_block;
       L.bcand = take(H * b * 4);
@@ -280,6 +284,7 @@ hipError_t run_weights(const wc_problem& p, const Layout& L, void* ws, const voi
   a.nchunk = L.nchunk; a.chunk_rows = L.chunk_rows;
   a.X = at<float>(ws, L.X);
   a.W = W;
+  a.Minv = blocked_solve(p) ? at<float>(ws, L.Minv) : nullptr;
   return wc::launch_weights(a, st);
 }
 

@@ -96,6 +96,8 @@ struct WeightsArgs {
   int nchunk, chunk_rows;
   float* X;               // ws [H][r][dv+1]
   float* W;               // out [H][r][dv+1]
+  float* Minv;            // ws [H][r/64][64][64] inverses of L's diagonal blocks, or NULL: the
+                          // blocked back substitution (r a multiple of 64) instead of trisolve
 };
 hipError_t launch_weights(const WeightsArgs& a, hipStream_t st);
 
@@ -187,6 +189,9 @@ struct UnionArgs {
 };
 hipError_t launch_union_gather(const UnionArgs& a, hipStream_t st);  // fills Qs
 hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st);   // A, Hd, M from Qs; X -> W
+// The blocked back substitution alone: W = L^{-T} X from the lower factor L (in A, leading
+// dimension rp, a multiple of 64), the inverses M of its diagonal blocks and X (overwritten).
+hipError_t launch_union_back(const UnionArgs& a, hipStream_t st);
 
 // ---- key centring: Kc = K - mean of the head's keys (fp64 mean, input-precision result) ----
 struct CenterArgs {

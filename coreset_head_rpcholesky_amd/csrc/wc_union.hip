@@ -364,9 +364,15 @@ hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(union_update_kernel, dim3(T * (T + 1) / 2 + T * nxz, a.H), dim3(256), 0, st, a, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  return launch_union_back(a, st);
+}
+
+hipError_t launch_union_back(const UnionArgs& a, hipStream_t st) {
+  const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB;
   for (int k = nb - 1; k >= 0; --k) {
     hipLaunchKernelGGL(union_back_kernel, dim3((k + 1) * nxz, a.H), dim3(256), 0, st, a, k);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -254,6 +254,39 @@ __global__ void __launch_bounds__(256) trisolve_kernel(WeightsArgs a) {
   }
 }
 
+// Inverses of L's 64 x 64 diagonal blocks (the part before the rank; zero past it), for the
+// blocked back substitution.  Grid (r/64, heads), one thread per column of the inverse: forward
+// substitution down the column, x_i = (delta_ic - sum_{c <= j < i} L_ij x_j) / L_ii.
+__global__ void __launch_bounds__(64) tri_inv_kernel(WeightsArgs a) {
+  constexpr int B = 64, P = B + 4;
+  __shared__ __attribute__((aligned(16))) float sL[B][P];
+  __shared__ float sR[B];
+  const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x, r = a.r;
+  const int b0 = b * B, bs = max(0, min(B, a.rank[h] - b0));
+  const float* L = a.L + (size_t)h * r * r;
+#pragma unroll 4
+  for (int i = 0; i < B; ++i) sL[i][c] = (i < bs && c < bs) ? L[(size_t)(b0 + i) * r + b0 + c] : 0.f;
+  __syncthreads();
+  sR[c] = c < bs ? 1.0f / sL[c][c] : 0.f;
+  __syncthreads();
+  float x[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    float acc0 = i == c ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j + 1 < i; j += 2) {
+      acc0 = fmaf(-sL[i][j], x[j], acc0);
+      acc1 = fmaf(-sL[i][j + 1], x[j + 1], acc1);
+    }
+    if (i & 1) acc0 = fmaf(-sL[i][i - 1], x[i - 1], acc0);
+    // x_j = 0 for j < c, so the sum may run over all j < i
+    x[i] = (i >= c && i < bs && c < bs) ? (acc0 + acc1) * sR[i] : 0.f;
+  }
+  float* M = a.Minv + ((size_t)h * (r / B) + b) * B * B;
+#pragma unroll
+  for (int i = 0; i < B; ++i) M[i * B + c] = x[i];
+}
+
 template <typename TV, int DV>
 static hipError_t run_weights(const WeightsArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(gather_L_kernel, dim3(a.r, a.H), dim3(256), 0, st, a);
@@ -268,6 +301,15 @@ static hipError_t run_weights(const WeightsArgs& a, hipStream_t st) {
   const size_t per = (size_t)a.r * (DV + 1);
   hipLaunchKernelGGL(x_reduce_kernel, dim3((unsigned)((per + 255) / 256), a.H), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.Minv) {
+    // blocked: every diagonal block inverted at once, then one launch per block
+    hipLaunchKernelGGL(tri_inv_kernel, dim3(a.r / 64, a.H), dim3(64), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    UnionArgs u{};
+    u.H = a.H; u.dv = a.dv; u.r = a.r; u.rp = a.r;
+    u.A = a.L; u.M = a.Minv; u.X = a.X; u.W = a.W;
+    return launch_union_back(u, st);
+  }
   hipLaunchKernelGGL(trisolve_kernel, dim3((DV + 1 + 31) / 32, a.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }

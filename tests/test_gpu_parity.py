@@ -235,3 +235,32 @@ def test_tiny_heads(wc, dtype, n, r):
         assert rel(O[h], ref["O"]) < TOL[dtype], (h, rel(O[h], ref["O"]))
         if r == n:
             assert rel(O[h], ow.exact_attention(Q[h], K[h], V[h])) < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,r,rk", [("bf16", 128, 512, 512), ("f32", 64, 576, 576),
+                                           ("bf16", 64, 512, 300), ("f32", 64, 512, 449)])
+def test_blocked_solve(wc, dtype, d, r, rk):
+    """Weights with r a multiple of 64 and at least 512 take the blocked back substitution.
+    Given the GPU's pivots, W and O are unique, so both are compared with the oracle's from
+    those pivots.  rk < r passes a smaller rank (the one a breakdown would leave): one block is
+    cut at the rank and the later ones lie past it, and their rows must be zero."""
+    import torch
+
+    H, n, m = 1, 2048, 120
+    Q, K, V = synth.random_inputs(H, n, m, d, d, seed=880 + r + rk, dtype=dtype, kind="kv_outlier")
+    Qd, Kd = dev(Q, dtype), dev(K, dtype)
+    rpc = wc.wc_rpcholesky(Kd, r, seed=3, with_diag=False)
+    assert int(host(rpc["rank"])[0]) == r
+    rank = torch.full((H,), rk, dtype=torch.int32, device="cuda")
+    W = wc.wc_weights(dev(V, dtype), rpc["pivots"], rank, rpc["F"])
+    Wh = host(W)[0]
+    S = host(rpc["pivots"])[0][:rk]
+    beta = 1.0 / np.sqrt(d)
+    Wo = ow.weights(K[0], V[0], S, beta)
+    assert rel(Wh[:rk], Wo) < 1e-3, rel(Wh[:rk], Wo)
+    assert np.all(Wh[rk:] == 0.0)
+    O, flags = wc.wc_attend(Qd, Kd, rpc["pivots"], rank, W)
+    Oo, den, kappa = ow.attend(Q[0], K[0], S, Wo, beta)
+    ok = kappa < 1e6
+    assert rel(host(O)[0][ok], Oo[ok]) < TOL[dtype], rel(host(O)[0][ok], Oo[ok])
+    assert np.all(host(flags) == 0)
