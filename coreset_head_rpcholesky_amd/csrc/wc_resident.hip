@@ -39,9 +39,18 @@ __device__ __forceinline__ double readlane_d(double x, int lane) {
   const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
   return __hiloint2double(hi, lo);
 }
+// Lane broadcast of an fp64 value into the rows of ROWMASK; the other rows read zero.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_rows_d(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, ROWMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, ROWMASK, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
 // Two independent inclusive fp64 scans over the wave, level by level side by side (the step is
 // latency-bound, so the two dependency chains overlap): row_shr within 16-lane rows, then the
-// row offsets.  Each scan adds in the same order as a scan of its own.
+// last lane of row 0 into row 1 and of row 2 into row 3 (row_bcast:15), then the last lane of
+// row 1 into rows 2 and 3 (row_bcast:31).  Each scan adds in the same order as a scan of its
+// own; rows that receive nothing add +0, which leaves their non-negative sums unchanged.
 __device__ __forceinline__ void wave_scan2(double& x, double& y) {
   x += dpp_d<0x111>(x);
   y += dpp_d<0x111>(y);
@@ -51,14 +60,10 @@ __device__ __forceinline__ void wave_scan2(double& x, double& y) {
   y += dpp_d<0x114>(y);
   x += dpp_d<0x118>(x);
   y += dpp_d<0x118>(y);
-  const double rx0 = readlane_d(x, 15), rx1 = readlane_d(x, 31), rx2 = readlane_d(x, 47);
-  const double ry0 = readlane_d(y, 15), ry1 = readlane_d(y, 31), ry2 = readlane_d(y, 47);
-  const double ox2 = rx0 + rx1, oy2 = ry0 + ry1;
-  const double ox3 = ox2 + rx2, oy3 = oy2 + ry2;
-  // row offsets by selection (adding +0 leaves row 0's non-negative sums unchanged)
-  const int row = (threadIdx.x & 63) >> 4;
-  x += row == 0 ? 0.0 : row == 1 ? rx0 : row == 2 ? ox2 : ox3;
-  y += row == 0 ? 0.0 : row == 1 ? ry0 : row == 2 ? oy2 : oy3;
+  x += dpp_rows_d<0x142, 0xa>(x);
+  y += dpp_rows_d<0x142, 0xa>(y);
+  x += dpp_rows_d<0x143, 0xc>(x);
+  y += dpp_rows_d<0x143, 0xc>(y);
 }
 
 // dot(k_a, k_b) of two keys held as packed bf16 pairs; fixed association order.
@@ -140,9 +145,9 @@ struct PairScan {
   bool pa, pb;  // rows with positive mass
 };
 // Both waves' row pairs at this lane position (rows 2l, 2l+1 and 128 + 2l, 128 + 2l + 1).
-__device__ __forceinline__ void pair_scan2(float2 d0, float2 d1, int lane, int n, PairScan& q0, PairScan& q1) {
-  const double m0a = 2 * lane < n ? mass_of(d0.x) : 0.0, m0b = 2 * lane + 1 < n ? mass_of(d0.y) : 0.0;
-  const double m1a = 128 + 2 * lane < n ? mass_of(d1.x) : 0.0, m1b = 129 + 2 * lane < n ? mass_of(d1.y) : 0.0;
+// Rows past the last key hold zero in both residual buffers.
+__device__ __forceinline__ void pair_scan2(float2 d0, float2 d1, PairScan& q0, PairScan& q1) {
+  const double m0a = mass_of(d0.x), m0b = mass_of(d0.y), m1a = mass_of(d1.x), m1b = mass_of(d1.y);
   double x0 = m0a + m0b, x1 = m1a + m1b;
   wave_scan2(x0, x1);
   q0 = {x0, x0 - m0b, m0a > 0.0, m0b > 0.0};
@@ -198,10 +203,9 @@ __global__ void __launch_bounds__(NT, (D == 64 && DV == 64) ? 2 : 1) resident_ke
     dg[p] = d0;
 #pragma unroll
     for (int j = 0; j < R; ++j) fr[p][j] = 0.f;
-    if (row < n) {
-      sF[row * FS + R] = d0;
-      sDg[row] = d0;
-    }
+    if (row < n) sF[row * FS + R] = d0;
+    sDg[row] = d0;          // zero past the last key, in both buffers
+    sDg[DGS + row] = 0.f;
   }
   if (tid == 0) s_flag = 0u;
   // the r pivot uniforms, drawn once (first use is after the first barrier)
@@ -222,7 +226,7 @@ __global__ void __launch_bounds__(NT, (D == 64 && DV == 64) ? 2 : 1) resident_ke
     const float2 d0p = reinterpret_cast<const float2*>(sDg + buf * DGS)[lane];
     const float2 d1p = reinterpret_cast<const float2*>(sDg + buf * DGS)[64 + lane];
     PairScan q0, q1;
-    pair_scan2(d0p, d1p, lane, n, q0, q1);
+    pair_scan2(d0p, d1p, q0, q1);
     const double w0 = readlane_d(q0.x, 63), w1 = readlane_d(q1.x, 63);
     T = w0 + w1;
     // Breakdown (T <= 0, no row claims the draw, g_s <= 0, anything non-finite) is collected
@@ -315,7 +319,7 @@ __global__ void __launch_bounds__(NT, (D == 64 && DV == 64) ? 2 : 1) resident_ke
       const float2 d0p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[lane];
       const float2 d1p = reinterpret_cast<const float2*>(sDg + (r & 1) * DGS)[64 + lane];
       PairScan q0, q1;
-      pair_scan2(d0p, d1p, lane, n, q0, q1);
+      pair_scan2(d0p, d1p, q0, q1);
       Tr = readlane_d(q0.x, 63) + readlane_d(q1.x, 63);
     }
     if (tid <= r && (tid > rk || tid == r)) a.trace[(size_t)h * (r + 1) + tid] = tid < r ? 0.0 : Tr;
