@@ -33,21 +33,30 @@ __device__ __forceinline__ bool slot_valid(const UnionArgs& a, int h, int j) {
   return j < a.r && a.pivots[(size_t)h * a.r + j] >= 0;
 }
 
-// One 64 x 64 x 64 product on a 256-thread workgroup: thread (ti, tc) = (tid / 16, tid % 16)
-// accumulates rows 4 ti .. 4 ti + 3 and columns 4 tc .. 4 tc + 3 of
-//     acc[i][c] += sum_t sP[t][i] sQ[t][c]
-// with both operands staged k-major in LDS.
-__device__ __forceinline__ void mm64(const float (*sP)[kLP], const float (*sQ)[kLP], float acc[4][4]) {
-  const int tid = threadIdx.x, i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
+// One 64 x 64 x 64 product on a 256-thread workgroup,
+//     acc[i][c] += sum_t sP[t][4 ti + i] sQ[t][4 tc + c],  (ti, tc) = (tid / 16, tid % 16),
+// with both operands staged k-major in LDS.  Wave w computes the 32 x 32 quarter (w / 2, w % 2)
+// on the fp32 matrix cores (32 x 32 x 2 steps over t), then the product passes through sP
+// (row-major) so that every thread picks up its 4 x 4 piece; sP is overwritten.  Every thread
+// of the workgroup must call it.
+__device__ __forceinline__ void mm64(float (*sP)[kLP], const float (*sQ)[kLP], float acc[4][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, kh = lane >> 5, m0 = 32 * (w >> 1), n0 = 32 * (w & 1);
+  f32x16 c;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) c[v] = 0.f;
 #pragma unroll 8
-  for (int t = 0; t < kUB; ++t) {
-    const float4 p = *reinterpret_cast<const float4*>(&sP[t][i0]);
-    const float4 q = *reinterpret_cast<const float4*>(&sQ[t][c0]);
-    const float pv[4] = {p.x, p.y, p.z, p.w}, qv[4] = {q.x, q.y, q.z, q.w};
+  for (int t = 0; t < kUB; t += 2)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(sP[t + kh][m0 + l32], sQ[t + kh][n0 + l32], c, 0, 0, 0);
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int v = 0; v < 16; ++v) sP[m0 + 8 * (v >> 2) + 4 * kh + (v & 3)][n0 + l32] = c[v];
+  __syncthreads();
+  const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(pv[i], qv[c], acc[i][c]);
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = *reinterpret_cast<const float4*>(&sP[i0 + i][c0]);
+    acc[i][0] += q.x; acc[i][1] += q.y; acc[i][2] += q.z; acc[i][3] += q.w;
   }
 }
 
