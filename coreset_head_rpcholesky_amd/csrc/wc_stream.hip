@@ -755,23 +755,38 @@ __global__ void __launch_bounds__(256) blk_column_mfma_kernel(BlockRpcArgs A) {
   int jc[NC];  // candidate slot of each tile's lane, clamped into [0, b)
 #pragma unroll
   for (int t = 0; t < NC; ++t) jc[t] = 32 * t + l32 < B ? 32 * t + l32 : 0;
-  for (int c = 0; c < f0; c += 16) {
-    float fa[8][NC], fb[8];
+  // Two register buffers alternate: a batch's products are issued after the next batch's
+  // loads (the last batch loads a clamped, unused copy), so each wave keeps one batch of loads
+  // in flight behind its matrix-core work.
+  float fa0[8][NC], fb0[8], fa1[8][NC], fb1[8];
+  auto load_batch = [&](int c, float (&xa)[8][NC], float (&xb)[8]) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int ck = min(c + 2 * m + g, f0 - 1);
-      fb[m] = F[(size_t)ck * n + rowc];
+      xb[m] = F[(size_t)ck * n + rowc];
 #pragma unroll
-      for (int t = 0; t < NC; ++t) fa[m][t] = FSh[(size_t)ck * B + jc[t]];
+      for (int t = 0; t < NC; ++t) xa[m][t] = FSh[(size_t)ck * B + jc[t]];
     }
+  };
+  auto products = [&](int c, float (&xa)[8][NC], float (&xb)[8]) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      if (c + 2 * m + g >= f0) fb[m] = 0.f;
+      if (c + 2 * m + g >= f0) xb[m] = 0.f;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int t = 0; t < NC; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[m][t], fb[m], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[m][t], xb[m], acc[t], 0, 0, 0);
+  };
+  if (f0 > 0) load_batch(0, fa0, fb0);
+  for (int c = 0; c < f0; c += 32) {
+    load_batch(c + 16, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    products(c, fa0, fb0);
+    if (c + 16 >= f0) break;
+    load_batch(c + 32, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    products(c + 16, fa1, fb1);
   }
   if (!rv) return;
   float* G = A.G + (size_t)h * B * n;
