@@ -755,10 +755,10 @@ __global__ void __launch_bounds__(256) blk_column_mfma_kernel(BlockRpcArgs A) {
   int jc[NC];  // candidate slot of each tile's lane, clamped into [0, b)
 #pragma unroll
   for (int t = 0; t < NC; ++t) jc[t] = 32 * t + l32 < B ? 32 * t + l32 : 0;
-  // Two register buffers alternate: a batch's products are issued after the next batch's
-  // loads (the last batch loads a clamped, unused copy), so each wave keeps one batch of loads
-  // in flight behind its matrix-core work.
-  float fa0[8][NC], fb0[8], fa1[8][NC], fb1[8];
+  // Three register buffers rotate: a batch's products are issued after the loads of the batch
+  // two ahead (the last batches load clamped, unused copies), so each wave keeps two batches of
+  // loads in flight behind its matrix-core work.
+  float fa0[8][NC], fb0[8], fa1[8][NC], fb1[8], fa2[8][NC], fb2[8];
   auto load_batch = [&](int c, float (&xa)[8][NC], float (&xb)[8]) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -778,15 +778,22 @@ __global__ void __launch_bounds__(256) blk_column_mfma_kernel(BlockRpcArgs A) {
       for (int t = 0; t < NC; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[m][t], xb[m], acc[t], 0, 0, 0);
   };
-  if (f0 > 0) load_batch(0, fa0, fb0);
-  for (int c = 0; c < f0; c += 32) {
-    load_batch(c + 16, fa1, fb1);
+  if (f0 > 0) {
+    load_batch(0, fa0, fb0);
+    load_batch(16, fa1, fb1);
+  }
+  for (int c = 0; c < f0; c += 48) {
+    load_batch(c + 32, fa2, fb2);
     __builtin_amdgcn_sched_barrier(0);
     products(c, fa0, fb0);
     if (c + 16 >= f0) break;
-    load_batch(c + 32, fa0, fb0);
+    load_batch(c + 48, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     products(c + 16, fa1, fb1);
+    if (c + 32 >= f0) break;
+    load_batch(c + 64, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    products(c + 32, fa2, fb2);
   }
   if (!rv) return;
   float* G = A.G + (size_t)h * B * n;
