@@ -52,7 +52,7 @@ bool resident_ok(const wc_problem& p) {
 bool binned(const wc_problem& p) { return p.bins > 1; }
 // Weights solve: blocked back substitution over 64-row blocks (one launch per block, all blocks
 // of the update in parallel) for large coresets, the one-pass trisolve otherwise.
-bool blocked_solve(const wc_problem& p) { return p.r % 64 == 0 && p.r >= 512; }
+bool blocked_solve(const wc_problem& p) { return p.r % 64 == 0 && p.r >= 256; }
 bool blocked(const wc_problem& p) { return p.pivot_block > 1; }
 // Bins go through the per-bin selection, the fold of the pivots and weights over the union.
 bool union_path(const wc_problem& p) { return binned(p); }

@@ -238,9 +238,10 @@ def test_tiny_heads(wc, dtype, n, r):
 
 
 @pytest.mark.parametrize("dtype,d,r,rk", [("bf16", 128, 512, 512), ("f32", 64, 576, 576),
-                                           ("bf16", 64, 512, 300), ("f32", 64, 512, 449)])
+                                           ("bf16", 64, 512, 300), ("f32", 64, 512, 449),
+                                           ("bf16", 64, 256, 256), ("f32", 128, 256, 200)])
 def test_blocked_solve(wc, dtype, d, r, rk):
-    """Weights with r a multiple of 64 and at least 512 take the blocked back substitution.
+    """Weights with r a multiple of 64 and at least 256 take the blocked back substitution.
     Given the GPU's pivots, W and O are unique, so both are compared with the oracle's from
     those pivots.  rk < r passes a smaller rank (the one a breakdown would leave): one block is
     cut at the rank and the later ones lie past it, and their rows must be zero."""
