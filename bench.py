@@ -292,7 +292,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU: every head is independent, so "
+        print(json.dumps({"error": "bench.py measures one GPU: every head is independent, so "
                           "more GPUs would shard heads with no communication; only --gpus 1 "
                           "is measured"}))
         sys.exit(2)
