@@ -243,25 +243,30 @@ def test_tiny_heads(wc, dtype, n, r):
 def test_blocked_solve(wc, dtype, d, r, rk):
     """Weights with r a multiple of 64 and at least 256 take the blocked back substitution.
     Given the GPU's pivots, W and O are unique, so both are compared with the oracle's from
-    those pivots.  rk < r passes a smaller rank (the one a breakdown would leave): one block is
-    cut at the rank and the later ones lie past it, and their rows must be zero."""
+    those pivots.  Head 0 gets rank rk (the rank a breakdown would leave: for rk < r one block
+    is cut at the rank and the later ones lie past it, and their rows must be zero); head 1
+    keeps the full rank, so the two heads' blocks differ within one launch."""
     import torch
 
-    H, n, m = 1, 2048, 120
+    H, n, m = 2, 2048, 120
     Q, K, V = synth.random_inputs(H, n, m, d, d, seed=880 + r + rk, dtype=dtype, kind="kv_outlier")
     Qd, Kd = dev(Q, dtype), dev(K, dtype)
     rpc = wc.wc_rpcholesky(Kd, r, seed=3, with_diag=False)
-    assert int(host(rpc["rank"])[0]) == r
-    rank = torch.full((H,), rk, dtype=torch.int32, device="cuda")
+    assert np.all(host(rpc["rank"]) == r)
+    ranks = [rk, r]
+    rank = torch.tensor(ranks, dtype=torch.int32, device="cuda")
     W = wc.wc_weights(dev(V, dtype), rpc["pivots"], rank, rpc["F"])
-    Wh = host(W)[0]
-    S = host(rpc["pivots"])[0][:rk]
-    beta = 1.0 / np.sqrt(d)
-    Wo = ow.weights(K[0], V[0], S, beta)
-    assert rel(Wh[:rk], Wo) < 1e-3, rel(Wh[:rk], Wo)
-    assert np.all(Wh[rk:] == 0.0)
+    Wh = host(W)
     O, flags = wc.wc_attend(Qd, Kd, rpc["pivots"], rank, W)
-    Oo, den, kappa = ow.attend(Q[0], K[0], S, Wo, beta)
-    ok = kappa < 1e6
-    assert rel(host(O)[0][ok], Oo[ok]) < TOL[dtype], rel(host(O)[0][ok], Oo[ok])
+    O = host(O)
+    beta = 1.0 / np.sqrt(d)
+    for h in range(H):
+        k = ranks[h]
+        S = host(rpc["pivots"])[h][:k]
+        Wo = ow.weights(K[h], V[h], S, beta)
+        assert rel(Wh[h][:k], Wo) < 1e-3, (h, rel(Wh[h][:k], Wo))
+        assert np.all(Wh[h][k:] == 0.0)
+        Oo, den, kappa = ow.attend(Q[h], K[h], S, Wo, beta)
+        ok = kappa < 1e6
+        assert rel(O[h][ok], Oo[ok]) < TOL[dtype], (h, rel(O[h][ok], Oo[ok]))
     assert np.all(host(flags) == 0)
