@@ -1,18 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the WildCat forward (coreset selection + weights + attention) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit197]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long128k] [--bins B]
+                    [--pivot-block b]
 
 A step is one whole forward (randomly pivoted Cholesky, Nystroem weights, attention over the
 coreset) over every head of one batch of seeded synthetic inputs that are already resident
-in HBM.  The default workload is the ViT-classification-shaped one (64 x 12 heads, n = 197,
-d = 64, r = 32, bf16); the other workloads of coreset_head_rpcholesky_amd.synth can be
-selected with --workload.  Prints one JSON line.
+in HBM.  The default workload is the long-context one (8 heads, n = m = 131072, d = dv = 128,
+r = 2048, bf16), run as the method is stated: one bin, one pivot per step.  The other
+workloads of coreset_head_rpcholesky_amd.synth can be selected with --workload.  Prints one
+JSON line.
 
 Beside the GPU number it reports:
-  * roofline of the dominant kernel: algorithmic bytes (or flops) of one launch over its
-    average duration, timed with HIP events on the stream the kernel is launched on;
-  * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same workload;
+  * roofline: the dominant kernel, its algorithmic bytes (or flops) over its measured time,
+    timed with HIP events on the stream the kernels are launched on (the streaming pivot
+    loop for every workload but the small-head one, whose whole forward is one kernel);
+  * roofline_attend: the attention pass (wc_attend) against the bf16 matrix-core peak;
+  * variants: the divide-and-conquer and block-pivot forwards of the same inputs, timed in
+    the same run;
+  * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same workload, and a
+    one-thread run of it on the image-shaped workload;
   * exact softmax attention (PyTorch SDPA) on the same tensors, for context.
 """
 from __future__ import annotations
@@ -32,13 +39,25 @@ FP32_PEAK_TFLOPS = 157.3  # MI355X fp32, vector and matrix, published
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
-# Kernel sources whose counters a stored traffic figure belongs to.
+# Kernel sources a stored counter summary belongs to.
 KERNEL_SOURCES = {
     "resident": ["wc_resident.hip", "wc_device.h", "wc_kernels.h"],
     "stream": ["wc_stream.hip", "wc_device.h", "wc_kernels.h"],
+    "attend": ["wc_attend.hip", "wc_device.h", "wc_kernels.h"],
 }
+# (workload, kernel kind) -> committed rocprofv3 counter summary
 COUNTER_FILES = {
-    "vit197": "profiles/resident_kernel_vit197_counters.txt",
+    ("vit197", "resident"): "profiles/resident_kernel_vit197_counters.txt",
+    ("long128k", "stream"): "profiles/rpc_step_kernel_long128k_counters.txt",
+    ("kv32k", "stream"): "profiles/rpc_step_kernel_kv32k_counters.txt",
+    ("img4096", "stream"): "profiles/rpc_step_kernel_img4096_counters.txt",
+    ("long128k", "attend"): "profiles/attend_bf16_kernel_long128k_counters.txt",
+}
+# Binned and block-pivot forwards timed beside the default one: (bins, pivot_block)
+DEFAULT_VARIANTS = {
+    "long128k": [(16, 1), (64, 1), (64, 32), (1, 64)],
+    "kv32k": [(16, 1), (64, 1), (16, 64)],
+    "img4096": [(4, 1), (16, 1), (4, 64)],
 }
 
 
@@ -50,10 +69,10 @@ def source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, kind: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel source changed since the counters were taken."""
-    path = COUNTER_FILES.get(workload)
+def stored_counters(workload: str, kind: str):
+    """key = value pairs of the committed rocprofv3 counter summary for this workload and
+    kernel, or None when there is none or the kernel source changed since it was taken."""
+    path = COUNTER_FILES.get((workload, kind))
     if not path or not os.path.exists(os.path.join(ROOT, path)):
         return None
     vals = {}
@@ -63,8 +82,12 @@ def stored_traffic(workload: str, kind: str):
             vals[k.strip()] = v.strip()
     if vals.get("source_sha") != source_hash(kind):
         return None
+    return vals
+
+
+def stored_float(vals, key):
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(vals[key]) if vals else None
     except (KeyError, ValueError):
         return None
 
@@ -77,6 +100,8 @@ def workload_accounting(w, bins: int = 1):
     H, n, m, d, dv, r = w.heads, w.n, w.m, w.d, w.dv, w.r
     compulsory = H * ((m * d + n * d + n * dv) * b + m * dv * b)
     Hs, ns, rs = H * bins, n // bins, r // bins
+    # per step t: K re-read (n d b), F columns 0..t-1 (4 n t), residual read and written and
+    # the new column written (12 n); summed over the r steps
     pivot_bytes = Hs * (ns * rs * d * b + 2 * ns * rs * (rs - 1) + 12 * ns * rs)
     # a sub-head small enough for the resident kernel keeps its factor on chip: only K in
     # and F, pivots out reach HBM
@@ -89,6 +114,38 @@ def workload_accounting(w, bins: int = 1):
                 weight_flops=weight_flops, attend_flops=attend_flops)
 
 
+def graph_of(fn, copies: int = 1):
+    """fn() (which launches on the current stream) captured `copies` times in one HIP graph."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(copies):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(g, reps: int, stream) -> float:
+    """Mean ms per replay of graph g: one untimed warm replay, then `reps` timed ones, HIP
+    events on the stream the replays run on."""
+    import torch
+
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def exact_attention_timing(w, Q, K, V, stream):
     """Exact softmax attention on the same tensors with PyTorch SDPA ([1, heads, len, d] so
     the fused backends are eligible); the first backend that runs is recorded."""
@@ -97,6 +154,7 @@ def exact_attention_timing(w, Q, K, V, stream):
     from torch.nn.attention import SDPBackend, sdpa_kernel
 
     q, k, v = Q.unsqueeze(0), K.unsqueeze(0), V.unsqueeze(0)
+    err = ""
     for name, backend in [("flash", SDPBackend.FLASH_ATTENTION),
                           ("efficient", SDPBackend.EFFICIENT_ATTENTION),
                           ("math", SDPBackend.MATH)]:
@@ -134,33 +192,52 @@ def error_vs_exact(w, Q, K, V, O, rows: int = 256):
     return round(float(err.mean()), 6)
 
 
-def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1, pivot_block: int = 1):
-    """The fp64 oracle on as many heads as fit in the time budget, going round the workload's
-    heads again when one pass takes less; tokens/s scaled to the whole workload (tokens per
-    head = tokens / heads)."""
+def _blas_threads():
+    """Threads the BLAS pools actually use (the largest pool), from threadpoolctl."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _oracle_head(ow, philox, w, Q, K, V, h, bins, pivot_block):
+    """One head of the oracle forward with the bench's Philox uniforms (seed 42); returns the
+    rank it reached."""
     import numpy as np
 
+    if bins > 1 or pivot_block > 1:
+        rb = w.r // bins
+        per = ow.BLOCK_DRAWS * rb if pivot_block > 1 else rb
+        # each bin (sub-head h B + b) draws its own Philox stream, as the device does
+        u = np.concatenate([philox.pivot_uniforms(42, h * bins + b, per) for b in range(bins)])
+        out = ow.forward_binned(Q[h], K[h], V[h], w.r, bins, u, pivot_block=pivot_block)
+    else:
+        out = ow.forward(Q[h], K[h], V[h], w.r, np.array(philox.pivot_uniforms(42, h, w.r)))
+    return int(out["rank"])
+
+
+def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1, pivot_block: int = 1, threads=None):
+    """The fp64 oracle on as many heads as fit in the time budget (at least one), going round
+    the workload's heads again when one pass takes less; tokens/s scaled to the whole workload
+    (tokens per head = tokens / heads).  threads: BLAS threads (None: the pools' default,
+    which follows OMP_NUM_THREADS)."""
     from oracle import philox
     from oracle import wildcat as ow
 
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        cores = min(16, os.cpu_count() or 1)
-        limiter = threadpool_limits(cores)
-        info = threadpool_info()
-        cores = max([p.get("num_threads", 1) for p in info] + [1])
-    except Exception:  # pragma: no cover
-        limiter, cores = None, 1
+    limiter = None
+    if threads is not None:
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(threads)
+        except Exception:  # pragma: no cover
+            limiter = None
+    cores = _blas_threads()
     t0 = time.perf_counter()
-    done = 0
+    done, ranks = 0, []
     while True:
-        h = done % w.heads
-        if bins > 1 or pivot_block > 1:
-            u = np.concatenate([philox.pivot_uniforms(42, h * bins + b, w.r // bins) for b in range(bins)])
-            ow.forward_binned(Q[h], K[h], V[h], w.r, bins, u, pivot_block=pivot_block)
-        else:
-            u = np.array(philox.pivot_uniforms(42, h, w.r))
-            ow.forward(Q[h], K[h], V[h], w.r, u)
+        h = done % min(w.heads, Q.shape[0])
+        ranks.append(_oracle_head(ow, philox, w, Q, K, V, h, bins, pivot_block))
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -170,8 +247,17 @@ def cpu_baseline(w, Q, K, V, budget_s: float, bins: int = 1, pivot_block: int = 
     tokens = w.tokens * done / w.heads
     what = (f"{done} of {w.heads} heads of one {w.name} forward" if done <= w.heads else
             f"{done} heads ({done / w.heads:.1f} passes over the {w.heads} heads of a {w.name} forward)")
+    extrap = (f"; tokens/s = {w.tokens // w.heads} tokens per head x {done} heads / {dt:.1f} s, i.e. the "
+              f"whole {w.heads}-head forward extrapolated as {w.heads / done:.2f} x the measured time"
+              if done < w.heads else "")
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{what}{f' with {bins} bins' if bins > 1 else ''}, fp64 numpy/scipy, {dt:.1f} s"}
+            "sample": f"{what}{f' with {bins} bins' if bins > 1 else ''}"
+                      f"{f', {pivot_block} candidates per round' if pivot_block > 1 else ''}, fp64 numpy/scipy, "
+                      f"{dt:.1f} s{extrap}",
+            "oracle_rank_min": int(min(ranks)),
+            "host_cpu_count": os.cpu_count(),
+            "host_cpus_in_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def run_decode(args, w, Q, K, V, dt_t, dev):
@@ -204,23 +290,7 @@ def run_decode(args, w, Q, K, V, dt_t, dev):
     def timed(fn, reps, per_graph):
         fn()
         torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for _ in range(per_graph):
-                    fn()
-        torch.cuda.current_stream().wait_stream(side)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * per_graph)
+        return time_replays(graph_of(fn, per_graph), reps, stream) / per_graph
 
     compress_ms = timed(compress, 3, 1)
     c = compress()
@@ -268,20 +338,113 @@ def run_decode(args, w, Q, K, V, dt_t, dev):
     print(json.dumps(line), flush=True)
 
 
+def pivot_loop_roofline(w, K, dt_t, dev, seed, bins, pb, stream, acc, reps):
+    """The selection loop alone (wc_rpcholesky on the per-bin view, graph-replayed, warm),
+    against HBM (one pivot per step: the streaming step kernel, or the resident kernel's loop)
+    or against the bf16 / fp32 matrix-core mix (block pivots)."""
+    from coreset_head_rpcholesky_amd import binding
+
+    Ksel = K.view(w.heads * bins, w.n // bins, w.d)
+    pws = binding.workspace(binding.problem(w.heads * bins, w.n // bins, 0, w.d, w.dv, w.r // bins, dt_t,
+                                            1, 0, pb), dev)
+    res = {}
+
+    def rpc():
+        res["out"] = binding.wc_rpcholesky(Ksel, w.r // bins, seed=seed, ws=pws, with_diag=False,
+                                           with_trace=False, pivot_block=pb)
+
+    rpc()
+    loop_ms = time_replays(graph_of(rpc), reps, stream)
+    Hs, ns, rs = w.heads * bins, w.n // bins, w.r // bins
+    sub_resident = w.dtype == "bf16" and ns <= 256 and rs <= 32 and pb == 1
+    if pb > 1:
+        name = (f"block pivot selection, {rs // pb} rounds of {pb} candidates"
+                f"{f', {Hs} bins' if bins > 1 else ''} (candidate columns: kernel part on "
+                f"bf16 MFMA, factor part on fp32 MFMA; factor update fp32 vector)")
+        # kernel part K K_S^T on the bf16 matrix cores; factor part F F_S^T and the update
+        # F_new = G M^T in fp32 (matrix cores and vector units share the 157.3 TFLOP/s peak).
+        # The roofline of the mix: the time both parts would take at their own peaks.
+        kflops = Hs * 2 * ns * rs * w.d
+        fflops = Hs * (ns * rs * (rs - pb) + 2 * ns * pb * rs)
+        flops = kflops + fflops
+        ideal_s = kflops / (MFMA_BF16_PEAK_TFLOPS * 1e12) + fflops / (FP32_PEAK_TFLOPS * 1e12)
+        peak = flops / ideal_s / 1e12
+        achieved = flops / (loop_ms / 1e3) / 1e12
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "peak_of_mix": f"bf16 {MFMA_BF16_PEAK_TFLOPS} for {kflops} flops, fp32 {FP32_PEAK_TFLOPS} for {fflops}",
+                "algorithmic_flops_per_loop": flops, "rounds": rs // pb, "loop_ms": round(loop_ms, 3)}
+        return roof, res["out"]
+    if sub_resident:
+        name = f"resident_kernel (pivot loop only, {Hs} sub-heads, factor on chip)"
+        loop_bytes, traffic = acc["pivot_resident_bytes"], None
+    else:
+        name = (f"rpc_step_kernel x {rs} launches (streaming pivot loop, one launch per pivot step over "
+                f"all {Hs} {'bins' if bins > 1 else 'heads'})")
+        loop_bytes = acc["pivot_bytes"]
+        traffic = stored_float(stored_counters(w.name, "stream"), "traffic_bytes_per_loop") if bins == 1 else None
+    achieved = loop_bytes / (loop_ms / 1e3) / 1e9
+    roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "unit_of_work": f"one pivot loop: {rs} step launches (plus the initial-residual and bookkeeping "
+                            f"kernels, timed with it)",
+            "algorithmic_bytes_per_loop": loop_bytes, "loop_ms": round(loop_ms, 3),
+            "launches": rs, "avg_launch_ms": round(loop_ms / rs, 5)}
+    return roof, res["out"]
+
+
+def attend_roofline(w, Q, K, V, rpc, stream, acc, reps):
+    """The attention pass alone (wc_attend: coreset staging plus the matrix-core kernel) on the
+    pivots of the selection loop and their weights, graph-replayed, against the bf16 peak."""
+    from coreset_head_rpcholesky_amd import binding
+
+    import torch
+
+    W = binding.wc_weights(V, rpc["pivots"], rpc["rank"], rpc["F"])
+    p = binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, Q.dtype)
+    ws = binding.workspace(p, Q.device)
+    flags = torch.zeros((w.heads,), dtype=torch.int32, device=Q.device)
+    O = torch.empty((w.heads, w.m, w.dv), dtype=Q.dtype, device=Q.device)
+
+    def att():
+        binding.wc_attend(Q, K, rpc["pivots"], rpc["rank"], W, flags=flags, ws=ws, out=O)
+
+    att()
+    ms = time_replays(graph_of(att), reps, stream)
+    flops = acc["attend_flops"]
+    achieved = flops / (ms / 1e3) / 1e12
+    cnt = stored_counters(w.name, "attend")
+    roof = {"kernel": "wc_attend: attend_prep_kernel (coreset staging) + attend_bf16_kernel (bf16 MFMA)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(ms, 5),
+            "flops_formula": "2 m r (d + dv + 1) per head"}
+    if cnt:
+        roof["counters"] = {k: cnt[k] for k in ("mfma_busy_frac", "mfma_flops_per_launch", "sclk_ghz")
+                            if k in cnt}
+    return roof, W
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="vit197")
+    ap.add_argument("--workload", default="long128k")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--bins", type=int, default=1,
                     help="divide-and-conquer selection with this many bins (must divide n and r)")
     ap.add_argument("--pivot-block", type=int, default=1,
                     help="block pivot selection: 16, 32 or 64 candidates per round (1: one pivot per step)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--variants", default=None,
+                    help="extra forwards timed in the same run, 'B:b,B:b' (bins:pivot_block); 'none' for none")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (at least one head)")
+    ap.add_argument("--cpu-1core-workload", default="img4096",
+                    help="workload of the one-thread oracle run ('none' to skip)")
+    ap.add_argument("--cpu-1core-budget", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true", help="skip the separate loop and attention timings")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--decode", action="store_true",
                     help="COMPRESSKV: compress the workload once, then time decode steps over the cache")
@@ -332,28 +495,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    stream = torch.cuda.current_stream()
+
     def fwd():
         binding.wc_forward(Q, K, V, w.r, seed=args.seed, bins=bins, pivot_block=pb, ws=ws, out=out)
 
-    # One forward is captured in a HIP graph and replayed: the host-side launch path (Python,
-    # ctypes, one launch per pivot step on the streaming path) would otherwise be what is timed.
-    # A graph holds `per_replay` consecutive forwards, so the replays' own launch gaps are
+    # One forward is captured in a HIP graph and replayed, so the host-side launch path
+    # (Python, ctypes, one launch per pivot step on the streaming path) is not what is timed.
+    # Short forwards are captured several to a graph, so the replays' own launch gaps are
     # amortised and back-to-back forwards run as they would inside a model.
+    fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fwd()
+    torch.cuda.synchronize()
+    once_ms = (time.perf_counter() - t0) * 1e3
     graph = None
     per_replay = 1
     if not args.no_graph:
-        per_replay = max(d for d in range(1, 11) if args.steps % d == 0)
-        fwd()
-        torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                for _ in range(per_replay):
-                    fwd()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
+        want = max(1, min(10, int(10.0 / max(once_ms, 1e-3))))
+        per_replay = max(d for d in range(1, want + 1) if args.steps % d == 0)
+        graph = graph_of(fwd, per_replay)
 
     def launch():
         if graph is not None:
@@ -365,9 +527,7 @@ def main():
     for _ in range(max(1, args.warmup // per_replay)):
         launch()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(nlaunch + 1)]
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     evs[0].record(stream)
     for i in range(nlaunch):
@@ -383,88 +543,70 @@ def main():
 
     acc = workload_accounting(w, bins)
     resident = w.dtype == "bf16" and w.n <= 256 and w.r <= 32 and bins == 1 and pb == 1
+    roof_att = None
+    reps = 2 if once_ms > 200 else 10
     if resident:
         # one launch per step: the resident kernel; only compulsory bytes reach HBM
         kernel_ms = float(np.mean(per))
         achieved = acc["compulsory_bytes"] / (kernel_ms / 1e3) / 1e9
-        traffic = stored_traffic(w.name, "resident")
+        traffic = stored_float(stored_counters(w.name, "resident"), "traffic_bytes_per_launch")
         roof = {"kernel": "resident_kernel (pivot loop + weights + attention, one workgroup per head)",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": acc["compulsory_bytes"],
                 "avg_launch_ms": round(kernel_ms, 5)}
+    elif args.no_roofline:
+        roof = None
     else:
-        # the pivot loop dominates: time wc_rpcholesky alone (graph replay) on the same stream;
-        # with bins, on the per-bin view (heads x bins sub-heads), which is what the forward runs
-        Ksel = K.view(w.heads * bins, w.n // bins, w.d)
-        pws = binding.workspace(binding.problem(w.heads * bins, w.n // bins, 0, w.d, w.dv, w.r // bins, dt_t,
-                                                1, 0, pb), dev)
-
-        def rpc():
-            binding.wc_rpcholesky(Ksel, w.r // bins, seed=args.seed, ws=pws, with_diag=False, with_trace=False,
-                                  pivot_block=pb)
-
-        rgraph = None
-        if not args.no_graph:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            rgraph = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(rgraph, stream=side):
-                    rpc()
-            torch.cuda.current_stream().wait_stream(side)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        rgraph.replay() if rgraph is not None else rpc()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        loop_ms = e0.elapsed_time(e1)
-        sub_resident = w.dtype == "bf16" and w.n // bins <= 256 and w.r // bins <= 32 and pb == 1
-        if pb > 1:
-            name = (f"block pivot selection, {w.r // bins // pb} rounds of {pb} candidates"
-                    f"{f', {w.heads * bins} bins' if bins > 1 else ''} (candidate columns: kernel part on "
-                    f"bf16 MFMA, factor part on fp32 MFMA; factor update fp32 vector)")
-            loop_bytes = None
-        elif sub_resident:
-            name = f"resident_kernel (pivot loop only, {w.heads * bins} sub-heads, factor on chip)"
-            loop_bytes = acc["pivot_resident_bytes"]
-        else:
-            name = (f"rpc_step_kernel x {w.r // bins} launches (streaming pivot loop"
-                    f"{f', {w.heads * bins} bins' if bins > 1 else ''})")
-            loop_bytes = acc["pivot_bytes"]
-        if pb > 1:
-            # candidate columns G = exp(beta K K_S^T) - F F_S^T and F_new = G M^T, per sub-head
-            Hs, ns, rs = w.heads * bins, w.n // bins, w.r // bins
-            rounds = rs // pb
-            # kernel part K K_S^T on the bf16 matrix cores; factor part F F_S^T and the update
-            # F_new = G M^T in fp32 (matrix cores and vector units share the 157.3 TFLOP/s peak).
-            # The roofline of the mix: the time both parts would take at their own peaks.
-            kflops = Hs * 2 * ns * rs * w.d
-            fflops = Hs * (ns * rs * (rs - pb) + 2 * ns * pb * rs)
-            flops = kflops + fflops
-            ideal_s = kflops / (MFMA_BF16_PEAK_TFLOPS * 1e12) + fflops / (FP32_PEAK_TFLOPS * 1e12)
-            peak = flops / ideal_s / 1e12
-            achieved = flops / (loop_ms / 1e3) / 1e12
-            roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                    "peak_of_mix": f"bf16 {MFMA_BF16_PEAK_TFLOPS} for {kflops} flops, fp32 {FP32_PEAK_TFLOPS} for {fflops}",
-                    "algorithmic_flops_per_loop": flops, "rounds": rounds, "loop_ms": round(loop_ms, 3)}
-        else:
-            achieved = loop_bytes / (loop_ms / 1e3) / 1e9
-            roof = {"kernel": name, "bound": "hbm",
-                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "algorithmic_bytes_per_loop": loop_bytes, "loop_ms": round(loop_ms, 3)}
+        roof, rpc = pivot_loop_roofline(w, K, dt_t, dev, args.seed, bins, pb, stream, acc, reps)
+        if bins == 1 and w.m > 0:
+            roof_att, _ = attend_roofline(w, Q, K, V, rpc, stream, acc, max(reps, 10))
+        del rpc
+        torch.cuda.empty_cache()
 
     exact = None
     if not args.no_exact:
         exact = exact_attention_timing(w, Q, K, V, stream)
         exact["rel_err_of_wildcat"] = error_vs_exact(w, Q, K, V, out["O"])
 
+    # the divide-and-conquer and block-pivot forwards of the same inputs
+    variants = []
+    vspec = args.variants if args.variants is not None else ",".join(
+        f"{b}:{c}" for b, c in DEFAULT_VARIANTS.get(w.name, []))
+    if vspec and vspec != "none":
+        for item in vspec.split(","):
+            vb, vp = (int(x) for x in item.split(":"))
+            if (vb, vp) == (bins, pb):
+                continue
+            vws = binding.workspace(binding.problem(w.heads, w.n, w.m, w.d, w.dv, w.r, dt_t, vb, 0, vp), dev)
+            vout = dict(O=torch.empty_like(out["O"]), pivots=torch.empty_like(out["pivots"]),
+                        rank=torch.empty_like(out["rank"]), flags=torch.empty_like(out["flags"]))
+
+            def vfwd(vb=vb, vp=vp, vws=vws, vout=vout):
+                binding.wc_forward(Q, K, V, w.r, seed=args.seed, bins=vb, pivot_block=vp, ws=vws, out=vout)
+
+            vfwd()
+            torch.cuda.synchronize()
+            vms = time_replays(graph_of(vfwd), 5, stream)
+            entry = {"bins": vb, "pivot_block": vp, "ms_per_step": round(vms, 4),
+                     "tokens_per_s": round(w.tokens / (vms / 1e3), 1),
+                     "rank_min": int(vout["rank"].min()), "flags_or": int(np.bitwise_or.reduce(vout["flags"].cpu().numpy()))}
+            if not args.no_exact:
+                entry["rel_err_vs_exact"] = error_vs_exact(w, Q, K, V, vout["O"])
+            variants.append(entry)
+            del vws, vout
+            torch.cuda.empty_cache()
+
     cpu = None
+    cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, Qn, Kn, Vn, args.cpu_budget, bins, pb)
+        if args.cpu_1core_workload != "none":
+            # the first few heads of the workload, generated alone (each head has its own stream)
+            w1 = synth.WORKLOADS[args.cpu_1core_workload]
+            Q1, K1, V1 = synth.make_inputs(w1.name, heads=range(min(w1.heads, 4)))
+            cpu1 = cpu_baseline(w1, Q1, K1, V1, args.cpu_1core_budget, threads=1)
+            cpu1["workload"] = w1.name
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -476,10 +618,14 @@ def main():
                    "tokens_per_step": w.tokens,
                    "pivot_uniforms": f"Philox4x64-10 seed {args.seed}"},
         "roofline": roof,
+        "roofline_attend": roof_att,
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
         "exact_attention": exact,
+        "variants": variants,
         "checks": {"rank_min": int(rank.min()), "flags_or": int(np.bitwise_or.reduce(flags)),
-                   "wall_s_timed": round(wall, 4), "launch": (f"hip graph replay, {per_replay} forwards per graph" if graph is not None
+                   "wall_s_timed": round(wall, 4),
+                   "launch": (f"hip graph replay, {per_replay} forwards per graph" if graph is not None
                               else "eager")},
     }
     print(json.dumps(line), flush=True)

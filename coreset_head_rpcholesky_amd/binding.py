@@ -170,7 +170,7 @@ def wc_weights(V: torch.Tensor, pivots, rank, F, *, ws=None, stream=None):
 
 
 def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, ws=None,
-              stream=None):
+              out=None, stream=None):
     """O = row-normalised exp(beta Q K_S^T) W; returns (O [H, m, dv], flags)."""
     H, m, d = Q.shape
     n = K.shape[1]
@@ -182,7 +182,11 @@ def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, 
     _check_in("W", W, torch.float32, (H, r, dv + 1), dev)
     if flags is None:
         flags = torch.zeros((H,), dtype=torch.int32, device=dev)
-    O = torch.empty((H, m, dv), dtype=Q.dtype, device=dev)
+    if out is None:
+        O = torch.empty((H, m, dv), dtype=Q.dtype, device=dev)
+    else:
+        _check_in("out", out, Q.dtype, (H, m, dv), dev)
+        O = out
     ws, nb = _ws(p, dev, ws)
     st = LIB.wc_attend(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(pivots), _ptr(rank), _ptr(W),
                        _ptr(O), _ptr(flags), _ptr(ws), nb, _stream(stream))

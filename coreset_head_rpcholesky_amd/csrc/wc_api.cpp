@@ -11,6 +11,7 @@
 #include <cstdint>
 
 #include "../../include/wc.h"
+#include "wc_host.h"
 #include "wc_kernels.h"
 
 namespace {
@@ -473,6 +474,21 @@ size_t decode_ws_bytes(const wc_problem& p, int rows) {
 
 }  // namespace
 
+namespace wc {
+
+wc_status forward_check(const wc_problem* p, const void* Q, const void* K, const void* V,
+                        const float* u_forced, const void* O, const int32_t* pivots,
+                        const int32_t* rank, const uint32_t* flags) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK || p->heads == 0) return st;
+  if (!req(K) || !req(V) || !req(rank) || !req(flags) || !opt(u_forced) || !opt(pivots))
+    return WC_ERR_INVALID_ARG;
+  if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
+  return WC_OK;
+}
+
+}  // namespace wc
+
 extern "C" {
 
 int32_t wc_abi_version(void) { return WC_ABI_VERSION; }
@@ -557,12 +573,8 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
 wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
                      const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
-  wc_status st = check_problem(p);
-  if (st != WC_OK) return st;
-  if (p->heads == 0) return WC_OK;
-  if (!req(K) || !req(V) || !req(rank) || !req(flags) || !opt(u_forced) || !opt(pivots))
-    return WC_ERR_INVALID_ARG;
-  if (p->m > 0 && (!req(Q) || !req(O))) return WC_ERR_INVALID_ARG;
+  wc_status st = wc::forward_check(p, Q, K, V, u_forced, O, pivots, rank, flags);
+  if (st != WC_OK || p->heads == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (centred(*p)) {
     // every step below runs on the centred keys, kept after the forward's own workspace

@@ -199,6 +199,8 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y, sp = blockIdx.z;
   const int m = a.m, rp = staged_rows(a), nchk = scanned_rows(a) / 32;
+  // rows at or past the scan bound carry no weight even when the staged row is not zero
+  const int lim = a.scan_rows ? a.scan_rows : rp;
   const int q = blockIdx.x * 128 + wid * 32 + l32;
   const bool qv = q < m;
   const float bl2e = a.beta_log2e;
@@ -260,7 +262,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int jj = 8 * (v >> 2) + 4 * g + (v & 3);
-      const float p = __builtin_amdgcn_exp2f(sc[v] * bl2e);
+      const float p = c * 32 + jj < lim ? __builtin_amdgcn_exp2f(sc[v] * bl2e) : 0.f;
       den = fmaf(p, sWd[jj], den);
       __bf16 hi, lo;
       split_bf16(p, hi, lo);
@@ -454,6 +456,19 @@ __device__ __forceinline__ void attend_step(const AttendChunk<D, DV>& bS, int uS
   }
 }
 
+// Scores of one 32-row unit whose rows from `left` on lie past the scan bound: set to -inf, so
+// that their probabilities are exactly zero (row of accumulator entry v: 8(v/4) + 4g + v%4).
+template <int NQ>
+__device__ __forceinline__ void attend_mask(f32x16 (&sc)[NQ], int left, int g) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const bool out = 8 * (v >> 2) + 4 * g + (v & 3) >= left;
+#pragma unroll
+    for (int s = 0; s < NQ; ++s)
+      if (out) sc[s][v] = -__builtin_inff();
+  }
+}
+
 // Workgroup of kAttendWaves waves (one per SIMD), each taking kAttendNQ groups of 32 queries.
 #ifndef WC_ATTEND_XCD
 #define WC_ATTEND_XCD 1
@@ -547,13 +562,19 @@ attend_bf16_kernel(AttendArgs a) {
     // c-1, with the chunks after it still in flight; that barrier also frees slot
     // (c+R-1) % R = (c-1) % R, whose last reads (values of unit 2c-1) come before it.
     constexpr int R = kAttendRing;
+    // rows at or past the scan bound carry no weight even when the staged row is not zero: the
+    // scores of a unit that crosses it are set to -inf before they are exponentiated
+    const int lim = a.scan_rows ? a.scan_rows : rp;
     for (int c = 0; c < nc; ++c) {
       const int bc = c % R, bn = (c + 1) % R, bl = c == 0 ? bc : (c + R - 1) % R;
+      const int left = lim - (c0 + c) * 64;  // rows of this chunk below the bound
+      if (left < 32) attend_mask<NQ>(scA, left, g);
       attend_step<D, DV, NQ>(sb[bc], 1, sb[bc], 0, sb[bl], c == 0 ? 0 : 1, qb, y, den, scA, scB, pbA, pbB, g, l32);
       // chunk c+1 landed; chunks c+2 .. c+R-2 (those issued) may still be loading
       attend_wait<D, DV>(min(nc, c + R - 1) - (c + 2), wid);
       __syncthreads();
       if (c + R - 1 < nc) attend_issue(sb[(c + R - 1) % R], KSh, Wph, Wdh, c0 + c + R - 1, wid, lane);
+      if (left < 64) attend_mask<NQ>(scB, left - 32, g);
       // the scores of unit 2c+2 are garbage past the last chunk and are never exponentiated
       attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
     }

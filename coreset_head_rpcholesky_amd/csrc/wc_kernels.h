@@ -138,7 +138,8 @@ struct AttendArgs {
   float* Yout;            // NULL, or [H][yrows][dv+1]: the unnormalised Y in fp32 instead of O
   int yrows;
   int ldrows;             // staged rows per head (0: attend_rows(r)); a cache uses its capacity
-  int scan_rows;          // rows the attention scans (0: all staged rows); rows past it are zero
+  int scan_rows;          // rows the attention scans (0: all staged rows); rows at or past it get
+                          // zero probability whatever the staged row holds
   int row0;               // first row written by the append staging
 };
 // coreset rows as the attention kernels store them: r rounded up to whole 128-row blocks

@@ -205,8 +205,8 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
  * the attention kernels: keys as bf16 (hi and lo parts for fp32 problems), weights as bf16
  * (hi and lo for fp32) with the normaliser column also in fp32.  `p` gives heads, d, dv and
  * dtype for every cache call, n and r for wc_compress, m for wc_decode; the same capacity
- * must be passed to every call on one cache.  Rows past the last written one must be zero
- * (wc_compress leaves them so; append in order).                                             */
+ * must be passed to every call on one cache.  wc_decode reads rows [0, rows) only: whatever
+ * rows at or past `rows` hold (later appends, stale rows) takes no part in the output.       */
 
 /* Bytes of a cache with `capacity` rows per head (capacity >= 1). */
 wc_status wc_cache_bytes(const wc_problem* p, int32_t capacity, size_t* bytes);

@@ -142,3 +142,27 @@ def test_decode_kernel_few_queries(wc, d, dv, n, m):
         assert rel(O[h], ow.exact_attention(Q[h][:m], K[h], V[h])) < TOL["bf16"]
     O9 = host(wc.wc_decode(Qd, cache, cap, n, dv)[0])
     assert rel(O, O9[:, :m]) < 5e-3, rel(O, O9[:, :m])
+
+
+@pytest.mark.parametrize("dtype,m,d,dv,n,rows", [("bf16", 9, 128, 128, 300, 200), ("bf16", 1, 64, 64, 300, 70),
+                                                 ("f32", 3, 64, 128, 250, 150), ("bf16", 40, 64, 64, 700, 513)])
+def test_decode_prefix_of_written_rows(wc, dtype, m, d, dv, n, rows):
+    """Rows written past `rows` (here every key is appended, then a shorter prefix is decoded)
+    take no part in the output, on the decode kernel (m <= 8, bf16) and on the attention
+    kernels (more queries, or fp32), whose scan covers whole 128-row blocks."""
+    import torch
+
+    H = 2
+    Q, K, V = synth.random_inputs(H, n, m, d, dv, seed=850 + rows, dtype=dtype, kind="iid_clip", clip=2.0)
+    cap = n + 30
+    p = wc.problem(H, n, m, d, dv, 1, wc.WC_BF16 if dtype == "bf16" else wc.WC_F32)
+    cache = torch.zeros(wc.wc_cache_bytes(p, cap), dtype=torch.uint8, device="cuda")
+    wc.wc_cache_append(cache, dev(K, dtype), dev(V, dtype), 0, cap)
+    O, flags = wc.wc_decode(dev(Q, dtype), cache, cap, rows, dv)
+    O = host(O)
+    assert np.all(host(flags) == 0)
+    for h in range(H):
+        ref = ow.exact_attention(Q[h], K[h][:rows], V[h][:rows])
+        assert rel(O[h], ref) < TOL[dtype], (h, rel(O[h], ref))
+        full = ow.exact_attention(Q[h], K[h], V[h])
+        assert rel(O[h], full) > 5 * TOL[dtype]  # the rows past the prefix would matter
