@@ -50,6 +50,7 @@ def _load():
         "wc_weights": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_attend": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_forward": ([P, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_forward_noalloc": ([P, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp], ctypes.c_int),
         "wc_cache_bytes": ([P, ctypes.c_int32, ctypes.POINTER(sz)], ctypes.c_int),
         "wc_compress": ([P, vp, vp, vp, u64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_cache_append": ([P, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int32, vp], ctypes.c_int),
@@ -222,6 +223,37 @@ def wc_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_f
                         _ptr(out["rank"]), _ptr(out["flags"]), _ptr(ws), nb, _stream(stream))
     if st != WC_OK:
         raise WcError("wc_forward", st)
+    return out
+
+
+WC_NOALLOC_MAX_WORKSPACE = 256 << 20  # bytes of the library's own workspace per device
+
+
+def wc_forward_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, r: int, *, u_forced=None,
+                       seed: int = 0, bins: int = 1, bin_weights: bool = False, center_keys: bool = False,
+                       pivot_block: int = 1, out=None, stream=None):
+    """wc_forward with the library's own workspace (no workspace argument); with ``out`` given
+    the call allocates nothing.  Returns dict(O, pivots, rank, flags)."""
+    H, m, d = Q.shape
+    n = K.shape[1]
+    dv = V.shape[2]
+    dev = Q.device
+    opts = (WC_OPT_BIN_WEIGHTS if bin_weights else 0) | (WC_OPT_CENTER_KEYS if center_keys else 0)
+    p = problem(H, n, m, d, dv, r, Q.dtype, bins, opts, pivot_block)
+    _check_in("K", K, Q.dtype, (H, n, d), dev)
+    _check_in("V", V, Q.dtype, (H, n, dv), dev)
+    if u_forced is not None:
+        _check_in("u_forced", u_forced, torch.float32, (H, _draws(r, pivot_block)), dev)
+    if out is None:
+        out = dict(O=torch.empty((H, m, dv), dtype=Q.dtype, device=dev),
+                   pivots=torch.empty((H, r), dtype=torch.int32, device=dev),
+                   rank=torch.empty((H,), dtype=torch.int32, device=dev),
+                   flags=torch.empty((H,), dtype=torch.int32, device=dev))
+    st = LIB.wc_forward_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(u_forced),
+                                int(seed) & (2**64 - 1), _ptr(out["O"]), _ptr(out["pivots"]),
+                                _ptr(out["rank"]), _ptr(out["flags"]), _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_forward_noalloc", st)
     return out
 
 

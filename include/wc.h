@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 6
+#define WC_ABI_VERSION 7
 
 typedef enum {
   WC_OK = 0,
@@ -191,6 +191,19 @@ wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int
 wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const void* V,
                      const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
                      int32_t* rank, uint32_t* flags, void* ws, size_t ws_bytes, void* stream);
+
+/* wc_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same arguments and results as
+ * wc_forward, with no workspace argument.  The workspace is a device array inside the library,
+ * WC_NOALLOC_MAX_WORKSPACE bytes, which every device the library runs on holds until the
+ * process ends.  A problem whose wc_workspace_bytes() exceeds it returns WC_ERR_WORKSPACE
+ * and enqueues nothing.  The call allocates and frees nothing.  All calls on one device share
+ * that device's array: calls that overlap on one device (different streams, or host threads)
+ * race on it and must be ordered by the caller.                                              */
+#define WC_NOALLOC_MAX_WORKSPACE ((size_t)256 << 20)
+wc_status wc_forward_noalloc(const wc_problem* p, const void* Q, const void* K, const void* V,
+                             const float* u_forced, uint64_t seed, void* O, int32_t* pivots,
+                             int32_t* rank, uint32_t* flags, void* stream);
 
 /* ---- COMPRESSKV: a compressed KV cache and decode over it ----------------------------------
  * gist.science/de/paper/2602.10056, "Zentrale Beitraege": a COMPRESSKV module shrinks the KV

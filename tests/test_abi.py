@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 6
+    assert lib.wc_abi_version() == 7
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
