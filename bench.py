@@ -61,6 +61,14 @@ DEFAULT_VARIANTS = {
 }
 
 
+_T0 = time.perf_counter()
+
+
+def log(msg: str) -> None:
+    """Progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"[bench {time.perf_counter() - _T0:7.1f}s] {msg}", file=sys.stderr, flush=True)
+
+
 def source_hash(kind: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
@@ -475,6 +483,7 @@ def main():
         return torch.from_numpy(x).to(dev, dt_t).contiguous()
 
     Q, K, V = up(Qn), up(Kn), up(Vn)
+    log(f"inputs of {w.name} resident on the GPU")
     if args.decode:
         run_decode(args, w, Q, K, V, dt_t, dev)
         return
@@ -510,6 +519,7 @@ def main():
     fwd()
     torch.cuda.synchronize()
     once_ms = (time.perf_counter() - t0) * 1e3
+    log(f"two forwards done ({once_ms:.1f} ms the second)")
     graph = None
     per_replay = 1
     if not args.no_graph:
@@ -535,6 +545,7 @@ def main():
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    log(f"{args.steps} timed forwards done")
     per = [evs[i].elapsed_time(evs[i + 1]) / per_replay for i in range(nlaunch)]
     ms = evs[0].elapsed_time(evs[nlaunch]) / args.steps
     value = w.tokens / (ms / 1e3)
@@ -564,6 +575,7 @@ def main():
         del rpc
         torch.cuda.empty_cache()
 
+    log("rooflines done")
     exact = None
     if not args.no_exact:
         exact = exact_attention_timing(w, Q, K, V, stream)
@@ -597,6 +609,7 @@ def main():
             del vws, vout
             torch.cuda.empty_cache()
 
+    log("exact attention and variants done")
     cpu = None
     cpu1 = None
     if not args.no_cpu_baseline:
