@@ -22,38 +22,74 @@ namespace wc {
 constexpr int NT = kStreamThreads;  // 256
 constexpr int NW = NT / 64;
 
-// dot(k_i, ks) for one key row against a key staged in LDS as fp32, fixed order.
-template <int D>
-__device__ __forceinline__ float row_dot(const uint16_t* krow, const float* ks) {
-  float a0 = 0.f, a1 = 0.f;
-  const uint4* src = reinterpret_cast<const uint4*>(krow);
-#pragma unroll 4
-  for (int q = 0; q < D / 8; ++q) {
-    const uint4 v = src[q];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a0 = fmaf(__uint_as_float(w[e] << 16), ks[8 * q + 2 * e], a0);
-      a1 = fmaf(__uint_as_float(w[e] & 0xffff0000u), ks[8 * q + 2 * e + 1], a1);
-    }
-  }
-  return a0 + a1;
-}
-template <int D>
-__device__ __forceinline__ float row_dot(const float* krow, const float* ks) {
-  float a0 = 0.f, a1 = 0.f;
-  const float4* src = reinterpret_cast<const float4*>(krow);
-#pragma unroll 4
-  for (int q = 0; q < D / 4; ++q) {
-    const float4 v = src[q];
-    a0 = fmaf(v.x, ks[4 * q], a0);
-    a1 = fmaf(v.y, ks[4 * q + 1], a1);
-    a0 = fmaf(v.z, ks[4 * q + 2], a0);
-    a1 = fmaf(v.w, ks[4 * q + 3], a1);
-  }
-  return a0 + a1;
+// ---- key dots k_i . k_s with one 16-byte piece of a key row per lane ------------------------
+// A key row is KL = D sizeof(T) / 16 pieces; KL consecutive lanes read one row (a wave reads
+// 64 / KL whole rows with one coalesced load), each lane forms the dot of its piece with the
+// same piece of k_s, and the KL partial sums are added by an xor butterfly.  Every lane of the
+// group ends with the same value, and any row, wherever it sits in a wave, is summed in the
+// same order, so the pivot's own entry H_ss equals the one its column holds.
+template <typename T, int D>
+struct KeyPieces {
+  static constexpr int KL = D * (int)sizeof(T) / 16;  // lanes per key row
+  static constexpr int RPL = 64 / KL;                 // key rows per wave load
+};
+
+typedef __attribute__((ext_vector_type(4))) float v4f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
+// Sum over aligned groups of G lanes (G = 8, 16 or 32), the result in every lane of the group.
+template <int G>
+__device__ __forceinline__ float group_sum(float a) {
+  a += dpp_f<0xB1>(a);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  a += dpp_f<0x4E>(a);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  a += dpp_f<0x141>(a);  // row_half_mirror: the other quad of the 8 lanes
+  if constexpr (G >= 16) a += dpp_f<0x140>(a);  // row_mirror: the other 8 lanes of the 16
+  if constexpr (G >= 32) a += __shfl_xor(a, 16, 64);
+  return a;
+}
+
+// Dot of one 16-byte piece of a key row with the same piece of k_s (fixed order).
+__device__ __forceinline__ float piece_dot(uint4 v, uint4 k, uint16_t) {
+  float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), __builtin_bit_cast(bf16x2, k.x), 0.f, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), __builtin_bit_cast(bf16x2, k.y), a, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), __builtin_bit_cast(bf16x2, k.z), a, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), __builtin_bit_cast(bf16x2, k.w), a, false);
+}
+__device__ __forceinline__ float piece_dot(uint4 v, uint4 k, float) {
+  float a = __uint_as_float(v.x) * __uint_as_float(k.x);
+  a = fmaf(__uint_as_float(v.y), __uint_as_float(k.y), a);
+  a = fmaf(__uint_as_float(v.z), __uint_as_float(k.z), a);
+  return fmaf(__uint_as_float(v.w), __uint_as_float(k.w), a);
+}
+
+// k_i . k_s for the key rows [r0, r0 + NT RPT) of a workgroup into s_dot (rows past n: 0).
+// kpiece: this lane's piece of k_s (piece lane % KL).  Wave w takes rows r0 + 64 RPT w + ...
+template <typename T, int D, int RPT>
+__device__ __forceinline__ void block_key_dots(const T* K, int r0, int n, uint4 kpiece, float* s_dot) {
+  using P = KeyPieces<T, D>;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int c = lane % P::KL, sub = lane / P::KL;
+  const int w0 = wid * 64 * RPT;
+  const uint4* Kp = reinterpret_cast<const uint4*>(K);
+#pragma unroll 8
+  for (int k = 0; k < RPT * P::KL; ++k) {
+    const int row = r0 + w0 + k * P::RPL + sub;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < n) v = Kp[(size_t)row * P::KL + c];
+    const float a = group_sum<P::KL>(piece_dot(v, kpiece, T{}));
+    if (c == 0) s_dot[w0 + k * P::RPL + sub] = a;
+  }
+}
+
+// Each step reads F[:, :t] once.  When the whole factor is larger than the 256 MB last-level
+// cache (MALL) it comes from HBM every step anyway, and nontemporal loads keep the stream from
+// displacing the keys and the residual; a smaller factor stays cached between steps and is
+// read with ordinary loads.
+constexpr size_t kMallBytes = size_t(256) << 20;
 // RPT contiguous floats (RPT = 4: one 16-byte access; the caller guarantees alignment).
 template <int RPT>
 __device__ __forceinline__ void load_rows(const float* p, float* v) {
@@ -65,6 +101,18 @@ __device__ __forceinline__ void load_rows(const float* p, float* v) {
     for (int e = 0; e < RPT; ++e) v[e] = p[e];
   }
 }
+template <int RPT, bool NTL>
+__device__ __forceinline__ void load_factor_rows(const float* p, float* v) {
+  if constexpr (!NTL) {
+    load_rows<RPT>(p, v);
+  } else if constexpr (RPT == 4) {
+    const v4f x = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) v[e] = __builtin_nontemporal_load(p + e);
+  }
+}
 template <int RPT>
 __device__ __forceinline__ void store_rows(float* p, const float* v) {
   if constexpr (RPT == 4) {
@@ -73,14 +121,6 @@ __device__ __forceinline__ void store_rows(float* p, const float* v) {
 #pragma unroll
     for (int e = 0; e < RPT; ++e) p[e] = v[e];
   }
-}
-
-// dot(k_i, k_s) for the RPT contiguous rows i0 .. i0 + RPT - 1 (k_s staged in LDS as fp32);
-// the same association order as row_dot.
-template <typename T, int D, int RPT>
-__device__ __forceinline__ void multi_row_dot(const T* K, int i0, int n, const float* ks, float* out) {
-#pragma unroll
-  for (int e = 0; e < RPT; ++e) out[e] = (i0 + e < n) ? row_dot<D>(K + (size_t)(i0 + e) * D, ks) : 0.f;
 }
 
 // Block-wide fp64 sum in a fixed order (wave trees, then waves in order); all threads get it.
@@ -128,11 +168,6 @@ __device__ __forceinline__ int block_min_int(int v, int* red) {
 }
 __device__ __forceinline__ int block_max_int(int v, int* red) {
   return -block_min_int(-v, red);
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void load_key_lds(const T* krow, float* ks) {
-  for (int e = threadIdx.x; e < D; e += NT) ks[e] = ld_elem<T>(krow + e);
 }
 
 // Pivot uniforms of every (head, step), drawn once before the loop.
@@ -188,11 +223,11 @@ __global__ void __launch_bounds__(NT) rpc_init_kernel(StreamRpcArgs a, int rows)
   }
 }
 
-template <typename T, int D, int RPT>
+template <typename T, int D, int RPT, bool NTL>
 __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows, int t) {
   __shared__ double red[NW];
   __shared__ int ired[NW];
-  __shared__ __attribute__((aligned(16))) float s_ks[D];
+  __shared__ __attribute__((aligned(16))) float s_dot[NT * RPT];
   extern __shared__ __attribute__((aligned(16))) double s_dyn[];
   double* s_part = s_dyn;                                   // [nblk]
   float* s_fs = reinterpret_cast<float*>(s_dyn + a.nblk);   // [r]
@@ -285,8 +320,8 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
     return;
   }
 
-  // ---- 3. gather k_s and F[s, :t]; g_s ----
-  load_key_lds<T, D>(K + (size_t)s * D, s_ks);
+  // ---- 3. gather k_s (this lane's piece) and F[s, :t]; g_s ----
+  const uint4 kpiece = reinterpret_cast<const uint4*>(K + (size_t)s * D)[(threadIdx.x & 63) % KeyPieces<T, D>::KL];
   double sq = 0.0;
   for (int j = tid; j < t; j += NT) {
     const float v = F[(size_t)j * n + s];
@@ -300,7 +335,7 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
     sq = (double)part_sq;
   }
   const double sqt = block_sum(sq, red);
-  hss = __builtin_amdgcn_exp2f(row_dot<D>(K + (size_t)s * D, s_ks) * a.beta_log2e);
+  hss = __builtin_amdgcn_exp2f(group_sum<KeyPieces<T, D>::KL>(piece_dot(kpiece, kpiece, T{})) * a.beta_log2e);
   const float gs = hss - (float)sqt;
   if (!(gs > 0.f) || !__builtin_isfinite(gs)) {
     if (lead) {
@@ -322,11 +357,12 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
   // flight at once to keep enough bytes outstanding per CU for HBM.
   double mass = 0.0;
   const int i0 = b * rows + tid * RPT;
+  block_key_dots<T, D, RPT>(K, b * rows, n, kpiece, s_dot);
+  __syncthreads();
   if (i0 < n) {
     float hcol[RPT];
-    multi_row_dot<T, D, RPT>(K, i0, n, s_ks, hcol);
 #pragma unroll
-    for (int e = 0; e < RPT; ++e) hcol[e] = __builtin_amdgcn_exp2f(hcol[e] * a.beta_log2e);
+    for (int e = 0; e < RPT; ++e) hcol[e] = __builtin_amdgcn_exp2f(s_dot[tid * RPT + e] * a.beta_log2e);
     float acc[RPT];
 #pragma unroll
     for (int e = 0; e < RPT; ++e) acc[e] = 0.f;
@@ -336,7 +372,7 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
     for (; j + U <= t; j += U) {
       float fv[U][RPT];
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_rows<RPT>(Fi + (size_t)(j + u) * n, fv[u]);
+      for (int u = 0; u < U; ++u) load_factor_rows<RPT, NTL>(Fi + (size_t)(j + u) * n, fv[u]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float fs = s_fs[j + u];
@@ -346,7 +382,7 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
     }
     for (; j < t; ++j) {
       float fv[RPT];
-      load_rows<RPT>(Fi + (size_t)j * n, fv);
+      load_factor_rows<RPT, NTL>(Fi + (size_t)j * n, fv);
       const float fs = s_fs[j];
 #pragma unroll
       for (int e = 0; e < RPT; ++e) acc[e] = fmaf(fv[e], fs, acc[e]);
@@ -408,11 +444,16 @@ static hipError_t run_rpc(StreamRpcArgs a, int rows, hipStream_t st) {
   hipLaunchKernelGGL((rpc_init_kernel<T, D>), grid, dim3(NT), 0, st, a, rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const bool nt = (size_t)a.H * a.r * a.n * sizeof(float) > kMallBytes;
   for (int t = 0; t < a.r; ++t) {
-    if (rows == 4 * NT)
-      hipLaunchKernelGGL((rpc_step_kernel<T, D, 4>), grid, dim3(NT), lds, st, a, rows, t);
+    if (rows == 4 * NT && nt)
+      hipLaunchKernelGGL((rpc_step_kernel<T, D, 4, true>), grid, dim3(NT), lds, st, a, rows, t);
+    else if (rows == 4 * NT)
+      hipLaunchKernelGGL((rpc_step_kernel<T, D, 4, false>), grid, dim3(NT), lds, st, a, rows, t);
+    else if (nt)
+      hipLaunchKernelGGL((rpc_step_kernel<T, D, 1, true>), grid, dim3(NT), lds, st, a, rows, t);
     else
-      hipLaunchKernelGGL((rpc_step_kernel<T, D, 1>), grid, dim3(NT), lds, st, a, rows, t);
+      hipLaunchKernelGGL((rpc_step_kernel<T, D, 1, false>), grid, dim3(NT), lds, st, a, rows, t);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -122,22 +122,60 @@ def rpcholesky(K, r, uniforms, beta=None):
     return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=rank, flags=flags)
 
 
+def rpcholesky_follow(K, pivots, uniforms, beta=None):
+    """The pivot loop of rpcholesky driven by a given pivot sequence instead of its own draws.
+
+    At step t the residual diagonal is that of the given pivots before t; the step records the
+    running-sum interval [C_{s-1}, C_s) of the given pivot s, the total T_t, and the index the
+    draw u_t itself selects there (sample_pivot), then eliminates s as rpcholesky does.  With
+    the loop's own pivots every u_t T_t lies in its interval; where another implementation's
+    pivots part from the draws, the intervals tell how far u_t T_t lies from the choice made.
+    Returns dict(lo, hi, T [len(pivots)] (fp64), chosen [len(pivots)] (the draw's own index),
+    F [n, len(pivots)]).  Stops early (arrays cut) when a given pivot has no residual left.
+    """
+    K = np.asarray(K, np.float64)
+    n, d = K.shape
+    beta = beta_of(d) if beta is None else beta
+    pivots = np.asarray(pivots, np.int64)
+    r = len(pivots)
+    diag = initial_residual(K, beta)
+    F = np.zeros((n, r))
+    lo, hi, T, chosen = np.zeros(r), np.zeros(r), np.zeros(r), -np.ones(r, np.int64)
+    for t in range(r):
+        s = int(pivots[t])
+        own, Tt, C = sample_pivot(diag, uniforms[t])
+        T[t], chosen[t] = Tt, own
+        lo[t] = C[s - 1] if s > 0 else 0.0
+        hi[t] = C[s]
+        g = np.exp(beta * (K @ K[s])) - F[:, :t] @ F[s, :t]
+        if not (np.isfinite(g[s]) and g[s] > 0.0):
+            return dict(lo=lo[:t], hi=hi[:t], T=T[:t], chosen=chosen[:t], F=F[:, :t])
+        F[:, t] = g / np.sqrt(g[s])
+        diag = diag - F[:, t] ** 2
+        diag[s] = 0.0
+    return dict(lo=lo, hi=hi, T=T, chosen=chosen, F=F)
+
+
 BLOCK_DRAWS = 4  # candidates drawn per pivot slot at most, in block pivot selection
 
 
-def round_candidates(diag, uniforms):
+def round_candidates(diag, uniforms, margins=None):
     """Candidates of one round of block pivot selection: drawn one after the other from the
     residual diagonal at the start of the round without replacement, i.e. candidate j is the
     inverse-CDF draw (sample_pivot) from the masses with the round's earlier candidates set to
-    zero.  Stops early when no mass is left."""
+    zero.  Stops early when no mass is left.  ``margins``: if given, a list that receives, per
+    draw, the distance from u T to the nearer end of the chosen interval, over T."""
     p = np.maximum(np.asarray(diag, np.float64), 0.0)
     S = []
     for u in uniforms:
         q = p.copy()
         q[S] = 0.0
-        s, _, _ = sample_pivot(q, u)
+        s, T, C = sample_pivot(q, u)
         if s < 0:
             break
+        if margins is not None:
+            lo = C[s - 1] if s > 0 else 0.0
+            margins.append(min(float(u) * T - lo, C[s] - float(u) * T) / T)
         S.append(s)
     return S
 
@@ -160,7 +198,9 @@ def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
     mass, or running out of draws, stops the loop with rank < r (breakdown).  Pivots fill
     slots 0 .. rank-1 in order, so F[S, :] is lower triangular as for single pivots; trace[t]
     is the total before the round that started with t slots full (other entries zero), and
-    trace[r] the total after the last one.
+    trace[r] the total after the last one.  Also returned: ``margins`` [BLOCK_DRAWS r], per
+    draw the distance from u T to the nearer end of the interval it selects over T (nan for
+    draws never made), and ``slot_round`` [r], the round that filled each slot (-1 if none).
     """
     K = np.asarray(K, np.float64)
     n, d = K.shape
@@ -172,13 +212,17 @@ def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
     F = np.zeros((n, r))
     pivots = -np.ones(r, np.int64)
     trace = np.zeros(r + 1)
+    margins = np.full(BLOCK_DRAWS * r, np.nan)
+    slot_round = -np.ones(r, np.int64)
     filled, flags = 0, 0
     if not np.all(np.isfinite(K)):
         flags |= FLAG_NONFINITE
     for k in range(BLOCK_DRAWS * r // b):
         if filled == r:
             break
-        S = round_candidates(diag, uniforms[k * b:(k + 1) * b])
+        mk = []
+        S = round_candidates(diag, uniforms[k * b:(k + 1) * b], mk)
+        margins[k * b:k * b + len(mk)] = mk
         T = np.cumsum(np.maximum(diag, 0.0))[-1]
         trace[filled] = T if np.isfinite(T) else 0.0
         if not S:
@@ -194,6 +238,7 @@ def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
                 continue
             F[:, filled] = g / np.sqrt(g[s])
             pivots[filled] = s
+            slot_round[filled] = k
             filled += 1
         diag = diag - np.sum(F[:, f0:filled] ** 2, axis=1)
         diag[pivots[f0:filled]] = 0.0
@@ -201,7 +246,8 @@ def rpcholesky_block(K, r, uniforms, b, beta=None, tol=DEPENDENT_TOL):
         trace[r] = np.cumsum(np.maximum(diag, 0.0))[-1]
     else:
         flags |= FLAG_BREAKDOWN
-    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=filled, flags=flags)
+    return dict(pivots=pivots, F=F, diag=diag, trace=trace, rank=filled, flags=flags, margins=margins,
+                slot_round=slot_round)
 
 
 def snap_uniforms_block(K, r, b, raw_uniforms, beta=None, tol=DEPENDENT_TOL):
@@ -255,7 +301,7 @@ def snap_uniforms_block(K, r, b, raw_uniforms, beta=None, tol=DEPENDENT_TOL):
     return out
 
 
-def snap_uniforms(K, r, raw_uniforms, beta=None):
+def snap_uniforms(K, r, raw_uniforms, beta=None, with_pivots=False):
     """Forced-uniform mode: move each u_t to the middle of the CDF interval it selects.
 
     Runs the pivot loop with the raw draws; at step t the selected index s keeps its
@@ -264,12 +310,14 @@ def snap_uniforms(K, r, raw_uniforms, beta=None):
     implementation whose running sum is within half the interval of the oracle's then picks
     the same pivot.  Returns (snapped [r] float32, margin [r]): margin_t is the distance
     from u_t T to the nearer interval end, over T.  Steps after a breakdown keep u = 0.
+    With ``with_pivots`` the pivots of the run (-1 after a breakdown) come third.
     """
     K = np.asarray(K, np.float64)
     n, d = K.shape
     beta = beta_of(d) if beta is None else beta
     snapped = np.zeros(r, np.float32)
     margin = np.zeros(r)
+    piv = -np.ones(r, np.int64)
     diag = initial_residual(K, beta)
     F = np.zeros((n, r))
     for t in range(r):
@@ -291,7 +339,8 @@ def snap_uniforms(K, r, raw_uniforms, beta=None):
         F[:, t] = g / np.sqrt(g[s])
         diag = diag - F[:, t] ** 2
         diag[s] = 0.0
-    return snapped, margin
+        piv[t] = s
+    return (snapped, margin, piv) if with_pivots else (snapped, margin)
 
 
 def weights(K, V, pivots, beta=None):

@@ -12,7 +12,7 @@ import pytest
 from coreset_head_rpcholesky_amd import synth
 from oracle import philox
 from oracle import wildcat as ow
-from tests.gpu_util import TOL, dev, host, rel, snapped_binned
+from tests.gpu_util import TOL, check_output, dev, host, pivot_report, rel, snapped_binned
 
 pytestmark = pytest.mark.gpu
 
@@ -56,8 +56,7 @@ def test_binned_forward_parity(wc, case, mode):
         ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h], weights_mode=mode)
         assert np.array_equal(piv[h], ref["pivots"]), (h, piv[h], ref["pivots"])
         assert rank[h] == ref["rank"] and flags[h] == ref["flags"], (rank[h], flags[h])
-        ok = ref["kappa"] < 1e6
-        assert rel(O[h][ok], ref["O"][ok]) < TOL[dtype], (h, rel(O[h][ok], ref["O"][ok]))
+        check_output(O[h], ref["O"], ref["kappa"], dtype, f"{__name__}:{h}")
 
 
 def test_one_bin_is_the_plain_forward(wc):
@@ -96,9 +95,16 @@ def test_binned_seeded_mode(wc, n, r, B):
     out = wc.wc_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), r, seed=seed, bins=B)
     piv = host(out["pivots"])
     agree = 0
+    nb, rb = n // B, r // B
     for h in range(H):
-        u = np.concatenate([philox.pivot_uniforms(seed, h * B + b, r // B) for b in range(B)])
-        agree += np.array_equal(piv[h], ow.forward_binned(Q[h], K[h], V[h], r, B, u)["pivots"])
+        u = np.concatenate([philox.pivot_uniforms(seed, h * B + b, rb) for b in range(B)])
+        same = np.array_equal(piv[h], ow.forward_binned(Q[h], K[h], V[h], r, B, u)["pivots"])
+        agree += same
+        if not same:  # bin by bin, only rounding may separate the device's choice from the draw
+            for b in range(B):
+                rep = pivot_report(K[h][b * nb:(b + 1) * nb], piv[h][b * rb:(b + 1) * rb] - b * nb,
+                                   u[b * rb:(b + 1) * rb])
+                assert rep["excess"] <= 1.0, (h, b, rep)
     assert agree >= H - 1, agree
 
 

@@ -10,7 +10,7 @@ import pytest
 from coreset_head_rpcholesky_amd import synth
 from oracle import philox
 from oracle import wildcat as ow
-from tests.gpu_util import TOL, dev, host, rel, snapped_block
+from tests.gpu_util import TOL, cdf_bound, check_output, dev, host, rel, snapped_block
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +71,7 @@ def test_block_forward_parity(wc, case):
         ref = ow.forward_binned(Q[h], K[h], V[h], r, B, U[h], weights_mode=mode, pivot_block=b)
         assert np.array_equal(piv[h], ref["pivots"]), h
         assert rank[h] == ref["rank"] and flags[h] == ref["flags"], (rank[h], flags[h], ref["rank"], ref["flags"])
-        ok = ref["kappa"] < 1e6
-        assert rel(O[h][ok], ref["O"][ok]) < TOL[dtype], (h, rel(O[h][ok], ref["O"][ok]))
+        check_output(O[h], ref["O"], ref["kappa"], dtype, f"{__name__}:{h}")
 
 
 def test_block_seeded_mode(wc):
@@ -81,8 +80,19 @@ def test_block_seeded_mode(wc):
     _, K, _ = synth.random_inputs(H, n, 1, 64, 64, seed=960, dtype="bf16", kind="mixture")
     out = wc.wc_rpcholesky(dev(K, "bf16"), r, seed=77, pivot_block=b)
     piv = host(out["pivots"])
-    agree = sum(np.array_equal(piv[h], ow.rpcholesky_block(
-        K[h], r, np.array(philox.pivot_uniforms(77, h, ow.BLOCK_DRAWS * r)), b)["pivots"]) for h in range(H))
+    agree = 0
+    for h in range(H):
+        ref = ow.rpcholesky_block(K[h], r, np.array(philox.pivot_uniforms(77, h, ow.BLOCK_DRAWS * r)), b)
+        diff = np.nonzero(piv[h] != ref["pivots"])[0]
+        agree += len(diff) == 0
+        if len(diff):
+            # only rounding may separate them: some draw of the rounds up to the one that
+            # filled the first differing slot lies within rounding of an interval end
+            k = ref["slot_round"][diff[0]]
+            f0 = int(np.nonzero(ref["slot_round"] == k)[0][0])
+            Hd = ow.initial_residual(K[h], 1.0 / np.sqrt(K.shape[2]))
+            bound = cdf_bound(f0, Hd.sum() - Hd[ref["pivots"][:f0]].sum(), ref["trace"][f0])
+            assert np.nanmin(ref["margins"][:(k + 1) * b]) <= bound, (h, diff[0], k)
     assert agree >= H - 1, agree
 
 

@@ -2,9 +2,10 @@
 (one wc_forward over all heads, captured in a HIP graph and replayed).
 
 vit197, iid1k and img4096 are checked element by element against the oracle under snapped
-forced uniforms.  kv32k and long128k are too large for the oracle's whole pivot loop, so they
-run in seeded (Philox) mode like the bench and are checked on sampled outputs the oracle can
-compute one by one:
+forced uniforms.  For kv32k and long128k one whole head runs through the oracle's pivot loop
+under snapped uniforms (test_full_head_snapped); the batched forwards of all their heads run in
+seeded (Philox) mode like the bench and are checked on sampled outputs the oracle can compute
+one by one:
   * the first pivots, which the oracle reproduces from the same Philox draws;
   * factor rows F[i, :] for sampled rows i, which are fixed once the pivots are
     (F[i, :] = L^{-1} H[S, i] with L the Cholesky factor of H_SS);
@@ -20,7 +21,7 @@ import pytest
 from coreset_head_rpcholesky_amd import synth
 from oracle import philox
 from oracle import wildcat as ow
-from tests.gpu_util import TOL, dev, host, rel, snapped
+from tests.gpu_util import TOL, check_output, dev, host, pivot_report, rel, snapped
 
 pytestmark = pytest.mark.gpu
 
@@ -67,9 +68,8 @@ def test_elementwise_full(wc, name, heads):
     for h in range(K.shape[0]):
         ref = ow.forward(Q[h], K[h], V[h], w.r, U[h])
         assert np.array_equal(piv[h], ref["pivots"]), h
-        e = rel(O[h], ref["O"])
+        e, _ = check_output(O[h], ref["O"], ref["kappa"], w.dtype, f"{name}:{h}")
         worst = max(worst, e)
-        assert e < TOL[w.dtype], (h, e)
     print(f"{name}: {K.shape[0]} heads, pivots exact, worst relative error {worst:.2e}")
 
 
@@ -82,10 +82,17 @@ def test_vit197_seeded_mode(wc):
     O, piv = host(out["O"]), host(out["pivots"])
     agree = 0
     for h in range(w.heads):
-        ref = ow.forward(Q[h], K[h], V[h], w.r, philox.pivot_uniforms(42, h, w.r))
+        u = philox.pivot_uniforms(42, h, w.r)
+        ref = ow.forward(Q[h], K[h], V[h], w.r, u)
         if np.array_equal(piv[h], ref["pivots"]):
             agree += 1
-            assert rel(O[h], ref["O"]) < TOL["bf16"], h
+            check_output(O[h], ref["O"], ref["kappa"], "bf16", f"vit197 seeded:{h}")
+        else:
+            # a head the oracle resolves differently: every draw within rounding of the
+            # device pivot's interval
+            rep = pivot_report(K[h], piv[h], u)
+            print(f"vit197 seeded head {h}: {rep}")
+            assert rep["excess"] <= 1.0, (h, rep)
     assert agree >= w.heads - 2, agree
 
 
@@ -122,8 +129,58 @@ def test_sampled_full(wc, name, check_heads, nq):
         Wo = ow.weights(K[h], V[h], S, beta)
         qs = np.arange(w.m) if nq is None else rng.choice(w.m, nq, replace=False)
         Oo, den, kappa = ow.attend(Q[h][qs], K[h], S, Wo, beta)
-        ok = kappa < 1e6
-        assert rel(O[h][qs][ok], Oo[ok]) < TOL["bf16"], rel(O[h][qs][ok], Oo[ok])
+        check_output(O[h][qs], Oo, kappa, "bf16", f"{__name__}:{h}")
+
+
+@pytest.mark.parametrize("name,h", [("kv32k", 5), ("long128k", 3)])
+def test_full_head_snapped(wc, name, h):
+    """One whole head of the two largest workloads under uniforms the oracle snapped on that
+    head (its full pivot loop, n = 32768 / 131072 keys, r = 1024 / 2048 steps): the device's
+    pivots against the oracle's, step by step.  Where they agree throughout, that is asserted;
+    where fp32 rounding of the device's residual moves a draw across an interval end, the
+    agreement rate and the first divergence are reported, and along the device's own path every
+    draw must lie within rounding (cdf_bound) of its pivot's interval.  Then the factor at
+    sampled rows, the weights and the outputs (a sample of queries, per head and per row) from
+    the device's pivots."""
+    import torch
+
+    w = synth.WORKLOADS[name]
+    Q, K, V = synth.make_inputs(name, heads=[h])
+    raw = synth.raw_uniforms(w.heads, w.r)[h]
+    U, margin, ref_piv = ow.snap_uniforms(K[0], w.r, raw, with_pivots=True)
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    Ud = dev(U[None, :])
+    rpc = wc.wc_rpcholesky(Kd, w.r, u_forced=Ud, with_diag=False)
+    out = wc.wc_forward(Qd, Kd, Vd, w.r, u_forced=Ud)
+    piv = host(out["pivots"])[0]
+    assert host(out["rank"])[0] == w.r and host(out["flags"])[0] == 0
+    assert np.array_equal(host(rpc["pivots"])[0], piv)
+    diff = np.nonzero(piv != ref_piv)[0]
+    beta = 1.0 / np.sqrt(w.d)
+    if len(diff) == 0:
+        print(f"{name} head {h}: all {w.r} pivots equal the oracle's")
+    else:
+        t = int(diff[0])
+        rep = pivot_report(K[0], piv, U, beta)
+        print(f"{name} head {h}: pivots agree on {t} of {w.r} steps ({t / w.r:.1%}); first divergence at "
+              f"step {t}, oracle margin {margin[t]:.3e} of T; along the device's path {rep}")
+        assert rep["first"] == t
+        assert rep["excess"] <= 1.0, rep
+    S = piv
+    trace = host(rpc["trace"])[0]
+    assert len(set(S.tolist())) == w.r and np.all(np.diff(trace) <= 1e-6 * trace[0])
+    rng = np.random.default_rng(h)
+    rows = np.concatenate([rng.choice(w.n, 48, replace=False), S[[0, 1, w.r // 2, w.r - 1]]])
+    Fr, _ = ow.factor_rows_given_pivots(K[0], S, rows, beta)
+    Fg = host(rpc["F"][0][:, torch.as_tensor(rows, device="cuda")]).T
+    assert rel(Fg, Fr) < 1e-3, rel(Fg, Fr)
+    del rpc
+    torch.cuda.empty_cache()
+    Wo = ow.weights(K[0], V[0], S, beta)
+    qs = np.arange(w.m) if w.m <= 4096 else np.unique(np.concatenate(
+        [np.linspace(0, w.m - 1, 2048).round().astype(np.int64), rng.choice(w.m, 2048, replace=False)]))
+    Oo, den, kappa = ow.attend(Q[0][qs], K[0], S, Wo, beta)
+    check_output(host(out["O"])[0][qs], Oo, kappa, "bf16", f"{name} full head {h}")
 
 
 @pytest.mark.parametrize("name,B,pb,h,nq", [("long128k", 64, 1, 0, 256), ("long128k", 64, 32, 5, 256),
@@ -157,8 +214,7 @@ def test_binned_full(wc, name, B, pb, h, nq):
     rng = np.random.default_rng(1)
     qs = np.arange(w.m) if nq is None else rng.choice(w.m, nq, replace=False)
     Oo, den, kappa = ow.attend(Q[h][qs], K[h], S, W, beta)
-    ok = kappa < 1e6
-    assert rel(O[h][qs][ok], Oo[ok]) < TOL["bf16"], rel(O[h][qs][ok], Oo[ok])
+    check_output(O[h][qs], Oo, kappa, "bf16", f"{__name__}:{h}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -192,5 +248,4 @@ def test_max_r(wc, dtype):
     assert rel(Fg, Fr) < 1e-3, rel(Fg, Fr)
     Wo = ow.weights(K[0], V[0], S, beta)
     Oo, den, kappa = ow.attend(Q[0], K[0], S, Wo, beta)
-    ok = kappa < 1e6
-    assert rel(O[0][ok], Oo[ok]) < TOL[dtype], rel(O[0][ok], Oo[ok])
+    check_output(O[0], Oo, kappa, dtype, f"{__name__}:max_r")

@@ -11,7 +11,7 @@ import pytest
 from coreset_head_rpcholesky_amd import synth
 from oracle import philox
 from oracle import wildcat as ow
-from tests.gpu_util import TOL, dev, host, rel, snapped
+from tests.gpu_util import TOL, check_output, dev, host, pivot_report, rel, snapped
 
 pytestmark = pytest.mark.gpu
 
@@ -88,8 +88,7 @@ def test_weights_and_attend_parity(wc, case):
     for h in range(H):
         S = piv[h][piv[h] >= 0]
         Oo, den, kappa = ow.attend(Q[h], K[h], S, Wor[h][: len(S)])
-        ok = kappa < 1e6
-        assert rel(O[h][ok], Oo[ok]) < TOL[dtype], (h, rel(O[h][ok], Oo[ok]))
+        check_output(O[h], Oo, kappa, dtype, f"{__name__}:{h}")
     assert np.all(host(flags) == 0)
 
 
@@ -104,8 +103,7 @@ def test_forward_parity(wc, case):
         ref = ow.forward(Q[h], K[h], V[h], r, U[h])
         assert np.array_equal(piv[h], ref["pivots"])
         assert rank[h] == ref["rank"]
-        ok = ref["kappa"] < 1e6
-        assert rel(O[h][ok], ref["O"][ok]) < TOL[dtype], (h, rel(O[h][ok], ref["O"][ok]))
+        check_output(O[h], ref["O"], ref["kappa"], dtype, f"{__name__}:{h}")
     if name == "resident_r_eq_n":  # r = n: the coreset is every key, so O is exact attention
         for h in range(H):
             assert rel(O[h], ow.exact_attention(Q[h], K[h], V[h])) < TOL[dtype]
@@ -123,7 +121,11 @@ def test_philox_stream_matches_oracle(wc, dtype, n):
     agree = 0
     for h in range(H):
         u = philox.pivot_uniforms(seed, h, r)
-        agree += np.array_equal(piv[h], ow.rpcholesky(K[h], r, u)["pivots"])
+        same = np.array_equal(piv[h], ow.rpcholesky(K[h], r, u)["pivots"])
+        agree += same
+        if not same:  # only rounding may separate the device's choice from the draw
+            rep = pivot_report(K[h], piv[h], u)
+            assert rep["excess"] <= 1.0, (h, rep)
     assert agree >= H - 1, agree
 
 
@@ -267,6 +269,5 @@ def test_blocked_solve(wc, dtype, d, r, rk):
         assert rel(Wh[h][:k], Wo) < 1e-3, (h, rel(Wh[h][:k], Wo))
         assert np.all(Wh[h][k:] == 0.0)
         Oo, den, kappa = ow.attend(Q[h], K[h], S, Wo, beta)
-        ok = kappa < 1e6
-        assert rel(O[h][ok], Oo[ok]) < TOL[dtype], (h, rel(O[h][ok], Oo[ok]))
+        check_output(O[h], Oo, kappa, dtype, f"{__name__}:{h}")
     assert np.all(host(flags) == 0)

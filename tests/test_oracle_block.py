@@ -177,3 +177,40 @@ def test_near_copy_of_a_long_key_is_passed_over():
     other = 60 if first == 10 else 10
     g = ow.kernel(K[[other]], K[[other]], beta)[0, 0] - ow.kernel(K[[other]], K[[first]], beta)[0, 0] ** 2 / ow.kernel(K[[first]], K[[first]], beta)[0, 0]
     assert 1e-3 < g < ow.DEPENDENT_TOL * ow.kernel(K[[other]], K[[other]], beta)[0, 0]
+
+
+def test_block_draw_margins_and_slot_rounds():
+    """The block loop's record of each draw: the distance from u T to the nearer end of the
+    interval it selects (over T), checked against a plain loop over the running sums of the
+    first round's masses with the earlier candidates removed; every slot's round is one that
+    ran, non-decreasing in slot order."""
+    rng = np.random.default_rng(41)
+    K = rng.standard_normal((60, 5)) * 0.6
+    r, b = 12, 4
+    u = rng.random(ow.BLOCK_DRAWS * r)
+    out = ow.rpcholesky_block(K, r, u, b)
+    p = ow.initial_residual(K, 1.0 / np.sqrt(5))
+    taken = []
+    for j in range(b):
+        q = [0.0 if i in taken else p[i] for i in range(len(p))]
+        T = sum(q)
+        run, s = 0.0, None
+        for i, x in enumerate(q):
+            if x > 0 and run + x > u[j] * T:
+                s, lo, hi = i, run, run + x
+                break
+            run += x
+        taken.append(s)
+        assert out["margins"][j] == pytest.approx(min(u[j] * T - lo, hi - u[j] * T) / T, rel=1e-9, abs=1e-15)
+    used = out["slot_round"][: out["rank"]]
+    assert np.all(used >= 0) and np.all(np.diff(used) >= 0)
+    assert np.all(np.isfinite(out["margins"][: b * (used[-1] + 1)]))
+
+
+def test_snap_with_pivots_returns_the_runs_pivots():
+    rng = np.random.default_rng(42)
+    K = rng.standard_normal((50, 4)) * 0.5
+    raw = rng.random(9)
+    U, margin, piv = ow.snap_uniforms(K, 9, raw, with_pivots=True)
+    assert np.array_equal(piv, ow.rpcholesky(K, 9, U)["pivots"])
+    assert np.array_equal(piv, ow.rpcholesky(K, 9, raw)["pivots"])

@@ -198,3 +198,41 @@ def test_snap_uniforms_keeps_pivots_and_centres():
     s, T, C = ow.sample_pivot(diag, snapped[0])
     lo = C[s - 1] if s else 0.0
     assert abs(snapped[0] * T - (lo + C[s]) / 2) <= 2.0**-24 * T
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_follow_own_pivots_reproduces_the_loop(seed):
+    """Driven by its own pivots, the follow loop is the pivot loop: the same factor, every draw
+    inside the interval of its pivot, and the draw's own choice equal to that pivot."""
+    K, beta = small(n=40, d=6, seed=seed)
+    r = 15
+    u = np.random.default_rng(300 + seed).random(r)
+    out = ow.rpcholesky(K, r, u, beta)
+    f = ow.rpcholesky_follow(K, out["pivots"], u, beta)
+    assert np.array_equal(f["chosen"], out["pivots"])
+    assert np.array_equal(f["F"], out["F"])
+    assert np.allclose(f["T"], out["trace"][:r], rtol=1e-13)
+    uT = u * f["T"]
+    assert np.all((f["lo"] <= uT) & (uT < f["hi"]))
+    # the interval of pivot s is [sum of masses before s, ... including s) at that step
+    diag = ow.initial_residual(K, beta)
+    s0 = out["pivots"][0]
+    assert f["lo"][0] == pytest.approx(np.sum(diag[:s0]), rel=1e-13)
+    assert f["hi"][0] - f["lo"][0] == pytest.approx(diag[s0], rel=1e-12)
+
+
+def test_follow_flags_a_pivot_the_draw_does_not_select():
+    """A pivot sequence that departs from the draws at step k: the draw's own choice differs
+    there, u_k T_k lies outside the given pivot's interval, and the steps before agree."""
+    K, beta = small(n=30, d=5, seed=7)
+    r, k = 10, 4
+    u = np.random.default_rng(9).random(r)
+    out = ow.rpcholesky(K, r, u, beta)
+    piv = out["pivots"].copy()
+    other = [i for i in range(30) if i not in piv[:k + 1]][0]
+    piv[k] = other
+    f = ow.rpcholesky_follow(K, piv, u, beta)
+    assert np.array_equal(f["chosen"][:k], piv[:k])
+    assert f["chosen"][k] == out["pivots"][k] != other
+    uT = u[k] * f["T"][k]
+    assert not (f["lo"][k] <= uT < f["hi"][k])
