@@ -367,18 +367,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Wait until at most `pending` chunks of this wave's direct loads are still in flight (loads
 // complete in order, so every older chunk has landed).  A chunk is KI + WI load instructions
 // per wave, plus the normaliser column's on wave 0.
+// s_waitcnt immediate for vmcnt <= n (6-bit count: low bits [3:0], high bits [15:14]).
+constexpr int vmcnt_imm(int n) { return kVmcnt0 | (n & 15) | ((n >> 4) & 3) << 14; }
+
 template <int D, int DV>
 __device__ __forceinline__ void attend_wait(int pending, int wid) {
   constexpr int per = D / (8 * kAttendWaves) + DV / (8 * kAttendWaves);
-  static_assert(2 * per + 2 < 16, "vmcnt field");
+  static_assert(2 * per + 2 < 64, "vmcnt field");
   if (pending <= 0) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
   } else if (pending == 1) {
-    if (wid == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0 | (per + 1));
-    else __builtin_amdgcn_s_waitcnt(kVmcnt0 | per);
+    if (wid == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per + 1));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(per));
   } else {
-    if (wid == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0 | (2 * per + 2));
-    else __builtin_amdgcn_s_waitcnt(kVmcnt0 | (2 * per));
+    if (wid == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per + 2));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
   }
 }
 
@@ -456,6 +459,19 @@ __device__ __forceinline__ void attend_step(const AttendChunk<D, DV>& bS, int uS
   }
 }
 
+// The probabilities and normaliser sums of a pipeline step, pinned where the step ends: an
+// empty asm statement that reads them keeps the compiler from sinking their exponentials past
+// the chunk's waits and barrier into the next step (which would run them as one burst with
+// the matrix cores idle instead of one per MFMA slot).
+template <int NQ>
+__device__ __forceinline__ void attend_pin(const bf16x8 (&pb)[NQ][2], const float (&den)[NQ][4]) {
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    asm volatile("" ::"v"(pb[s][0]), "v"(pb[s][1]));
+    asm volatile("" ::"v"(den[s][0]), "v"(den[s][1]), "v"(den[s][2]), "v"(den[s][3]));
+  }
+}
+
 // Scores of one 32-row unit whose rows from `left` on lie past the scan bound: set to -inf, so
 // that their probabilities are exactly zero (row of accumulator entry v: 8(v/4) + 4g + v%4).
 template <int NQ>
@@ -469,162 +485,226 @@ __device__ __forceinline__ void attend_mask(f32x16 (&sc)[NQ], int left, int g) {
   }
 }
 
-// Workgroup of kAttendWaves waves (one per SIMD), each taking kAttendNQ groups of 32 queries.
-#ifndef WC_ATTEND_XCD
-#define WC_ATTEND_XCD 1
-#endif
-// Workgroups are dealt to the 8 XCDs round-robin by linear id.  The id is remapped so that each
-// XCD takes a contiguous run of (head, coreset split, query tile) triples, head-major: a head's
-// coreset is then read through one or two XCDs' L2 instead of all eight.
-__device__ __forceinline__ void attend_tile(int& qt, int& h, int& sp) {
-  const int QT = gridDim.x, NH = gridDim.y, NS = gridDim.z;
-  qt = blockIdx.x; h = blockIdx.y; sp = blockIdx.z;
-#if WC_ATTEND_XCD
-  const int T = QT * NH * NS;
-  if (T % 8 == 0) {
-    const int L = blockIdx.x + QT * (blockIdx.y + NH * blockIdx.z);
-    const int p = (L % 8) * (T / 8) + L / 8;
-    qt = p % QT;
-    const int hs = p / QT;
-    h = hs / NS;
-    sp = hs % NS;
-  }
-#endif
+// The work of the attention is a list of tiles: (query tile of 256 queries, head, coreset split),
+// query tile fastest, then split, then head.  The kernel is persistent: a grid of one workgroup
+// per compute unit walks its tiles one after the other, and the coreset chunks of consecutive
+// tiles form one stream through the LDS ring, so the loads of the next tile's first chunks and
+// its query fragments overlap the end of the current tile instead of a new workgroup starting
+// cold.  Workgroups are dealt to the 8 XCDs round-robin by id; when the counts allow, the
+// workgroups of one XCD take a contiguous range of tiles, so a head's coreset is read through
+// one or two XCDs' L2 instead of all eight.
+struct AttendTile {
+  int qt, h, sp, c0, nc;
+};
+
+__device__ __forceinline__ AttendTile attend_tile_at(const AttendArgs& a, int t, int QT, int nchk, int per) {
+  AttendTile x;
+  x.qt = t % QT;
+  const int hs = t / QT;
+  x.h = hs / a.nsplit;
+  x.sp = hs % a.nsplit;
+  x.c0 = x.sp * per;
+  x.nc = min(nchk, x.c0 + per) - x.c0;
+  return x;
 }
 
-template <int D, int DV>
-__global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
-attend_bf16_kernel(AttendArgs a) {
-  constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ;
-  __shared__ AttendChunk<D, DV> sb[kAttendRing];
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int qt, h, sp;
-  attend_tile(qt, h, sp);
-  const int m = a.m, rp = staged_rows(a);
-  const float bl2e = a.beta_log2e;
-  const int q0 = qt * kAttendQueries + wid * 32 * NQ + l32;
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * m * D;
+// Index of this workgroup's j-th tile, or -1 past its last.
+__device__ __forceinline__ int attend_wg_tile(int j, int T) {
+  const int G = gridDim.x, b = blockIdx.x;
+  if (T % 8 == 0 && G % 8 == 0) {
+    const int per_xcd = G / 8, k = b / 8 + j * per_xcd;
+    return k < T / 8 ? (b % 8) * (T / 8) + k : -1;
+  }
+  const int t = b + j * G;
+  return t < T ? t : -1;
+}
 
-  // query fragments scaled by beta log2(e) (one bf16 rounding, relative 2^-9 per element), so
-  // the score MFMA yields the base-2 exponent directly
-  bf16x8 qb[NQ][NK];
+// Query fragments of 32 NQ queries of one tile (raw bf16, zero past the last query).
+template <int D, int NQ>
+__device__ __forceinline__ void attend_load_q(const AttendArgs& a, int h, int q0, int g, bf16x8 (&raw)[NQ][D / 16]) {
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * a.m * D;
 #pragma unroll
   for (int s = 0; s < NQ; ++s)
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk) {
       const int q = q0 + 32 * s;
-      bf16x8 raw;
-      if (q < m) {
-        raw = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
+      if (q < a.m) {
+        raw[s][kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw[e] = (__bf16)0.f;
+        for (int e = 0; e < 8; ++e) raw[s][kk][e] = (__bf16)0.f;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)((float)raw[e] * bl2e);
     }
-  f32x16 y[NQ][NCT];
-  float den[NQ][4];
-#pragma unroll
-  for (int s = 0; s < NQ; ++s) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) y[s][ct] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) den[s][i] = 0.f;
-  }
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the query fragments have arrived
-  // this workgroup's share of the coreset: chunks c0 .. c0+nc-1 of 64 rows
+}
+
+// MASK: the scan bound falls inside a 128-row block (a cache decoded over a prefix of its
+// rows), so the units that cross it are masked; without it every scanned row counts.
+template <int D, int DV, bool MASK>
+__global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
+attend_bf16_kernel(AttendArgs a) {
+  constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ, R = kAttendRing;
+  __shared__ AttendChunk<D, DV> sb[R];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = a.m, rp = staged_rows(a);
+  const float bl2e = a.beta_log2e;
+  const int QT = (m + kAttendQueries - 1) / kAttendQueries, T = QT * a.H * a.nsplit;
   const int nchk = scanned_rows(a) / 64, per = (nchk + a.nsplit - 1) / a.nsplit;
-  const int c0 = sp * per, nc = min(nchk, c0 + per) - c0;
-  const uint16_t* KSh = a.KSh + (size_t)h * rp * D;
-  const uint16_t* Wph = a.Wph + (size_t)h * DV * rp;
-  const uint16_t* Wdh = a.Wdh + (size_t)h * rp;
-  if (nc > 0) {
-    // chunks 0 .. kAttendRing-2 in flight; chunk 0 waited for
-    for (int i = 0; i < kAttendRing - 1 && i < nc; ++i) attend_issue(sb[i], KSh, Wph, Wdh, c0 + i, wid, lane);
-    attend_wait<D, DV>(min(nc, kAttendRing - 1) - 1, wid);
-    __syncthreads();
+  // rows at or past the scan bound carry no weight even when the staged row is not zero: the
+  // scores of a unit that crosses it are set to -inf before they are exponentiated
+  const int lim = a.scan_rows ? a.scan_rows : rp;
+  const int qoff = wid * 32 * NQ + l32;
+
+  // chunk loads run R-1 chunks ahead of the computation, through the tiles in order: the issue
+  // cursor is (tile ij, chunk ic of it); `issued` counts the chunks issued so far
+  int ij = 0, ic = 0, issued = 0;
+  int it = attend_wg_tile(0, T);
+  if (it < 0) return;
+  AttendTile ti = attend_tile_at(a, it, QT, nchk, per);
+  auto issue_next = [&]() {
+    if (it < 0) return;
+    attend_issue(sb[issued % R], a.KSh + (size_t)ti.h * rp * D, a.Wph + (size_t)ti.h * DV * rp,
+                 a.Wdh + (size_t)ti.h * rp, ti.c0 + ic, wid, lane);
+    ++issued;
+    if (++ic == ti.nc) {
+      ic = 0;
+      it = attend_wg_tile(++ij, T);
+      if (it >= 0) ti = attend_tile_at(a, it, QT, nchk, per);
+    }
+  };
+  for (int i = 0; i < R - 1; ++i) issue_next();
+
+  AttendTile tc = attend_tile_at(a, attend_wg_tile(0, T), QT, nchk, per);
+  bf16x8 qraw[NQ][NK];
+  attend_load_q<D, NQ>(a, tc.h, tc.qt * kAttendQueries + qoff, g, qraw);
+  // the query fragments were loaded last: every chunk issued before them has landed too
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  int gbase = 0;  // global index of the current tile's first chunk
+  for (int j = 0;;) {
+    // query fragments scaled by beta log2(e) (one bf16 rounding, relative 2^-9 per element),
+    // so the score MFMA yields the base-2 exponent directly
+    bf16x8 qb[NQ][NK];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s)
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)((float)qraw[s][kk][e] * bl2e);
+    f32x16 y[NQ][NCT];
+    float den[NQ][4];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) y[s][ct] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) den[s][i] = 0.f;
+    }
+    const int nc = tc.nc, c0 = tc.c0;
+    const int jn = attend_wg_tile(j + 1, T);  // the next tile, whose queries load during the last chunk
     // scores of unit 0 alone; the values of the (nonexistent) unit -1 get zero probabilities
     f32x16 scA[NQ], scB[NQ];
     bf16x8 pbA[NQ][2], pbB[NQ][2];
+    const AttendChunk<D, DV>& b0 = sb[gbase % R];
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
       scA[s] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        scA[s] = mfma32(__builtin_bit_cast(bf16x8, sb[0].k[(2 * kk + g) * 64 + l32]), qb[s][kk], scA[s]);
+        scA[s] = mfma32(__builtin_bit_cast(bf16x8, b0.k[(2 * kk + g) * 64 + l32]), qb[s][kk], scA[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) pbA[s][0][e] = pbA[s][1][e] = (__bf16)0.f;
     }
-    // Unit 2c is in ring slot c % R (upper half of the chunk: unit 2c+1), R = kAttendRing.
-    // Chunk c's loads were issued R-1 chunks ahead and are waited for at the barrier of chunk
-    // c-1, with the chunks after it still in flight; that barrier also frees slot
-    // (c+R-1) % R = (c-1) % R, whose last reads (values of unit 2c-1) come before it.
-    constexpr int R = kAttendRing;
-    // rows at or past the scan bound carry no weight even when the staged row is not zero: the
-    // scores of a unit that crosses it are set to -inf before they are exponentiated
-    const int lim = a.scan_rows ? a.scan_rows : rp;
-    for (int c = 0; c < nc; ++c) {
-      const int bc = c % R, bn = (c + 1) % R, bl = c == 0 ? bc : (c + R - 1) % R;
+    // Chunk gc = gbase + c sits in ring slot gc % R (unit 2c in its lower half, 2c+1 in the
+    // upper).  Its loads were issued R-1 chunks ahead and are waited for at the barrier of chunk
+    // gc-1, with the chunks after it still in flight; that barrier also frees slot
+    // (gc-1) % R, whose last reads (values of unit 2c-1) come before it.  The last chunk is
+    // peeled off the loop: it also loads the next tile's query fragments, and only there do
+    // they need registers beside the current ones.
+    auto chunk = [&](int c, bool last) {
+      const int gc = gbase + c;
+      const int bc = gc % R, bn = (gc + 1) % R, bl = c == 0 ? bc : (gc + R - 1) % R;
       const int left = lim - (c0 + c) * 64;  // rows of this chunk below the bound
-      if (left < 32) attend_mask<NQ>(scA, left, g);
+      if (MASK && left < 32) attend_mask<NQ>(scA, left, g);
       attend_step<D, DV, NQ>(sb[bc], 1, sb[bc], 0, sb[bl], c == 0 ? 0 : 1, qb, y, den, scA, scB, pbA, pbB, g, l32);
-      // chunk c+1 landed; chunks c+2 .. c+R-2 (those issued) may still be loading
-      attend_wait<D, DV>(min(nc, c + R - 1) - (c + 2), wid);
+      attend_pin<NQ>(pbB, den);
+      // chunk gc+1 landed; the chunks issued after it (at most R-2) may still be loading
+      attend_wait<D, DV>(issued - (gc + 2), wid);
       __syncthreads();
-      if (c + R - 1 < nc) attend_issue(sb[(c + R - 1) % R], KSh, Wph, Wdh, c0 + c + R - 1, wid, lane);
-      if (left < 64) attend_mask<NQ>(scB, left - 32, g);
-      // the scores of unit 2c+2 are garbage past the last chunk and are never exponentiated
+      const int before = issued;
+      if (last && jn >= 0) {
+        const AttendTile tn = attend_tile_at(a, jn, QT, nchk, per);
+        attend_load_q<D, NQ>(a, tn.h, tn.qt * kAttendQueries + qoff, g, qraw);
+      }
+      issue_next();
+      if (MASK && left < 64) attend_mask<NQ>(scB, left - 32, g);
+      // at the last chunk, the scores of the next unit are those of the next tile's first chunk
+      // under this tile's queries: never exponentiated
       attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
-    }
+      attend_pin<NQ>(pbA, den);
+      return issued - before;
+    };
+    for (int c = 0; c < nc - 1; ++c) chunk(c, false);
+    // chunk loads issued after the next tile's query fragments
+    const int after_q = chunk(nc - 1, true);
     // values of the last unit
-    const AttendChunk<D, DV>& bz = sb[(nc - 1) % R];
+    const AttendChunk<D, DV>& bz = sb[(gbase + nc - 1) % R];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const bf16x8 wf = __builtin_bit_cast(bf16x8, bz.w[(4 + 2 * (i & 1) + g) * DV + 32 * (i >> 1) + l32]);
 #pragma unroll
       for (int s = 0; s < NQ; ++s) y[s][i >> 1] = mfma32(wf, pbA[s][i & 1], y[s][i >> 1]);
     }
-  }
+    // the next tile's query fragments have landed once at most the chunk loads issued after
+    // them are in flight (waited for before this tile's outputs are stored, so that the
+    // stores do not join the count)
+    if (jn >= 0) attend_wait<D, DV>(after_q, wid);
+    // outputs of this tile
+    const int h = tc.h, sp = tc.sp, q0 = tc.qt * kAttendQueries + qoff;
 #pragma unroll
-  for (int s = 0; s < NQ; ++s) {
-    float dn = (den[s][0] + den[s][1]) + (den[s][2] + den[s][3]);
-    dn += __shfl_xor(dn, 32, 64);
-    const int q = q0 + 32 * s;
-    if (q >= m) continue;
-    if (a.nsplit == 1 && a.Yout) {
-      float* Y = yout_row(a, h, q);
+    for (int s = 0; s < NQ; ++s) {
+      float dn = (den[s][0] + den[s][1]) + (den[s][2] + den[s][3]);
+      dn += __shfl_xor(dn, 32, 64);
+      const int q = q0 + 32 * s;
+      if (q >= m) continue;
+      if (a.nsplit == 1 && a.Yout) {
+        float* Y = yout_row(a, h, q);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Y[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
-      if (g == 0) Y[DV] = dn;
-    } else if (a.nsplit == 1) {
-      if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
-      const float inv = 1.0f / dn;
-      uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
+          for (int v = 0; v < 16; ++v) Y[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
+        if (g == 0) Y[DV] = dn;
+      } else if (a.nsplit == 1) {
+        if (!(dn > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
+        const float inv = 1.0f / dn;
+        uint16_t* O = reinterpret_cast<uint16_t*>(a.O) + ((size_t)h * m + q) * DV;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int col = ct * 32 + 8 * v4 + 4 * g;
-          uint16_t o[4];
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int col = ct * 32 + 8 * v4 + 4 * g;
+            uint16_t o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[s][ct][4 * v4 + e] * inv));
-          uint2 pk;
-          pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-          pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-          *reinterpret_cast<uint2*>(O + col) = pk;
-        }
-    } else {
-      float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
+            for (int e = 0; e < 4; ++e) o[e] = bf16_bits((__bf16)(y[s][ct][4 * v4 + e] * inv));
+            uint2 pk;
+            pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+            pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+            *reinterpret_cast<uint2*>(O + col) = pk;
+          }
+      } else {
+        float* Yp = a.Ypart + (((size_t)h * a.nsplit + sp) * m + q) * (DV + 1);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
-      if (g == 0) Yp[DV] = dn;
+          for (int v = 0; v < 16; ++v) Yp[ct * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = y[s][ct][v];
+        if (g == 0) Yp[DV] = dn;
+      }
     }
+    if (jn < 0) break;
+    // the next tile (its first chunk landed at the last barrier)
+    gbase += nc;
+    tc = attend_tile_at(a, jn, QT, nchk, per);
+    ++j;
   }
 }
 
@@ -767,6 +847,15 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_kernel(AttendArgs a)
   }
 }
 
+// Workgroups of the persistent attention kernel: the compute units of the current device (one
+// workgroup each, its LDS ring takes most of a unit's LDS).
+static int attend_workgroups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
 template <typename T, int D, int DV>
 static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st);
 
@@ -804,10 +893,15 @@ static hipError_t run_attend_all_keys(const AttendArgs& a, hipStream_t st) {
 template <typename T, int D, int DV>
 static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st) {
   hipError_t e;
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((attend_bf16_kernel<D, DV>), dim3((a.m + kAttendQueries - 1) / kAttendQueries, a.H, a.nsplit),
-                       dim3(64 * kAttendWaves), 0, st, a);
-  else
+  if constexpr (sizeof(T) == 2) {
+    // persistent: one workgroup per compute unit (never more than the tiles)
+    const long tiles = (long)((a.m + kAttendQueries - 1) / kAttendQueries) * a.H * a.nsplit;
+    const dim3 grid((unsigned)(tiles < attend_workgroups() ? tiles : attend_workgroups()));
+    if (a.scan_rows % 128 != 0)
+      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, true>), grid, dim3(64 * kAttendWaves), 0, st, a);
+    else
+      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, false>), grid, dim3(64 * kAttendWaves), 0, st, a);
+  } else
     hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.nsplit > 1) {
