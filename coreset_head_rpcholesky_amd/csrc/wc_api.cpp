@@ -38,6 +38,11 @@ wc_status check_problem(const wc_problem* p) {
   }
   if (p->bins > 1 && (p->n % p->bins != 0 || p->r % p->bins != 0)) return WC_ERR_UNSUPPORTED;
   if ((int64_t)p->n > (int64_t)kMaxBlocks * 1024) return WC_ERR_UNSUPPORTED;
+  // sizes whose buffers could not exist on any device (and whose workspace arithmetic would
+  // leave 64 bits): more than 2^48 elements in one array
+  const double rows = (double)p->heads * (p->n > p->m ? p->n : p->m);
+  const double width = (double)(p->r > 128 ? p->r : 128) + 1.0;
+  if (rows * width > 281474976710656.0) return WC_ERR_UNSUPPORTED;
   return WC_OK;
 }
 

@@ -11,8 +11,6 @@ namespace wc {
 
 namespace {
 
-constexpr int kCenterRows = 1024;
-
 // Block sums: thread t adds column t % d over rows t / d, t / d + 256 / d, ... of the block;
 // the 256 / d row lanes of a column are then added in order.
 template <typename T>
@@ -66,8 +64,6 @@ hipError_t run_center(const CenterArgs& a, hipStream_t st) {
 }
 
 }  // namespace
-
-int center_blocks(int n) { return (n + kCenterRows - 1) / kCenterRows; }
 
 hipError_t launch_center(const CenterArgs& a, hipStream_t st) {
   return a.bf16 ? run_center<uint16_t>(a, st) : run_center<float>(a, st);

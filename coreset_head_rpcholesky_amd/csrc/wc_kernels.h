@@ -204,7 +204,8 @@ struct CenterArgs {
   double* mean;           // ws [H][d]
   void* Kc;               // ws [H][n][d], input dtype
 };
-int center_blocks(int n);
+constexpr int kCenterRows = 1024;  // key rows per workgroup of the column sums
+inline int center_blocks(int n) { return (n + kCenterRows - 1) / kCenterRows; }
 hipError_t launch_center(const CenterArgs& a, hipStream_t st);
 
 }  // namespace wc
