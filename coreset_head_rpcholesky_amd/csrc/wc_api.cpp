@@ -119,9 +119,9 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
   // otherwise 256 rows (one per thread)
   L.rows = (n % 4 == 0 && H * ((n + 1023) / 1024) >= 512) ? 1024 : 256;
   L.nblk = (int)((n + L.rows - 1) / L.rows);
-  // weights: row chunks so that (r/128 groups) x chunks x heads >= 1024 workgroups
-  const size_t jg = (r + 127) / 128;
-  size_t nchunk = (1024 + jg * H - 1) / (jg * H);
+  // weights: key chunks so that (r/256 row groups) x chunks x heads >= 512 workgroups
+  const size_t jg = (r + 255) / 256;
+  size_t nchunk = (512 + jg * H - 1) / (jg * H);
   const size_t maxchunk = (n + 63) / 64;
   if (nchunk > maxchunk) nchunk = maxchunk;
   if (nchunk < 1) nchunk = 1;

@@ -29,146 +29,168 @@ __global__ void __launch_bounds__(256) gather_L_kernel(WeightsArgs a) {
     L[j] = (t < rk && j <= t) ? F[(size_t)j * a.n + s] : 0.f;
 }
 
-// X partial over rows [i0, i0 + chunk_rows) for 128 rows of X (j0 .. j0 + 127).
-// 4 waves; MFMA tiles (jt < 4) x (ct < DV/32), tile k of wave w is w + 4k.  Each 64-row
-// sub-pass of F (hi/lo bf16) and V^T is staged in LDS; the next sub-pass is loaded into
-// registers while the matrix cores work on the current one.
-constexpr int XJG = 128;  // rows of X per workgroup
-constexpr int XSUB = 64;  // key rows per sub-pass
+// X partial over the key rows [i0, i0 + chunk_rows) for XJG rows of X.  Eight waves; wave w
+// owns the 32 rows j0 + 32 w .. of X and forms them on the bf16 matrix cores,
+//   X[j, c] += sum_i F[j, i] V[i, c]   (32 x 32 x 16 MFMAs, one tile per 32 value columns),
+// its A operand (8 consecutive keys of one row of F) loaded straight from global memory into
+// registers and split there into hi + lo bf16 parts, so each element of F is read once in the
+// whole grid.  The B operand, V transposed, is staged in LDS once per 128-key sub-pass for all
+// eight waves (double-buffered: the next sub-pass's F and V loads are in flight during the
+// current MFMAs).  The ones column X[j, dv] = sum_i F[j, i] is an fp32 sum in registers.
+// Workgroups that share a chunk of keys (and so its rows of V) are dealt to one XCD, so V is
+// read from HBM about once and from that XCD's L2 by the others.
+constexpr int XW = 8;           // waves per workgroup
+constexpr int XJG = 32 * XW;    // rows of X per workgroup
+constexpr int XKS = 128;        // key rows per sub-pass
+constexpr int XKK = XKS / 16;   // 16-key MFMA steps per sub-pass
+constexpr int XVP = XKS + 8;    // LDS pitch (bf16) of one transposed value column
 
 template <typename TV, int DV, bool VEC>
-__global__ void __launch_bounds__(256) x_partial_kernel(WeightsArgs a) {
-  constexpr int SP = XSUB + 8;          // padded LDS row (bf16)
+__global__ void __launch_bounds__(64 * XW) x_partial_kernel(WeightsArgs a) {
   constexpr bool SPLITV = sizeof(TV) == 4;
-  constexpr int NCT = DV / 32, NTILE = 4 * NCT, TPW = NTILE / 4;
-  constexpr int VPT = DV / 4;           // V elements per thread per sub-pass (row ii, quarter cq)
-  __shared__ __attribute__((aligned(16))) __bf16 sFh[XJG * SP];
-  __shared__ __attribute__((aligned(16))) __bf16 sFl[XJG * SP];
-  __shared__ __attribute__((aligned(16))) __bf16 sVh[DV * SP];
-  __shared__ __attribute__((aligned(16))) __bf16 sVl[SPLITV ? DV * SP : 8];
-  const int jg = blockIdx.x, chunk = blockIdx.y, h = blockIdx.z;
+  constexpr int NCT = DV / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 sVh[2][DV * XVP];
+  __shared__ __attribute__((aligned(16))) __bf16 sVl[SPLITV ? 2 : 1][SPLITV ? DV * XVP : 8];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int n = a.n, r = a.r;
+  // workgroup -> (row group, key chunk, head); the row groups of one chunk are consecutive
+  // among the workgroups of one XCD (workgroups are dealt to the XCDs round-robin by id)
+  const int JG = (r + XJG - 1) / XJG, total = JG * a.nchunk * a.H, L = blockIdx.x;
+  const int p = total % 8 == 0 ? (L % 8) * (total / 8) + L / 8 : L;
+  const int jg = p % JG, chunk = (p / JG) % a.nchunk, h = p / JG / a.nchunk;
   const int j0 = jg * XJG;
   const int i0 = chunk * a.chunk_rows;
   const int i1 = min(n, i0 + a.chunk_rows);
-  const float* F = a.F + (size_t)h * r * n;
+  const int j = j0 + 32 * wid + l32;  // this lane's row of X (and of F)
+  const bool jv = j < r;
+  const float* Fj = a.F + ((size_t)h * r + (jv ? j : 0)) * n;
   const TV* V = reinterpret_cast<const TV*>(a.V) + (size_t)h * n * DV;
-  f32x16 acc[TPW];
+
+  // MFMA step kk takes, in lane half g, the keys key_of(kk) .. + 7 of the sub-pass (A and B alike)
+  auto key_of = [&](int kk) { return 16 * kk + 8 * g; };
+  // F: keys ib + key_of(kk) .. + 7 of row j, kk = 0 .. XKK - 1
+  auto load_f = [&](int ib, float (&f)[XKK][8]) {
 #pragma unroll
-  for (int k = 0; k < TPW; ++k)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
-  // F: thread owns row j0 + fj, keys 32 fq .. 32 fq + 31 of the sub-pass
-  const int fj = tid >> 1, fq = tid & 1;
-  const bool frow = j0 + fj < r;
-  // V: thread owns key row ii of the sub-pass, value columns VPT cq .. VPT cq + VPT - 1
-  const int ii = tid >> 2, cq = tid & 3;
-  float colsum = 0.f;
-  float fr[32];
-  float vr[VPT];
-  auto load = [&](int ib) {
-    const int ibase = ib + 32 * fq;
-    const float* src = F + (size_t)(j0 + fj) * n + ibase;
-    if (VEC && frow && ibase + 32 <= i1) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 x = reinterpret_cast<const float4*>(src)[q];
-        fr[4 * q] = x.x; fr[4 * q + 1] = x.y; fr[4 * q + 2] = x.z; fr[4 * q + 3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) fr[e] = (frow && ibase + e < i1) ? src[e] : 0.f;
-    }
-    const int i = ib + ii;
-    const TV* vs = V + (size_t)i * DV + cq * VPT;
-    if (i < i1) {
-      if constexpr (sizeof(TV) == 2) {
-#pragma unroll
-        for (int q = 0; q < VPT / 8; ++q) {
-          const uint4 x = reinterpret_cast<const uint4*>(vs)[q];
-          const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vr[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
-            vr[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-          }
-        }
+    for (int kk = 0; kk < XKK; ++kk) {
+      const int i = ib + key_of(kk);
+      if (VEC && jv && i + 8 <= i1) {
+        const float4 x0 = *reinterpret_cast<const float4*>(Fj + i);
+        const float4 x1 = *reinterpret_cast<const float4*>(Fj + i + 4);
+        f[kk][0] = x0.x; f[kk][1] = x0.y; f[kk][2] = x0.z; f[kk][3] = x0.w;
+        f[kk][4] = x1.x; f[kk][5] = x1.y; f[kk][6] = x1.z; f[kk][7] = x1.w;
       } else {
 #pragma unroll
-        for (int q = 0; q < VPT / 4; ++q) {
-          const float4 x = reinterpret_cast<const float4*>(vs)[q];
-          vr[4 * q] = x.x; vr[4 * q + 1] = x.y; vr[4 * q + 2] = x.z; vr[4 * q + 3] = x.w;
-        }
+        for (int e = 0; e < 8; ++e) f[kk][e] = (jv && i + e < i1) ? Fj[i + e] : 0.f;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < VPT; ++e) vr[e] = 0.f;
     }
   };
-  if (i0 < i1) load(i0);
-  for (int ib = i0; ib < i1; ib += XSUB) {
-    __syncthreads();
+  // V: thread owns key pair (2 kp, 2 kp + 1) of the sub-pass and 16 bytes of value columns;
+  // the two keys of each column are packed into one 32-bit LDS word of the transposed layout
+  constexpr int CPL = 16 / (int)sizeof(TV);        // value columns per 16-byte load
+  constexpr int CG = DV / CPL;                     // column groups
+  constexpr int NUNIT = (XKS / 2) * CG;                       // (key pair, column group) units
+  constexpr int VPASS = (NUNIT + 64 * XW - 1) / (64 * XW);    // units per thread
+  auto load_v = [&](int ib, uint4 (&v)[VPASS][2]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x8 hv, lv;
+    for (int u = 0; u < VPASS; ++u) {
+      const int unit = tid + u * 64 * XW, kp = unit / CG, cg = unit % CG;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        colsum += fr[8 * q + e];
-        __bf16 hi, lo;
-        split_bf16(fr[8 * q + e], hi, lo);
-        hv[e] = hi;
-        lv[e] = lo;
+      for (int q = 0; q < 2; ++q) {
+        const int i = ib + 2 * kp + q;
+        v[u][q] = (unit < NUNIT && i < i1) ? *reinterpret_cast<const uint4*>(V + (size_t)i * DV + cg * CPL)
+                                           : make_uint4(0u, 0u, 0u, 0u);
       }
-      *reinterpret_cast<bf16x8*>(sFh + fj * SP + 32 * fq + 8 * q) = hv;
-      *reinterpret_cast<bf16x8*>(sFl + fj * SP + 32 * fq + 8 * q) = lv;
     }
+  };
+  auto store_v = [&](int buf, const uint4 (&v)[VPASS][2]) {
 #pragma unroll
-    for (int e = 0; e < VPT; ++e) {
-      const int c = cq * VPT + e;
-      if (SPLITV) {
-        __bf16 hi, lo;
-        split_bf16(vr[e], hi, lo);
-        sVh[c * SP + ii] = hi;
-        sVl[c * SP + ii] = lo;
+    for (int u = 0; u < VPASS; ++u) {
+      const int unit = tid + u * 64 * XW, kp = unit / CG, cg = unit % CG;
+      if (unit >= NUNIT) continue;
+      const uint32_t w0[4] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w};
+      const uint32_t w1[4] = {v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+      if constexpr (!SPLITV) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // columns 8 cg + 2 e and + 1: (key 2kp, key 2kp+1)
+          const int c = cg * CPL + 2 * e;
+          *reinterpret_cast<uint32_t*>(&sVh[buf][c * XVP + 2 * kp]) = (w0[e] & 0xffffu) | (w1[e] << 16);
+          *reinterpret_cast<uint32_t*>(&sVh[buf][(c + 1) * XVP + 2 * kp]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+        }
       } else {
-        sVh[c * SP + ii] = (__bf16)vr[e];
-      }
-    }
-    __syncthreads();
-    if (ib + XSUB < i1) load(ib + XSUB);  // next sub-pass in flight during the MFMAs
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      const int tile = wid + 4 * k;
-      const int jt = tile / NCT, ct = tile % NCT;
-      if (j0 + jt * 32 >= r) continue;
-#pragma unroll
-      for (int kk = 0; kk < XSUB; kk += 16) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sFh + (jt * 32 + l32) * SP + kk + 8 * g);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sFl + (jt * 32 + l32) * SP + kk + 8 * g);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sVh + (ct * 32 + l32) * SP + kk + 8 * g);
-        acc[k] = mfma32(ah, bh, acc[k]);
-        acc[k] = mfma32(al, bh, acc[k]);
-        if (SPLITV) {
-          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sVl + (ct * 32 + l32) * SP + kk + 8 * g);
-          acc[k] = mfma32(ah, bl, acc[k]);
+        for (int e = 0; e < 4; ++e) {  // column 4 cg + e, fp32 split into hi + lo bf16 parts
+          const int c = cg * CPL + e;
+          __bf16 h0, l0, h1, l1;
+          split_bf16(__uint_as_float(w0[e]), h0, l0);
+          split_bf16(__uint_as_float(w1[e]), h1, l1);
+          const bf16x2 hh = {h0, h1}, ll = {l0, l1};
+          *reinterpret_cast<bf16x2*>(&sVh[buf][c * XVP + 2 * kp]) = hh;
+          *reinterpret_cast<bf16x2*>(&sVl[buf][c * XVP + 2 * kp]) = ll;
         }
       }
     }
+  };
+
+  f32x16 acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x16{};
+  float colsum = 0.f;
+  float fc[XKK][8], fn[XKK][8];
+  uint4 vn[VPASS][2];
+  if (i0 < i1) {
+    load_f(i0, fc);
+    load_v(i0, vn);
+    store_v(0, vn);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int ib = i0; ib < i1; ib += XKS) {
+    const bool more = ib + XKS < i1;
+    if (more) {
+      load_f(ib + XKS, fn);
+      load_v(ib + XKS, vn);
+    }
+#pragma unroll
+    for (int kk = 0; kk < XKK; ++kk) {
+      bf16x8 ah, al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        colsum += fc[kk][e];
+        __bf16 hi, lo;
+        split_bf16(fc[kk][e], hi, lo);
+        ah[e] = hi;
+        al[e] = lo;
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int o = (ct * 32 + l32) * XVP + key_of(kk);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&sVh[buf][o]);
+        acc[ct] = mfma32(ah, bh, acc[ct]);
+        acc[ct] = mfma32(al, bh, acc[ct]);
+        if constexpr (SPLITV) {
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&sVl[buf][o]);
+          acc[ct] = mfma32(ah, bl, acc[ct]);
+        }
+      }
+    }
+    if (more) store_v(buf ^ 1, vn);
+    __syncthreads();
+    buf ^= 1;
+#pragma unroll
+    for (int kk = 0; kk < XKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fc[kk][e] = fn[kk][e];
   }
   float* X = a.Xpart + (((size_t)h * a.nchunk + chunk) * r) * (DV + 1);
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const int tile = wid + 4 * k;
-    const int jt = tile / NCT, ct = tile % NCT;
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int j = j0 + jt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (j < r) X[(size_t)j * (DV + 1) + ct * 32 + l32] = acc[k][v];
+      const int jr = j0 + 32 * wid + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (jr < r) X[(size_t)jr * (DV + 1) + ct * 32 + l32] = acc[ct][v];
     }
-  }
-  colsum += __shfl_xor(colsum, 1, 64);
-  if (fq == 0 && frow) X[(size_t)(j0 + fj) * (DV + 1) + DV] = colsum;
+  colsum += __shfl_xor(colsum, 32, 64);
+  if (g == 0 && jv) X[(size_t)j * (DV + 1) + DV] = colsum;
 }
 
 __global__ void __launch_bounds__(256) x_reduce_kernel(WeightsArgs a) {
@@ -292,11 +314,11 @@ static hipError_t run_weights(const WeightsArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(gather_L_kernel, dim3(a.r, a.H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 xg((a.r + XJG - 1) / XJG, a.nchunk, a.H);
+  const dim3 xg((unsigned)(((a.r + XJG - 1) / XJG) * a.nchunk * a.H));
   if (a.n % 4 == 0 && a.chunk_rows % 4 == 0)
-    hipLaunchKernelGGL((x_partial_kernel<TV, DV, true>), xg, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((x_partial_kernel<TV, DV, true>), xg, dim3(64 * XW), 0, st, a);
   else
-    hipLaunchKernelGGL((x_partial_kernel<TV, DV, false>), xg, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((x_partial_kernel<TV, DV, false>), xg, dim3(64 * XW), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t per = (size_t)a.r * (DV + 1);
   hipLaunchKernelGGL(x_reduce_kernel, dim3((unsigned)((per + 255) / 256), a.H), dim3(256), 0, st, a);
