@@ -10,7 +10,12 @@
 //            MFMA holds, in lane l, coreset rows 8(v/4) + 4(l/32) + v%4 of query l%32; packed
 //            to bf16 it is directly the B operand of the value MFMA provided W^T's columns
 //            (coreset index) are stored in the matching permuted order (perm32).
-//   normaliser Y[:, dv] is an fp32 dot product of P with W[:, dv] on the vector units.
+//   normaliser Y[:, dv] on the vector units: for bf16 inputs, packed bf16 dot products of the
+//            same bf16-rounded P as the values with W[:, dv] rounded to bf16 (fp32 sums); for
+//            fp32 inputs, fp32 products of P with the fp32 W[:, dv].  In bf16 each of P and
+//            W[:, dv] carries a relative rounding of at most 2^-9, so a row whose normaliser
+//            condition sum |P| |W[:, dv]| / |Y[:, dv]| is kappa has a normaliser error of at most
+//            about 2^-8 kappa relative.
 // No row-max shift is needed: any per-row factor cancels in the ratio, and the inputs are
 // bounded.  fp32 inputs use hi + lo bf16 splits (three products per MFMA step).
 #include "wc_device.h"
@@ -370,18 +375,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // s_waitcnt immediate for vmcnt <= n (6-bit count: low bits [3:0], high bits [15:14]).
 constexpr int vmcnt_imm(int n) { return kVmcnt0 | (n & 15) | ((n >> 4) & 3) << 14; }
 
-template <int D, int DV>
+// EXTRA: further loads of this wave issued after those chunks (the next tile's query fragments)
+// that may stay in flight too.
+template <int D, int DV, int EXTRA = 0>
 __device__ __forceinline__ void attend_wait(int pending, int wid) {
   constexpr int per = D / (8 * kAttendWaves) + DV / (8 * kAttendWaves);
-  static_assert(2 * per + 2 < 64, "vmcnt field");
+  static_assert(2 * per + 2 + EXTRA < 64, "vmcnt field");
   if (pending <= 0) {
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(EXTRA));
   } else if (pending == 1) {
-    if (wid == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per + 1));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(per));
+    if (wid == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per + 1 + EXTRA));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(per + EXTRA));
   } else {
-    if (wid == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per + 2));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
+    if (wid == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per + 2 + EXTRA));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per + EXTRA));
   }
 }
 
@@ -519,22 +526,35 @@ __device__ __forceinline__ int attend_wg_tile(int j, int T) {
   return t < T ? t : -1;
 }
 
-// Query fragments of 32 NQ queries of one tile (raw bf16, zero past the last query).
+// Query fragments of 32 NQ queries of one tile, raw bf16.  Exactly NQ * D/16 load instructions
+// per lane whatever the tile (rows past the last query read the last query's row, and are zeroed
+// when scaled), so that the chunk waits can count them.
 template <int D, int NQ>
 __device__ __forceinline__ void attend_load_q(const AttendArgs& a, int h, int q0, int g, bf16x8 (&raw)[NQ][D / 16]) {
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Q) + (size_t)h * a.m * D;
 #pragma unroll
-  for (int s = 0; s < NQ; ++s)
+  for (int s = 0; s < NQ; ++s) {
+    const int q = min(q0 + 32 * s, a.m - 1);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int q = q0 + 32 * s;
-      if (q < a.m) {
-        raw[s][kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
-      } else {
+    for (int kk = 0; kk < D / 16; ++kk)
+      raw[s][kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)q * D + 16 * kk + 8 * g);
+  }
+}
+
+// The B operands of the score MFMA: query fragments scaled by beta log2(e) (one bf16 rounding,
+// relative 2^-9 per element), so that the score is already a base-2 exponent; zero for rows
+// past the last query.
+template <int D, int NQ>
+__device__ __forceinline__ void attend_scale_q(const bf16x8 (&raw)[NQ][D / 16], int q0, int m, float bl2e,
+                                               bf16x8 (&qb)[NQ][D / 16]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw[s][kk][e] = (__bf16)0.f;
-      }
-    }
+  for (int s = 0; s < NQ; ++s) {
+    const float f = q0 + 32 * s < m ? bl2e : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)((float)raw[s][kk][e] * f);
+  }
 }
 
 // MASK: the scan bound falls inside a 128-row block (a cache decoded over a prefix of its
@@ -542,7 +562,7 @@ __device__ __forceinline__ void attend_load_q(const AttendArgs& a, int h, int q0
 template <int D, int DV, bool MASK>
 __global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
 attend_bf16_kernel(AttendArgs a) {
-  constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ, R = kAttendRing;
+  constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ, R = kAttendRing, QN = NQ * NK;
   __shared__ AttendChunk<D, DV> sb[R];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -575,22 +595,25 @@ attend_bf16_kernel(AttendArgs a) {
   for (int i = 0; i < R - 1; ++i) issue_next();
 
   AttendTile tc = attend_tile_at(a, attend_wg_tile(0, T), QT, nchk, per);
-  bf16x8 qraw[NQ][NK];
+  bf16x8 qraw[NQ][NK], qb[NQ][NK];
   attend_load_q<D, NQ>(a, tc.h, tc.qt * kAttendQueries + qoff, g, qraw);
   // the query fragments were loaded last: every chunk issued before them has landed too
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
+  attend_scale_q<D, NQ>(qraw, tc.qt * kAttendQueries + qoff, m, bl2e, qb);
+  // scores of the first tile's unit 0; later tiles get theirs from the last step of the tile
+  // before
+  f32x16 scA[NQ], scB[NQ];
+  bf16x8 pbA[NQ][2], pbB[NQ][2];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    scA[s] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      scA[s] = mfma32(__builtin_bit_cast(bf16x8, sb[0].k[(2 * kk + g) * 64 + l32]), qb[s][kk], scA[s]);
+  }
   int gbase = 0;  // global index of the current tile's first chunk
   for (int j = 0;;) {
-    // query fragments scaled by beta log2(e) (one bf16 rounding, relative 2^-9 per element),
-    // so the score MFMA yields the base-2 exponent directly
-    bf16x8 qb[NQ][NK];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s)
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[s][kk][e] = (__bf16)((float)qraw[s][kk][e] * bl2e);
     f32x16 y[NQ][NCT];
     float den[NQ][4];
 #pragma unroll
@@ -599,54 +622,61 @@ attend_bf16_kernel(AttendArgs a) {
       for (int ct = 0; ct < NCT; ++ct) y[s][ct] = f32x16{};
 #pragma unroll
       for (int i = 0; i < 4; ++i) den[s][i] = 0.f;
-    }
-    const int nc = tc.nc, c0 = tc.c0;
-    const int jn = attend_wg_tile(j + 1, T);  // the next tile, whose queries load during the last chunk
-    // scores of unit 0 alone; the values of the (nonexistent) unit -1 get zero probabilities
-    f32x16 scA[NQ], scB[NQ];
-    bf16x8 pbA[NQ][2], pbB[NQ][2];
-    const AttendChunk<D, DV>& b0 = sb[gbase % R];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s) {
-      scA[s] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        scA[s] = mfma32(__builtin_bit_cast(bf16x8, b0.k[(2 * kk + g) * 64 + l32]), qb[s][kk], scA[s]);
+      // the values of the (nonexistent) unit -1 get zero probabilities
 #pragma unroll
       for (int e = 0; e < 8; ++e) pbA[s][0][e] = pbA[s][1][e] = (__bf16)0.f;
     }
+    const int nc = tc.nc, c0 = tc.c0;
+    const int jn = attend_wg_tile(j + 1, T);  // the next tile
+    const AttendTile tn = attend_tile_at(a, jn < 0 ? 0 : jn, QT, nchk, per);
+    const int qn0 = tn.qt * kAttendQueries + qoff;
+    bf16x8 qbn[NQ][NK];
     // Chunk gc = gbase + c sits in ring slot gc % R (unit 2c in its lower half, 2c+1 in the
     // upper).  Its loads were issued R-1 chunks ahead and are waited for at the barrier of chunk
     // gc-1, with the chunks after it still in flight; that barrier also frees slot
-    // (gc-1) % R, whose last reads (values of unit 2c-1) come before it.  The last chunk is
-    // peeled off the loop: it also loads the next tile's query fragments, and only there do
-    // they need registers beside the current ones.
-    auto chunk = [&](int c, bool last) {
+    // (gc-1) % R, whose last reads (values of unit 2c-1) come before it.
+    // The next tile's query fragments are requested two chunks before the end of this one
+    // (MODE 1, after that chunk's loads) and stay in flight behind the chunk awaited at the
+    // next barrier (MODE 2).  At the last chunk (MODE 3) they are scaled right after its
+    // barrier, before any further load is issued, so that the wait the compiler puts in front
+    // of their first use covers nothing younger than them; its second step then scores the
+    // next tile's first unit (the first chunk of the next tile is resident by then) under the
+    // next tile's queries.  A one-chunk tile requests and scales them after its barrier
+    // (MODE 4), and the last tile of the workgroup has none to request (MODE 0 throughout).
+    auto chunk = [&](int c, auto mode_c) {
+      constexpr int MODE = decltype(mode_c)::value;
       const int gc = gbase + c;
       const int bc = gc % R, bn = (gc + 1) % R, bl = c == 0 ? bc : (gc + R - 1) % R;
       const int left = lim - (c0 + c) * 64;  // rows of this chunk below the bound
       if (MASK && left < 32) attend_mask<NQ>(scA, left, g);
       attend_step<D, DV, NQ>(sb[bc], 1, sb[bc], 0, sb[bl], c == 0 ? 0 : 1, qb, y, den, scA, scB, pbA, pbB, g, l32);
       attend_pin<NQ>(pbB, den);
-      // chunk gc+1 landed; the chunks issued after it (at most R-2) may still be loading
-      attend_wait<D, DV>(issued - (gc + 2), wid);
+      // chunk gc+1 landed; the chunks issued after it (at most R-2) may still be loading, and
+      // so may the next tile's query fragments once requested
+      attend_wait<D, DV, (MODE == 2 || MODE == 3) ? QN : 0>(issued - (gc + 2), wid);
       __syncthreads();
-      const int before = issued;
-      if (last && jn >= 0) {
-        const AttendTile tn = attend_tile_at(a, jn, QT, nchk, per);
-        attend_load_q<D, NQ>(a, tn.h, tn.qt * kAttendQueries + qoff, g, qraw);
-      }
+      if constexpr (MODE == 4) attend_load_q<D, NQ>(a, tn.h, qn0, g, qraw);
+      if constexpr (MODE == 3 || MODE == 4) attend_scale_q<D, NQ>(qraw, qn0, m, bl2e, qbn);
       issue_next();
+      if constexpr (MODE == 1) attend_load_q<D, NQ>(a, tn.h, qn0, g, qraw);
       if (MASK && left < 64) attend_mask<NQ>(scB, left - 32, g);
-      // at the last chunk, the scores of the next unit are those of the next tile's first chunk
-      // under this tile's queries: never exponentiated
-      attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
+      if constexpr (MODE == 3 || MODE == 4)
+        attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qbn, y, den, scB, scA, pbB, pbA, g, l32);
+      else  // at the last chunk of the last tile the next unit's scores are never used
+        attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
       attend_pin<NQ>(pbA, den);
-      return issued - before;
     };
-    for (int c = 0; c < nc - 1; ++c) chunk(c, false);
-    // chunk loads issued after the next tile's query fragments
-    const int after_q = chunk(nc - 1, true);
+    if (jn < 0) {
+      for (int c = 0; c < nc; ++c) chunk(c, std::integral_constant<int, 0>{});
+    } else if (nc == 1) {
+      chunk(0, std::integral_constant<int, 4>{});
+    } else {
+      const int cq = nc >= 3 ? nc - 3 : 0;
+      for (int c = 0; c < cq; ++c) chunk(c, std::integral_constant<int, 0>{});
+      chunk(cq, std::integral_constant<int, 1>{});
+      if (nc >= 3) chunk(nc - 2, std::integral_constant<int, 2>{});
+      chunk(nc - 1, std::integral_constant<int, 3>{});
+    }
     // values of the last unit
     const AttendChunk<D, DV>& bz = sb[(gbase + nc - 1) % R];
 #pragma unroll
@@ -655,10 +685,6 @@ attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
       for (int s = 0; s < NQ; ++s) y[s][i >> 1] = mfma32(wf, pbA[s][i & 1], y[s][i >> 1]);
     }
-    // the next tile's query fragments have landed once at most the chunk loads issued after
-    // them are in flight (waited for before this tile's outputs are stored, so that the
-    // stores do not join the count)
-    if (jn >= 0) attend_wait<D, DV>(after_q, wid);
     // outputs of this tile
     const int h = tc.h, sp = tc.sp, q0 = tc.qt * kAttendQueries + qoff;
 #pragma unroll
@@ -701,9 +727,13 @@ attend_bf16_kernel(AttendArgs a) {
       }
     }
     if (jn < 0) break;
-    // the next tile (its first chunk landed at the last barrier)
+    // the next tile: its queries are scaled and its first unit scored
     gbase += nc;
-    tc = attend_tile_at(a, jn, QT, nchk, per);
+    tc = tn;
+#pragma unroll
+    for (int s = 0; s < NQ; ++s)
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) qb[s][kk] = qbn[s][kk];
     ++j;
   }
 }

@@ -138,7 +138,10 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
 
 /* Nystroem weights W = H_SS^{-1} H_{S,:} [V, 1] for the first rank[h] pivots
  * (gist.science/de/paper/2602.10056, "Methodik" part 2: W = h(K_S,K_S)^+ h(K_S,K), V_S = W V).
- * Computed through the factor of wc_rpcholesky, so the keys are not needed again: with
+ * Takes the factor F of wc_rpcholesky in place of the keys, a deliberate departure from a
+ * keys-in signature: the factor yields the weights without a second pass over the keys and is
+ * the more accurate order in fp32.  Pivots that come without their factor need H_SS formed
+ * from the keys, which the union weights of wc_forward with bins do.  With
  * L = F[S, :] (lower triangular, L L^T = H_SS) and H_{:,S} = F L^T, W = L^{-T} F^T [V, 1].
  *   V             in  [heads][n][dv], dtype
  *   pivots, rank  in  as returned by wc_rpcholesky
@@ -150,7 +153,11 @@ wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
 
 /* Attention of every query over the weighted coreset (page gptget.net/papers/2602.10056,
  * Abstract: attend only over a small weighted coreset): Y = exp(beta Q K_S^T) W,
- * O = Y[:, :dv] / Y[:, dv], with K_S the keys at the first rank[h] pivots.
+ * O = Y[:, :dv] / Y[:, dv], with K_S the keys at the first rank[h] pivots.  Precision: bf16
+ * problems round the probabilities and W (the normaliser column included) to bf16 on the
+ * matrix cores with fp32 sums, so a query row whose normaliser condition number
+ * sum |P| |W[:, dv]| / |Y[:, dv]| is kappa carries a relative error of about 2^-8 (1 + kappa);
+ * fp32 problems use hi + lo bf16 splits (about 2^-16 relative).
  *   Q           in  [heads][m][d], dtype
  *   K, pivots, rank, W   in  as above
  *   O           out [heads][m][dv], dtype
