@@ -340,6 +340,82 @@ __global__ void __launch_bounds__(256) union_back_kernel(UnionArgs a, int k) {
       if (col0 + c0 + c < nc) Xj[(size_t)(i0 + r4) * nc + col0 + c0 + c] -= acc[r4][c];
 }
 
+// ---- backward substitution in one launch, for rp <= kBackMaxRows ----------------------------
+// The columns of W = L^{-T} Z are independent, so one workgroup takes kBackCols of them for one
+// head and runs every block step k = nb-1 .. 0 itself, its slice of Z resident in LDS:
+//     W_k = M_kk^T Z_k,   then Z_j -= L_kj^T W_k for every j < k.
+// Products on the fp32 matrix cores, 16 x 16 x 4 (lane l: A[l % 16][l / 16], B[l / 16][l % 16],
+// D rows 4 (l / 16) .. + 3 of column l % 16).  The A operands (M_kk and L_kj, read transposed)
+// come straight from global memory, one step ahead of their products; the B operands (Z_k,
+// W_k) from LDS.  Per step: waves 0-3 form the four 16-row tiles of W_k, then all waves share
+// the 4 k tiles of the update.
+constexpr int kBackCols = 16;
+constexpr int kBackMaxRows = 2048;  // the Z slice: kBackMaxRows x kBackCols floats, 128 KB
+constexpr int kBackWaves = 8;
+
+__global__ void __launch_bounds__(64 * kBackWaves) union_back_slices_kernel(UnionArgs a) {
+  __shared__ __attribute__((aligned(16))) float sZ[kBackMaxRows][kBackCols];
+  __shared__ __attribute__((aligned(16))) float sW[kUB][kBackCols];
+  const int h = blockIdx.y, col0 = blockIdx.x * kBackCols, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int nb = a.rp / kUB, nc = a.dv + 1;
+  const float* Mh = a.M + (size_t)h * nb * kUB * kUB;
+  const float* A = a.A + (size_t)h * a.rp * a.rp;
+  const float* X = a.X + (size_t)h * a.rp * nc;
+  float* W = a.W + (size_t)h * a.r * nc;
+  for (int e = tid; e < a.rp * kBackCols; e += 64 * kBackWaves) {
+    const int row = e / kBackCols, c = e % kBackCols;
+    sZ[row][c] = col0 + c < nc ? X[(size_t)row * nc + col0 + c] : 0.f;
+  }
+  // A operand of a 16-row tile: av[s] = G[(4 s + lk) * ld + lr], t = 4 s + lk the summed index
+  auto load_a = [&](float (&av)[16], const float* G, size_t ld) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) av[s] = G[(size_t)(4 * s + lk) * ld + lr];
+  };
+  // update tile `tile` of step k: rows 16 (tile % 4) .. of block j = tile / 4, L_kj read transposed
+  auto tile_src = [&](int k, int tile) {
+    return A + (size_t)k * kUB * a.rp + (size_t)(tile >> 2) * kUB + 16 * (tile & 3);
+  };
+  float am[16], at[16];
+  if (wid < 4) load_a(am, Mh + (size_t)(nb - 1) * kUB * kUB + 16 * wid, kUB);
+  if (wid < 4 * (nb - 1)) load_a(at, tile_src(nb - 1, wid), a.rp);
+  __syncthreads();
+  for (int k = nb - 1; k >= 0; --k) {
+    if (wid < 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am[s], sZ[k * kUB + 4 * s + lk][lr], acc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * wid + 4 * lk + v, wr = k * kUB + row;
+        sW[row][lr] = acc[v];
+        if (wr < a.r && col0 + lr < nc) W[(size_t)wr * nc + col0 + lr] = acc[v];
+      }
+      if (k > 0) load_a(am, Mh + (size_t)(k - 1) * kUB * kUB + 16 * wid, kUB);
+    }
+    __syncthreads();
+    // (a wave without a tile in this step has none in the next either)
+    for (int tile = wid; tile < 4 * k; tile += kBackWaves) {
+      float an[16];
+      const int next = tile + kBackWaves;
+      // the next tile of this step, or the first of the next step
+      if (next < 4 * k) load_a(an, tile_src(k, next), a.rp);
+      else if (wid < 4 * (k - 1)) load_a(an, tile_src(k - 1, wid), a.rp);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at[s], sW[4 * s + lk][lr], acc, 0, 0, 0);
+      const int r0 = (tile >> 2) * kUB + 16 * (tile & 3) + 4 * lk;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sZ[r0 + v][lr] -= acc[v];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) at[s] = an[s];
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T, int D>
 hipError_t run_gather(const UnionArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((union_gather_kernel<T, D>), dim3(a.r, a.H), dim3(64), 0, st, a);
@@ -377,6 +453,11 @@ hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_union_back(const UnionArgs& a, hipStream_t st) {
+  if (a.rp <= kBackMaxRows) {
+    const int ns = (a.dv + 1 + kBackCols - 1) / kBackCols;
+    hipLaunchKernelGGL(union_back_slices_kernel, dim3(ns, a.H), dim3(64 * kBackWaves), 0, st, a);
+    return hipGetLastError();
+  }
   const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB;
   for (int k = nb - 1; k >= 0; --k) {
     hipLaunchKernelGGL(union_back_kernel, dim3((k + 1) * nxz, a.H), dim3(256), 0, st, a, k);
