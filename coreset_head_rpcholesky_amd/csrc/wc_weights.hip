@@ -34,14 +34,18 @@ __global__ void __launch_bounds__(256) gather_L_kernel(WeightsArgs a) {
 //   X[j, c] += sum_i F[j, i] V[i, c]   (32 x 32 x 16 MFMAs, one tile per 32 value columns),
 // its A operand (8 consecutive keys of one row of F) loaded straight from global memory into
 // registers and split there into hi + lo bf16 parts, so each element of F is read once in the
-// whole grid.  The B operand, V transposed, is staged in LDS once per 128-key sub-pass for all
+// whole grid.  The B operand, V transposed, is staged in LDS once per 64-key sub-pass for all
 // eight waves (double-buffered: the next sub-pass's F and V loads are in flight during the
 // current MFMAs).  The ones column X[j, dv] = sum_i F[j, i] is an fp32 sum in registers.
+// The loads are branch-free (clamped addresses, out-of-range values zeroed where they are
+// used), V's before F's in each sub-pass, and the two F buffers alternate without copies, so
+// that no wait for one load holds up the loads behind it: the compiler waits for each F
+// fragment just before its products and for V just before it is staged.
 // Workgroups that share a chunk of keys (and so its rows of V) are dealt to one XCD, so V is
 // read from HBM about once and from that XCD's L2 by the others.
 constexpr int XW = 8;           // waves per workgroup
 constexpr int XJG = 32 * XW;    // rows of X per workgroup
-constexpr int XKS = 128;        // key rows per sub-pass
+constexpr int XKS = 64;         // key rows per sub-pass
 constexpr int XKK = XKS / 16;   // 16-key MFMA steps per sub-pass
 constexpr int XVP = XKS + 8;    // LDS pitch (bf16) of one transposed value column
 
@@ -69,13 +73,17 @@ __global__ void __launch_bounds__(64 * XW) x_partial_kernel(WeightsArgs a) {
   // MFMA step kk takes, in lane half g, the keys key_of(kk) .. + 7 of the sub-pass (A and B alike)
   auto key_of = [&](int kk) { return 16 * kk + 8 * g; };
   // F: keys ib + key_of(kk) .. + 7 of row j, kk = 0 .. XKK - 1
+  // (VEC: 16-byte loads with no conditions around them.  i1 is a multiple of 4, so each
+  // 4-key piece lies wholly inside or wholly past the chunk; a piece past it reads the row's
+  // first keys instead, as rows past r read row 0 of the head, and all are zeroed where they
+  // are used)
   auto load_f = [&](int ib, float (&f)[XKK][8]) {
 #pragma unroll
     for (int kk = 0; kk < XKK; ++kk) {
       const int i = ib + key_of(kk);
-      if (VEC && jv && i + 8 <= i1) {
-        const float4 x0 = *reinterpret_cast<const float4*>(Fj + i);
-        const float4 x1 = *reinterpret_cast<const float4*>(Fj + i + 4);
+      if constexpr (VEC) {
+        const float4 x0 = *reinterpret_cast<const float4*>(Fj + (i < i1 ? i : 0));
+        const float4 x1 = *reinterpret_cast<const float4*>(Fj + (i + 4 < i1 ? i + 4 : 0));
         f[kk][0] = x0.x; f[kk][1] = x0.y; f[kk][2] = x0.z; f[kk][3] = x0.w;
         f[kk][4] = x1.x; f[kk][5] = x1.y; f[kk][6] = x1.z; f[kk][7] = x1.w;
       } else {
@@ -90,25 +98,24 @@ __global__ void __launch_bounds__(64 * XW) x_partial_kernel(WeightsArgs a) {
   constexpr int CG = DV / CPL;                     // column groups
   constexpr int NUNIT = (XKS / 2) * CG;                       // (key pair, column group) units
   constexpr int VPASS = (NUNIT + 64 * XW - 1) / (64 * XW);    // units per thread
+  // (keys past the chunk read its last key, and are zeroed when staged)
   auto load_v = [&](int ib, uint4 (&v)[VPASS][2]) {
 #pragma unroll
     for (int u = 0; u < VPASS; ++u) {
-      const int unit = tid + u * 64 * XW, kp = unit / CG, cg = unit % CG;
+      const int unit = min(tid + u * 64 * XW, NUNIT - 1), kp = unit / CG, cg = unit % CG;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int i = ib + 2 * kp + q;
-        v[u][q] = (unit < NUNIT && i < i1) ? *reinterpret_cast<const uint4*>(V + (size_t)i * DV + cg * CPL)
-                                           : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int q = 0; q < 2; ++q)
+        v[u][q] = *reinterpret_cast<const uint4*>(V + (size_t)min(ib + 2 * kp + q, i1 - 1) * DV + cg * CPL);
     }
   };
-  auto store_v = [&](int buf, const uint4 (&v)[VPASS][2]) {
+  auto store_v = [&](int ib, int buf, const uint4 (&v)[VPASS][2]) {
 #pragma unroll
     for (int u = 0; u < VPASS; ++u) {
       const int unit = tid + u * 64 * XW, kp = unit / CG, cg = unit % CG;
       if (unit >= NUNIT) continue;
-      const uint32_t w0[4] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w};
-      const uint32_t w1[4] = {v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+      const bool in0 = ib + 2 * kp < i1, in1 = ib + 2 * kp + 1 < i1;
+      const uint32_t w0[4] = {in0 ? v[u][0].x : 0u, in0 ? v[u][0].y : 0u, in0 ? v[u][0].z : 0u, in0 ? v[u][0].w : 0u};
+      const uint32_t w1[4] = {in1 ? v[u][1].x : 0u, in1 ? v[u][1].y : 0u, in1 ? v[u][1].z : 0u, in1 ? v[u][1].w : 0u};
       if constexpr (!SPLITV) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // columns 8 cg + 2 e and + 1: (key 2kp, key 2kp+1)
@@ -135,29 +142,18 @@ __global__ void __launch_bounds__(64 * XW) x_partial_kernel(WeightsArgs a) {
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x16{};
   float colsum = 0.f;
-  float fc[XKK][8], fn[XKK][8];
-  uint4 vn[VPASS][2];
-  if (i0 < i1) {
-    load_f(i0, fc);
-    load_v(i0, vn);
-    store_v(0, vn);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int ib = i0; ib < i1; ib += XKS) {
-    const bool more = ib + XKS < i1;
-    if (more) {
-      load_f(ib + XKS, fn);
-      load_v(ib + XKS, vn);
-    }
+  // products of one sub-pass; F's keys past the chunk and its rows past r count as zero
+  auto products = [&](int ib, int buf, const float (&fc)[XKK][8]) {
+    const int lim = jv ? i1 - ib - 8 * g : 0;  // keys 16 kk + e of this lane below lim are in range
 #pragma unroll
     for (int kk = 0; kk < XKK; ++kk) {
       bf16x8 ah, al;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        colsum += fc[kk][e];
+        const float x = 16 * kk + e < lim ? fc[kk][e] : 0.f;
+        colsum += x;
         __bf16 hi, lo;
-        split_bf16(fc[kk][e], hi, lo);
+        split_bf16(x, hi, lo);
         ah[e] = hi;
         al[e] = lo;
       }
@@ -173,13 +169,31 @@ __global__ void __launch_bounds__(64 * XW) x_partial_kernel(WeightsArgs a) {
         }
       }
     }
-    if (more) store_v(buf ^ 1, vn);
+  };
+  float fa[XKK][8], fb[XKK][8];
+  uint4 vn[VPASS][2];
+  if (i0 < i1) {
+    load_v(i0, vn);
+    load_f(i0, fa);
+    store_v(i0, 0, vn);
+  }
+  __syncthreads();
+  // one sub-pass on the F fragments fc, with the next sub-pass's loaded into fn
+  // (the loads and the staging run even after the chunk's last sub-pass, from clamped
+  // addresses: with no branch around them the compiler neither sinks the loads to their use
+  // nor loses count of those in flight; the fence keeps them ahead of the products)
+  auto sub_pass = [&](int ib, int buf, const float (&fc)[XKK][8], float (&fn)[XKK][8]) {
+    load_v(ib + XKS, vn);
+    load_f(ib + XKS, fn);
+    __builtin_amdgcn_sched_barrier(0);
+    products(ib, buf, fc);
+    store_v(ib + XKS, buf ^ 1, vn);
     __syncthreads();
-    buf ^= 1;
-#pragma unroll
-    for (int kk = 0; kk < XKK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fc[kk][e] = fn[kk][e];
+  };
+  // sub-passes in pairs (an odd count ends with one wholly past the chunk, all of it zeroed)
+  for (int ib = i0; ib < i1; ib += 2 * XKS) {
+    sub_pass(ib, 0, fa, fb);
+    sub_pass(ib + XKS, 1, fb, fa);
   }
   float* X = a.Xpart + (((size_t)h * a.nchunk + chunk) * r) * (DV + 1);
 #pragma unroll
