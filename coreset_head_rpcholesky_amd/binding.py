@@ -13,11 +13,14 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwc.so")
+# WC_DEBUG=1 selects the debug build, whose kernels check the pivot indices they read
+# (WC_FLAG_BOUNDS); both are built by coreset_head_rpcholesky_amd.build
+LIB_PATH = os.path.join(_HERE, "libwc_debug.so" if os.environ.get("WC_DEBUG") == "1" else "libwc.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libwc_debug.so")
 
 WC_OK, WC_ERR_INVALID_ARG, WC_ERR_UNSUPPORTED, WC_ERR_WORKSPACE, WC_ERR_DEVICE = range(5)
 WC_F32, WC_BF16 = 0, 1
-WC_FLAG_BREAKDOWN, WC_FLAG_NONFINITE, WC_FLAG_DENOM, WC_FLAG_DEPENDENT = 1, 2, 4, 8
+WC_FLAG_BREAKDOWN, WC_FLAG_NONFINITE, WC_FLAG_DENOM, WC_FLAG_DEPENDENT, WC_FLAG_BOUNDS = 1, 2, 4, 8, 16
 WC_OPT_BIN_WEIGHTS = 1
 WC_OPT_CENTER_KEYS = 2
 

@@ -279,7 +279,7 @@ hipError_t run_rpc_stream(const wc_problem& p, const Layout& L, void* ws, const 
 
 hipError_t run_weights(const wc_problem& p, const Layout& L, void* ws, const void* V,
                        const int32_t* pivots, const int32_t* rank, const float* F, float* W,
-                       hipStream_t st) {
+                       hipStream_t st, uint32_t* flags = nullptr) {
   wc::WeightsArgs a{};
   a.V = V;
   a.bf16 = p.dtype == WC_BF16;
@@ -291,6 +291,7 @@ hipError_t run_weights(const wc_problem& p, const Layout& L, void* ws, const voi
   a.X = at<float>(ws, L.X);
   a.W = W;
   a.Minv = blocked_solve(p) ? at<float>(ws, L.Minv) : nullptr;
+  a.flags = flags;
   return wc::launch_weights(a, st);
 }
 
@@ -377,7 +378,7 @@ wc_status forward_binned(const wc_problem& p, const void* Q, const void* K, cons
   float* F = at<float>(ws, B.sub.F);
   float* W = at<float>(ws, B.sub.W);
   hipError_t e = run_select(sp, B.sub, ws, K, u_forced, seed, piv_sub, F, rank_sub, flags_sub, s);
-  if (e == hipSuccess && !union_weights(p)) e = run_weights(sp, B.sub, ws, V, piv_sub, rank_sub, F, W, s);
+  if (e == hipSuccess && !union_weights(p)) e = run_weights(sp, B.sub, ws, V, piv_sub, rank_sub, F, W, s, flags_sub);
   int32_t* piv = pivots ? pivots : at<int32_t>(ws, B.piv);
   int32_t* slots = at<int32_t>(ws, B.rank_slots);
   if (e == hipSuccess) {
@@ -613,7 +614,7 @@ wc_status wc_forward(const wc_problem* p, const void* Q, const void* K, const vo
   float* F = at<float>(ws, L.F);
   float* W = at<float>(ws, L.W);
   hipError_t e = run_select(*p, L, ws, K, u_forced, seed, piv, F, rank, flags, s);
-  if (e == hipSuccess) e = run_weights(*p, L, ws, V, piv, rank, F, W, s);
+  if (e == hipSuccess) e = run_weights(*p, L, ws, V, piv, rank, F, W, s, flags);
   if (e == hipSuccess) e = run_attend(*p, L, ws, Q, K, piv, rank, W, O, flags, s);
   return dev(e);
 }
@@ -659,7 +660,7 @@ wc_status wc_compress(const wc_problem* p, const void* K, const void* V, const f
     float* F = at<float>(ws, L.F);
     float* W = at<float>(ws, L.W);
     e = run_select(q, L, ws, K, u_forced, seed, piv, F, rank, flags, s);
-    if (e == hipSuccess) e = run_weights(q, L, ws, V, piv, rank, F, W, s);
+    if (e == hipSuccess) e = run_weights(q, L, ws, V, piv, rank, F, W, s, flags);
     if (e != hipSuccess) return dev(e);
     a.pivots = piv; a.rank = rank; a.W = W;
   }

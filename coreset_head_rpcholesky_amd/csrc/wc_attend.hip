@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(128) attend_prep_kernel(AttendArgs a) {
   // slots past the rank, and slots a bin left empty (pivot -1), carry zero weight
   const int rk = a.rank[h];
   const int sj = j < rk ? a.pivots[(size_t)h * a.r + j] : -1;
-  const bool valid = sj >= 0;
+  const bool valid = sj >= 0 && wc_index_ok(sj, a.n, a.flags ? a.flags + h : nullptr);
   const int s = valid ? sj : 0;
   const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + s) * D;
   for (int e = tid; e < D; e += 128) {

@@ -21,6 +21,25 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
+// Debug builds (WC_DEBUG=1) check every index that a kernel reads from device memory before
+// dereferencing it: the pivot indices handed in by the caller, which the host cannot see.  An
+// index outside [0, n) is not used (the slot counts as empty) and flag bit 16 (WC_FLAG_BOUNDS)
+// is OR-ed into the head's flags when the kernel has them; the checks report instead of
+// trapping, so the device stays usable and the flags name the head.  Other builds trust the
+// ranges the entry points document.
+#ifndef WC_DEBUG
+#define WC_DEBUG 0
+#endif
+__device__ __forceinline__ bool wc_index_ok(int i, int n, uint32_t* flag) {
+  if constexpr (WC_DEBUG == 0) {
+    return true;
+  } else {
+    const bool ok = i >= 0 && i < n;
+    if (!ok && flag) atomicOr(flag, 16u);  // WC_DFLAG_BOUNDS
+    return ok;
+  }
+}
+
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -9,6 +9,7 @@
 #define WC_DFLAG_NONFINITE 2u
 #define WC_DFLAG_DENOM 4u
 #define WC_DFLAG_DEPENDENT 8u
+#define WC_DFLAG_BOUNDS 16u  // WC_DEBUG builds: an out-of-range pivot index (see wc_index_ok)
 
 namespace wc {
 
@@ -98,6 +99,7 @@ struct WeightsArgs {
   float* W;               // out [H][r][dv+1]
   float* Minv;            // ws [H][r/64][64][64] inverses of L's diagonal blocks, or NULL: the
                           // blocked back substitution (r a multiple of 64) instead of trisolve
+  uint32_t* flags;        // [H] or NULL: WC_DFLAG_BOUNDS for an out-of-range pivot (WC_DEBUG)
 };
 hipError_t launch_weights(const WeightsArgs& a, hipStream_t st);
 

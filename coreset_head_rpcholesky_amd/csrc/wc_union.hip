@@ -103,9 +103,10 @@ template <typename T, int D>
 __global__ void __launch_bounds__(64) union_gather_kernel(UnionArgs a) {
   const int j = blockIdx.x, h = blockIdx.y;
   const int s = a.pivots[(size_t)h * a.r + j];
-  const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + (s >= 0 ? s : 0)) * D;
+  const bool valid = s >= 0 && wc_index_ok(s, a.n, a.flags ? a.flags + h : nullptr);
+  const T* K = reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + (valid ? s : 0)) * D;
   T* Qs = reinterpret_cast<T*>(a.Qs) + ((size_t)h * a.r + j) * D;
-  for (int e = threadIdx.x; e < D; e += 64) Qs[e] = s >= 0 ? K[e] : T(0);
+  for (int e = threadIdx.x; e < D; e += 64) Qs[e] = valid ? K[e] : T(0);
 }
 
 // ---- gram: A = exp(beta K_S K_S^T) on the lower blocks, its diagonal, zero X padding -------

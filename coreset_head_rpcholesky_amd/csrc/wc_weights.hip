@@ -22,11 +22,13 @@ namespace wc {
 __global__ void __launch_bounds__(256) gather_L_kernel(WeightsArgs a) {
   const int t = blockIdx.x, h = blockIdx.y;
   const int r = a.r, rk = a.rank[h];
-  const int s = (t < rk) ? a.pivots[(size_t)h * r + t] : 0;
+  const int sp = (t < rk) ? a.pivots[(size_t)h * r + t] : 0;
+  const bool valid = t < rk && wc_index_ok(sp, a.n, a.flags ? a.flags + h : nullptr);
+  const int s = valid ? sp : 0;
   const float* F = a.F + (size_t)h * r * a.n;
   float* L = a.L + ((size_t)h * r + t) * r;
   for (int j = threadIdx.x; j < r; j += 256)
-    L[j] = (t < rk && j <= t) ? F[(size_t)j * a.n + s] : 0.f;
+    L[j] = (valid && j <= t) ? F[(size_t)j * a.n + s] : 0.f;
 }
 
 // X partial over the key rows [i0, i0 + chunk_rows) for XJG rows of X.  Eight waves; wave w

@@ -42,6 +42,9 @@
  *       WC_FLAG_DENOM      some query row had a normaliser Y[:, dv] <= 0
  *       WC_FLAG_DEPENDENT  (bins > 1) the union weights left out a coreset point that is
  *                          numerically dependent on earlier ones (see wc_forward)
+ *       WC_FLAG_BOUNDS     (debug library libwc_debug.so only) a pivot index read from device
+ *                          memory lay outside [0, n); the slot was treated as empty.  The
+ *                          regular library does not check pivot indices it is handed.
  *    After a breakdown pivots[rank..r-1] = -1, F columns rank..r-1 = 0, and weights and
  *    attention use the first rank pivots only.
  *  - Workspace: `ws` must hold at least wc_workspace_bytes() bytes for the same problem.
@@ -68,7 +71,13 @@ typedef enum {
 
 typedef enum { WC_F32 = 0, WC_BF16 = 1 } wc_dtype;
 
-enum { WC_FLAG_BREAKDOWN = 1u, WC_FLAG_NONFINITE = 2u, WC_FLAG_DENOM = 4u, WC_FLAG_DEPENDENT = 8u };
+enum {
+  WC_FLAG_BREAKDOWN = 1u,
+  WC_FLAG_NONFINITE = 2u,
+  WC_FLAG_DENOM = 4u,
+  WC_FLAG_DEPENDENT = 8u,
+  WC_FLAG_BOUNDS = 16u
+};
 
 /* wc_problem.options bits */
 enum {

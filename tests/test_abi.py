@@ -264,3 +264,16 @@ def test_pivot_block_validation(lib):
     assert lib.wc_weights(ctypes.byref(blk), A, None, A, A, A, big, big, None) == 1
     # the selection holds the candidate columns G [b][n]: more workspace than one pivot a step
     assert ws_bytes(lib, blk)[1] > ws_bytes(lib, Problem(2, 4096, 64, 64, 64, 256, 1, 1, 0, 0))[1]
+
+
+DEBUG_LIB = os.path.join(ROOT, "coreset_head_rpcholesky_amd", "libwc_debug.so")
+
+
+@pytest.mark.skipif(not os.path.exists(DEBUG_LIB), reason="libwc_debug.so not built")
+def test_debug_library_exports_the_same_abi():
+    """The debug build (pivot indices checked in the kernels that read them) is the same ABI."""
+    dbg = ctypes.CDLL(DEBUG_LIB)
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
+    dbg.wc_abi_version.restype = ctypes.c_int32
+    assert dbg.wc_abi_version() == 7
