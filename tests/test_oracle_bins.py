@@ -221,3 +221,41 @@ def test_union_is_more_accurate_than_per_bin_weights():
         eu.append(ow.rel_fro(ow.forward_binned(Q, K, V, 32, 4, u)["O"], exact))
         eb.append(ow.rel_fro(ow.forward_binned(Q, K, V, 32, 4, u, weights_mode="bin")["O"], exact))
     assert np.mean(eu) < 0.5 * np.mean(eb), (eu, eb)
+
+
+@pytest.mark.parametrize("delta,kept_expected", [(0.06, True), (0.007, False)])
+def test_near_dependent_pair_on_either_side_of_the_tolerance(delta, kept_expected):
+    """A key near an earlier coreset key, its relative Schur residual g / H_jj a few times above
+    (delta 0.06, about 2^-9) or below (delta 0.007, about 2^-15) DEPENDENT_TOL.  Above, the pair
+    is kept and W is numpy's pseudo-inverse form, as for distinct keys.  Below, the point is left
+    out: its weight row is zero and the others are the weights of the coreset without it, again
+    in numpy's pseudo-inverse form.  Kept, the output equals the full pseudo-inverse's; left
+    out, it differs from it (here by about 2 %): that is the cost of the leave-out reading on a
+    12-key head whose coreset is nearly all of it, where one more point still moves the
+    interpolation."""
+    rng = np.random.default_rng(40)
+    d, beta = 3, 0.6
+    X = rng.standard_normal((12, d)) * 0.9
+    e = rng.standard_normal(d)
+    X[7] = X[2] + delta * e / np.linalg.norm(e)
+    V = rng.standard_normal((12, 2))
+    slots = np.arange(9)
+    H = ow.kernel(X[slots], X[slots], beta)
+    P = [j for j in range(7)]
+    g = H[7, 7] - H[7, P] @ np.linalg.solve(H[np.ix_(P, P)], H[P, 7])
+    rel = g / H[7, 7]
+    assert (rel > ow.DEPENDENT_TOL) == kept_expected
+    assert (rel > 2 * ow.DEPENDENT_TOL) if kept_expected else (rel < ow.DEPENDENT_TOL / 2)
+    W, kept = ow.weights_union(X, V, slots, beta)
+    V1 = np.hstack([V, np.ones((12, 1))])
+    keep_idx = slots if kept_expected else np.delete(slots, 7)
+    assert kept.tolist() == [True] * 7 + [kept_expected] + [True]
+    Wp = np.linalg.pinv(ow.kernel(X[keep_idx], X[keep_idx], beta)) @ ow.kernel(X[keep_idx], X, beta) @ V1
+    Wfull = np.zeros_like(W)
+    Wfull[keep_idx] = Wp
+    assert np.allclose(W, Wfull, rtol=1e-6, atol=1e-8 * np.abs(Wp).max())
+    Q = rng.standard_normal((5, d)) * 0.9
+    Wall = np.linalg.pinv(H) @ ow.kernel(X[slots], X, beta) @ V1
+    Ya, Yb = ow.kernel(Q, X[slots], beta) @ W, ow.kernel(Q, X[slots], beta) @ Wall
+    err = ow.rel_fro(Ya[:, :2] / Ya[:, 2:], Yb[:, :2] / Yb[:, 2:])
+    assert (err < 1e-8) if kept_expected else (1e-4 < err < 0.1)
