@@ -71,61 +71,123 @@ __device__ __forceinline__ bool elim_block(float* sA, const float* hd, float tol
   return dependent;
 }
 
-// The same elimination of a 64 x 64 block by one wave, without barriers (same results up to
-// rounding order).  Called by every thread of the workgroup; wave 0 works and the others wait at
-// the final barrier.  Lane i holds row i of the block and column i of G.  Step j reads column j
-// of the block (every lane's A[i][j], written to LDS at the end of step j-1) and takes the
-// pivot p = A[j][j] and the leave-out scale hd[j] by readlane; rows i > j subtract
-// f_i = A[i][j] / p times row j, whose entries past j equal column j's (the block is
-// symmetric); column c of G subtracts f_i G[j][c] from its rows i > j.  Row j of
-// M = G[j][:] rsq(p) (G's row j is final once step j begins) goes into row j of sA, which was
-// read into registers at the start.  One wave's LDS accesses complete in order, so no barrier
-// separates a column's write from its reads; the two column buffers alternate.  Returns, in
-// thread 0, whether a point with hd > 0 was left out.
+// The elimination of a 32 x 32 block by one wave, rows and identity image side by side: lanes
+// 0-31 hold the rows of the block, lanes 32-63 the columns of G (the image of the identity), so
+// one fused multiply-add per entry and pivot updates both (rows i > j subtract f_i times row j,
+// column c of G subtracts G[j][c] / p times column j of the block: the same form
+// w[k] -= c[k] (w[j] / p) with c column j of the block).  Column j is written to LDS by the row
+// lanes at the end of step j-1 and read back by every lane (one wave's LDS accesses complete in
+// order, so no barrier separates them; two buffers alternate); the pivot p and its leave-out
+// scale come by readlane.  Row j of M = G[j][:] rsq(p) is written by the G lanes to sM (pitch
+// PM): G's row j is final once step j begins.
+// The block sits in sA with pitch PA, hd are the 32 leave-out scales.  Wave 0 only; returns,
+// in every lane of it, whether a point with hd > 0 was left out.
+template <int PA, int PM>
+__device__ __forceinline__ bool elim32_wave(const float* sA, const float* hd, float tol, float (*sCol)[64],
+                                            float* sM) {
+  constexpr int B = 32;
+  const int lane = threadIdx.x & 63, i = lane & 31;
+  const bool rowlane = lane < 32;
+  const float hdl = hd[i];
+  float w[B];
+#pragma unroll
+  for (int e = 0; e < B; e += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(sA + i * PA + e);
+    w[e] = rowlane ? x.x : (e == i ? 1.f : 0.f);
+    w[e + 1] = rowlane ? x.y : (e + 1 == i ? 1.f : 0.f);
+    w[e + 2] = rowlane ? x.z : (e + 2 == i ? 1.f : 0.f);
+    w[e + 3] = rowlane ? x.w : (e + 3 == i ? 1.f : 0.f);
+  }
+  if (rowlane) sCol[0][i] = w[0];
+  bool dependent = false;
+  static_for<0, B>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const float* col = sCol[j & 1];
+    const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[j]), j));
+    const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hdl), j));
+    const bool keep = p > tol * hj;
+    dependent |= !keep && hj > 0.f;
+    if (!rowlane) sM[j * PM + i] = w[j] * (keep ? __builtin_amdgcn_rsqf(p) : 0.f);
+    if (keep) {
+      const float sc = w[j] * __builtin_amdgcn_rcpf(p);
+      constexpr int k0 = (j + 1) & ~3;
+#pragma unroll
+      for (int k4 = k0; k4 < B; k4 += 4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(col + k4);
+        const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k4 + e > j) w[k4 + e] = fmaf(-c[e], sc, w[k4 + e]);
+      }
+    }
+    if constexpr (j + 1 < B) {
+      if (rowlane) sCol[(j + 1) & 1][i] = w[j + 1];
+    }
+  });
+  return dependent;
+}
+
+// 32 x 32 x 32 product on a 256-thread workgroup: wave w forms the 16 x 16 quarter
+// (w / 2, w % 2) on the fp32 matrix cores (16 x 16 x 4: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; the result rows are 4 (l / 16) .. + 3 of column l % 16) and hands each
+// entry (row, column, value) to out.
+template <class FA, class FB, class FO>
+__device__ __forceinline__ void mm32_quarters(FA a_at, FB b_at, FO out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = lane >> 4, r0 = 16 * (w >> 1), c0 = 16 * (w & 1);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a_at(r0 + lr, 4 * s + lk), b_at(4 * s + lk, c0 + lr), acc, 0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) out(r0 + 4 * lk + v, c0 + lr, acc[v]);
+}
+
+// M = inverse of the Cholesky factor of the kept part of a 64 x 64 block (elim_block's result,
+// up to rounding order), in two halves of 32 pivots, for a 256-thread workgroup.  With
+// D = [D11 D21^T; D21 D22]:
+//   M11 = elimination of D11 (elim32_wave),  L21 = D21 M11^T,  D22' = D22 - L21 L21^T,
+//   M22 = elimination of D22',  M21 = -M22 L21 M11,
+// and M = [M11 0; M21 M22] replaces the block in sA (pitch P).  A point left out in the first
+// half has a zero row in M11 and so a zero column in L21; one left out in the second half has a
+// zero row in M22 and so in M21: M is the inverse of the kept part's factor with zero rows for
+// the left-out points, as before.  sS holds 4 x 32 x 33 floats of scratch.  Every thread calls
+// it; ends with a barrier; returns, in thread 0, whether a point with hd > 0 was left out.
 template <int P>
-__device__ __forceinline__ bool elim_block64_wave(float* sA, const float* hd, float tol, float (*sCol)[64]) {
-  constexpr int B = 64;
+__device__ __forceinline__ bool elim_block64_split(float* sA, const float* hd, float tol, float* sS,
+                                                   float (*sCol)[64]) {
+  constexpr int PS = 33;
+  float* sM1 = sS;
+  float* sL = sS + 32 * PS;
+  float* sM2 = sS + 2 * 32 * PS;
+  float* sT = sS + 3 * 32 * PS;
+  const int tid = threadIdx.x;
   bool dependent = false;
   __syncthreads();  // the block and hd are complete in LDS
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const float hdl = hd[lane];  // leave-out scale of the lane's point, broadcast by readlane
-    float v[B], g[B];
-#pragma unroll
-    for (int e = 0; e < B; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(sA + lane * P + e);
-      v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
-    }
-#pragma unroll
-    for (int e = 0; e < B; ++e) g[e] = e == lane ? 1.f : 0.f;
-    sCol[0][lane] = v[0];
-    static_for<0, B>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const float* col = sCol[j & 1];
-      const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), j));
-      const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hdl), j));
-      const bool keep = p > tol * hj;
-      dependent |= !keep && hj > 0.f;
-      sA[j * P + lane] = g[j] * (keep ? __builtin_amdgcn_rsqf(p) : 0.f);
-      if (keep) {
-        const float rp = __builtin_amdgcn_rcpf(p);
-        const float f = v[j] * rp, t = g[j] * rp;
-        constexpr int k0 = (j + 1) & ~3;
-#pragma unroll
-        for (int k4 = k0; k4 < B; k4 += 4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(col + k4);
-          const float c[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (k4 + e > j) {
-              v[k4 + e] = fmaf(-f, c[e], v[k4 + e]);
-              g[k4 + e] = fmaf(-c[e], t, g[k4 + e]);
-            }
-          }
-        }
-      }
-      if constexpr (j + 1 < B) sCol[(j + 1) & 1][lane] = v[j + 1];
-    });
+  if (tid < 64) dependent = elim32_wave<P, PS>(sA, hd, tol, sCol, sM1);
+  __syncthreads();
+  // L21 = D21 M11^T
+  mm32_quarters([&](int r, int t) { return sA[(32 + r) * P + t]; }, [&](int t, int c) { return sM1[c * PS + t]; },
+                [&](int r, int c, float v) { sL[r * PS + c] = v; });
+  __syncthreads();
+  // D22 -= L21 L21^T
+  mm32_quarters([&](int r, int t) { return sL[r * PS + t]; }, [&](int t, int c) { return sL[c * PS + t]; },
+                [&](int r, int c, float v) { sA[(32 + r) * P + 32 + c] -= v; });
+  __syncthreads();
+  if (tid < 64) dependent |= elim32_wave<P, PS>(sA + 32 * P + 32, hd + 32, tol, sCol, sM2);
+  __syncthreads();
+  // T = L21 M11
+  mm32_quarters([&](int r, int t) { return sL[r * PS + t]; }, [&](int t, int c) { return sM1[t * PS + c]; },
+                [&](int r, int c, float v) { sT[r * PS + c] = v; });
+  __syncthreads();
+  // M21 = -M22 T, and M assembled over the block
+  mm32_quarters([&](int r, int t) { return sM2[r * PS + t]; }, [&](int t, int c) { return sT[t * PS + c]; },
+                [&](int r, int c, float v) { sA[(32 + r) * P + c] = -v; });
+  for (int e = tid; e < 32 * 32; e += blockDim.x) {
+    const int r = e >> 5, c = e & 31;
+    sA[r * P + c] = sM1[r * PS + c];
+    sA[r * P + 32 + c] = 0.f;
+    sA[(32 + r) * P + 32 + c] = sM2[r * PS + c];
   }
   __syncthreads();
   return dependent;

@@ -165,13 +165,14 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
 }
 
 // ---- diag: M_kk = inverse of the Cholesky factor of the kept part of A_kk -------------------
-// Wave 0 of the workgroup eliminates the (already updated) block in sA with the leave-out rule
-// (elim_block64_wave); left-out points of valid slots set WC_DFLAG_DEPENDENT.  The diagonal
-// entries H_jj (the scale of the leave-out test) are staged in LDS first.
-__device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, float (*sA)[kLP],
-                                           float (*sCol)[kUB], float (*sRow)[kUB], float* sHd) {
+// The workgroup eliminates the (already updated) block in sA with the leave-out rule, in two
+// halves of 32 pivots on one wave joined by 32 x 32 products on the matrix cores
+// (elim_block64_split, sS its scratch); left-out points of valid slots set WC_DFLAG_DEPENDENT.
+// The diagonal entries H_jj (the scale of the leave-out test) are staged in LDS first.
+__device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, float (*sA)[kLP], float* sS,
+                                           float (*sCol)[kUB], float* sHd) {
   if (threadIdx.x < kUB) sHd[threadIdx.x] = a.Hd[(size_t)h * a.rp + (size_t)k * kUB + threadIdx.x];
-  const bool dependent = elim_block64_wave<kLP>(&sA[0][0], sHd, a.tol, sCol);
+  const bool dependent = elim_block64_split<kLP>(&sA[0][0], sHd, a.tol, sS, sCol);
   store_block<kUB, kLP>(&sA[0][0], a.M + ((size_t)h * (a.rp / kUB) + k) * kUB * kUB);
   if (dependent && threadIdx.x == 0) atomicOr(&a.flags[h], WC_DFLAG_DEPENDENT);
 }
@@ -179,14 +180,14 @@ __device__ __forceinline__ void diag_block(const UnionArgs& a, int h, int k, flo
 // The first diagonal block (later ones are factored by the update of the step before).
 __global__ void __launch_bounds__(256) union_diag0_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(16))) float sA[kUB][kLP];
+  __shared__ __attribute__((aligned(16))) float sS[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
-  __shared__ __attribute__((aligned(16))) float sRow[2][kUB];
   __shared__ float sHd[kUB];
   const int h = blockIdx.x;
   const float* A = a.A + (size_t)h * a.rp * a.rp;
   stage_direct(sA, A, a.rp);
   __syncthreads();
-  diag_block(a, h, 0, sA, sCol, sRow, sHd);
+  diag_block(a, h, 0, sA, &sS[0][0], sCol, sHd);
 }
 
 // ---- panel: L_ik = A_ik M_kk^T (i > k) and Z_k = M_kk X_k ------------------------------------
@@ -236,7 +237,6 @@ __global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
   __shared__ __attribute__((aligned(16))) float sP[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sQ[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
-  __shared__ __attribute__((aligned(16))) float sRow[2][kUB];
   __shared__ float sHd[kUB];
   const int h = blockIdx.y, tid = threadIdx.x, nb = a.rp / kUB, T = nb - k - 1;
   const int nc = a.dv + 1;
@@ -267,7 +267,7 @@ __global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
             make_float4(o.x - acc[r4][0], o.y - acc[r4][1], o.z - acc[r4][2], o.w - acc[r4][3]);
       }
       __syncthreads();
-      diag_block(a, h, k + 1, sP, sCol, sRow, sHd);
+      diag_block(a, h, k + 1, sP, &sQ[0][0], sCol, sHd);
       return;
     }
 #pragma unroll
