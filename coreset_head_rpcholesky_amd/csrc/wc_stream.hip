@@ -232,7 +232,10 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
   double* s_part = s_dyn;                                   // [nblk]
   float* s_fs = reinterpret_cast<float*>(s_dyn + a.nblk);   // [r]
   const int h = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
-  if (a.rank[h] < t) return;  // this head broke down at an earlier step
+  // the loads that depend on nothing go out together, before the first test: the head's rank,
+  // this step's uniform and (below) the block masses
+  const int rk = a.rank[h];
+  const float u_t = a.uniforms[(size_t)h * a.r + t];
   const int n = a.n, nblk = a.nblk;
   const double* part = (t & 1) ? a.part1 : a.part0;
   double* part_nx = (t & 1) ? a.part0 : a.part1;
@@ -253,6 +256,7 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
       mine += v;
     }
   }
+  if (rk < t) return;  // this head broke down at an earlier step
   double Ttot;
   const double excl = block_excl_scan(mine, red, &Ttot);
   const bool lead = (b == 0 && tid == 0);
@@ -264,7 +268,7 @@ __global__ void __launch_bounds__(NT) rpc_step_kernel(StreamRpcArgs a, int rows,
     }
     return;
   }
-  const double uT = (double)a.uniforms[(size_t)h * a.r + t] * Ttot;
+  const double uT = (double)u_t * Ttot;
   int cand = 0x7fffffff, lastpos = -1;
   double run = excl;
   for (int e = 0; e < per; ++e) {
