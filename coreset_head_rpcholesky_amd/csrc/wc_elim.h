@@ -75,11 +75,13 @@ __device__ __forceinline__ bool elim_block(float* sA, const float* hd, float tol
 // 0-31 hold the rows of the block, lanes 32-63 the columns of G (the image of the identity), so
 // one fused multiply-add per entry and pivot updates both (rows i > j subtract f_i times row j,
 // column c of G subtracts G[j][c] / p times column j of the block: the same form
-// w[k] -= c[k] (w[j] / p) with c column j of the block).  Column j is written to LDS by the row
-// lanes at the end of step j-1 and read back by every lane (one wave's LDS accesses complete in
-// order, so no barrier separates them; two buffers alternate); the pivot p and its leave-out
-// scale come by readlane.  Row j of M = G[j][:] rsq(p) is written by the G lanes to sM (pitch
-// PM): G's row j is final once step j begins.
+// w[k] -= c[k] (w[j] / p) with c column j of the block).  Column j+1 is written to LDS by the
+// row lanes as soon as step j has updated it, before the rest of step j, and read back by every
+// lane in step j+1 (one wave's LDS accesses complete in order, so no barrier separates them; two
+// buffers alternate).  The pivot p and its leave-out scale come by readlane; a left-out pivot
+// turns the step's multiplier to zero rather than skipping it, so the step is straight-line
+// code.  Row j of M = G[j][:] rsq(p) is written by the G lanes to sM (pitch PM): G's row j is
+// final once step j begins.
 // The block sits in sA with pitch PA, hd are the 32 leave-out scales.  Wave 0 only; returns,
 // in every lane of it, whether a point with hd > 0 was left out.
 template <int PA, int PM>
@@ -107,21 +109,32 @@ __device__ __forceinline__ bool elim32_wave(const float* sA, const float* hd, fl
     const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hdl), j));
     const bool keep = p > tol * hj;
     dependent |= !keep && hj > 0.f;
-    if (!rowlane) sM[j * PM + i] = w[j] * (keep ? __builtin_amdgcn_rsqf(p) : 0.f);
-    if (keep) {
-      const float sc = w[j] * __builtin_amdgcn_rcpf(p);
-      constexpr int k0 = (j + 1) & ~3;
-#pragma unroll
-      for (int k4 = k0; k4 < B; k4 += 4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(col + k4);
+    const float rs = keep ? __builtin_amdgcn_rsqf(p) : 0.f;
+    const float sc = keep ? w[j] * __builtin_amdgcn_rcpf(p) : 0.f;
+    if (!rowlane) sM[j * PM + i] = w[j] * rs;
+    if constexpr (j + 1 < B) {
+      // the float4 group holding column j+1 first, then its publication, then the rest
+      constexpr int g1 = (j + 1) & ~3;
+      {
+        const float4 c4 = *reinterpret_cast<const float4*>(col + g1);
         const float c[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (k4 + e > j) w[k4 + e] = fmaf(-c[e], sc, w[k4 + e]);
+          if (g1 + e > j) w[g1 + e] = fmaf(-c[e], sc, w[g1 + e]);
       }
-    }
-    if constexpr (j + 1 < B) {
       if (rowlane) sCol[(j + 1) & 1][i] = w[j + 1];
+#pragma unroll
+      for (int k4 = g1 + 4; k4 < B; k4 += 4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(col + k4);
+        w[k4] = fmaf(-c4.x, sc, w[k4]);
+        w[k4 + 1] = fmaf(-c4.y, sc, w[k4 + 1]);
+        w[k4 + 2] = fmaf(-c4.z, sc, w[k4 + 2]);
+        w[k4 + 3] = fmaf(-c4.w, sc, w[k4 + 3]);
+      }
+      // the step's updates happen in this step: otherwise the compiler defers them to each
+      // entry's first use and keeps every earlier column and multiplier live in registers
+#pragma unroll
+      for (int k = j + 1; k < B; ++k) asm volatile("" : "+v"(w[k]));
     }
   });
   return dependent;

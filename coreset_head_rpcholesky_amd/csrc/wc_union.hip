@@ -110,54 +110,84 @@ __global__ void __launch_bounds__(64) union_gather_kernel(UnionArgs a) {
 }
 
 // ---- gram: A = exp(beta K_S K_S^T) on the lower blocks, its diagonal, zero X padding -------
+// One workgroup per lower 64 x 64 block; the blocks of the heads go round-robin over the
+// workgroups (consecutive workgroups land on different XCDs, so with 8 heads each XCD's L2
+// holds one head's coreset keys).  bf16 keys: each wave forms a 32 x 32 quarter of the dot
+// products on the bf16 matrix cores (the products of bf16 values are exact in fp32), its
+// operands straight from global memory; fp32 keys: fp32 fused multiply-adds from LDS.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
-  __shared__ __attribute__((aligned(16))) float sI[32][kLP];
-  __shared__ __attribute__((aligned(16))) float sJ[32][kLP];
-  const int h = blockIdx.y, tid = threadIdx.x;
-  int x = blockIdx.x, bi = 0;
+  const int h = blockIdx.x % a.H, tid = threadIdx.x;
+  int x = blockIdx.x / a.H, bi = 0;
   while (x > bi) x -= ++bi;
   const int bj = x;
   const T* Qs = reinterpret_cast<const T*>(a.Qs) + (size_t)h * a.r * D;
-  float acc[4][4];
-  zero_acc(acc);
-  for (int e0 = 0; e0 < D; e0 += 32) {
-    __syncthreads();
-    for (int q = tid; q < 2 * kUB * 32; q += 256) {
-      const int side = q >> 11, row = (q >> 5) & 63, e = q & 31;
-      const int slot = (side ? bj : bi) * kUB + row;
-      const float v = slot < a.r ? ld_elem<T>(Qs + (size_t)slot * D + e0 + e) : 0.f;
-      (side ? sJ : sI)[e][row] = v;
-    }
-    __syncthreads();
-    const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
-#pragma unroll 8
-    for (int e = 0; e < 32; ++e) {
-      const float4 p = *reinterpret_cast<const float4*>(&sI[e][i0]);
-      const float4 q = *reinterpret_cast<const float4*>(&sJ[e][c0]);
-      const float pv[4] = {p.x, p.y, p.z, p.w}, qv[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(pv[i], qv[c], acc[i][c]);
-    }
-  }
-  const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
   float* A = a.A + (size_t)h * a.rp * a.rp;
+  auto finish = [&](int si, int sj, float dot) {
+    const float out = slot_valid(a, h, si) && slot_valid(a, h, sj) ? expf(a.beta * dot) : 0.f;
+    if (bi == bj && si == sj) a.Hd[(size_t)h * a.rp + si] = out;
+    return out;
+  };
+  if constexpr (sizeof(T) == 2) {
+    const int lane = tid & 63, w = tid >> 6, g = lane >> 5;
+    const int qm = 32 * (w >> 1), qn = 32 * (w & 1);
+    // rows past r (padding slots) read row r-1 and are zeroed by finish()
+    const int rm = min(bi * kUB + qm + (lane & 31), a.r - 1), rn = min(bj * kUB + qn + (lane & 31), a.r - 1);
+    const bf16x8* pm = reinterpret_cast<const bf16x8*>(Qs + (size_t)rm * D + 8 * g);
+    const bf16x8* pn = reinterpret_cast<const bf16x8*>(Qs + (size_t)rn * D + 8 * g);
+    bf16x8 fm[D / 16], fn[D / 16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int si = bi * kUB + i0 + i;
-    const bool vi = slot_valid(a, h, si);
-    float out[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int sj = bj * kUB + c0 + c;
-      out[c] = vi && slot_valid(a, h, sj) ? expf(a.beta * acc[i][c]) : 0.f;
-      if (bi == bj && si == sj) a.Hd[(size_t)h * a.rp + si] = out[c];
+    for (int s = 0; s < D / 16; ++s) {
+      fm[s] = pm[2 * s];
+      fn[s] = pn[2 * s];
     }
-    *reinterpret_cast<float4*>(A + (size_t)si * a.rp + bj * kUB + c0) = make_float4(out[0], out[1], out[2], out[3]);
+    f32x16 c;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) c[v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) c = mfma32(fm[s], fn[s], c);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int si = bi * kUB + qm + 8 * (v >> 2) + 4 * g + (v & 3), sj = bj * kUB + qn + (lane & 31);
+      A[(size_t)si * a.rp + sj] = finish(si, sj, c[v]);
+    }
+  } else {
+    __shared__ __attribute__((aligned(16))) float sI[32][kLP];
+    __shared__ __attribute__((aligned(16))) float sJ[32][kLP];
+    float acc[4][4];
+    zero_acc(acc);
+    for (int e0 = 0; e0 < D; e0 += 32) {
+      __syncthreads();
+      for (int q = tid; q < 2 * kUB * 32; q += 256) {
+        const int side = q >> 11, row = (q >> 5) & 63, e = q & 31;
+        const int slot = (side ? bj : bi) * kUB + row;
+        const float v = slot < a.r ? ld_elem<T>(Qs + (size_t)slot * D + e0 + e) : 0.f;
+        (side ? sJ : sI)[e][row] = v;
+      }
+      __syncthreads();
+      const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
+#pragma unroll 8
+      for (int e = 0; e < 32; ++e) {
+        const float4 p = *reinterpret_cast<const float4*>(&sI[e][i0]);
+        const float4 q = *reinterpret_cast<const float4*>(&sJ[e][c0]);
+        const float pv[4] = {p.x, p.y, p.z, p.w}, qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(pv[i], qv[c], acc[i][c]);
+      }
+    }
+    const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int si = bi * kUB + i0 + i;
+      float out[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) out[c] = finish(si, bj * kUB + c0 + c, acc[i][c]);
+      *reinterpret_cast<float4*>(A + (size_t)si * a.rp + bj * kUB + c0) = make_float4(out[0], out[1], out[2], out[3]);
+    }
   }
-  if (blockIdx.x == 0) {
+  if (blockIdx.x < (unsigned)a.H) {
     const int nc = a.dv + 1;
     float* X = a.X + (size_t)h * a.rp * nc;
     for (int e = a.r * nc + tid; e < a.rp * nc; e += 256) X[e] = 0.f;
@@ -190,107 +220,174 @@ __global__ void __launch_bounds__(256) union_diag0_kernel(UnionArgs a) {
   diag_block(a, h, 0, sA, &sS[0][0], sCol, sHd);
 }
 
-// ---- panel: L_ik = A_ik M_kk^T (i > k) and Z_k = M_kk X_k ------------------------------------
-__global__ void __launch_bounds__(256) union_panel_kernel(UnionArgs a, int k) {
-  __shared__ __attribute__((aligned(16))) float sP[kUB][kLP];
-  __shared__ __attribute__((aligned(16))) float sQ[kUB][kLP];
-  const int h = blockIdx.y, tid = threadIdx.x, nb = a.rp / kUB, T = nb - k - 1;
-  const int nc = a.dv + 1;
+// ---- 32 x 32 products with the operands straight from global memory ----------------------
+// One wave forms C = sum_t P[m][t] R[t][n] over t < 64 for a 32 x 32 tile on the fp32 matrix
+// cores, in 32 steps of 32 x 32 x 2: lane l supplies P[l % 32][t] and R[t][l % 32] for the two
+// values t of the step, and holds the result elements v = 0..15 at row 8 (v / 4) + 4 (l / 32) +
+// v % 4, column l % 32.  Lane l takes t = 32 (l / 32) + s in step s for both operands (the 64
+// terms in another order, the same sum), so that each lane reads 32 consecutive floats of a
+// row-major operand row.
+__device__ __forceinline__ int tile_row(int v) { return 8 * (v >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (v & 3); }
+__device__ __forceinline__ int tile_col() { return threadIdx.x & 31; }
+
+// f[s] = G[(l % 32) * ld + 32 (l / 32) + s]: 32 rows of a 64-wide block as the P operand (or
+// as R transposed: R[t][n] = G[n][t]); ld % 4 == 0, G 16-byte aligned.
+__device__ __forceinline__ void load_rows(float (&f)[32], const float* G, size_t ld) {
+  const int lane = threadIdx.x & 63;
+  const float4* p = reinterpret_cast<const float4*>(G + (size_t)(lane & 31) * ld + 32 * (lane >> 5));
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 v = p[q];
+    f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+  }
+}
+
+// f[s] = G[(32 (l / 32) + s) * ld + col + l % 32], zero for columns at or past ncol: 32 columns
+// of a 64-row block as the R operand.  The address is clamped, so every load is in bounds.
+__device__ __forceinline__ void load_cols(float (&f)[32], const float* G, int ld, int col, int ncol) {
+  const int lane = threadIdx.x & 63, c = col + (lane & 31);
+  const bool ok = c < ncol;
+  const float* p = G + (size_t)(32 * (lane >> 5)) * ld + (ok ? c : ncol - 1);
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    const float v = p[(size_t)s * ld];
+    f[s] = ok ? v : 0.f;
+  }
+}
+
+__device__ __forceinline__ f32x16 mm32(const float (&fp)[32], const float (&fr)[32]) {
+  f32x16 c;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) c[v] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(fp[s], fr[s], c, 0, 0, 0);
+  return c;
+}
+
+// mm32 with mid() issued after the first 16 steps, when their operand registers are free (the
+// loads of the block to be updated go there, so that they overlap the second half).
+template <class F>
+__device__ __forceinline__ f32x16 mm32_mid(const float (&fp)[32], const float (&fr)[32], F mid) {
+  __builtin_amdgcn_sched_barrier(0);   // the operand loads all issued before the first product
+  f32x16 c;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) c[v] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(fp[s], fr[s], c, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 16; s < 32; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(fp[s], fr[s], c, 0, 0, 0);
+  return c;
+}
+
+// ---- panel: L_ik = A_ik M_kk^T (i > k) and Z_k = M_kk X_k, in place ----------------------------
+// One wave per item, so that every block a wave overwrites was read by that wave alone: a
+// 32-row slice of some A_ik (both 32-column halves, P = its rows, R = M_kk^T), or a 32-column
+// slice of X_k (both 32-row halves, P = rows of M_kk, R = those columns of X_k).  The items of
+// the heads go round-robin over the workgroups.
+__global__ void __launch_bounds__(64) union_panel_kernel(UnionArgs a, int k) {
+  const int nb = a.rp / kUB, T = nb - k - 1, nc = a.dv + 1;
+  const int h = blockIdx.x % a.H, x = blockIdx.x / a.H;
   const float* M = a.M + ((size_t)h * nb + k) * kUB * kUB;
   float* A = a.A + (size_t)h * a.rp * a.rp;
-  float* X = a.X + (size_t)h * a.rp * nc;
-  float acc[4][4];
-  zero_acc(acc);
-  const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
-  if ((int)blockIdx.x < T) {
-    const int i = k + 1 + blockIdx.x;
-    float* Aik = A + (size_t)i * kUB * a.rp + (size_t)k * kUB;
-    stage_transposed(sP, Aik, a.rp);   // sP[t][row] = A_ik[row][t]
-    stage_transposed(sQ, M, kUB);      // sQ[t][c] = M[c][t]
-    __syncthreads();
-    mm64(sP, sQ, acc);
-    __syncthreads();
+  float fp[32], fr[32], fq[32];
+  f32x16 c0, c1;
+  if (x < 2 * T) {
+    float* Ls = A + ((size_t)(k + 1) * kUB + 32 * x) * a.rp + (size_t)k * kUB;   // rows 32 x of the panel
+    load_rows(fp, Ls, a.rp);
+    load_rows(fr, M, kUB);
+    load_rows(fq, M + 32 * kUB, kUB);
+    __builtin_amdgcn_sched_barrier(0);   // all operand loads in flight before the first product
+    c0 = mm32(fp, fr);
+    c1 = mm32(fp, fq);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<float4*>(Aik + (size_t)(i0 + r4) * a.rp + c0) =
-          make_float4(acc[r4][0], acc[r4][1], acc[r4][2], acc[r4][3]);
+    for (int v = 0; v < 16; ++v) {
+      Ls[(size_t)tile_row(v) * a.rp + tile_col()] = c0[v];
+      Ls[(size_t)tile_row(v) * a.rp + 32 + tile_col()] = c1[v];
+    }
   } else {
-    const int col0 = (blockIdx.x - T) * kUB;
-    float* Xk = X + (size_t)k * kUB * nc;
-    stage_transposed(sP, M, kUB);      // sP[t][row] = M[row][t]
-    stage_x(sQ, Xk, nc, col0, nc);
-    __syncthreads();
-    mm64(sP, sQ, acc);
-    __syncthreads();
+    const int col = 32 * (x - 2 * T);
+    float* Xk = a.X + ((size_t)h * a.rp + (size_t)k * kUB) * nc;
+    load_cols(fr, Xk, nc, col, nc);
+    load_rows(fp, M, kUB);
+    load_rows(fq, M + 32 * kUB, kUB);
+    __builtin_amdgcn_sched_barrier(0);
+    c0 = mm32(fp, fr);
+    c1 = mm32(fq, fr);
+    if (col + tile_col() < nc) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (col0 + c0 + c < nc) Xk[(size_t)(i0 + r4) * nc + col0 + c0 + c] = acc[r4][c];
+      for (int v = 0; v < 16; ++v) {
+        Xk[(size_t)tile_row(v) * nc + col + tile_col()] = c0[v];
+        Xk[(size_t)(32 + tile_row(v)) * nc + col + tile_col()] = c1[v];
+      }
+    }
   }
 }
 
 // ---- update: A_ij -= L_ik L_jk^T (k < j <= i), X_i -= L_ik Z_k --------------------------------
-// The block (k+1, k+1) has no other writer in this step, so its workgroup also factors it
-// (diag_block for block column k+1) once updated.
-__global__ void __launch_bounds__(256) union_update_kernel(UnionArgs a, int k) {
-  __shared__ __attribute__((aligned(16))) float sP[kUB][kLP];
-  __shared__ __attribute__((aligned(16))) float sQ[kUB][kLP];
+// A workgroup takes one 64 x 64 block, each wave a 32 x 32 quarter of it.  The first H
+// workgroups take block (k+1, k+1) of each head: it has no other writer in this step, so its
+// workgroup also factors it (diag_block for block column k+1) from LDS; that is the longest
+// path of the step, so it starts first.  The other blocks go round-robin over the heads.
+__global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k) {
+  __shared__ __attribute__((aligned(16))) float sA[kUB][kLP];
+  __shared__ __attribute__((aligned(16))) float sS[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
   __shared__ float sHd[kUB];
-  const int h = blockIdx.y, tid = threadIdx.x, nb = a.rp / kUB, T = nb - k - 1;
-  const int nc = a.dv + 1;
-  float* A = a.A + (size_t)h * a.rp * a.rp;
-  float* X = a.X + (size_t)h * a.rp * nc;
+  const int nb = a.rp / kUB, T = nb - k - 1, nc = a.dv + 1, nxz = (nc + kUB - 1) / kUB;
   const int npairs = T * (T + 1) / 2;
-  float acc[4][4];
-  zero_acc(acc);
-  const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
-  if ((int)blockIdx.x < npairs) {
-    int x = blockIdx.x, ii = 0;
-    while (x > ii) x -= ++ii;
-    const int i = k + 1 + ii, j = k + 1 + x;
-    const float* Lik = A + (size_t)i * kUB * a.rp + (size_t)k * kUB;
-    const float* Ljk = A + (size_t)j * kUB * a.rp + (size_t)k * kUB;
-    stage_transposed(sP, Lik, a.rp);   // sP[t][row] = L_ik[row][t]
-    stage_transposed(sQ, Ljk, a.rp);   // sQ[t][c] = L_jk[c][t]
-    __syncthreads();
-    mm64(sP, sQ, acc);
-    float* Aij = A + (size_t)i * kUB * a.rp + (size_t)j * kUB;
-    if (i == k + 1) {
-      // i == j == k + 1: the next diagonal block, factored here from LDS
-      __syncthreads();
+  int h, x;
+  if ((int)blockIdx.x < a.H) {
+    h = blockIdx.x;
+    x = 0;
+  } else {
+    const int y = blockIdx.x - a.H;
+    h = y % a.H;
+    x = 1 + y / a.H;
+  }
+  const int w = threadIdx.x >> 6, qm = 32 * (w >> 1), qn = 32 * (w & 1);
+  float* A = a.A + (size_t)h * a.rp * a.rp;
+  float fp[32], fr[32];
+  if (x < npairs) {
+    int xx = x, ii = 0;
+    while (xx > ii) xx -= ++ii;
+    const int i = k + 1 + ii, j = k + 1 + xx;
+    load_rows(fp, A + ((size_t)i * kUB + qm) * a.rp + (size_t)k * kUB, a.rp);
+    load_rows(fr, A + ((size_t)j * kUB + qn) * a.rp + (size_t)k * kUB, a.rp);
+    float* Aij = A + ((size_t)i * kUB + qm) * a.rp + (size_t)j * kUB + qn;
+    float old[16];
+    const f32x16 c = mm32_mid(fp, fr, [&] {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 o = *reinterpret_cast<const float4*>(Aij + (size_t)(i0 + r4) * a.rp + c0);
-        *reinterpret_cast<float4*>(&sP[i0 + r4][c0]) =
-            make_float4(o.x - acc[r4][0], o.y - acc[r4][1], o.z - acc[r4][2], o.w - acc[r4][3]);
-      }
-      __syncthreads();
-      diag_block(a, h, k + 1, sP, &sQ[0][0], sCol, sHd);
+      for (int v = 0; v < 16; ++v) old[v] = Aij[(size_t)tile_row(v) * a.rp + tile_col()];
+    });
+    if (x == 0) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sA[qm + tile_row(v)][qn + tile_col()] = old[v] - c[v];
+      diag_block(a, h, k + 1, sA, &sS[0][0], sCol, sHd);
       return;
     }
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      float4* p = reinterpret_cast<float4*>(Aij + (size_t)(i0 + r4) * a.rp + c0);
-      float4 o = *p;
-      o.x -= acc[r4][0]; o.y -= acc[r4][1]; o.z -= acc[r4][2]; o.w -= acc[r4][3];
-      *p = o;
-    }
+    for (int v = 0; v < 16; ++v) Aij[(size_t)tile_row(v) * a.rp + tile_col()] = old[v] - c[v];
   } else {
-    const int nxz = (nc + kUB - 1) / kUB;
-    const int x = blockIdx.x - npairs, i = k + 1 + x / nxz, col0 = (x % nxz) * kUB;
-    const float* Lik = A + (size_t)i * kUB * a.rp + (size_t)k * kUB;
-    stage_transposed(sP, Lik, a.rp);
-    stage_x(sQ, X + (size_t)k * kUB * nc, nc, col0, nc);
-    __syncthreads();
-    mm64(sP, sQ, acc);
-    float* Xi = X + (size_t)i * kUB * nc;
+    const int y = x - npairs, i = k + 1 + y / nxz, col = (y % nxz) * kUB + qn;
+    if (col >= nc) return;
+    float* X = a.X + (size_t)h * a.rp * nc;
+    load_rows(fp, A + ((size_t)i * kUB + qm) * a.rp + (size_t)k * kUB, a.rp);
+    load_cols(fr, X + (size_t)k * kUB * nc, nc, col, nc);
+    float* Xi = X + ((size_t)i * kUB + qm) * nc + col;
+    const bool ok = col + tile_col() < nc;
+    const int cc = ok ? tile_col() : nc - 1 - col;   // clamped: every load in bounds
+    float old[16];
+    const f32x16 c = mm32_mid(fp, fr, [&] {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
+      for (int v = 0; v < 16; ++v) old[v] = Xi[(size_t)tile_row(v) * nc + cc];
+    });
+    if (ok) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (col0 + c0 + c < nc) Xi[(size_t)(i0 + r4) * nc + col0 + c0 + c] -= acc[r4][c];
+      for (int v = 0; v < 16; ++v) Xi[(size_t)tile_row(v) * nc + tile_col()] = old[v] - c[v];
+    }
   }
 }
 
@@ -349,7 +446,8 @@ __global__ void __launch_bounds__(256) union_back_kernel(UnionArgs a, int k) {
 // D rows 4 (l / 16) .. + 3 of column l % 16).  The A operands (M_kk and L_kj, read transposed)
 // come straight from global memory, one step ahead of their products; the B operands (Z_k,
 // W_k) from LDS.  Per step: waves 0-3 form the four 16-row tiles of W_k, then all waves share
-// the 4 k tiles of the update.
+// the 4 k tiles of the update.  The slices of the heads go round-robin over the workgroups, so
+// that with 8 heads the slices of one head share an XCD and its L2 copy of L.
 constexpr int kBackCols = 16;
 constexpr int kBackMaxRows = 2048;  // the Z slice: kBackMaxRows x kBackCols floats, 128 KB
 constexpr int kBackWaves = 8;
@@ -357,7 +455,7 @@ constexpr int kBackWaves = 8;
 __global__ void __launch_bounds__(64 * kBackWaves) union_back_slices_kernel(UnionArgs a) {
   __shared__ __attribute__((aligned(16))) float sZ[kBackMaxRows][kBackCols];
   __shared__ __attribute__((aligned(16))) float sW[kUB][kBackCols];
-  const int h = blockIdx.y, col0 = blockIdx.x * kBackCols, tid = threadIdx.x;
+  const int h = blockIdx.x % a.H, col0 = (blockIdx.x / a.H) * kBackCols, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6, lr = lane & 15, lk = lane >> 4;
   const int nb = a.rp / kUB, nc = a.dv + 1;
   const float* Mh = a.M + (size_t)h * nb * kUB * kUB;
@@ -426,7 +524,7 @@ hipError_t run_gather(const UnionArgs& a, hipStream_t st) {
 template <typename T, int D>
 hipError_t run_gram(const UnionArgs& a, hipStream_t st) {
   const int nb = a.rp / kUB;
-  hipLaunchKernelGGL((union_gram_kernel<T, D>), dim3(nb * (nb + 1) / 2, a.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((union_gram_kernel<T, D>), dim3(a.H * (nb * (nb + 1) / 2)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -441,13 +539,13 @@ hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st) {
   hipError_t e = a.bf16 ? (a.d == 64 ? run_gram<uint16_t, 64>(a, st) : run_gram<uint16_t, 128>(a, st))
                         : (a.d == 64 ? run_gram<float, 64>(a, st) : run_gram<float, 128>(a, st));
   if (e != hipSuccess) return e;
-  const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB;
+  const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB, nxs = (a.dv + 1 + 31) / 32;
   hipLaunchKernelGGL(union_diag0_kernel, dim3(a.H), dim3(256), 0, st, a);
   for (int k = 0; k < nb; ++k) {
     const int T = nb - k - 1;
-    hipLaunchKernelGGL(union_panel_kernel, dim3(T + nxz, a.H), dim3(256), 0, st, a, k);
+    hipLaunchKernelGGL(union_panel_kernel, dim3(a.H * (2 * T + nxs)), dim3(64), 0, st, a, k);
     if (T > 0)
-      hipLaunchKernelGGL(union_update_kernel, dim3(T * (T + 1) / 2 + T * nxz, a.H), dim3(256), 0, st, a, k);
+      hipLaunchKernelGGL(union_update_kernel, dim3(a.H * (T * (T + 1) / 2 + T * nxz)), dim3(256), 0, st, a, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_union_back(a, st);
@@ -456,7 +554,7 @@ hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st) {
 hipError_t launch_union_back(const UnionArgs& a, hipStream_t st) {
   if (a.rp <= kBackMaxRows) {
     const int ns = (a.dv + 1 + kBackCols - 1) / kBackCols;
-    hipLaunchKernelGGL(union_back_slices_kernel, dim3(ns, a.H), dim3(64 * kBackWaves), 0, st, a);
+    hipLaunchKernelGGL(union_back_slices_kernel, dim3(ns * a.H), dim3(64 * kBackWaves), 0, st, a);
     return hipGetLastError();
   }
   const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB;

@@ -34,6 +34,9 @@ CASES = [
     ("stream_bins_ragged_m", "bf16", "iid_clip", 3, 1536, 257, 64, 128, 48, 3),
     ("stream_bins_ragged_r", "bf16", "mixture", 2, 6000, 130, 128, 64, 200, 8),
     ("stream_bins_f32_d64", "f32", "mixture", 1, 3000, 50, 64, 128, 150, 3),
+    # unions of 8 and 6 blocks of 64: several trailing-update and panel steps, more heads
+    ("stream_bins_r512_h5", "bf16", "iid_clip", 5, 8192, 96, 64, 128, 512, 8),
+    ("stream_bins_r384_f32", "f32", "iid_clip", 3, 6144, 70, 128, 64, 384, 6),
 ]
 
 
