@@ -511,10 +511,16 @@ __device__ __forceinline__ double lane_d(double x, int lane) {
   const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
   return __hiloint2double(hi, lo);
 }
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
-  return v;
+// The value of the lowest (or highest) lane for which `has` holds, or `none`: the minimum (or
+// maximum) over the wave of a quantity that increases with the lane, by one ballot instead of a
+// shuffle tree.
+__device__ __forceinline__ int first_lane_value(bool has, int v, int none) {
+  const uint64_t m = __ballot(has);
+  return m ? __builtin_amdgcn_readlane(v, __builtin_ctzll(m)) : none;
+}
+__device__ __forceinline__ int last_lane_value(bool has, int v, int none) {
+  const uint64_t m = __ballot(has);
+  return m ? __builtin_amdgcn_readlane(v, 63 - __builtin_clzll(m)) : none;
 }
 
 // One wave per head draws the round's b candidates one after the other, without replacement:
@@ -603,8 +609,9 @@ __global__ void __launch_bounds__(64) blk_sample_kernel(BlockRpcArgs A, int k) {
         if (v > 0.0) lastpos = bb;
       }
     }
-    int bstar = wave_min_int(bc);
-    if (bstar == 0x7fffffff) bstar = -wave_min_int(-lastpos);
+    // blocks go to the lanes in index order: the wave's first such block is the lowest lane's
+    int bstar = first_lane_value(bc != 0x7fffffff, bc, 0x7fffffff);
+    if (bstar == 0x7fffffff) bstar = last_lane_value(lastpos >= 0, lastpos, -1);
     if (bstar < 0) {  // no block with mass (excluded by T > 0; kept as a guard)
       for (int jj = j + lane; jj < B; jj += 64) cand[jj] = -1;
       break;
@@ -630,7 +637,7 @@ __global__ void __launch_bounds__(64) blk_sample_kernel(BlockRpcArgs A, int k) {
       c += pm[e];
       if (scand == 0x7fffffff && c > x && pm[e] > 0.0) scand = r0 + lane * RPT + e;
     }
-    const int s = wave_min_int(scand);
+    const int s = first_lane_value(scand != 0x7fffffff, scand, 0x7fffffff);
     if (s == 0x7fffffff || s >= n) {  // rounding left no row to claim x: no more candidates
       for (int jj = j + lane; jj < B; jj += 64) cand[jj] = -1;
       break;

@@ -229,6 +229,17 @@ __global__ void __launch_bounds__(256) union_diag0_kernel(UnionArgs a) {
 // row-major operand row.
 __device__ __forceinline__ int tile_row(int v) { return 8 * (v >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (v & 3); }
 __device__ __forceinline__ int tile_col() { return threadIdx.x & 31; }
+// Element v of the lane's tile result in a row-major matrix with leading dimension ld: the
+// lane's offset (one register) plus a part common to the wave.
+__device__ __forceinline__ uint32_t tile_lane_off(uint32_t ld) {
+  return 4 * ((threadIdx.x >> 5) & 1) * ld + (threadIdx.x & 31);
+}
+__device__ __forceinline__ uint32_t tile_v_off(int v, uint32_t ld) { return (uint32_t)(8 * (v >> 2) + (v & 3)) * ld; }
+// Element `idx` (a 32-bit element offset) of the matrix at base, addressed as a byte offset
+// from the wave's common base.
+__device__ __forceinline__ float& at32(float* base, uint32_t idx) {
+  return *reinterpret_cast<float*>(reinterpret_cast<char*>(base) + 4u * idx);
+}
 
 // f[s] = G[(l % 32) * ld + 32 (l / 32) + s]: 32 rows of a 64-wide block as the P operand (or
 // as R transposed: R[t][n] = G[n][t]); ld % 4 == 0, G 16-byte aligned.
@@ -247,10 +258,12 @@ __device__ __forceinline__ void load_rows(float (&f)[32], const float* G, size_t
 __device__ __forceinline__ void load_cols(float (&f)[32], const float* G, int ld, int col, int ncol) {
   const int lane = threadIdx.x & 63, c = col + (lane & 31);
   const bool ok = c < ncol;
-  const float* p = G + (size_t)(32 * (lane >> 5)) * ld + (ok ? c : ncol - 1);
+  // byte offsets from the wave's common base: one register per lane, not one address per load
+  const uint32_t off = 4u * ((uint32_t)(32 * (lane >> 5)) * ld + (ok ? c : ncol - 1));
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
-    const float v = p[(size_t)s * ld];
+    const char* base = reinterpret_cast<const char*>(G + (size_t)s * ld);   // common to the wave
+    const float v = *reinterpret_cast<const float*>(base + off);
     f[s] = ok ? v : 0.f;
   }
 }
@@ -357,10 +370,11 @@ __global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k
     load_rows(fp, A + ((size_t)i * kUB + qm) * a.rp + (size_t)k * kUB, a.rp);
     load_rows(fr, A + ((size_t)j * kUB + qn) * a.rp + (size_t)k * kUB, a.rp);
     float* Aij = A + ((size_t)i * kUB + qm) * a.rp + (size_t)j * kUB + qn;
+    const uint32_t lo = tile_lane_off(a.rp);
     float old[16];
     const f32x16 c = mm32_mid(fp, fr, [&] {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) old[v] = Aij[(size_t)tile_row(v) * a.rp + tile_col()];
+      for (int v = 0; v < 16; ++v) old[v] = at32(Aij + tile_v_off(v, a.rp), lo);
     });
     if (x == 0) {
 #pragma unroll
@@ -369,24 +383,25 @@ __global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k
       return;
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) Aij[(size_t)tile_row(v) * a.rp + tile_col()] = old[v] - c[v];
+    for (int v = 0; v < 16; ++v) at32(Aij + tile_v_off(v, a.rp), lo) = old[v] - c[v];
   } else {
     const int y = x - npairs, i = k + 1 + y / nxz, col = (y % nxz) * kUB + qn;
-    if (col >= nc) return;
+    if (col >= nc) return;   // a quarter wholly past the last column
     float* X = a.X + (size_t)h * a.rp * nc;
     load_rows(fp, A + ((size_t)i * kUB + qm) * a.rp + (size_t)k * kUB, a.rp);
     load_cols(fr, X + (size_t)k * kUB * nc, nc, col, nc);
     float* Xi = X + ((size_t)i * kUB + qm) * nc + col;
     const bool ok = col + tile_col() < nc;
-    const int cc = ok ? tile_col() : nc - 1 - col;   // clamped: every load in bounds
+    // clamped column: every load in bounds
+    const uint32_t lo = tile_lane_off(nc) - tile_col() + (ok ? tile_col() : nc - 1 - col);
     float old[16];
     const f32x16 c = mm32_mid(fp, fr, [&] {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) old[v] = Xi[(size_t)tile_row(v) * nc + cc];
+      for (int v = 0; v < 16; ++v) old[v] = at32(Xi + tile_v_off(v, nc), lo);
     });
     if (ok) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) Xi[(size_t)tile_row(v) * nc + tile_col()] = old[v] - c[v];
+      for (int v = 0; v < 16; ++v) at32(Xi + tile_v_off(v, nc), lo) = old[v] - c[v];
     }
   }
 }
