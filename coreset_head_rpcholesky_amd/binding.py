@@ -51,6 +51,8 @@ def _load():
         "wc_workspace_bytes": ([P, ctypes.POINTER(sz)], ctypes.c_int),
         "wc_rpcholesky": ([P, vp, vp, u64, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_weights": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_weights_keys_workspace_bytes": ([P, ctypes.POINTER(sz)], ctypes.c_int),
+        "wc_weights_keys": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_attend": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_forward": ([P, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "wc_forward_noalloc": ([P, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -171,6 +173,33 @@ def wc_weights(V: torch.Tensor, pivots, rank, F, *, ws=None, stream=None):
     if st != WC_OK:
         raise WcError("wc_weights", st)
     return W
+
+
+def wc_weights_keys(K: torch.Tensor, V: torch.Tensor, pivots, rank, *, flags=None, ws=None, stream=None):
+    """Nystroem weights W [H, r, dv+1] (fp32) from the keys, for any pivots (slots past rank
+    and pivots -1 empty); returns (W, flags)."""
+    H, n, d = K.shape
+    dv = V.shape[2]
+    r = pivots.shape[1]
+    dev = K.device
+    p = problem(H, n, 0, d, dv, r, K.dtype)
+    _check_in("V", V, K.dtype, (H, n, dv), dev)
+    _check_in("pivots", pivots, torch.int32, (H, r), dev)
+    _check_in("rank", rank, torch.int32, (H,), dev)
+    if flags is None:
+        flags = torch.zeros((H,), dtype=torch.int32, device=dev)
+    W = torch.empty((H, r, dv + 1), dtype=torch.float32, device=dev)
+    if ws is None:
+        nb = ctypes.c_size_t(0)
+        st = LIB.wc_weights_keys_workspace_bytes(ctypes.byref(p), ctypes.byref(nb))
+        if st != WC_OK:
+            raise WcError("wc_weights_keys_workspace_bytes", st)
+        ws = torch.empty((max(nb.value, 1),), dtype=torch.uint8, device=dev)
+    st = LIB.wc_weights_keys(ctypes.byref(p), _ptr(K), _ptr(V), _ptr(pivots), _ptr(rank), _ptr(W),
+                             _ptr(flags), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_weights_keys", st)
+    return W, flags
 
 
 def wc_attend(Q: torch.Tensor, K: torch.Tensor, pivots, rank, W, *, flags=None, ws=None,

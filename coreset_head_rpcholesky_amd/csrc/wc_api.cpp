@@ -170,15 +170,47 @@ Layout make_layout(const wc_problem& p, int parts = kSelect | kAttend) {
   return L;
 }
 
+// Buffers of the union weights W = H_SS^+ H_{S,:} [V, 1] for r slots per head, from `base` on:
+// the slots' pivots (a copy masked by rank, for wc_weights_keys), the coreset keys as rows,
+// the all-keys pass X = exp(beta K_S K^T) [V, 1] and the blocked solve.
+struct UnionLayout {
+  int urp, xsplit;
+  size_t piv, Qs, A, Hd, M, X, xKSh, xKSl, xWph, xWpl, xWden, xWdh, xYpart, total;
+};
+
+UnionLayout make_union_layout(const wc_problem& p, size_t base) {
+  UnionLayout U{};
+  const size_t H = (size_t)p.heads, r = (size_t)p.r, n = (size_t)p.n, nc = (size_t)p.dv + 1;
+  const size_t esz = p.dtype == WC_F32 ? 4 : 2, lo = p.dtype == WC_F32 ? 1 : 0;
+  const size_t urp = (r + 63) & ~size_t(63), np = (size_t)wc::attend_rows(p.n);
+  size_t off = align_up(base);
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  U.urp = (int)urp;
+  U.xsplit = attend_split(p, r, n);
+  U.piv = take(H * r * 4);
+  U.Qs = take(H * r * p.d * esz);
+  U.A = take(H * urp * urp * 4);
+  U.Hd = take(H * urp * 4);
+  U.M = take(H * urp * 64 * 4);
+  U.X = take(H * urp * nc * 4);
+  U.xKSh = take(H * np * p.d * 2);
+  U.xKSl = take(lo * H * np * p.d * 2);
+  U.xWph = take(H * p.dv * np * 2);
+  U.xWpl = take(lo * H * p.dv * np * 2);
+  U.xWden = take(H * np * 4);
+  U.xWdh = take(H * np * 2);
+  U.xYpart = take(U.xsplit > 1 ? H * U.xsplit * r * nc * 4 : 0);
+  U.total = off;
+  return U;
+}
+
 // Workspace of a binned forward: the per-bin selection and weights (the sub-head layout, whose
 // W is the heads' W), the heads' attention buffers, the per-bin outputs, and for the union
-// weights the all-keys pass X = exp(beta K_S K^T) [V, 1] and the blocked solve.
+// weights the union buffers.
 struct BinnedLayout {
   Layout sub, head;
   size_t head_base, piv_sub, rank_sub, flags_sub, rank_slots, piv, total;
-  // union weights
-  int urp, xsplit;
-  size_t Qs, A, Hd, M, X, xKSh, xKSl, xWph, xWpl, xWden, xWdh, xYpart;
+  UnionLayout U;
 };
 
 BinnedLayout make_binned_layout(const wc_problem& p) {
@@ -197,23 +229,8 @@ BinnedLayout make_binned_layout(const wc_problem& p) {
   B.rank_slots = take(H * 4);
   B.piv = take(H * r * 4);
   if (union_weights(p)) {
-    const size_t n = (size_t)p.n, nc = (size_t)p.dv + 1, esz = p.dtype == WC_F32 ? 4 : 2;
-    const size_t lo = p.dtype == WC_F32 ? 1 : 0;
-    const size_t urp = (r + 63) & ~size_t(63), np = (size_t)wc::attend_rows(p.n);
-    B.urp = (int)urp;
-    B.xsplit = attend_split(p, r, n);
-    B.Qs = take(H * r * p.d * esz);
-    B.A = take(H * urp * urp * 4);
-    B.Hd = take(H * urp * 4);
-    B.M = take(H * urp * 64 * 4);
-    B.X = take(H * urp * nc * 4);
-    B.xKSh = take(H * np * p.d * 2);
-    B.xKSl = take(lo * H * np * p.d * 2);
-    B.xWph = take(H * p.dv * np * 2);
-    B.xWpl = take(lo * H * p.dv * np * 2);
-    B.xWden = take(H * np * 4);
-    B.xWdh = take(H * np * 2);
-    B.xYpart = take(B.xsplit > 1 ? H * B.xsplit * r * nc * 4 : 0);
+    B.U = make_union_layout(p, off);
+    off = B.U.total;
   }
   B.total = off;
   return B;
@@ -363,6 +380,46 @@ hipError_t run_select(const wc_problem& p, const Layout& L, void* ws, const void
   return run_rpc_stream(p, L, ws, K, u_forced, seed, pivots, F, nullptr, nullptr, rank, flags, st);
 }
 
+// W = H_SS^+ H_{S,:} [V, 1] over the slots `piv` (-1: empty) of every head, into W
+// [heads][r][dv+1] (gist.science/de/paper/2602.10056, "Methodik" part 2, with the
+// pseudo-inverse taken by the leave-out Cholesky of the union kernels).
+hipError_t run_union_weights(const wc_problem& p, const UnionLayout& U, void* ws, const void* K,
+                             const void* V, const int32_t* piv, float* W, uint32_t* flags,
+                             hipStream_t s) {
+  wc::UnionArgs u{};
+  u.K = K; u.bf16 = p.dtype == WC_BF16;
+  u.H = p.heads; u.n = p.n; u.d = p.d; u.dv = p.dv; u.r = p.r; u.rp = U.urp;
+  u.beta = (float)(1.0 / std::sqrt((double)p.d));
+  u.tol = 0x1p-12f;
+  u.pivots = piv;
+  u.Qs = at<void>(ws, U.Qs);
+  u.A = at<float>(ws, U.A); u.Hd = at<float>(ws, U.Hd); u.M = at<float>(ws, U.M);
+  u.X = at<float>(ws, U.X); u.W = W; u.flags = flags;
+  hipError_t e = wc::launch_union_gather(u, s);
+  if (e == hipSuccess) {
+    // X = exp(beta K_S K^T) [V, 1]: the attention kernels with the coreset keys as queries
+    // and every key as a coreset row
+    wc::AttendArgs x{};
+    x.Q = u.Qs; x.K = K; x.V = V;
+    x.bf16 = u.bf16;
+    x.H = p.heads; x.n = p.n; x.m = p.r; x.d = p.d; x.dv = p.dv; x.r = p.n;
+    x.beta_log2e = beta_log2e(p.d);
+    x.KSh = at<uint16_t>(ws, U.xKSh);
+    x.KSl = p.dtype == WC_F32 ? at<uint16_t>(ws, U.xKSl) : nullptr;
+    x.Wph = at<uint16_t>(ws, U.xWph);
+    x.Wpl = p.dtype == WC_F32 ? at<uint16_t>(ws, U.xWpl) : nullptr;
+    x.Wden = at<float>(ws, U.xWden);
+    x.Wdh = at<uint16_t>(ws, U.xWdh);
+    x.nsplit = U.xsplit;
+    x.Ypart = U.xsplit > 1 ? at<float>(ws, U.xYpart) : nullptr;
+    x.flags = flags;
+    x.Yout = u.X; x.yrows = U.urp;
+    e = wc::launch_attend_all_keys(x, s);
+  }
+  if (e == hipSuccess) e = wc::launch_union_solve(u, s);
+  return e;
+}
+
 // Divide-and-conquer forward: selection and weights per bin on the sub-head view (the keys,
 // values and forced uniforms of bin b of head h are those of sub-head h B + b, contiguous),
 // pivots folded back to key indices of the head, then attention over the union.
@@ -388,39 +445,7 @@ wc_status forward_binned(const wc_problem& p, const void* Q, const void* K, cons
     a.pivots = piv; a.rank = rank; a.flags = flags; a.rank_slots = slots;
     e = wc::launch_bins_combine(a, s);
   }
-  if (e == hipSuccess && union_weights(p)) {
-    wc::UnionArgs u{};
-    u.K = K; u.bf16 = p.dtype == WC_BF16;
-    u.H = p.heads; u.n = p.n; u.d = p.d; u.dv = p.dv; u.r = p.r; u.rp = B.urp;
-    u.beta = (float)(1.0 / std::sqrt((double)p.d));
-    u.tol = 0x1p-12f;
-    u.pivots = piv;
-    u.Qs = at<void>(ws, B.Qs);
-    u.A = at<float>(ws, B.A); u.Hd = at<float>(ws, B.Hd); u.M = at<float>(ws, B.M);
-    u.X = at<float>(ws, B.X); u.W = W; u.flags = flags;
-    e = wc::launch_union_gather(u, s);
-    if (e == hipSuccess) {
-      // X = exp(beta K_S K^T) [V, 1]: the attention kernels with the coreset keys as queries
-      // and every key as a coreset row
-      wc::AttendArgs x{};
-      x.Q = u.Qs; x.K = K; x.V = V;
-      x.bf16 = u.bf16;
-      x.H = p.heads; x.n = p.n; x.m = p.r; x.d = p.d; x.dv = p.dv; x.r = p.n;
-      x.beta_log2e = beta_log2e(p.d);
-      x.KSh = at<uint16_t>(ws, B.xKSh);
-      x.KSl = p.dtype == WC_F32 ? at<uint16_t>(ws, B.xKSl) : nullptr;
-      x.Wph = at<uint16_t>(ws, B.xWph);
-      x.Wpl = p.dtype == WC_F32 ? at<uint16_t>(ws, B.xWpl) : nullptr;
-      x.Wden = at<float>(ws, B.xWden);
-      x.Wdh = at<uint16_t>(ws, B.xWdh);
-      x.nsplit = B.xsplit;
-      x.Ypart = B.xsplit > 1 ? at<float>(ws, B.xYpart) : nullptr;
-      x.flags = flags;
-      x.Yout = u.X; x.yrows = B.urp;
-      e = wc::launch_attend_all_keys(x, s);
-    }
-    if (e == hipSuccess) e = wc::launch_union_solve(u, s);
-  }
+  if (e == hipSuccess && union_weights(p)) e = run_union_weights(p, B.U, ws, K, V, piv, W, flags, s);
   wc_problem hp = p;
   hp.bins = 1;
   if (e == hipSuccess && p.m > 0)
@@ -559,6 +584,32 @@ wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
   Layout L;
   if ((st = check_ws(*p, ws, ws_bytes, &L)) != WC_OK) return st;
   return dev(run_weights(*p, L, ws, V, pivots, rank, F, W, static_cast<hipStream_t>(stream)));
+}
+
+wc_status wc_weights_keys_workspace_bytes(const wc_problem* p, size_t* bytes) {
+  const wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (centred(*p) || binned(*p)) return WC_ERR_UNSUPPORTED;
+  if (!bytes) return WC_ERR_INVALID_ARG;
+  *bytes = p->heads == 0 ? 0 : make_union_layout(*p, 0).total;
+  return WC_OK;
+}
+
+wc_status wc_weights_keys(const wc_problem* p, const void* K, const void* V, const int32_t* pivots,
+                          const int32_t* rank, float* W, uint32_t* flags, void* ws, size_t ws_bytes,
+                          void* stream) {
+  wc_status st = check_problem(p);
+  if (st != WC_OK) return st;
+  if (centred(*p) || binned(*p)) return WC_ERR_UNSUPPORTED;
+  if (p->heads == 0) return WC_OK;
+  if (!req(K) || !req(V) || !req(pivots) || !req(rank) || !req(W) || !req(flags)) return WC_ERR_INVALID_ARG;
+  const UnionLayout U = make_union_layout(*p, 0);
+  if (!ws || !aligned16(ws) || ws_bytes < U.total) return WC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* piv = at<int32_t>(ws, U.piv);
+  hipError_t e = wc::launch_union_mask(pivots, rank, piv, p->heads, p->r, s);
+  if (e == hipSuccess) e = run_union_weights(*p, U, ws, K, V, piv, W, flags, s);
+  return dev(e);
 }
 
 wc_status wc_attend(const wc_problem* p, const void* Q, const void* K, const int32_t* pivots,

@@ -190,6 +190,8 @@ struct UnionArgs {
   float* W;               // out [H][r][dv+1]
   uint32_t* flags;        // [H]: WC_DFLAG_DEPENDENT when a point of a valid slot is left out
 };
+// out[h][j] = pivots[h][j] for j < rank[h], else -1 (the slots of wc_weights_keys)
+hipError_t launch_union_mask(const int32_t* pivots, const int32_t* rank, int32_t* out, int H, int r, hipStream_t st);
 hipError_t launch_union_gather(const UnionArgs& a, hipStream_t st);  // fills Qs
 hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st);   // A, Hd, M from Qs; X -> W
 // The blocked back substitution alone: W = L^{-T} X from the lower factor L (in A, leading

@@ -98,6 +98,13 @@ __device__ __forceinline__ void zero_acc(float acc[4][4]) {
     for (int c = 0; c < 4; ++c) acc[i][c] = 0.f;
 }
 
+// ---- the slots of wc_weights_keys: pivots past the head's rank become empty (-1) -----------
+__global__ void __launch_bounds__(256) union_mask_kernel(const int32_t* pivots, const int32_t* rank, int32_t* out,
+                                                         int r) {
+  const int h = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  if (j < r) out[(size_t)h * r + j] = j < rank[h] ? pivots[(size_t)h * r + j] : -1;
+}
+
 // ---- gather: the coreset keys as rows, zero rows for empty slots ---------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(64) union_gather_kernel(UnionArgs a) {
@@ -544,6 +551,11 @@ hipError_t run_gram(const UnionArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_union_mask(const int32_t* pivots, const int32_t* rank, int32_t* out, int H, int r, hipStream_t st) {
+  hipLaunchKernelGGL(union_mask_kernel, dim3((r + 255) / 256, H), dim3(256), 0, st, pivots, rank, out, r);
+  return hipGetLastError();
+}
 
 hipError_t launch_union_gather(const UnionArgs& a, hipStream_t st) {
   if (a.bf16) return a.d == 64 ? run_gather<uint16_t, 64>(a, st) : run_gather<uint16_t, 128>(a, st);

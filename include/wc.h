@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 7
+#define WC_ABI_VERSION 8
 
 typedef enum {
   WC_OK = 0,
@@ -147,10 +147,9 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
 
 /* Nystroem weights W = H_SS^{-1} H_{S,:} [V, 1] for the first rank[h] pivots
  * (gist.science/de/paper/2602.10056, "Methodik" part 2: W = h(K_S,K_S)^+ h(K_S,K), V_S = W V).
- * Takes the factor F of wc_rpcholesky in place of the keys, a deliberate departure from a
- * keys-in signature: the factor yields the weights without a second pass over the keys and is
- * the more accurate order in fp32.  Pivots that come without their factor need H_SS formed
- * from the keys, which the union weights of wc_forward with bins do.  With
+ * Takes the factor F of wc_rpcholesky in place of the keys: the factor yields the weights
+ * without a second pass over the keys and is the more accurate order in fp32.  Pivots that
+ * come without their factor take wc_weights_keys below (keys in).  With
  * L = F[S, :] (lower triangular, L L^T = H_SS) and H_{:,S} = F L^T, W = L^{-T} F^T [V, 1].
  *   V             in  [heads][n][dv], dtype
  *   pivots, rank  in  as returned by wc_rpcholesky
@@ -159,6 +158,29 @@ wc_status wc_rpcholesky(const wc_problem* p, const void* K, const float* u_force
 wc_status wc_weights(const wc_problem* p, const void* V, const int32_t* pivots,
                      const int32_t* rank, const float* F, float* W, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Nystroem weights from the keys, for any pivots (gist.science/de/paper/2602.10056, "Methodik"
+ * part 2: W = h(K_S,K_S)^+ h(K_S,K)): W = H_SS^+ H_{S,:} [V, 1] over the slots j < rank[h]
+ * (slots past the rank, and pivots -1, are empty: zero weight rows).  H_{S,:} [V, 1] comes
+ * from one pass of the attention kernels over all n keys, and the pseudo-inverse is the
+ * Cholesky of H_SS in slot order that leaves out every point whose residual is at most
+ * 2^-12 H_jj (a repeated pivot, or one numerically in the span of the earlier ones): its weight
+ * row is zero and WC_FLAG_DEPENDENT is OR-ed into flags[h].  For distinct, independent pivots
+ * (those of wc_rpcholesky) this is the inverse, and W equals wc_weights' up to rounding.
+ * Precision: bf16 problems form H_{S,:} [V, 1] with bf16 probabilities (fp32 sums), so its
+ * rounding reaches W amplified by the conditioning of H_SS.  Pivot indices must lie in
+ * [0, n) or be -1; the debug library flags others (WC_FLAG_BOUNDS) and treats them as empty.
+ *   K             in  [heads][n][d], dtype
+ *   V             in  [heads][n][dv], dtype
+ *   pivots        in  [heads][r] key indices or -1;  rank in [heads]
+ *   W             out [heads][r][dv+1]
+ *   flags         in/out [heads]: WC_FLAG_DEPENDENT is OR-ed in
+ *   ws            at least wc_weights_keys_workspace_bytes() bytes (its own size: the all-keys
+ *                 pass and the blocked solve, not the other entry points' workspace)           */
+wc_status wc_weights_keys_workspace_bytes(const wc_problem* p, size_t* bytes);
+wc_status wc_weights_keys(const wc_problem* p, const void* K, const void* V, const int32_t* pivots,
+                          const int32_t* rank, float* W, uint32_t* flags, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Attention of every query over the weighted coreset (page gptget.net/papers/2602.10056,
  * Abstract: attend only over a small weighted coreset): Y = exp(beta Q K_S^T) W,

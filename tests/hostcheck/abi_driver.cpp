@@ -64,6 +64,20 @@ void run_valid(const wc_problem& p) {
       EXPECT(wc_weights(&p, buf(3), buf(5), buf(6), buf(9), buf(12), kWs, ws, nullptr) == WC_OK);
       EXPECT(wc_attend(&p, buf(1), buf(2), buf(5), buf(6), buf(12), buf(4), buf(7), kWs, ws, nullptr) == WC_OK);
     }
+    // weights from the keys: their own workspace size, refused one byte short
+    size_t kws = 0;
+    EXPECT(wc_weights_keys_workspace_bytes(&p, &kws) == WC_OK);
+    wc_hostcheck_set_ws((void*)kWs, kws);
+    EXPECT(wc_weights_keys(&p, buf(2), buf(3), buf(5), buf(6), buf(12), buf(7), kWs, kws, nullptr) == WC_OK);
+    if (kws > 0) {
+      const long n0 = wc_hostcheck_calls();
+      EXPECT(wc_weights_keys(&p, buf(2), buf(3), buf(5), buf(6), buf(12), buf(7), kWs, kws - 1, nullptr) == WC_ERR_WORKSPACE);
+      EXPECT(wc_weights_keys(&p, buf(2), nullptr, buf(5), buf(6), buf(12), buf(7), kWs, kws, nullptr) == WC_ERR_INVALID_ARG);
+      EXPECT(wc_hostcheck_calls() == n0);
+    }
+  } else {
+    size_t kws = 1234;
+    EXPECT(wc_weights_keys_workspace_bytes(&p, &kws) == WC_ERR_UNSUPPORTED && kws == 1234);
   }
 }
 

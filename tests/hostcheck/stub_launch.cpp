@@ -99,6 +99,11 @@ hipError_t launch_union_gather(const UnionArgs& a, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_union_solve(const UnionArgs& a, hipStream_t s) { return launch_union_gather(a, s); }
+hipError_t launch_union_mask(const int32_t* pivots, const int32_t* rank, int32_t* out, int, int, hipStream_t) {
+  check(pivots, "pivots"); check(rank, "rank"); check(out, "out");
+  ++g_calls;
+  return hipSuccess;
+}
 hipError_t launch_union_back(const UnionArgs& a, hipStream_t s) { return launch_union_gather(a, s); }
 hipError_t launch_center(const CenterArgs& a, hipStream_t) {
   CHK(K); CHK(part); CHK(mean); CHK(Kc);

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 7
+    assert lib.wc_abi_version() == 8
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -276,4 +276,4 @@ def test_debug_library_exports_the_same_abi():
     for name in declared_functions():
         assert hasattr(dbg, name), name
     dbg.wc_abi_version.restype = ctypes.c_int32
-    assert dbg.wc_abi_version() == 7
+    assert dbg.wc_abi_version() == 8
