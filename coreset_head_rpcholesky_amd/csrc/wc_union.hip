@@ -260,6 +260,26 @@ __device__ __forceinline__ void load_rows(float (&f)[32], const float* G, size_t
   }
 }
 
+// The L blocks in operand order.  The strictly upper 64 x 64 blocks of A are never used, so
+// block (k, i) above the diagonal holds L_ik (i > k) a second time, arranged so that a wave
+// reads the operand of a 32-row half with coalesced loads: element (rho, t) of half hh (row
+// 32 hh + rho of L_ik, column t) sits at float f = 2048 hh + 256 (s / 4) + 4 lane + s % 4 with
+// lane = rho + 32 (t / 32), s = t % 32, and float f of the block at row f / 64, column f % 64
+// of block (k, i) of A.  Load q of a lane then reads 16 bytes of one of 4 consecutive 256-byte
+// row pieces (8 cache lines per wave) instead of one of 64 rows (64 lines).
+__device__ __forceinline__ float* frag_at(float* A, int rp, int k, int i, int f) {
+  return A + (size_t)(k * kUB + (f >> 6)) * rp + (size_t)i * kUB + (f & 63);
+}
+// f[s] = rows 32 hh .. 32 hh + 31 of L_ik in the operand order of load_rows
+__device__ __forceinline__ void load_frag(float (&f)[32], float* A, int rp, int k, int i, int hh) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(frag_at(A, rp, k, i, 2048 * hh + 256 * q + 4 * lane));
+    f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+  }
+}
+
 // f[s] = G[(32 (l / 32) + s) * ld + col + l % 32], zero for columns at or past ncol: 32 columns
 // of a 64-row block as the R operand.  The address is clamped, so every load is in bounds.
 __device__ __forceinline__ void load_cols(float (&f)[32], const float* G, int ld, int col, int ncol) {
@@ -327,6 +347,14 @@ __global__ void __launch_bounds__(64) union_panel_kernel(UnionArgs a, int k) {
       Ls[(size_t)tile_row(v) * a.rp + tile_col()] = c0[v];
       Ls[(size_t)tile_row(v) * a.rp + 32 + tile_col()] = c1[v];
     }
+    // the operand-order copy in block (k, i): rows 32 (x % 2) .. of L_ik are half x % 2
+    const int i = k + 1 + (x >> 1), hh = x & 1, n = tile_col();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rho = tile_row(v), fb = 2048 * hh + 256 * (n >> 2) + (n & 3);
+      *frag_at(A, a.rp, k, i, fb + 4 * rho) = c0[v];
+      *frag_at(A, a.rp, k, i, fb + 4 * (rho + 32)) = c1[v];
+    }
   } else {
     const int col = 32 * (x - 2 * T);
     float* Xk = a.X + ((size_t)h * a.rp + (size_t)k * kUB) * nc;
@@ -374,8 +402,8 @@ __global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k
     int xx = x, ii = 0;
     while (xx > ii) xx -= ++ii;
     const int i = k + 1 + ii, j = k + 1 + xx;
-    load_rows(fp, A + ((size_t)i * kUB + qm) * a.rp + (size_t)k * kUB, a.rp);
-    load_rows(fr, A + ((size_t)j * kUB + qn) * a.rp + (size_t)k * kUB, a.rp);
+    load_frag(fp, A, a.rp, k, i, qm >> 5);
+    load_frag(fr, A, a.rp, k, j, qn >> 5);
     float* Aij = A + ((size_t)i * kUB + qm) * a.rp + (size_t)j * kUB + qn;
     const uint32_t lo = tile_lane_off(a.rp);
     float old[16];
@@ -395,7 +423,7 @@ __global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k
     const int y = x - npairs, i = k + 1 + y / nxz, col = (y % nxz) * kUB + qn;
     if (col >= nc) return;   // a quarter wholly past the last column
     float* X = a.X + (size_t)h * a.rp * nc;
-    load_rows(fp, A + ((size_t)i * kUB + qm) * a.rp + (size_t)k * kUB, a.rp);
+    load_frag(fp, A, a.rp, k, i, qm >> 5);
     load_cols(fr, X + (size_t)k * kUB * nc, nc, col, nc);
     float* Xi = X + ((size_t)i * kUB + qm) * nc + col;
     const bool ok = col + tile_col() < nc;
