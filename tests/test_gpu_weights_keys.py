@@ -99,3 +99,21 @@ def test_repeats_rank_and_empty_slots(wc):
         assert np.all(W[h][~kept] == 0.0)
         assert rel(W[h], Wo) < 1e-3, (h, rel(W[h], Wo))
         assert kept.sum() == (r - 1 if h == 0 else 79)
+
+
+def test_union_past_the_one_launch_back_substitution(wc):
+    """r = 2560 > 2048: the backward substitution runs block by block (one launch per block)
+    instead of the one-launch column slices; still the oracle's weights."""
+    import torch
+
+    H, n, d, dv, r = 1, 8192, 64, 64, 2560
+    _, K, V = _inputs(H, n, 1, d, dv, "f32", seed=985)
+    K = K * 2.0   # spread keys: H_SS of 2560 random points at condition about 1e3
+    rng = np.random.default_rng(986)
+    piv = np.stack([rng.choice(n, r, replace=False) for _ in range(H)]).astype(np.int32)
+    rank = torch.full((H,), r, dtype=torch.int32, device="cuda")
+    W, flags = wc.wc_weights_keys(dev(K), dev(V), torch.from_numpy(piv).cuda(), rank)
+    W, flags = host(W), host(flags)
+    Wo, kept = ow.weights_union(K[0], V[0], piv[0])
+    assert kept.all() and not flags[0] & FLAG_DEPENDENT
+    assert rel(W[0], Wo) < 1e-3, rel(W[0], Wo)
