@@ -29,50 +29,6 @@ namespace {
 constexpr int kUB = 64;   // block size
 constexpr int kLP = 68;   // LDS row pitch (floats) of the staged 64 x 64 operands
 
-__device__ __forceinline__ bool slot_valid(const UnionArgs& a, int h, int j) {
-  return j < a.r && a.pivots[(size_t)h * a.r + j] >= 0;
-}
-
-// One 64 x 64 x 64 product on a 256-thread workgroup,
-//     acc[i][c] += sum_t sP[t][4 ti + i] sQ[t][4 tc + c],  (ti, tc) = (tid / 16, tid % 16),
-// with both operands staged k-major in LDS.  Wave w computes the 32 x 32 quarter (w / 2, w % 2)
-// on the fp32 matrix cores (32 x 32 x 2 steps over t), then the product passes through sP
-// (row-major) so that every thread picks up its 4 x 4 piece; sP is overwritten.  Every thread
-// of the workgroup must call it.
-__device__ __forceinline__ void mm64(float (*sP)[kLP], const float (*sQ)[kLP], float acc[4][4]) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, kh = lane >> 5, m0 = 32 * (w >> 1), n0 = 32 * (w & 1);
-  f32x16 c;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) c[v] = 0.f;
-#pragma unroll 8
-  for (int t = 0; t < kUB; t += 2)
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(sP[t + kh][m0 + l32], sQ[t + kh][n0 + l32], c, 0, 0, 0);
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < 16; ++v) sP[m0 + 8 * (v >> 2) + 4 * kh + (v & 3)][n0 + l32] = c[v];
-  __syncthreads();
-  const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 q = *reinterpret_cast<const float4*>(&sP[i0 + i][c0]);
-    acc[i][0] += q.x; acc[i][1] += q.y; acc[i][2] += q.z; acc[i][3] += q.w;
-  }
-}
-
-// sT[t][i] = G[i * ld + t] for a 64 x 64 block of a row-major matrix with ld % 4 == 0.
-__device__ __forceinline__ void stage_transposed(float (*sT)[kLP], const float* G, size_t ld) {
-  const int tid = threadIdx.x, i = tid >> 2, t0 = 16 * (tid & 3);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 v = *reinterpret_cast<const float4*>(G + (size_t)i * ld + t0 + 4 * q);
-    sT[t0 + 4 * q + 0][i] = v.x;
-    sT[t0 + 4 * q + 1][i] = v.y;
-    sT[t0 + 4 * q + 2][i] = v.z;
-    sT[t0 + 4 * q + 3][i] = v.w;
-  }
-}
-
 // sN[t][c] = G[t * ld + c] for a 64 x 64 block of a row-major matrix with ld % 4 == 0.
 __device__ __forceinline__ void stage_direct(float (*sN)[kLP], const float* G, size_t ld) {
   const int tid = threadIdx.x, t = tid >> 2, c0 = 16 * (tid & 3);
@@ -82,13 +38,10 @@ __device__ __forceinline__ void stage_direct(float (*sN)[kLP], const float* G, s
         *reinterpret_cast<const float4*>(G + (size_t)t * ld + c0 + 4 * q);
 }
 
-// sN[t][c] = X[t][col0 + c] over the columns col0 .. col0 + 63 of an X block (ld = dv + 1,
-// not a multiple of 4); columns past ncol are zero.
-__device__ __forceinline__ void stage_x(float (*sN)[kLP], const float* X, int ld, int col0, int ncol) {
-  for (int e = threadIdx.x; e < kUB * kUB; e += 256) {
-    const int t = e >> 6, c = e & 63;
-    sN[t][c] = col0 + c < ncol ? X[(size_t)t * ld + col0 + c] : 0.f;
-  }
+// x where keep holds, else +0 (also for a non-finite x), by a bit mask: no select that the
+// compiler could turn into a branch around the load that produced x
+__device__ __forceinline__ float keep_if(float x, bool keep) {
+  return __uint_as_float(__float_as_uint(x) & (keep ? 0xffffffffu : 0u));
 }
 
 __device__ __forceinline__ void zero_acc(float acc[4][4]) {
@@ -130,8 +83,13 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
   const int bj = x;
   const T* Qs = reinterpret_cast<const T*>(a.Qs) + (size_t)h * a.r * D;
   float* A = a.A + (size_t)h * a.rp * a.rp;
-  auto finish = [&](int si, int sj, float dot) {
-    const float out = slot_valid(a, h, si) && slot_valid(a, h, sj) ? expf(a.beta * dot) : 0.f;
+  // slot validity, branch-free (the index clamped, so the load is always in bounds), so that all
+  // of a thread's tests are requested together rather than one round trip per entry
+  auto valid_at = [&](int j) {
+    return (j < a.r) & (a.pivots[(size_t)h * a.r + min(j, a.r - 1)] >= 0);
+  };
+  auto finish = [&](int si, int sj, bool ok, float dot) {
+    const float out = ok ? expf(a.beta * dot) : 0.f;
     if (bi == bj && si == sj) a.Hd[(size_t)h * a.rp + si] = out;
     return out;
   };
@@ -140,6 +98,10 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
     const int qm = 32 * (w >> 1), qn = 32 * (w & 1);
     // rows past r (padding slots) read row r-1 and are zeroed by finish()
     const int rm = min(bi * kUB + qm + (lane & 31), a.r - 1), rn = min(bj * kUB + qn + (lane & 31), a.r - 1);
+    // lane l tests row qm + l % 32 of block bi and column qn + l % 32 of block bj; the rows'
+    // results reach every lane by ballot (bit rho: row qm + rho)
+    const bool vn = valid_at(bj * kUB + qn + (lane & 31));
+    const uint64_t vrows = __ballot(valid_at(bi * kUB + qm + (lane & 31)));
     const bf16x8* pm = reinterpret_cast<const bf16x8*>(Qs + (size_t)rm * D + 8 * g);
     const bf16x8* pn = reinterpret_cast<const bf16x8*>(Qs + (size_t)rn * D + 8 * g);
     bf16x8 fm[D / 16], fn[D / 16];
@@ -155,8 +117,9 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
     for (int s = 0; s < D / 16; ++s) c = mfma32(fm[s], fn[s], c);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int si = bi * kUB + qm + 8 * (v >> 2) + 4 * g + (v & 3), sj = bj * kUB + qn + (lane & 31);
-      A[(size_t)si * a.rp + sj] = finish(si, sj, c[v]);
+      const int rho = 8 * (v >> 2) + 4 * g + (v & 3);
+      const int si = bi * kUB + qm + rho, sj = bj * kUB + qn + (lane & 31);
+      A[(size_t)si * a.rp + sj] = finish(si, sj, vn && ((vrows >> rho) & 1u), c[v]);
     }
   } else {
     __shared__ __attribute__((aligned(16))) float sI[32][kLP];
@@ -185,12 +148,18 @@ __global__ void __launch_bounds__(256) union_gram_kernel(UnionArgs a) {
       }
     }
     const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
+    bool vi[4], vc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vi[i] = valid_at(bi * kUB + i0 + i);
+      vc[i] = valid_at(bj * kUB + c0 + i);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int si = bi * kUB + i0 + i;
       float out[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) out[c] = finish(si, bj * kUB + c0 + c, acc[i][c]);
+      for (int c = 0; c < 4; ++c) out[c] = finish(si, bj * kUB + c0 + c, vi[i] && vc[c], acc[i][c]);
       *reinterpret_cast<float4*>(A + (size_t)si * a.rp + bj * kUB + c0) = make_float4(out[0], out[1], out[2], out[3]);
     }
   }
@@ -379,7 +348,9 @@ __global__ void __launch_bounds__(64) union_panel_kernel(UnionArgs a, int k) {
 // workgroups take block (k+1, k+1) of each head: it has no other writer in this step, so its
 // workgroup also factors it (diag_block for block column k+1) from LDS; that is the longest
 // path of the step, so it starts first.  The other blocks go round-robin over the heads.
-__global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k) {
+// Launch bounds of three workgroups per CU (up to 168 registers) rather than four (128), which
+// measured about 25 us faster over the 31 update launches of r = 2048.
+__global__ void __launch_bounds__(256, 3) union_update_kernel(UnionArgs a, int k) {
   __shared__ __attribute__((aligned(16))) float sA[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sS[kUB][kLP];
   __shared__ __attribute__((aligned(16))) float sCol[2][kUB];
@@ -441,116 +412,85 @@ __global__ void __launch_bounds__(256, 4) union_update_kernel(UnionArgs a, int k
   }
 }
 
-// ---- backward substitution step k: W_k = M_kk^T Z_k; Z_j -= L_kj^T W_k (j < k) ---------------
-__global__ void __launch_bounds__(256) union_back_kernel(UnionArgs a, int k) {
-  __shared__ __attribute__((aligned(16))) float sP[kUB][kLP];
-  __shared__ __attribute__((aligned(16))) float sQ[kUB][kLP];
-  const int h = blockIdx.y, tid = threadIdx.x, nb = a.rp / kUB;
-  const int nc = a.dv + 1, nxz = (nc + kUB - 1) / kUB;
-  const int j = blockIdx.x / nxz, col0 = (blockIdx.x % nxz) * kUB;
-  const float* M = a.M + ((size_t)h * nb + k) * kUB * kUB;
-  const float* A = a.A + (size_t)h * a.rp * a.rp;
-  float* X = a.X + (size_t)h * a.rp * nc;
-  float acc[4][4];
-  zero_acc(acc);
-  const int i0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
-  stage_direct(sP, M, kUB);   // sP[t][row] = M[t][row] = (M^T)[row][t]
-  stage_x(sQ, X + (size_t)k * kUB * nc, nc, col0, nc);
-  __syncthreads();
-  mm64(sP, sQ, acc);          // acc = rows of W_k, columns col0 + c
-  if (j == k) {
-    float* W = a.W + (size_t)h * a.r * nc;
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int wr = k * kUB + i0 + r4;
-      if (wr >= a.r) continue;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (col0 + c0 + c < nc) W[(size_t)wr * nc + col0 + c0 + c] = acc[r4][c];
-    }
-    return;
-  }
-  __syncthreads();
-  // sQ <- W_k block, sP[t][row] = L_kj[t][row] (so that the product is L_kj^T W_k)
-#pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sQ[i0 + r4][c0 + c] = acc[r4][c];
-  stage_direct(sP, A + (size_t)k * kUB * a.rp + (size_t)j * kUB, a.rp);
-  __syncthreads();
-  zero_acc(acc);
-  mm64(sP, sQ, acc);
-  float* Xj = X + (size_t)j * kUB * nc;
-#pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (col0 + c0 + c < nc) Xj[(size_t)(i0 + r4) * nc + col0 + c0 + c] -= acc[r4][c];
-}
-
-// ---- backward substitution in one launch, for rp <= kBackMaxRows ----------------------------
+// ---- backward substitution, a range of block steps per launch ------------------------------
 // The columns of W = L^{-T} Z are independent, so one workgroup takes kBackCols of them for one
-// head and runs every block step k = nb-1 .. 0 itself, its slice of Z resident in LDS:
-//     W_k = M_kk^T Z_k,   then Z_j -= L_kj^T W_k for every j < k.
+// head and runs the block steps k = khi-1 .. klo of a range itself, the range's slice of Z
+// resident in LDS:
+//     W_k = M_kk^T Z_k,   then Z_j -= L_kj^T W_k for every klo <= j < k.
+// The blocks below the range then take all of the range's W in one product
+// (union_back_gemm_kernel) before the next range down, so that most of the work runs on the
+// whole chip instead of on one workgroup per head and column slice.
 // Products on the fp32 matrix cores, 16 x 16 x 4 (lane l: A[l % 16][l / 16], B[l / 16][l % 16],
 // D rows 4 (l / 16) .. + 3 of column l % 16).  The A operands (M_kk and L_kj, read transposed)
 // come straight from global memory, one step ahead of their products; the B operands (Z_k,
 // W_k) from LDS.  Per step: waves 0-3 form the four 16-row tiles of W_k, then all waves share
-// the 4 k tiles of the update.  The slices of the heads go round-robin over the workgroups, so
-// that with 8 heads the slices of one head share an XCD and its L2 copy of L.
+// the 4 (k - klo) tiles of the update.  The slices of the heads go round-robin over the
+// workgroups, so that with 8 heads the slices of one head share an XCD and its L2 copy of L.
 constexpr int kBackCols = 16;
-constexpr int kBackMaxRows = 2048;  // the Z slice: kBackMaxRows x kBackCols floats, 128 KB
+constexpr int kBackRange = 8;   // blocks per range: 512 rows x kBackCols floats of Z in LDS
 constexpr int kBackWaves = 8;
 
-__global__ void __launch_bounds__(64 * kBackWaves) union_back_slices_kernel(UnionArgs a) {
-  __shared__ __attribute__((aligned(16))) float sZ[kBackMaxRows][kBackCols];
+__global__ void __launch_bounds__(64 * kBackWaves) union_back_slices_kernel(UnionArgs a, int klo, int khi) {
+  __shared__ __attribute__((aligned(16))) float sZ[kBackRange * kUB][kBackCols];
   __shared__ __attribute__((aligned(16))) float sW[kUB][kBackCols];
   const int h = blockIdx.x % a.H, col0 = (blockIdx.x / a.H) * kBackCols, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6, lr = lane & 15, lk = lane >> 4;
-  const int nb = a.rp / kUB, nc = a.dv + 1;
+  const int nb = a.rp / kUB, nc = a.dv + 1, top = khi - 1;
   const float* Mh = a.M + (size_t)h * nb * kUB * kUB;
   const float* A = a.A + (size_t)h * a.rp * a.rp;
-  const float* X = a.X + (size_t)h * a.rp * nc;
+  const float* X = a.X + ((size_t)h * a.rp + (size_t)klo * kUB) * nc;
   float* W = a.W + (size_t)h * a.r * nc;
-  for (int e = tid; e < a.rp * kBackCols; e += 64 * kBackWaves) {
-    const int row = e / kBackCols, c = e % kBackCols;
-    sZ[row][c] = col0 + c < nc ? X[(size_t)row * nc + col0 + c] : 0.f;
+  {
+    // the range's Z slice into LDS: a fixed number of unconditional (clamped) loads per thread,
+    // all requested before the first LDS store
+    constexpr int per = kBackRange * kUB * kBackCols / (64 * kBackWaves), step = 64 * kBackWaves / kBackCols;
+    const int nrows = (khi - klo) * kUB, c = tid % kBackCols;
+    const bool cok = col0 + c < nc;
+    float z[per];
+#pragma unroll
+    for (int i = 0; i < per; ++i)
+      z[i] = keep_if(X[(size_t)min(tid / kBackCols + step * i, nrows - 1) * nc + (cok ? col0 + c : nc - 1)], cok);
+#pragma unroll
+    for (int i = 0; i < per; ++i)
+      if (tid / kBackCols + step * i < nrows) sZ[tid / kBackCols + step * i][c] = z[i];
   }
   // A operand of a 16-row tile: av[s] = G[(4 s + lk) * ld + lr], t = 4 s + lk the summed index
   auto load_a = [&](float (&av)[16], const float* G, size_t ld) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) av[s] = G[(size_t)(4 * s + lk) * ld + lr];
   };
-  // update tile `tile` of step k: rows 16 (tile % 4) .. of block j = tile / 4, L_kj read transposed
+  // update tile `tile` of step k: rows 16 (tile % 4) .. of block j = klo + tile / 4, L_kj read
+  // transposed
   auto tile_src = [&](int k, int tile) {
-    return A + (size_t)k * kUB * a.rp + (size_t)(tile >> 2) * kUB + 16 * (tile & 3);
+    return A + (size_t)k * kUB * a.rp + (size_t)(klo + (tile >> 2)) * kUB + 16 * (tile & 3);
   };
   float am[16], at[16];
-  if (wid < 4) load_a(am, Mh + (size_t)(nb - 1) * kUB * kUB + 16 * wid, kUB);
-  if (wid < 4 * (nb - 1)) load_a(at, tile_src(nb - 1, wid), a.rp);
+  if (wid < 4) load_a(am, Mh + (size_t)top * kUB * kUB + 16 * wid, kUB);
+  if (wid < 4 * (top - klo)) load_a(at, tile_src(top, wid), a.rp);
   __syncthreads();
-  for (int k = nb - 1; k >= 0; --k) {
+  for (int k = top; k >= klo; --k) {
+    const int kl = k - klo;   // blocks of the range below block k
     if (wid < 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am[s], sZ[k * kUB + 4 * s + lk][lr], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am[s], sZ[kl * kUB + 4 * s + lk][lr], acc, 0, 0, 0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 16 * wid + 4 * lk + v, wr = k * kUB + row;
         sW[row][lr] = acc[v];
         if (wr < a.r && col0 + lr < nc) W[(size_t)wr * nc + col0 + lr] = acc[v];
       }
-      if (k > 0) load_a(am, Mh + (size_t)(k - 1) * kUB * kUB + 16 * wid, kUB);
+      if (k > klo) load_a(am, Mh + (size_t)(k - 1) * kUB * kUB + 16 * wid, kUB);
     }
     __syncthreads();
     // (a wave without a tile in this step has none in the next either)
-    for (int tile = wid; tile < 4 * k; tile += kBackWaves) {
+    for (int tile = wid; tile < 4 * kl; tile += kBackWaves) {
       float an[16];
       const int next = tile + kBackWaves;
       // the next tile of this step, or the first of the next step
-      if (next < 4 * k) load_a(an, tile_src(k, next), a.rp);
-      else if (wid < 4 * (k - 1)) load_a(an, tile_src(k - 1, wid), a.rp);
+      if (next < 4 * kl) load_a(an, tile_src(k, next), a.rp);
+      else if (wid < 4 * (kl - 1)) load_a(an, tile_src(k - 1, wid), a.rp);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s)
@@ -563,6 +503,70 @@ __global__ void __launch_bounds__(64 * kBackWaves) union_back_slices_kernel(Unio
     }
     __syncthreads();
   }
+}
+
+// Z_j -= sum over k in [klo, khi) of L_kj^T W_k for every block j < klo: the rows below a range
+// take all of its weights in one product.  One workgroup per 32 x 32 tile of Z (rows row0 ..,
+// columns col0 ..) of a head; each of its four waves sums a quarter of the range's rows on the
+// fp32 matrix cores (32 x 32 x 2, lane l supplying L[kk][row0 + l % 32] and W[kk][col0 + l % 32]
+// for the step's row kk = k0 + 2 s + l / 32; rows of W at or past r and columns past dv are
+// zero), and the quarters are added through LDS in a fixed order.
+__global__ void __launch_bounds__(256) union_back_gemm_kernel(UnionArgs a, int klo) {
+  // a range with blocks below it is always a whole one (the ranges are cut from the top)
+  constexpr int q = kBackRange * kUB / 4;   // range rows per wave
+  constexpr int ng = q / 16;                // groups of 8 steps (16 rows)
+  __shared__ float sC[3][16][64];
+  const int nc = a.dv + 1, nct = (nc + 31) / 32;
+  const int h = blockIdx.x % a.H, tile = blockIdx.x / a.H;
+  const int row0 = (tile / nct) * 32, col0 = (tile % nct) * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31;
+  const int k0 = klo * kUB + w * q + (lane >> 5);
+  const int c = col0 + l32;
+  const bool cok = c < nc;
+  const float* L = a.A + (size_t)h * a.rp * a.rp + row0 + l32;
+  const float* Wc = a.W + (size_t)h * a.r * nc + (cok ? c : nc - 1);
+  // the loads are unconditional (clamped row of W); rows at or past r and columns past dv are
+  // zeroed at the point of use
+  float pg[2][8], wg[2][8];
+  auto load_group = [&](int grp, float (&pv)[8], float (&wv)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kk = k0 + 16 * grp + 2 * s;
+      pv[s] = L[(size_t)kk * a.rp];
+      wv[s] = Wc[(size_t)min(kk, a.r - 1) * nc];
+    }
+  };
+  load_group(0, pg[0], wg[0]);
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int grp = 0; grp < ng; ++grp) {
+    // scheduling fences: the next group's loads all go out before this group's products
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp + 1 < ng) load_group(grp + 1, pg[(grp + 1) & 1], wg[(grp + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kk = k0 + 16 * grp + 2 * s;
+      const float wv = keep_if(wg[grp & 1][s], cok && kk < a.r);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pg[grp & 1][s], wv, acc, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (w > 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sC[w - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (w > 0 || !cok) return;
+  float* Z = a.X + ((size_t)h * a.rp + row0) * nc + c;
+  float z[16];   // all of the tile's old values requested before the first store
+#pragma unroll
+  for (int v = 0; v < 16; ++v) z[v] = Z[(size_t)tile_row(v) * nc];
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    Z[(size_t)tile_row(v) * nc] = z[v] - (((acc[v] + sC[0][v][lane]) + sC[1][v][lane]) + sC[2][v][lane]);
 }
 
 template <typename T, int D>
@@ -607,14 +611,12 @@ hipError_t launch_union_solve(const UnionArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_union_back(const UnionArgs& a, hipStream_t st) {
-  if (a.rp <= kBackMaxRows) {
-    const int ns = (a.dv + 1 + kBackCols - 1) / kBackCols;
-    hipLaunchKernelGGL(union_back_slices_kernel, dim3(ns * a.H), dim3(64 * kBackWaves), 0, st, a);
-    return hipGetLastError();
-  }
-  const int nb = a.rp / kUB, nxz = (a.dv + 1 + kUB - 1) / kUB;
-  for (int k = nb - 1; k >= 0; --k) {
-    hipLaunchKernelGGL(union_back_kernel, dim3((k + 1) * nxz, a.H), dim3(256), 0, st, a, k);
+  const int nb = a.rp / kUB, ns = (a.dv + 1 + kBackCols - 1) / kBackCols, nct = (a.dv + 1 + 31) / 32;
+  for (int khi = nb; khi > 0; khi -= kBackRange) {
+    const int klo = khi > kBackRange ? khi - kBackRange : 0;
+    hipLaunchKernelGGL(union_back_slices_kernel, dim3(ns * a.H), dim3(64 * kBackWaves), 0, st, a, klo, khi);
+    if (klo > 0)
+      hipLaunchKernelGGL(union_back_gemm_kernel, dim3(a.H * 2 * klo * nct), dim3(256), 0, st, a, klo);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -102,8 +102,9 @@ def test_repeats_rank_and_empty_slots(wc):
 
 
 def test_union_past_the_one_launch_back_substitution(wc):
-    """r = 2560 > 2048: the backward substitution runs block by block (one launch per block)
-    instead of the one-launch column slices; still the oracle's weights."""
+    """r = 2560: five ranges of the backward substitution (the top one holding the padding
+    rows past r is full, the products below each range span 32 row blocks), still the oracle's
+    weights."""
     import torch
 
     H, n, d, dv, r = 1, 8192, 64, 64, 2560
