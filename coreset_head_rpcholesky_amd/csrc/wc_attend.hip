@@ -741,29 +741,34 @@ attend_bf16_kernel(AttendArgs a) {
 // Sum of the coreset-split partials: one wave per query row, lanes over the columns.
 template <typename T, int DV>
 __global__ void __launch_bounds__(64) attend_reduce_kernel(AttendArgs a) {
+  constexpr int NCOL = DV / 64;  // value columns per lane: lane, lane + 64, ...
   const int q = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const size_t stride = (size_t)a.m * (DV + 1);
   const float* Yp = a.Ypart + ((size_t)h * a.nsplit * a.m + q) * (DV + 1);
-  float den = 0.f;
-  for (int sp = 0; sp < a.nsplit; ++sp) den += Yp[sp * stride + DV];
+  // one pass over the splits, in split order, for the normaliser and the lane's columns at once
+  // (the loads of several splits go out together)
+  float den = 0.f, y[NCOL];
+#pragma unroll
+  for (int j = 0; j < NCOL; ++j) y[j] = 0.f;
+#pragma unroll 4
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* row = Yp + sp * stride;
+    den += row[DV];
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) y[j] += row[lane + 64 * j];
+  }
   if (a.Yout) {
     float* Y = yout_row(a, h, q);
-    for (int c = lane; c < DV; c += 64) {
-      float y = 0.f;
-      for (int sp = 0; sp < a.nsplit; ++sp) y += Yp[sp * stride + c];
-      Y[c] = y;
-    }
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) Y[lane + 64 * j] = y[j];
     if (lane == 0) Y[DV] = den;
     return;
   }
   if (lane == 0 && !(den > 0.f)) atomicOr(&a.flags[h], WC_DFLAG_DENOM);
   const float inv = 1.0f / den;
   T* O = reinterpret_cast<T*>(a.O) + ((size_t)h * a.m + q) * DV;
-  for (int c = lane; c < DV; c += 64) {
-    float y = 0.f;
-    for (int sp = 0; sp < a.nsplit; ++sp) y += Yp[sp * stride + c];
-    st_elem<T>(O + c, y * inv);
-  }
+#pragma unroll
+  for (int j = 0; j < NCOL; ++j) st_elem<T>(O + lane + 64 * j, y[j] * inv);
 }
 
 // A few queries per head over a bf16 staged coreset (the compressed cache's decode step).  Each

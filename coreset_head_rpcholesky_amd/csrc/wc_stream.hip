@@ -531,8 +531,10 @@ __device__ __forceinline__ int last_lane_value(bool has, int v, int none) {
 // exclusive sums sit in LDS for the round and the drawn candidates in registers (lane q the
 // q-th in index order); a draw is a wave scan for the shifted target, a wave search over the
 // blocks, one load of the chosen block's rows (RPT per lane), a wave scan and a shuffle to
-// insert the new candidate, with no barrier.
-template <int RPT>
+// insert the new candidate, with no barrier.  NBR > 0: the sub-head has at most NBR blocks,
+// whose rows the wave loads into registers once, before the draws (all requested together), so
+// that a draw picks the chosen block's rows from registers instead of waiting on a load.
+template <int RPT, int NBR>
 __global__ void __launch_bounds__(64) blk_sample_kernel(BlockRpcArgs A, int k) {
   extern __shared__ __attribute__((aligned(16))) double s_blk[];  // [nblk] masses, [nblk] exclusive sums
   const StreamRpcArgs& a = A.s;
@@ -545,6 +547,13 @@ __global__ void __launch_bounds__(64) blk_sample_kernel(BlockRpcArgs A, int k) {
   const double* part = ((k & 1) ? a.part1 : a.part0) + (size_t)h * nblk;
   const float* dg_in = ((k & 1) ? a.diag1 : a.diag0) + (size_t)h * n;
   const int per = (nblk + 63) / 64;
+  float dres[NBR > 0 ? NBR : 1][RPT];
+  if constexpr (NBR > 0) {
+#pragma unroll
+    for (int q = 0; q < NBR; ++q)
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) dres[q][e] = dg_in[min(q * 64 * RPT + lane * RPT + e, n - 1)];
+  }
   double mine = 0.0;
   for (int e = 0; e < per; ++e) {
     const int bb = lane * per + e;
@@ -619,8 +628,18 @@ __global__ void __launch_bounds__(64) blk_sample_kernel(BlockRpcArgs A, int k) {
     // row inside it: unconditional loads (clamped indices), rows past n weigh nothing
     const int r0 = bstar * 64 * RPT;
     float dv[RPT];
+    if constexpr (NBR > 0) {
 #pragma unroll
-    for (int e = 0; e < RPT; ++e) dv[e] = dg_in[min(r0 + lane * RPT + e, n - 1)];
+      for (int e = 0; e < RPT; ++e) {
+        float v = dres[0][e];
+#pragma unroll
+        for (int q = 1; q < NBR; ++q) v = bstar == q ? dres[q][e] : v;
+        dv[e] = v;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) dv[e] = dg_in[min(r0 + lane * RPT + e, n - 1)];
+    }
     double pm[RPT];
     double tmass = 0.0;
 #pragma unroll
@@ -1014,16 +1033,18 @@ static hipError_t run_block(BlockRpcArgs A, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t lds = 2 * (size_t)a.nblk * sizeof(double);
   const bool wide = a.rows == 1024;  // rows per block: 1024 (16 per lane) or 256 (4 per lane)
+  const bool resident = wide && a.nblk <= 2;  // the sub-head's rows in registers (2048 rows at most)
   if (lds > 48 * 1024) {
-    const void* fn = wide ? reinterpret_cast<const void*>(&blk_sample_kernel<16>)
-                          : reinterpret_cast<const void*>(&blk_sample_kernel<4>);
+    const void* fn = wide ? reinterpret_cast<const void*>(&blk_sample_kernel<16, 0>)
+                          : reinterpret_cast<const void*>(&blk_sample_kernel<4, 0>);
     if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) return e;
   }
   const int colgrid = (a.n + NT - 1) / NT;
   const int rounds = kBlockDraws * a.r / B;
   for (int k = 0; k < rounds; ++k) {
-    if (wide) hipLaunchKernelGGL(blk_sample_kernel<16>, dim3(a.H), dim3(64), lds, st, A, k);
-    else hipLaunchKernelGGL(blk_sample_kernel<4>, dim3(a.H), dim3(64), lds, st, A, k);
+    if (resident) hipLaunchKernelGGL((blk_sample_kernel<16, 2>), dim3(a.H), dim3(64), lds, st, A, k);
+    else if (wide) hipLaunchKernelGGL((blk_sample_kernel<16, 0>), dim3(a.H), dim3(64), lds, st, A, k);
+    else hipLaunchKernelGGL((blk_sample_kernel<4, 0>), dim3(a.H), dim3(64), lds, st, A, k);
     if constexpr (sizeof(T) == 2) {
       hipLaunchKernelGGL((blk_gather_kernel<B>), dim3((a.r * B + 255) / 256, a.H), dim3(256), 0, st, A);
       hipLaunchKernelGGL((blk_column_mfma_kernel<D, B>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, A);

@@ -361,21 +361,33 @@ hipError_t launch_weights(const WeightsArgs& a, hipStream_t st) {
 // indices of the head (offset b n/B) in slots b r/B .., empty slots keep -1, and the ranks
 // and flags of the bins are folded per head.
 __global__ void __launch_bounds__(256) bins_combine_kernel(BinsArgs a) {
+  __shared__ int s_taken;
+  __shared__ uint32_t s_fl;
   const int h = blockIdx.x, r = a.B * a.rb;
-  int taken = 0;
-  uint32_t fl = 0u;
+  if (threadIdx.x == 0) {
+    s_taken = 0;
+    s_fl = 0u;
+  }
   for (int j = threadIdx.x; j < r; j += 256) {
     const int b = j / a.rb, sub = h * a.B + b;
     const int s = a.piv_sub[(size_t)sub * a.rb + j % a.rb];
     a.pivots[(size_t)h * r + j] = s >= 0 ? s + b * a.nb : -1;
   }
+  // the bins' ranks and flags: one thread per bin, summed in LDS (an integer sum and an OR, so
+  // the order does not matter)
+  int taken = 0;
+  uint32_t fl = 0u;
+  for (int b = threadIdx.x; b < a.B; b += 256) {
+    taken += a.rank_sub[h * a.B + b];
+    fl |= a.flags_sub[h * a.B + b];
+  }
+  __syncthreads();
+  if (taken) atomicAdd(&s_taken, taken);
+  if (fl) atomicOr(&s_fl, fl);
+  __syncthreads();
   if (threadIdx.x == 0) {
-    for (int b = 0; b < a.B; ++b) {
-      taken += a.rank_sub[h * a.B + b];
-      fl |= a.flags_sub[h * a.B + b];
-    }
-    a.rank[h] = taken;
-    a.flags[h] = fl;
+    a.rank[h] = s_taken;
+    a.flags[h] = s_fl;
     a.rank_slots[h] = r;
   }
 }
