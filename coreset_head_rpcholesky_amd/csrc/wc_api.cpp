@@ -193,7 +193,7 @@ UnionLayout make_union_layout(const wc_problem& p, size_t base) {
   U.Hd = take(H * urp * 4);
   U.M = take(H * urp * 64 * 4);
   U.X = take(H * urp * nc * 4);
-  U.xKSh = take(H * np * p.d * 2);
+  U.xKSh = take(lo * H * np * p.d * 2);   // bf16 keys are read in place by the all-keys pass
   U.xKSl = take(lo * H * np * p.d * 2);
   U.xWph = take(H * p.dv * np * 2);
   U.xWpl = take(lo * H * p.dv * np * 2);
@@ -404,7 +404,7 @@ hipError_t run_union_weights(const wc_problem& p, const UnionLayout& U, void* ws
     x.bf16 = u.bf16;
     x.H = p.heads; x.n = p.n; x.m = p.r; x.d = p.d; x.dv = p.dv; x.r = p.n;
     x.beta_log2e = beta_log2e(p.d);
-    x.KSh = at<uint16_t>(ws, U.xKSh);
+    x.KSh = p.dtype == WC_F32 ? at<uint16_t>(ws, U.xKSh) : nullptr;   // bf16: keys read in place
     x.KSl = p.dtype == WC_F32 ? at<uint16_t>(ws, U.xKSl) : nullptr;
     x.Wph = at<uint16_t>(ws, U.xWph);
     x.Wpl = p.dtype == WC_F32 ? at<uint16_t>(ws, U.xWpl) : nullptr;

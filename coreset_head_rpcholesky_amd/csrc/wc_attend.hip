@@ -100,33 +100,35 @@ __global__ void __launch_bounds__(256) attend_prep_keys_kernel(AttendArgs a) {
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int rp = staged_rows(a);
   const int j0 = c * 64;
-  // keys
-  for (int e = tid; e < 64 * D / E; e += 256) {
-    const int row = e / (D / E), col = (e % (D / E)) * E, j = j0 + row;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (j < a.n) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + j) * D + col);
-    *reinterpret_cast<uint4*>(&sX[row * W + col]) = v;
-  }
-  __syncthreads();
-  const size_t kbase = (size_t)h * rp * D + (size_t)j0 * D;
-  for (int u = tid; u < 64 * (D / 8); u += 256) {   // output unit (column group u / 64, row u % 64)
-    const int cg = u >> 6, row = u & 63;
-    if constexpr (!SPLIT) {
-      *reinterpret_cast<uint4*>(a.KSh + kbase + 8 * (size_t)u) = *reinterpret_cast<const uint4*>(&sX[row * W + 8 * cg]);
-      continue;
+  // keys (none with KSh NULL: the attention then reads the bf16 keys in place)
+  if (a.KSh) {
+    for (int e = tid; e < 64 * D / E; e += 256) {
+      const int row = e / (D / E), col = (e % (D / E)) * E, j = j0 + row;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (j < a.n) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.K) + ((size_t)h * a.n + j) * D + col);
+      *reinterpret_cast<uint4*>(&sX[row * W + col]) = v;
     }
-    bf16x8 hi8, lo8;
+    __syncthreads();
+    const size_t kbase = (size_t)h * rp * D + (size_t)j0 * D;
+    for (int u = tid; u < 64 * (D / 8); u += 256) {   // output unit (column group u / 64, row u % 64)
+      const int cg = u >> 6, row = u & 63;
+      if constexpr (!SPLIT) {
+        *reinterpret_cast<uint4*>(a.KSh + kbase + 8 * (size_t)u) = *reinterpret_cast<const uint4*>(&sX[row * W + 8 * cg]);
+        continue;
+      }
+      bf16x8 hi8, lo8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16 hi, lo;
-      split_bf16(ld_elem<T>(&sX[row * W + 8 * cg + e]), hi, lo);
-      hi8[e] = hi;
-      lo8[e] = lo;
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hi, lo;
+        split_bf16(ld_elem<T>(&sX[row * W + 8 * cg + e]), hi, lo);
+        hi8[e] = hi;
+        lo8[e] = lo;
+      }
+      *reinterpret_cast<bf16x8*>(a.KSh + kbase + 8 * (size_t)u) = hi8;
+      *reinterpret_cast<bf16x8*>(a.KSl + kbase + 8 * (size_t)u) = lo8;
     }
-    *reinterpret_cast<bf16x8*>(a.KSh + kbase + 8 * (size_t)u) = hi8;
-    *reinterpret_cast<bf16x8*>(a.KSl + kbase + 8 * (size_t)u) = lo8;
+    __syncthreads();
   }
-  __syncthreads();
   // values
   for (int e = tid; e < 64 * DV / E; e += 256) {
     const int row = e / (DV / E), col = (e % (DV / E)) * E, j = j0 + row;
@@ -392,16 +394,27 @@ __device__ __forceinline__ void attend_wait(int pending, int wid) {
   }
 }
 
-template <int D, int DV>
-__device__ __forceinline__ void attend_issue(AttendChunk<D, DV>& b, const uint16_t* KSh, const uint16_t* Wph,
+// KROW: the coreset rows are the rows of a row-major key matrix K with nrm rows (the all-keys
+// pass, bf16 keys), read in place of a staged copy: lane l loads row 64 c + l (the last row for
+// rows past nrm, which carry zero weight) at the instruction's column group, so that the chunk
+// lands in LDS in the same [D/8][64][8] order.  Otherwise K is the staged layout.
+template <int D, int DV, bool KROW>
+__device__ __forceinline__ void attend_issue(AttendChunk<D, DV>& b, const uint16_t* K, int nrm, const uint16_t* Wph,
                                              const uint16_t* Wdh, int c, int wid, int lane) {
   constexpr int KI = D / (8 * kAttendWaves), WI = DV / (8 * kAttendWaves);  // 1 KB wave instructions per tile
-  const char* kbase = reinterpret_cast<const char*>(KSh) + (size_t)c * 64 * D * 2;
   const char* wbase = reinterpret_cast<const char*>(Wph) + (size_t)c * 64 * DV * 2;
   const uint32_t lo = 16 * lane;
+  if constexpr (KROW) {
+    const char* krow = reinterpret_cast<const char*>(K) + (size_t)min(c * 64 + lane, nrm - 1) * D * 2;
 #pragma unroll
-  for (int i = 0; i < KI; ++i)
-    dma16(kbase + 1024 * (kAttendWaves * i + wid) + lo, lds_addr(&b.k[64 * (kAttendWaves * i + wid)]));
+    for (int i = 0; i < KI; ++i)
+      dma16(krow + 16 * (kAttendWaves * i + wid), lds_addr(&b.k[64 * (kAttendWaves * i + wid)]));
+  } else {
+    const char* kbase = reinterpret_cast<const char*>(K) + (size_t)c * 64 * D * 2;
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      dma16(kbase + 1024 * (kAttendWaves * i + wid) + lo, lds_addr(&b.k[64 * (kAttendWaves * i + wid)]));
+  }
 #pragma unroll
   for (int i = 0; i < WI; ++i)
     dma16(wbase + 1024 * (kAttendWaves * i + wid) + lo, lds_addr(&b.w[64 * (kAttendWaves * i + wid)]));
@@ -559,7 +572,8 @@ __device__ __forceinline__ void attend_scale_q(const bf16x8 (&raw)[NQ][D / 16], 
 
 // MASK: the scan bound falls inside a 128-row block (a cache decoded over a prefix of its
 // rows), so the units that cross it are masked; without it every scanned row counts.
-template <int D, int DV, bool MASK>
+// KROW: the coreset rows are the bf16 keys K themselves, read in place (attend_issue).
+template <int D, int DV, bool MASK, bool KROW>
 __global__ void __launch_bounds__(64 * kAttendWaves) __attribute__((amdgpu_waves_per_eu(kAttendWaves / 4, kAttendWaves / 4)))
 attend_bf16_kernel(AttendArgs a) {
   constexpr int NK = D / 16, NW = DV / 16, NCT = DV / 32, NQ = kAttendNQ, R = kAttendRing, QN = NQ * NK;
@@ -583,8 +597,10 @@ attend_bf16_kernel(AttendArgs a) {
   AttendTile ti = attend_tile_at(a, it, QT, nchk, per);
   auto issue_next = [&]() {
     if (it < 0) return;
-    attend_issue(sb[issued % R], a.KSh + (size_t)ti.h * rp * D, a.Wph + (size_t)ti.h * DV * rp,
-                 a.Wdh + (size_t)ti.h * rp, ti.c0 + ic, wid, lane);
+    const uint16_t* kh = KROW ? reinterpret_cast<const uint16_t*>(a.K) + (size_t)ti.h * a.n * D
+                              : a.KSh + (size_t)ti.h * rp * D;
+    attend_issue<D, DV, KROW>(sb[issued % R], kh, a.n, a.Wph + (size_t)ti.h * DV * rp, a.Wdh + (size_t)ti.h * rp,
+                              ti.c0 + ic, wid, lane);
     ++issued;
     if (++ic == ti.nc) {
       ic = 0;
@@ -917,7 +933,10 @@ static hipError_t run_attend_append(const AttendArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D, int DV>
-static hipError_t run_attend_all_keys(const AttendArgs& a, hipStream_t st) {
+static hipError_t run_attend_all_keys(const AttendArgs& a0, hipStream_t st) {
+  // bf16 keys are read by the attention in place (row-major), so only the weights are staged
+  AttendArgs a = a0;
+  if constexpr (sizeof(T) == 2) a.KSh = nullptr;
   const int rp = staged_rows(a);
   hipLaunchKernelGGL((attend_prep_keys_kernel<T, D, DV>), dim3(rp / 64, a.H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
@@ -932,10 +951,12 @@ static hipError_t run_attend_core(const AttendArgs& a, hipStream_t st) {
     // persistent: one workgroup per compute unit (never more than the tiles)
     const long tiles = (long)((a.m + kAttendQueries - 1) / kAttendQueries) * a.H * a.nsplit;
     const dim3 grid((unsigned)(tiles < attend_workgroups() ? tiles : attend_workgroups()));
-    if (a.scan_rows % 128 != 0)
-      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, true>), grid, dim3(64 * kAttendWaves), 0, st, a);
+    if (!a.KSh)   // the all-keys pass over bf16 keys (no scan bound)
+      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, false, true>), grid, dim3(64 * kAttendWaves), 0, st, a);
+    else if (a.scan_rows % 128 != 0)
+      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, true, false>), grid, dim3(64 * kAttendWaves), 0, st, a);
     else
-      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, false>), grid, dim3(64 * kAttendWaves), 0, st, a);
+      hipLaunchKernelGGL((attend_bf16_kernel<D, DV, false, false>), grid, dim3(64 * kAttendWaves), 0, st, a);
   } else
     hipLaunchKernelGGL((attend_kernel<T, D, DV>), dim3((a.m + 127) / 128, a.H, a.nsplit), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
