@@ -365,7 +365,9 @@ constexpr int kVmcnt0 = 0x0F70;
 #ifndef WC_ATTEND_RING
 #define WC_ATTEND_RING 4
 #endif
-constexpr int kAttendRing = WC_ATTEND_RING;  // LDS chunk buffers: chunks in use, resident, loading
+constexpr int kAttendRing = WC_ATTEND_RING;
+// tiles of at least this many chunks take the deferred tile-end schedule (MODE 5, MODE 6)
+constexpr int kAttendLongTile = 6;  // LDS chunk buffers: chunks in use, resident, loading
 static_assert(kAttendRing == 3 || kAttendRing == 4, "ring of three or four chunks");
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void)const_cast<void*>(p);
@@ -570,6 +572,18 @@ __device__ __forceinline__ void attend_scale_q(const bf16x8 (&raw)[NQ][D / 16], 
   }
 }
 
+// The scaled query fragments, pinned where they are formed: an empty asm statement that reads
+// them keeps the compiler from sinking the scaling (and the waits for the raw fragments in
+// front of it) past the chunk loads issued next, where those waits would also cover the loads
+// just issued.
+template <int D, int NQ>
+__device__ __forceinline__ void attend_pin_q(const bf16x8 (&qb)[NQ][D / 16]) {
+#pragma unroll
+  for (int s = 0; s < NQ; ++s)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" ::"v"(qb[s][kk]));
+}
+
 // MASK: the scan bound falls inside a 128-row block (a cache decoded over a prefix of its
 // rows), so the units that cross it are masked; without it every scanned row counts.
 // KROW: the coreset rows are the bf16 keys K themselves, read in place (attend_issue).
@@ -629,6 +643,7 @@ attend_bf16_kernel(AttendArgs a) {
       scA[s] = mfma32(__builtin_bit_cast(bf16x8, sb[0].k[(2 * kk + g) * 64 + l32]), qb[s][kk], scA[s]);
   }
   int gbase = 0;  // global index of the current tile's first chunk
+  bool drained = false;  // the tile before ended with every load of the wave drained
   for (int j = 0;;) {
     f32x16 y[NQ][NCT];
     float den[NQ][4];
@@ -659,6 +674,16 @@ attend_bf16_kernel(AttendArgs a) {
     // next tile's first unit (the first chunk of the next tile is resident by then) under the
     // next tile's queries.  A one-chunk tile requests and scales them after its barrier
     // (MODE 4), and the last tile of the workgroup has none to request (MODE 0 throughout).
+    // A tile of at least kAttendLongTile chunks moves both tile-end costs off the chunk waits:
+    //  * its next queries are requested five chunks before the end (MODE 1) and scaled after
+    //    the barrier three chunks before it (MODE 5), where the compiler's wait for them also
+    //    drains the chunks requested before that barrier, which were due one chunk later;
+    //  * its last chunk (MODE 6) issues no load at its barrier.  At the tile end every load of
+    //    the wave is drained before the output stores, and the deferred chunk is requested
+    //    after them.  The first chunk of the next tile then waits for nothing (its chunk
+    //    landed before the stores), so the stores complete behind a whole chunk of work
+    //    instead of holding up the first count-based wait that follows them (stores and loads
+    //    share the one vector-memory counter).
     auto chunk = [&](int c, auto mode_c) {
       constexpr int MODE = decltype(mode_c)::value;
       const int gc = gbase + c;
@@ -669,14 +694,19 @@ attend_bf16_kernel(AttendArgs a) {
       attend_pin<NQ>(pbB, den);
       // chunk gc+1 landed; the chunks issued after it (at most R-2) may still be loading, and
       // so may the next tile's query fragments once requested
-      attend_wait<D, DV, (MODE == 2 || MODE == 3) ? QN : 0>(issued - (gc + 2), wid);
+      // (after a tile end that drained every load, the first chunk's is already resident)
+      if (!(c == 0 && drained))
+        attend_wait<D, DV, (MODE == 2 || MODE == 3 || MODE == 5) ? QN : 0>(issued - (gc + 2), wid);
       __syncthreads();
       if constexpr (MODE == 4) attend_load_q<D, NQ>(a, tn.h, qn0, g, qraw);
-      if constexpr (MODE == 3 || MODE == 4) attend_scale_q<D, NQ>(qraw, qn0, m, bl2e, qbn);
-      issue_next();
+      if constexpr (MODE == 3 || MODE == 4 || MODE == 5) {
+        attend_scale_q<D, NQ>(qraw, qn0, m, bl2e, qbn);
+        attend_pin_q<D, NQ>(qbn);
+      }
+      if constexpr (MODE != 6) issue_next();
       if constexpr (MODE == 1) attend_load_q<D, NQ>(a, tn.h, qn0, g, qraw);
       if (MASK && left < 64) attend_mask<NQ>(scB, left - 32, g);
-      if constexpr (MODE == 3 || MODE == 4)
+      if constexpr (MODE == 3 || MODE == 4 || MODE == 6)
         attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qbn, y, den, scB, scA, pbB, pbA, g, l32);
       else  // at the last chunk of the last tile the next unit's scores are never used
         attend_step<D, DV, NQ>(sb[bn], 0, sb[bc], 1, sb[bc], 0, qb, y, den, scB, scA, pbB, pbA, g, l32);
@@ -686,6 +716,13 @@ attend_bf16_kernel(AttendArgs a) {
       for (int c = 0; c < nc; ++c) chunk(c, std::integral_constant<int, 0>{});
     } else if (nc == 1) {
       chunk(0, std::integral_constant<int, 4>{});
+    } else if (nc >= kAttendLongTile) {
+      for (int c = 0; c < nc - 5; ++c) chunk(c, std::integral_constant<int, 0>{});
+      chunk(nc - 5, std::integral_constant<int, 1>{});
+      chunk(nc - 4, std::integral_constant<int, 2>{});
+      chunk(nc - 3, std::integral_constant<int, 5>{});
+      chunk(nc - 2, std::integral_constant<int, 0>{});
+      chunk(nc - 1, std::integral_constant<int, 6>{});
     } else {
       const int cq = nc >= 3 ? nc - 3 : 0;
       for (int c = 0; c < cq; ++c) chunk(c, std::integral_constant<int, 0>{});
@@ -701,7 +738,10 @@ attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
       for (int s = 0; s < NQ; ++s) y[s][i >> 1] = mfma32(wf, pbA[s][i & 1], y[s][i >> 1]);
     }
-    // outputs of this tile
+    // outputs of this tile (after a MODE 6 chunk: behind a drain of every load in flight,
+    // with the chunk its barrier did not request issued after them)
+    const bool defer = jn >= 0 && nc >= kAttendLongTile;
+    if (defer) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int h = tc.h, sp = tc.sp, q0 = tc.qt * kAttendQueries + qoff;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
@@ -742,6 +782,8 @@ attend_bf16_kernel(AttendArgs a) {
         if (g == 0) Yp[DV] = dn;
       }
     }
+    if (defer) issue_next();
+    drained = defer;
     if (jn < 0) break;
     // the next tile: its queries are scaled and its first unit scored
     gbase += nc;

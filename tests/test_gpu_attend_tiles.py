@@ -2,9 +2,11 @@
 of consecutive tiles form one stream: the next tile's queries are requested chunks ahead and its
 first unit is scored in the current tile's last pipeline step.  These cases force each schedule
 of that hand-over against the oracle's attend: tiles of 2, 3, 4, 6 and 8 chunks of 64 coreset
-rows with more tiles than compute units, coreset splits down to one chunk per tile, a ragged last
-query tile, and slots past the rank that carry pivots and weights the kernel must ignore.  The
-pivots and weights are random, so the oracle is the plain definition of the output."""
+rows with more tiles than compute units, a workgroup walking tiles of 6 and of 4 chunks (the
+long tiles' deferred tile-end loads followed by the short tiles' schedule), coreset splits down
+to one chunk per tile, a ragged last query tile, and slots past the rank that carry pivots and
+weights the kernel must ignore.  The pivots and weights are random, so the oracle is the plain
+definition of the output."""
 import numpy as np
 import pytest
 
@@ -31,6 +33,7 @@ CASES = [
     (4, 3000, 33000, 64, 128, 320, 300),    # 516 tiles of 6 chunks, 20 slots past the rank
     (2, 2500, 66000, 128, 128, 512, 512),   # 516 tiles of 8 chunks
     (1, 2000, 90000, 128, 64, 384, 384),    # 2 splits: 704 tiles of 3 chunks
+    (1, 2000, 51200, 128, 128, 1000, 990),  # 3 splits: 600 tiles of 6, 6 and 4 chunks, mixed
     (300, 400, 256, 64, 128, 128, 100),     # 2 splits: 600 tiles of 1 chunk
     (40, 700, 300, 128, 128, 320, 320),     # 6 splits: 480 tiles of 1 chunk, ragged query tile
 ]
