@@ -219,6 +219,56 @@ def test_graph_replay_matches_eager(wc, n, dtype):
         torch.cuda.synchronize()
 
 
+# (n, r, bins, pivot_block, options, dtype): the binned forward (union and per-bin weights), the
+# block-pivot selection with and without bins, and key centring, as bench.py times them
+GRAPH_PATHS = [
+    (2048, 128, 4, 1, 0, "bf16"),
+    (2048, 256, 4, 32, 0, "bf16"),
+    (1024, 128, 1, 32, 0, "bf16"),
+    (1536, 192, 3, 16, 1, "bf16"),      # per-bin weights (WC_OPT_BIN_WEIGHTS)
+    (1024, 96, 2, 16, 2, "bf16"),       # centred keys (WC_OPT_CENTER_KEYS)
+    (1024, 128, 4, 32, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_PATHS, ids=[f"n{c[0]}_r{c[1]}_B{c[2]}_b{c[3]}_o{c[4]}_{c[5]}" for c in GRAPH_PATHS])
+def test_graph_replay_binned_block(wc, case):
+    """The binned, block-pivot and centred-key forwards captured in a HIP graph give the eager
+    result bit for bit on every replay, with unrelated eager work (another seed, so other pivots
+    in the same workspace) and synchronisations between the replays: the graph holds no memset
+    nodes, and nothing in it depends on what the call before left in the workspace."""
+    import torch
+
+    n, r, B, pb, opt, dtype = case
+    H, m = 3, 300
+    Q, K, V = synth.random_inputs(H, n, m, 64, 64, seed=41 + n + r, dtype=dtype, kind="mixture")
+    Qd, Kd, Vd = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    p = wc.problem(H, n, m, 64, 64, r, Qd.dtype, B, opt, pb)
+    ws = wc.workspace(p, "cuda")
+    kw = dict(seed=123, bins=B, pivot_block=pb, bin_weights=bool(opt & 1), center_keys=bool(opt & 2), ws=ws)
+    out = wc.wc_forward(Qd, Kd, Vd, r, **kw)
+    ref = {k: v.clone() for k, v in out.items()}
+    assert int(host(out["rank"]).min()) == r and int(host(out["flags"]).max()) == 0
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            wc.wc_forward(Qd, Kd, Vd, r, out=out, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for v in out.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (rep, k)
+        other = dict(kw, seed=9 + rep)
+        wc.wc_forward(Qd, Kd, Vd, r, **other)  # unrelated eager work in between
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("n,r", [(1, 1), (2, 1), (2, 2), (3, 3), (5, 2)])
 def test_tiny_heads(wc, dtype, n, r):
