@@ -20,7 +20,11 @@ Beside the GPU number it reports:
     the same run;
   * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same workload, and a
     one-thread run of it on the image-shaped workload;
-  * exact softmax attention (PyTorch SDPA) on the same tensors, for context.
+  * exact softmax attention (PyTorch SDPA) on the same tensors, for context;
+  * attainable: what this GPU sustains on the operations that bound the hot path (an HBM read
+    stream, a copy, bf16 and fp32 matrix-core chains, and the clock under the bf16 load), from
+    the library's calibration kernels, with each roofline's fraction of it beside the fraction
+    of the datasheet peak.
 """
 from __future__ import annotations
 
@@ -434,6 +438,52 @@ def attend_roofline(w, Q, K, V, rpc, stream, acc, reps):
     return roof, W
 
 
+def attainable(dev, stream) -> dict:
+    """Rates this GPU sustains on the operations that bound the hot path's kernels
+    (wc_calibrate), each the mean of several launches timed with HIP events on `stream`:
+    a 4 GiB read stream, a 2 GiB copy (read + write bytes), bf16 and fp32 MFMA chains on
+    register operands (two waves per SIMD), and the shader clock under the bf16 chains."""
+    import torch
+
+    from coreset_head_rpcholesky_amd import binding as b
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = torch.empty(b.WC_CAL_RESULT_BYTES, dtype=torch.uint8, device=dev)
+    nb = 4 << 30
+    buf = torch.full((nb,), 0x5A, dtype=torch.uint8, device=dev)
+    read_ms = timed(lambda: b.wc_calibrate(b.WC_CAL_READ, res, src=buf, nbytes=nb, stream=stream), 10)
+    half = nb // 2
+    src, dst = buf[:half], buf[half:]
+    copy_ms = timed(lambda: b.wc_calibrate(b.WC_CAL_COPY, dst, src=src, nbytes=half, stream=stream), 10)
+    del buf, src, dst
+    clocks = torch.zeros(4, dtype=torch.int64, device=dev)
+    waves = 512 * 4
+    it16, it32 = 80000, 40000
+    bf16_ms = timed(lambda: b.wc_calibrate(b.WC_CAL_MFMA_BF16, res, iters=it16, clocks=clocks, stream=stream), 3)
+    c = clocks.cpu().tolist()
+    sclk = (c[2] - c[0]) / (c[3] - c[1]) * 0.1 if c[3] > c[1] else None  # reference clock 100 MHz
+    f32_ms = timed(lambda: b.wc_calibrate(b.WC_CAL_MFMA_F32, res, iters=it32, stream=stream), 3)
+    torch.cuda.empty_cache()
+    return {"kernels": "wc_calibrate (READ, COPY, MFMA_BF16, MFMA_F32)",
+            "hbm_read_GBps": round(nb / (read_ms / 1e3) / 1e9, 1),
+            "hbm_copy_GBps": round(2 * half / (copy_ms / 1e3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(waves * it16 * 8 * 32768 / (bf16_ms / 1e3) / 1e12, 1),
+            "mfma_f32_TFLOPs": round(waves * it32 * 8 * 4096 / (f32_ms / 1e3) / 1e12, 2),
+            "sclk_GHz_under_bf16_mfma": round(sclk, 3) if sclk else None,
+            "datasheet": {"hbm_GBps": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                          "mfma_f32_TFLOPs": 157.3, "sclk_GHz": 2.4}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -611,6 +661,14 @@ def main():
             torch.cuda.empty_cache()
 
     log("exact attention and variants done")
+    att = None
+    if not args.no_roofline:
+        att = attainable(dev, stream)
+        if roof and roof.get("unit") == "GB/s":
+            roof["frac_of_attainable"] = round(roof["achieved"] / att["hbm_read_GBps"], 4)
+        if roof_att:
+            roof_att["frac_of_attainable"] = round(roof_att["achieved"] / att["mfma_bf16_TFLOPs"], 4)
+        log("attainable rates measured")
     cpu = None
     cpu1 = None
     if not args.no_cpu_baseline:
@@ -637,6 +695,7 @@ def main():
         "cpu_baseline_1thread": cpu1,
         "exact_attention": exact,
         "variants": variants,
+        "attainable": att,
         "checks": {"rank_min": int(rank.min()), "flags_or": int(np.bitwise_or.reduce(flags)),
                    "wall_s_timed": round(wall, 4),
                    "launch": (f"hip graph replay, {per_replay} forwards per graph" if graph is not None

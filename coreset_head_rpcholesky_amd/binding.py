@@ -61,6 +61,7 @@ def _load():
         "wc_cache_append": ([P, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int32, vp], ctypes.c_int),
         "wc_decode_workspace_bytes": ([P, ctypes.c_int32, ctypes.POINTER(sz)], ctypes.c_int),
         "wc_decode": ([P, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "wc_calibrate": ([ctypes.c_int32, vp, vp, sz, ctypes.c_int32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -361,3 +362,17 @@ def wc_decode(Q: torch.Tensor, cache: torch.Tensor, capacity: int, rows: int, dv
     if st != WC_OK:
         raise WcError("wc_decode", st)
     return O, flags
+
+
+# Calibration kinds (include/wc.h): measurement helpers beside the hot path, not steps of it.
+WC_CAL_READ, WC_CAL_COPY, WC_CAL_MFMA_BF16, WC_CAL_MFMA_F32 = 0, 1, 2, 3
+WC_CAL_RESULT_BYTES = 131072
+
+
+def wc_calibrate(kind: int, dst: torch.Tensor, *, src=None, nbytes: int = 0, iters: int = 0, clocks=None,
+                 stream=None) -> None:
+    """Enqueue one calibration kernel (see wc.h); dst, src and clocks are device tensors."""
+    st = LIB.wc_calibrate(int(kind), _ptr(src) if src is not None else None, _ptr(dst), int(nbytes), int(iters),
+                          _ptr(clocks) if clocks is not None else None, _stream(stream))
+    if st != WC_OK:
+        raise WcError("wc_calibrate", st)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define WC_ABI_VERSION 8
+#define WC_ABI_VERSION 9
 
 typedef enum {
   WC_OK = 0,
@@ -287,6 +287,37 @@ wc_status wc_decode_workspace_bytes(const wc_problem* p, int32_t rows, size_t* b
 wc_status wc_decode(const wc_problem* p, const void* Q, const void* cache, int32_t capacity,
                     int32_t rows, void* O, uint32_t* flags, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Calibration (a measurement helper, not a step of the method).  The rooflines of the hot
+ * path are quoted against the datasheet peaks of the part (HBM 8 TB/s; dense matrix cores:
+ * bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s, both at 2.4 GHz).  These kernels measure what the part
+ * attains on the same operations, so that the attainable rates can be reported beside them:
+ *   WC_CAL_READ       reads `bytes` of src (16-byte nontemporal loads, sixteen in flight
+ *                     per lane, 8192 workgroups of 256 threads); dst receives one XOR word
+ *                     per wave (128 KiB);
+ *   WC_CAL_COPY       copies `bytes` of src to dst (the ranges must not overlap);
+ *   WC_CAL_MFMA_BF16  512 workgroups of 4 waves (two per SIMD) each run `iters` rounds of 8
+ *                     independent v_mfma_f32_32x32x16_bf16 on register operands, 2^15 flops
+ *                     each; all operands are 1, so dst[w] (one float per wave, 8 KiB) is
+ *                     2048 iters exactly while that is below 2^24;
+ *   WC_CAL_MFMA_F32   the same with v_mfma_f32_32x32x2_f32 (2^12 flops each); dst[w] =
+ *                     256 iters.
+ * src and dst are 16-byte aligned device pointers (src unused by the MFMA kinds; bytes a
+ * nonzero multiple of 16 for READ and COPY; iters >= 1 for the MFMA kinds).  clocks is NULL
+ * or a device pointer to 4 uint64: the shader clock (s_memtime) and the 100 MHz reference
+ * clock (s_memrealtime) read by workgroup 0 at its start and its end, MFMA kinds only.  An
+ * unknown kind or a bad argument returns WC_ERR_INVALID_ARG before any HIP call; the work is
+ * enqueued on `stream` otherwise.                                                          */
+typedef enum {
+  WC_CAL_READ = 0,
+  WC_CAL_COPY = 1,
+  WC_CAL_MFMA_BF16 = 2,
+  WC_CAL_MFMA_F32 = 3
+} wc_cal_kind;
+#define WC_CAL_RESULT_BYTES 131072 /* dst size that every kind but COPY needs */
+wc_status wc_calibrate(int32_t kind, const void* src, void* dst, size_t bytes, int32_t iters,
+                       uint64_t* clocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.wc_abi_version.restype = ctypes.c_int32
-    assert lib.wc_abi_version() == 8
+    assert lib.wc_abi_version() == 9
     lib.wc_status_string.restype = ctypes.c_char_p
     seen = set()
     for s in range(6):
@@ -276,4 +276,26 @@ def test_debug_library_exports_the_same_abi():
     for name in declared_functions():
         assert hasattr(dbg, name), name
     dbg.wc_abi_version.restype = ctypes.c_int32
-    assert dbg.wc_abi_version() == 8
+    assert dbg.wc_abi_version() == 9
+
+
+def test_calibrate_argument_errors(lib):
+    """The calibration helper refuses unknown kinds and bad buffers before any HIP call."""
+    cal = lib.wc_calibrate
+    cal.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                    ctypes.c_void_p, ctypes.c_void_p]
+    cal.restype = ctypes.c_int
+    B = ctypes.c_void_p(0x20000000)  # a second aligned fake address, far from A
+    assert cal(7, A, B, 4096, 1, None, None) == 1         # unknown kind
+    assert cal(-1, A, B, 4096, 1, None, None) == 1
+    for kind in (0, 1):                                   # READ, COPY
+        assert cal(kind, None, B, 4096, 1, None, None) == 1
+        assert cal(kind, A, None, 4096, 1, None, None) == 1
+        assert cal(kind, MIS, B, 4096, 1, None, None) == 1
+        assert cal(kind, A, B, 0, 1, None, None) == 1
+        assert cal(kind, A, B, 4100, 1, None, None) == 1  # not a multiple of 16
+    assert cal(1, A, ctypes.c_void_p(0x10000 + 4096), 8192, 1, None, None) == 1  # overlapping copy
+    for kind in (2, 3):                                   # MFMA_BF16, MFMA_F32
+        assert cal(kind, None, B, 0, 0, None, None) == 1  # iters < 1
+        assert cal(kind, None, None, 0, 10, None, None) == 1
+        assert cal(kind, None, B, 0, 10, ctypes.c_void_p(0x10004), None) == 1  # misaligned clocks
